@@ -1,0 +1,162 @@
+"""The whole SC matmul for a chosen set of output rows (test
+infrastructure; see package docstring).
+
+Steps, in the order the pages give them ("Precision As You Need" paper
+notes, Key designs 1-3; K-band pull request, "How the banding works"):
+Sobol table -> symmetric quantisation -> bipolar levels -> row metric and
+rung -> per-(band, rung) stream length -> materialised C-BSG streams and
+XNOR counts -> decode.
+
+Output rows are independent of one another once their length and scales are
+known, so a subset of rows is an exact sub-problem of the full product.
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional, Sequence
+
+import numpy as np
+
+from .cbsg import xnor_count_row
+from .decode import decode
+from .mp import (
+    assign_rungs,
+    attention_row_metric,
+    band_columns,
+    normalise_metric,
+    row_metric,
+    rung_cuts,
+    tilt_band_ladder,
+)
+from .quant import QMAX, bipolar_level, quantize
+from .sobol import sobol_points
+from .table import indicator_table
+
+
+@dataclass
+class OraclePlan:
+    """What one SC matmul needs: precision, ladder, fractions and bands."""
+
+    p: int = 8
+    Lmax: int = 256
+    D: int = 64
+    chunk_d: int = 0
+    levels: Sequence[int] = (256,)
+    fractions: Optional[Sequence[float]] = None
+    n_bands: int = 1
+    band_chunks: Optional[Sequence[int]] = None
+    tilt: float = 0.0
+    band_L: Optional[np.ndarray] = None
+    ceiling: int = 0
+    metric: str = "linear"  # "linear": max |X_i|; "av": max_j A_ij
+    _cache: dict = field(default_factory=dict, repr=False)
+
+    @property
+    def n_rungs(self) -> int:
+        return len(self.levels)
+
+    @property
+    def n_chunks(self) -> int:
+        return 1 if self.chunk_d <= 0 else (self.D + self.chunk_d - 1) // self.chunk_d
+
+    def chunk_bounds(self):
+        if self.chunk_d <= 0:
+            return [(0, self.D)]
+        return [(c, min(c + self.chunk_d, self.D)) for c in range(0, self.D, self.chunk_d)]
+
+    def bands(self):
+        """(band column starts, band of each chunk)."""
+        if self.n_bands == 1:
+            return np.asarray([0, self.D]), np.zeros(self.n_chunks, dtype=np.int64)
+        widths = self.band_chunks
+        if widths is None:
+            if self.n_chunks % self.n_bands:
+                raise ValueError("equal split needs n_chunks divisible by n_bands")
+            widths = [self.n_chunks // self.n_bands] * self.n_bands
+        cols = band_columns(self.D, self.chunk_d, widths)
+        owner = np.repeat(np.arange(self.n_bands), widths)
+        return cols, owner
+
+    def ladder(self) -> np.ndarray:
+        """L[b][k] (n_bands x n_rungs)."""
+        if self.band_L is not None:
+            return np.asarray(self.band_L, dtype=np.int64)
+        ceiling = self.ceiling if self.ceiling > 0 else self.Lmax
+        return tilt_band_ladder(self.levels, self.n_bands, self.tilt, ceiling)
+
+    def table(self):
+        key = (self.p, self.Lmax)
+        if key not in self._cache:
+            r = sobol_points(self.p, self.Lmax)
+            self._cache[key] = indicator_table(r, 1 << self.p)
+        return self._cache[key]
+
+
+def sc_matmul_rows(A, B, plan: OraclePlan, rows=None, metric=None):
+    """SC product of A (M x D, the row side) with B (N x D, the weight side)
+    restricted to the output rows ``rows`` (all rows when None).
+
+    Returns a dict with
+      ``x_a``, ``s_a``, ``x_b``, ``s_b``: quantised integers and scales;
+      ``metric``, ``g_hat``, ``rung``, ``order``, ``cuts``: the MP decision;
+      ``rows``: the rows computed;
+      ``counts``: int64 (len(rows), N, n_chunks) XNOR counts per chunk;
+      ``band_counts``: int64 (len(rows), N, n_bands);
+      ``L``: (len(rows), n_chunks) lengths used;
+      ``C``: float64 (len(rows), N) decoded products;
+      ``C_abs``: float64 (len(rows), N) sum of |chunk terms| (tolerance scale).
+    """
+    A = np.asarray(A, dtype=np.float32)
+    B = np.asarray(B, dtype=np.float32)
+    M, D = A.shape
+    N, D2 = B.shape
+    if D != plan.D or D2 != plan.D:
+        raise ValueError("contraction length does not match the plan")
+    q = QMAX(plan.p)
+    K = plan.table()
+
+    x_a, s_a = quantize(A, plan.p, plan.chunk_d)
+    x_b, s_b = quantize(B, plan.p, plan.chunk_d)
+    u_a = bipolar_level(x_a, plan.p)
+    u_b = bipolar_level(x_b, plan.p)
+
+    if metric is None:
+        metric = attention_row_metric(A) if plan.metric == "av" else row_metric(A)
+    g_hat = normalise_metric(metric)
+    if plan.n_rungs > 1:
+        rung, order = assign_rungs(g_hat, plan.n_rungs, plan.fractions)
+    else:
+        rung = np.zeros(M, dtype=np.int64)
+        order = np.arange(M, dtype=np.int64)
+    cuts = rung_cuts(M, plan.n_rungs, plan.fractions)
+
+    ladder = plan.ladder()
+    band_cols, chunk_band = plan.bands()
+    bounds = plan.chunk_bounds()
+    widths = np.asarray([c1 - c0 for c0, c1 in bounds], dtype=np.int64)
+    band_of_d = np.zeros(D, dtype=np.int64)
+    for b in range(plan.n_bands):
+        band_of_d[band_cols[b]:band_cols[b + 1]] = b
+
+    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
+    counts = np.zeros((rows.shape[0], N, len(bounds)), dtype=np.int64)
+    Lrc = np.zeros((rows.shape[0], len(bounds)), dtype=np.int64)
+    for t, i in enumerate(rows):
+        k = int(rung[i])
+        L_per_d = ladder[band_of_d, k]
+        per_d = xnor_count_row(K, u_a[i], u_b, L_per_d)
+        for c, (c0, c1) in enumerate(bounds):
+            counts[t, :, c] = per_d[:, c0:c1].sum(axis=1)
+            Lrc[t, c] = ladder[chunk_band[c], k]
+
+    band_counts = np.zeros((rows.shape[0], N, plan.n_bands), dtype=np.int64)
+    for c in range(len(bounds)):
+        band_counts[:, :, chunk_band[c]] += counts[:, :, c]
+
+    C, C_abs = decode(counts, s_a[rows], s_b, Lrc, widths, q)
+    return {
+        "x_a": x_a, "s_a": s_a, "x_b": x_b, "s_b": s_b,
+        "metric": np.asarray(metric, dtype=np.float32), "g_hat": g_hat,
+        "rung": rung, "order": order, "cuts": cuts, "rows": rows,
+        "counts": counts, "band_counts": band_counts, "L": Lrc,
+        "C": C, "C_abs": C_abs, "ladder": ladder,
+    }
