@@ -1,0 +1,238 @@
+"""Benchmark of the SC bipolar XNOR matmul hot path on one MI355X.
+
+One step is one pass of the whole hot path over one batch of synthetic input
+already resident in device memory: quantise + encode the row side X and the
+weight side W, classify the rows into stream-length rungs and bucket them,
+run the XNOR contraction with K-band partial sums and the fused decode.  The
+Sobol table is built once before timing (it is resident, built at layer
+load) and its build time is reported separately.
+
+Prints one JSON line.  ``value`` is SC bit-MACs per second,
+sum over output elements of D * L (L the element's stream length).
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+                    [--algo auto|mfma|bitserial] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import subprocess
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SC bit-MACs/s (M*N*D*L_eff) + % of int-VALU/HBM roofline, ViT-L fc1 MP"
+DEFAULT_WORKLOAD = "vitl_fc1_mp"
+
+# MI355X published peaks used for the roofline fractions.
+PEAK_INT8_TOPS = 5000.0          # dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0            # HBM3E, 8 TB/s
+# Vector-ALU bit-serial bound: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz int32
+# ops, two ops (bit-select, popcount) per 32 stream positions.
+PEAK_VALU_BITMACS = 256 * 4 * 16 * 2.4e9 * 16
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "bitserial"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle sample (0 = 2 per worker)")
+    return ap.parse_args()
+
+
+def git_sha():
+    try:
+        return subprocess.run(["git", "rev-parse", "--short", "HEAD"], cwd=ROOT, capture_output=True,
+                              text=True, timeout=10).stdout.strip() or None
+    except Exception:
+        return None
+
+
+def work_per_step(plan, M, N, G):
+    """Algorithmic work of one product: bit-MACs sum_i N * sum_b D_b L[b][rung_i],
+    and the paired int8 MACs sum_i N * sum_b D_b ceil(L/2) of the matrix-core form."""
+    cuts = plan.row_cuts(M)
+    cols = plan.band_columns()
+    L = plan.band_lengths()
+    bitmacs = 0
+    paired = 0
+    for k in range(plan.n_rungs):
+        rows = cuts[k + 1] - cuts[k]
+        for b in range(plan.n_bands):
+            Db = cols[b + 1] - cols[b]
+            bitmacs += rows * Db * L[b][k]
+            paired += rows * Db * ((L[b][k] + 1) // 2)
+    return bitmacs * N * G, paired * N * G
+
+
+def cpu_baseline(w, A, B, n_rows_req):
+    """Time the CPU oracle, as it stands, on a bounded sample of output rows
+    of the same workload (all columns, all of D), one worker process per core."""
+    import numpy as np
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import oracle as o
+    from _oracle_pool import pooled_rows_product, workers
+    from mixed_precision_quantization_amd.workloads import sample_rows
+
+    okw = dict(p=8, Lmax=256, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
+               n_bands=w.n_bands, tilt=w.tilt, metric=w.metric)
+    A0 = A[0] if A.ndim == 3 else A
+    B0 = B[0] if B.ndim == 3 else B
+    nw = workers()
+    want = n_rows_req or 2 * nw
+    t0 = time.perf_counter()
+    cls = o.classify(A0, o.OraclePlan(**okw))
+    per = max(1, -(-want // len(w.levels)))
+    pos = sample_rows(w.M, cls["cuts"], per_rung=max(2, per), seed=11)[:want]
+    rows = cls["order"][pos]
+    out = pooled_rows_product(A0[rows], cls["rung"][rows], B0, okw, n_workers=nw)
+    dt = time.perf_counter() - t0
+    bitmacs = int(np.sum(out["L"] * np.diff(o.OraclePlan(**okw).chunk_bounds(), axis=1).T)) * B0.shape[0]
+    return {
+        "value": bitmacs / dt,
+        "unit": "bit-MAC/s",
+        "cores": nw,
+        "kind": "oracle",
+        "sample": f"{len(rows)} output rows (every rung, sorted-position edges plus seeded picks) x all "
+                  f"{B0.shape[0]} columns x all D={w.D}, materialised C-BSG streams, "
+                  f"{bitmacs:.3e} bit-MACs in {dt:.1f} s wall incl. classification and quantisation",
+        "seconds": dt,
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
+              f"mode: each GPU would take its own rows (see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from mixed_precision_quantization_amd import scmp
+    from mixed_precision_quantization_amd.workloads import WORKLOADS, draw
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    A_np, B_np = draw(w)
+    dev = torch.device("cuda:0")
+    A = torch.from_numpy(A_np).to(dev)
+    B = torch.from_numpy(B_np).to(dev)
+    if A.dim() == 2:
+        A, B = A.unsqueeze(0), B.unsqueeze(0)
+    G, M, D = A.shape
+    N = B.shape[1]
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    table = scmp.scmp_build_sobol_table(8, 256)
+    torch.cuda.synchronize()
+    table_ms = (time.perf_counter() - t0) * 1e3
+    plan = scmp.scmp_plan_create(op=w.kind, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
+                                 n_bands=w.n_bands, tilt=w.tilt)
+    nch = plan.n_chunks
+    # Every buffer of the step is allocated before timing.
+    qA = torch.empty((G, M, D), dtype=torch.int8, device=dev)
+    sA = torch.empty((G, M, nch), dtype=torch.float32, device=dev)
+    mA = torch.empty((G, M), dtype=torch.float32, device=dev)
+    qB = torch.empty((G, N, D), dtype=torch.int8, device=dev)
+    sB = torch.empty((G, N, nch), dtype=torch.float32, device=dev)
+    pB = torch.empty((G, N, D, table.words), dtype=torch.int32, device=dev) if args.algo == "bitserial" else None
+    gh = torch.empty((G, M), dtype=torch.float32, device=dev)
+    rg = torch.empty((G, M), dtype=torch.uint8, device=dev)
+    pm = torch.empty((G, M), dtype=torch.int32, device=dev)
+    th = torch.empty((G, max(plan.n_rungs - 1, 1)), dtype=torch.float32, device=dev)
+    C = torch.empty((G, M, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = []
+
+    def step(timed):
+        scmp.scmp_quantize_encode(table, plan, A, q_out=qA, scales_out=sA, metric_out=mA, stream=stream)
+        scmp.scmp_quantize_encode(table, plan, B, q_out=qB, scales_out=sB, packed_out=pB, want_metric=False,
+                                  stream=stream)
+        perm = None
+        if plan.n_rungs > 1:
+            scmp.scmp_classify_rows(plan, mA, ghat_out=gh, rung_out=rg, perm_out=pm, thresholds_out=th,
+                                    stream=stream)
+            perm = pm
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        scmp.scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, packedB=pB, algo=args.algo, C_out=C,
+                         want_C=True, stream=stream)
+        if timed:
+            e1.record(stream)
+            ev.append((e0, e1))
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step(True)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    bitmacs, paired = work_per_step(plan, M, N, G)
+    value = bitmacs / (ms_per_step / 1e3)
+    L_eff = bitmacs / (G * M * N * D)
+
+    if args.algo == "bitserial":
+        achieved = bitmacs / (kern_ms / 1e3) / 1e12
+        roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_BITMACS / 1e12,
+                "unit": "T bit-MAC/s", "frac": achieved / (PEAK_VALU_BITMACS / 1e12), "traffic": None}
+    else:
+        achieved = 2.0 * paired / (kern_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
+                "frac": achieved / PEAK_INT8_TOPS, "traffic": None}
+    roof["kernel"] = "k_matmul_bitserial" if args.algo == "bitserial" else "k_matmul_mfma"
+    roof["kernel_ms"] = kern_ms
+    roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
+    roof["valu_bitserial_frac"] = bitmacs / (kern_ms / 1e3) / PEAK_VALU_BITMACS
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "bit-MAC/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "i8",
+        "data": "synthetic",
+        "config": {
+            "workload": w.name, "G": G, "M": M, "N": N, "D": D, "levels": list(w.levels),
+            "fractions": list(w.fractions) if w.fractions else None, "chunk_d": w.chunk_d,
+            "n_bands": w.n_bands, "tilt": w.tilt, "L_eff": L_eff, "algo": args.algo,
+            "bit_macs_per_step": bitmacs,
+        },
+        "roofline": roof,
+        "table_build_ms": table_ms,
+        "device": torch.cuda.get_device_name(0),
+        "git": git_sha(),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, A_np, B_np, args.cpu_rows)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

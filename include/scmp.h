@@ -1,0 +1,241 @@
+/*
+ * scmp.h -- C ABI of libscmp, the MI355X (gfx950) stochastic-computing (SC)
+ * bipolar XNOR matmul with dynamic mixed precision.
+ *
+ * What the library computes is defined on these pages:
+ *  [PAYN]  "Precision As You Need: Stochastic Computing Is a Dense Adaptive
+ *          Quantizer" (paper notes): Key design 1 (Sobol-8 cumulative
+ *          indicator table, conditional bitstream generator C-BSG, bipolar
+ *          XNOR decode equation), Key design 2 (row metrics, threshold
+ *          ladder), Key design 3 (early termination per row).
+ *  [VIT]   scmp_vit README: "Why it works" (per-row bipolar quantisation,
+ *          scale = row abs-max / 127), the mixed-precision flag table, and
+ *          the SC early-termination note for non-power-of-two lengths.
+ *  [KBAND] pull request "feat(mp): per-group (K-band) stream lengths on the
+ *          contraction axis": "How the banding works", "Guards", "Tooling".
+ *
+ * Conventions shared by every call
+ *  - Every pointer named *_dev is a device pointer (HIP global memory) owned
+ *    by the caller; it must stay valid until the work queued on `stream`
+ *    has finished.  Host pointers are only read during the call.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every device call is asynchronous on that stream and never
+ *    synchronises the device, except scmp_error_flags.
+ *  - Calls never allocate device memory, except scmp_build_sobol_table (the
+ *    one-time table) which allocates the table it returns.
+ *  - Arguments and plans are validated on the host before any launch.  On
+ *    error nothing is launched and the status is returned;
+ *    scmp_last_error() then describes the failure (thread-local string).
+ *  - Sizes of 0 (G, rows, M or N) are valid and launch nothing.
+ *  - Supported precision: 2 <= p <= 8 (q = 2^(p-1) - 1, P = 2^p levels + 1),
+ *    1 <= Lmax <= 2^p.  The workloads use p = 8, Lmax = 256.
+ *
+ * Layouts (row-major, C order)
+ *  - Quantised integers: int8 [G][rows][cols], values in [-q, q].
+ *  - Scales: float [G][rows][n_chunks] (n_chunks = 1 without chunk_d).
+ *  - Packed streams (weight side, optional): uint32 [G][rows][cols][Wl],
+ *    Wl = ceil(Lmax / 32); bit b of word w is K[u][32 w + b].
+ *  - Row metric, normalised metric: float [G][rows]; rungs: uint8 [G][M];
+ *    permutation: int32 [G][M] (sorted position -> row).
+ *  - Counts: int32 [G][M][N][n_bands]; outputs C: float with element
+ *    (g, i, j) at C_dev[g * batch_stride_c + i * ldc + j].
+ */
+#ifndef SCMP_H
+#define SCMP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SCMP_OK = 0,
+  SCMP_ERR_ARG = 1,            /* bad argument: null pointer, bad size or stride */
+  SCMP_ERR_CEILING = 2,        /* a (band) length above the ceiling [KBAND] "Guards" */
+  SCMP_ERR_ISO_COMPUTE = 3,    /* per-rung iso-compute identity overspent [KBAND] */
+  SCMP_ERR_UNSUPPORTED = 4,    /* K-bands on qk/av, K-bands with range MP, range MP [KBAND] "Guards" */
+  SCMP_ERR_PLAN_MISMATCH = 5,  /* table priced at another chunk_d or width; shapes vs plan [KBAND] "Guards" */
+  SCMP_ERR_NONFINITE = 6,      /* a non-finite input was seen (reported by scmp_error_flags) */
+  SCMP_ERR_WORKSPACE = 7,      /* reserved */
+  SCMP_ERR_HIP = 8             /* a HIP runtime call or launch failed */
+} scmp_status;
+
+typedef enum { SCMP_OP_LINEAR = 0, SCMP_OP_QK = 1, SCMP_OP_AV = 2 } scmp_op;
+
+/* Contraction kernel.  Both give bit-identical counts.
+ *  AUTO/MFMA: windowed ternary x paired-binary contraction on the int8
+ *             matrix cores (v_mfma_i32_32x32x32_i8).
+ *  BITSERIAL: one bit-select + popcount per 32 stream positions on the
+ *             vector ALU; needs the packed weight-side streams. */
+typedef enum { SCMP_ALGO_AUTO = 0, SCMP_ALGO_BITSERIAL = 1, SCMP_ALGO_MFMA = 2 } scmp_algo;
+
+typedef struct scmp_table_s* scmp_table_t; /* opaque, library-owned */
+typedef struct scmp_plan_s* scmp_plan_t;   /* opaque, library-owned, host only */
+
+#define SCMP_MAX_RUNGS 8
+#define SCMP_MAX_BANDS 16
+
+/* Description of one SC matmul: [PAYN] Key designs 2-3, [VIT] MP flags,
+ * [KBAND] "How the banding works" and "Tooling". */
+typedef struct {
+  int op;                    /* scmp_op */
+  int p;                     /* integer bits; must match the table */
+  int Lmax;                  /* table length; must match the table */
+  int D;                     /* contraction length */
+  int chunk_d;               /* 0: one scale per row; >0: one scale per (row, chunk of chunk_d
+                                columns), the last chunk may be short; must be a multiple of 16 */
+  int n_rungs;               /* 1..SCMP_MAX_RUNGS; 1 = uniform length */
+  const int* levels;         /* [n_rungs] stream lengths, strictly descending, >= 1 */
+  const double* fractions;   /* [n_rungs] row fractions in the same order, sum 1; NULL = equal */
+  int n_bands;               /* 1..SCMP_MAX_BANDS; >1 needs chunk_d > 0 and op LINEAR */
+  const int* band_chunks;    /* [n_bands] band widths in whole chunks; NULL = equal split */
+  double tilt;               /* straight-line tilt t (used when band_L is NULL) */
+  const int* band_L;         /* [n_bands][n_rungs] explicit L[b][k], or NULL */
+  int table_chunk_d;         /* chunk_d the explicit band_L was priced at (0 = not stated) */
+  int table_D;               /* contraction width band_L was priced at (0 = not stated) */
+  int ceiling;               /* largest allowed length; 0 = Lmax; must be <= Lmax */
+  int range_mp;              /* nonzero requests range-based MP (not provided here) */
+} scmp_plan_desc;
+
+typedef struct {
+  int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling;
+} scmp_plan_info;
+
+/* Name of a status code (static string). */
+const char* scmp_status_string(int status);
+
+/* Description of the last failure on the calling thread ("" if none). */
+const char* scmp_last_error(void);
+
+/* Build the device-resident Sobol table ([PAYN] Key design 1): Sobol points
+ * r_l (unscrambled, Gray-code order, r_0 = 0) for l < Lmax, the indicator
+ * table K[u][l] = 1[r_l < u] for levels u in [0, 2^p] (row u = b + 1 of the
+ * page's 1[r_l <= b]), its prefix sums cum[u][n], and for every length
+ * L <= Lmax the paired-position tables the MFMA contraction reads.
+ * Allocates device memory (a few MB) owned by the returned table; the
+ * build is queued on `stream`.  Errors: ARG (p or Lmax out of range), HIP. */
+int scmp_build_sobol_table(int p, int Lmax, void* stream, scmp_table_t* out);
+
+/* Free a table (synchronises the device first).  NULL is ignored. */
+int scmp_table_destroy(scmp_table_t table);
+
+/* p and Lmax of a table.  Errors: ARG. */
+int scmp_table_info(scmp_table_t table, int* p, int* Lmax);
+
+/* Copy the table to caller buffers (device): r_dev uint16 [Lmax],
+ * K_dev uint32 [2^p + 1][ceil(Lmax/32)], cum_dev uint16 [2^p + 1][Lmax + 1].
+ * Any pointer may be NULL.  Errors: ARG, HIP. */
+int scmp_table_export(scmp_table_t table, uint16_t* r_dev, uint32_t* K_dev, uint16_t* cum_dev,
+                      void* stream);
+
+/* Validate a description and build the plan (host only, the "startup" of
+ * [KBAND] "Guards").  Band lengths come from band_L or from the straight-
+ * line tilt: for rungs below the ceiling raw_b = L_k (1 + t x_b),
+ * x_b = (2b - (B-1)) / (B-1), rounded down, single units handed back to the
+ * bands with the largest lost fraction (ties to the lower band); rungs at
+ * the ceiling stay untilted ([KBAND] "Tooling"); the tilt needs bands of
+ * equal column width.
+ * Errors: ARG, CEILING (any length above the ceiling), ISO_COMPUTE
+ * (sum_b D_b L[b][k] > D L_k), UNSUPPORTED (n_bands > 1 with op QK or AV;
+ * range_mp with or without bands; chunk_d not a multiple of 16),
+ * PLAN_MISMATCH (table_chunk_d / table_D differ from chunk_d / D). */
+int scmp_plan_create(const scmp_plan_desc* desc, scmp_plan_t* out);
+
+/* Free a plan.  NULL is ignored. */
+int scmp_plan_destroy(scmp_plan_t plan);
+
+int scmp_plan_query(scmp_plan_t plan, scmp_plan_info* out);
+
+/* L[b][k] as int [n_bands][n_rungs]. */
+int scmp_plan_band_lengths(scmp_plan_t plan, int* L_out);
+
+/* Band column boundaries, int [n_bands + 1]. */
+int scmp_plan_band_columns(scmp_plan_t plan, int* cols_out);
+
+/* Per-rung budget use sum_b D_b L[b][k] / (D L_k), double [n_rungs]. */
+int scmp_plan_budget_use(scmp_plan_t plan, double* use_out);
+
+/* Sorted-position cuts for M rows, int [n_rungs + 1]: cut_0 = 0,
+ * cut_(k+1) = floor(F_k M + 0.5) with F_k the running float64 sum of the
+ * fractions (last cut M).  Rung k holds sorted positions [cut_k, cut_(k+1)). */
+int scmp_plan_row_cuts(scmp_plan_t plan, int M, int* cuts_out);
+
+/* Fused symmetric quantisation and C-BSG encoding ([VIT] "Why it works";
+ * [PAYN] Key design 1).  For each of the G x rows rows of X (or each chunk
+ * of chunk_d columns when the plan has chunk_d): a = max |x| (float32),
+ * s = a / q (IEEE float32 division), x_int = clamp(rint(x / s), -q, q)
+ * (float32 division, round half to even); an all-zero row or chunk gives
+ * s = 0 and integers 0.  Element (g, r, c) of X is read at
+ * X_dev[g * batch_stride + r * row_stride + c * col_stride].
+ *   q_dev       int8 [G][rows][cols]               (required)
+ *   scales_dev  float [G][rows][n_chunks]          (required)
+ *   metric_dev  float [G][rows]: max_c |x| of the whole row; this is the
+ *               MP row metric ||X_i||_inf, and max_j A_ij for non-negative
+ *               attention rows ([PAYN] Key design 2)            (nullable)
+ *   packed_dev  uint32 [G][rows][cols][ceil(Lmax/32)]: the weight side's
+ *               full-length counter-domain stream K[u][0..Lmax) with
+ *               u = round(P (x_int + q) / (2 q))                (nullable)
+ * cols must equal the plan's D.  Non-finite inputs set a device flag read
+ * by scmp_error_flags.  Errors: ARG, PLAN_MISMATCH, HIP. */
+int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const float* X_dev, int G, int rows,
+                         int cols, int64_t batch_stride, int64_t row_stride, int64_t col_stride,
+                         int8_t* q_dev, float* scales_dev, float* metric_dev, uint32_t* packed_dev,
+                         void* stream);
+
+/* Row classification ([PAYN] Key design 2): per group g, the normalised
+ * metric g_hat = metric / max(metric) (float32; 0 when the max is 0; NaN
+ * ranks last), the sorted order by g_hat descending with ties by row index,
+ * the rung of each row from the plan's cuts, and thresholds tau_k
+ * (k = 1..K-1) = g_hat at sorted position cut_k - 1 (1.0 if none).
+ *   metric_dev float [G][M]; ghat_dev float [G][M] (required);
+ *   rung_dev uint8 [G][M] (nullable); perm_dev int32 [G][M] (required):
+ *   perm[g][pos] = row at sorted position pos; thresholds_dev float
+ *   [G][n_rungs - 1] (nullable).  Errors: ARG, HIP. */
+int scmp_classify_rows(scmp_plan_t plan, const float* metric_dev, int G, int M, float* ghat_dev,
+                       uint8_t* rung_dev, int32_t* perm_dev, float* thresholds_dev, void* stream);
+
+/* The SC matmul C = A x B^T ([PAYN] Key designs 1 and 3; [KBAND] "How the
+ * banding works").  Rows of A are taken bucket by bucket in sorted order
+ * (rung k = sorted positions [cut_k, cut_(k+1)), all at one length), so
+ * every tile runs one stream length.  Row i of rung k contracts index d of
+ * band b at L = L[b][k]; A's stream is the L-prefix of its table row and B's
+ * stream is generated by two counters gated by A's bits (C-BSG), and the
+ * XNOR count is exact.  Per chunk c (the whole row when chunk_d is 0) the
+ * decode is s^A_ic s^B_jc q^2 (2 count_ijc - L_c |c|) / L_c, summed over
+ * chunks in float32 ([PAYN] Key design 1, decode equation).
+ *   qA_dev int8 [G][M][D], sA_dev float [G][M][n_chunks],
+ *   permA_dev int32 [G][M] (NULL only for one rung: identity order),
+ *   qB_dev int8 [G][N][D], sB_dev float [G][N][n_chunks],
+ *   packedB_dev uint32 [G][N][D][ceil(Lmax/32)] (needed by BITSERIAL only),
+ *   counts_dev int32 [G][M][N][n_bands] (nullable): per-band XNOR counts,
+ *   C_dev float (nullable): decoded output at original row order.
+ * At least one of counts_dev and C_dev must be given; ldc >= N.
+ * Errors: ARG, PLAN_MISMATCH (table vs plan), HIP. */
+int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
+                const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
+                int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
+                void* stream);
+
+/* Decode counts produced without chunk scales ([PAYN] Key design 1, decode
+ * equation): C_ij = s^A_i s^B_j q^2 (2 count_ij - L_i D) / L_i with
+ * L_i = L[0][rung_i].  counts_dev int32 [G][M][N][1]; rung_dev uint8 [G][M]
+ * (NULL only for one rung).  Errors: ARG, UNSUPPORTED (plan has chunk_d
+ * or bands), HIP. */
+int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts_dev,
+                const float* sA_dev, const float* sB_dev, const uint8_t* rung_dev, float* C_dev,
+                int64_t ldc, int64_t batch_stride_c, void* stream);
+
+/* Synchronise `stream`, return the device error flags raised since the last
+ * call (bit 0: a non-finite input to scmp_quantize_encode or
+ * scmp_classify_rows) and clear them.  Returns NONFINITE when bit 0 is set,
+ * OK otherwise, HIP on a runtime failure. */
+int scmp_error_flags(void* stream, int* flags_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SCMP_H */

@@ -55,7 +55,7 @@ from .mp import (
     check_band_ladder,
 )
 from .decode import decode_terms, decode
-from .matmul import OraclePlan, sc_matmul_rows
+from .matmul import OraclePlan, classify, rows_product, sc_matmul_rows
 
 __all__ = [
     "sobol_points",
@@ -82,5 +82,7 @@ __all__ = [
     "decode_terms",
     "decode",
     "OraclePlan",
+    "classify",
+    "rows_product",
     "sc_matmul_rows",
 ]

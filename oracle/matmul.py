@@ -91,43 +91,26 @@ class OraclePlan:
         return self._cache[key]
 
 
-def sc_matmul_rows(A, B, plan: OraclePlan, rows=None, metric=None):
-    """SC product of A (M x D, the row side) with B (N x D, the weight side)
-    restricted to the output rows ``rows`` (all rows when None).
+def rows_product(A_rows, rung_rows, B, plan: OraclePlan):
+    """Counts and decoded products of some A rows whose rungs are known.
 
-    Returns a dict with
-      ``x_a``, ``s_a``, ``x_b``, ``s_b``: quantised integers and scales;
-      ``metric``, ``g_hat``, ``rung``, ``order``, ``cuts``: the MP decision;
-      ``rows``: the rows computed;
-      ``counts``: int64 (len(rows), N, n_chunks) XNOR counts per chunk;
-      ``band_counts``: int64 (len(rows), N, n_bands);
-      ``L``: (len(rows), n_chunks) lengths used;
-      ``C``: float64 (len(rows), N) decoded products;
-      ``C_abs``: float64 (len(rows), N) sum of |chunk terms| (tolerance scale).
+    ``A_rows``: (R, D) float32 rows of A; ``rung_rows``: (R,) their rungs;
+    ``B``: (N, D).  Returns a dict with ``x_a``, ``s_a`` (of these rows),
+    ``x_b``, ``s_b``, ``counts`` (R, N, n_chunks), ``band_counts``
+    (R, N, n_bands), ``L`` (R, n_chunks), ``C`` and ``C_abs`` (R, N).
     """
-    A = np.asarray(A, dtype=np.float32)
+    A_rows = np.asarray(A_rows, dtype=np.float32)
     B = np.asarray(B, dtype=np.float32)
-    M, D = A.shape
+    R, D = A_rows.shape
     N, D2 = B.shape
     if D != plan.D or D2 != plan.D:
         raise ValueError("contraction length does not match the plan")
     q = QMAX(plan.p)
     K = plan.table()
-
-    x_a, s_a = quantize(A, plan.p, plan.chunk_d)
+    x_a, s_a = quantize(A_rows, plan.p, plan.chunk_d)
     x_b, s_b = quantize(B, plan.p, plan.chunk_d)
     u_a = bipolar_level(x_a, plan.p)
     u_b = bipolar_level(x_b, plan.p)
-
-    if metric is None:
-        metric = attention_row_metric(A) if plan.metric == "av" else row_metric(A)
-    g_hat = normalise_metric(metric)
-    if plan.n_rungs > 1:
-        rung, order = assign_rungs(g_hat, plan.n_rungs, plan.fractions)
-    else:
-        rung = np.zeros(M, dtype=np.int64)
-        order = np.arange(M, dtype=np.int64)
-    cuts = rung_cuts(M, plan.n_rungs, plan.fractions)
 
     ladder = plan.ladder()
     band_cols, chunk_band = plan.bands()
@@ -137,26 +120,53 @@ def sc_matmul_rows(A, B, plan: OraclePlan, rows=None, metric=None):
     for b in range(plan.n_bands):
         band_of_d[band_cols[b]:band_cols[b + 1]] = b
 
-    rows = np.arange(M) if rows is None else np.asarray(rows, dtype=np.int64)
-    counts = np.zeros((rows.shape[0], N, len(bounds)), dtype=np.int64)
-    Lrc = np.zeros((rows.shape[0], len(bounds)), dtype=np.int64)
-    for t, i in enumerate(rows):
-        k = int(rung[i])
+    counts = np.zeros((R, N, len(bounds)), dtype=np.int64)
+    Lrc = np.zeros((R, len(bounds)), dtype=np.int64)
+    for t in range(R):
+        k = int(rung_rows[t])
         L_per_d = ladder[band_of_d, k]
-        per_d = xnor_count_row(K, u_a[i], u_b, L_per_d)
+        per_d = xnor_count_row(K, u_a[t], u_b, L_per_d)
         for c, (c0, c1) in enumerate(bounds):
             counts[t, :, c] = per_d[:, c0:c1].sum(axis=1)
             Lrc[t, c] = ladder[chunk_band[c], k]
 
-    band_counts = np.zeros((rows.shape[0], N, plan.n_bands), dtype=np.int64)
+    band_counts = np.zeros((R, N, plan.n_bands), dtype=np.int64)
     for c in range(len(bounds)):
         band_counts[:, :, chunk_band[c]] += counts[:, :, c]
 
-    C, C_abs = decode(counts, s_a[rows], s_b, Lrc, widths, q)
-    return {
-        "x_a": x_a, "s_a": s_a, "x_b": x_b, "s_b": s_b,
-        "metric": np.asarray(metric, dtype=np.float32), "g_hat": g_hat,
-        "rung": rung, "order": order, "cuts": cuts, "rows": rows,
-        "counts": counts, "band_counts": band_counts, "L": Lrc,
-        "C": C, "C_abs": C_abs, "ladder": ladder,
-    }
+    C, C_abs = decode(counts, s_a, s_b, Lrc, widths, q)
+    return {"x_a": x_a, "s_a": s_a, "x_b": x_b, "s_b": s_b, "counts": counts,
+            "band_counts": band_counts, "L": Lrc, "C": C, "C_abs": C_abs, "ladder": ladder}
+
+
+def classify(A, plan: OraclePlan, metric=None):
+    """Row metric, normalised metric, rung of every row, sorted order, cuts."""
+    A = np.asarray(A, dtype=np.float32)
+    M = A.shape[0]
+    if metric is None:
+        metric = attention_row_metric(A) if plan.metric == "av" else row_metric(A)
+    g_hat = normalise_metric(metric)
+    if plan.n_rungs > 1:
+        rung, order = assign_rungs(g_hat, plan.n_rungs, plan.fractions)
+    else:
+        rung = np.zeros(M, dtype=np.int64)
+        order = np.arange(M, dtype=np.int64)
+    cuts = rung_cuts(M, plan.n_rungs, plan.fractions)
+    return {"metric": np.asarray(metric, dtype=np.float32), "g_hat": g_hat, "rung": rung,
+            "order": order, "cuts": cuts}
+
+
+def sc_matmul_rows(A, B, plan: OraclePlan, rows=None, metric=None):
+    """SC product of A (M x D, the row side) with B (N x D, the weight side)
+    restricted to the output rows ``rows`` (all rows when None).
+
+    Returns the union of ``classify`` (metric, g_hat, rung, order, cuts for
+    every row) and ``rows_product`` for the requested rows, plus ``rows``.
+    """
+    A = np.asarray(A, dtype=np.float32)
+    cls = classify(A, plan, metric)
+    rows = np.arange(A.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = rows_product(A[rows], cls["rung"][rows], B, plan)
+    out.update(cls)
+    out["rows"] = rows
+    return out

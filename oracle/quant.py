@@ -51,16 +51,15 @@ def quantize(X: np.ndarray, p: int = 8, chunk_d: int = 0):
     qf = np.float32(q)
     for ci, (c0, c1) in enumerate(bounds):
         block = X[:, c0:c1]
-        amax = np.max(np.abs(block), axis=1).astype(np.float32)
-        for row in range(R):
-            a = np.float32(amax[row])
-            if a == np.float32(0.0):
-                scales[row, ci] = np.float32(0.0)
-                continue
-            s = np.float32(a / qf)
-            scales[row, ci] = s
-            v = np.rint(block[row] / s)  # float32 / float32 -> float32
-            x_int[row, c0:c1] = np.clip(v, -q, q).astype(np.int64)
+        a = np.max(np.abs(block), axis=1).astype(np.float32)     # (R,)
+        s = (a / qf).astype(np.float32)                          # float32 division
+        scales[:, ci] = s
+        nz = a != np.float32(0.0)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            v = np.rint(block / s[:, None])                      # float32 / float32
+        v = np.clip(v, -q, q)
+        x_int[:, c0:c1] = np.where(nz[:, None], v, 0).astype(np.int64)
+        scales[~nz, ci] = np.float32(0.0)
     return x_int, scales
 
 

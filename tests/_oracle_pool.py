@@ -1,0 +1,40 @@
+"""Run the CPU oracle over many output rows in a process pool.
+
+Workers are spawned (not forked) and import only NumPy and ``oracle``, so
+they never touch the GPU or torch.
+"""
+
+import multiprocessing as mp
+import os
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+import oracle as o
+
+
+def workers() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+def _task(args):
+    A_rows, rung_rows, B, plan_kw = args
+    return o.rows_product(A_rows, rung_rows, B, o.OraclePlan(**plan_kw))
+
+
+def pooled_rows_product(A_rows, rung_rows, B, plan_kw, n_workers=None):
+    """rows_product over ``A_rows`` split across worker processes."""
+    R = A_rows.shape[0]
+    n = min(n_workers or workers(), max(R, 1))
+    if n <= 1 or R <= 1:
+        return o.rows_product(A_rows, rung_rows, B, o.OraclePlan(**plan_kw))
+    parts = [p for p in np.array_split(np.arange(R), n) if p.size]
+    ctx = mp.get_context("spawn")
+    with ProcessPoolExecutor(max_workers=len(parts), mp_context=ctx) as ex:
+        outs = list(ex.map(_task, [(A_rows[p], rung_rows[p], B, plan_kw) for p in parts]))
+    merged = {}
+    for key in ("x_a", "s_a", "counts", "band_counts", "L", "C", "C_abs"):
+        merged[key] = np.concatenate([r[key] for r in outs], axis=0)
+    for key in ("x_b", "s_b", "ladder"):
+        merged[key] = outs[0][key]
+    return merged
