@@ -224,7 +224,7 @@ def test_ragged_chunks_and_uneven_bands(table, algo):
     M, N, D = 150, 90, 150
     A = rng.standard_normal((M, D)).astype(np.float32)
     B = (0.02 * rng.standard_normal((N, D))).astype(np.float32)
-    band_L = [[120, 100, 40], [128, 96, 64]]        # columns 128 + 22
+    band_L = [[120, 90, 40], [128, 96, 64]]         # columns 128 + 22, within budget
     kw = dict(D=D, chunk_d=64, levels=(128, 96, 60), fractions=(0.2, 0.5, 0.3), n_bands=2,
               band_chunks=(2, 1), band_L=band_L)
     plan = scmp.scmp_plan_create(op="linear", **kw)
