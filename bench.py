@@ -154,6 +154,8 @@ def main():
     pm = torch.empty((G, M), dtype=torch.int32, device=dev)
     th = torch.empty((G, max(plan.n_rungs - 1, 1)), dtype=torch.float32, device=dev)
     C = torch.empty((G, M, N), dtype=torch.float32, device=dev)
+    ws_bytes = scmp.scmp_matmul_workspace_bytes(table, plan, G, M, N, args.algo)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ev = []
 
@@ -171,7 +173,7 @@ def main():
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         scmp.scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, packedB=pB, algo=args.algo, C_out=C,
-                         want_C=True, stream=stream)
+                         want_C=True, workspace=ws, stream=stream)
         if timed:
             e1.record(stream)
             ev.append((e0, e1))

@@ -22,7 +22,8 @@
  *    Every device call is asynchronous on that stream and never
  *    synchronises the device, except scmp_error_flags.
  *  - Calls never allocate device memory, except scmp_build_sobol_table (the
- *    one-time table) which allocates the table it returns.
+ *    one-time table) which allocates the table it returns.  Scratch memory
+ *    comes from the caller (scmp_matmul_workspace_bytes).
  *  - Arguments and plans are validated on the host before any launch.  On
  *    error nothing is launched and the status is returned;
  *    scmp_last_error() then describes the failure (thread-local string).
@@ -58,7 +59,7 @@ typedef enum {
   SCMP_ERR_UNSUPPORTED = 4,    /* K-bands on qk/av, K-bands with range MP, range MP [KBAND] "Guards" */
   SCMP_ERR_PLAN_MISMATCH = 5,  /* table priced at another chunk_d or width; shapes vs plan [KBAND] "Guards" */
   SCMP_ERR_NONFINITE = 6,      /* a non-finite input was seen (reported by scmp_error_flags) */
-  SCMP_ERR_WORKSPACE = 7,      /* reserved */
+  SCMP_ERR_WORKSPACE = 7,      /* workspace smaller than scmp_matmul_workspace_bytes */
   SCMP_ERR_HIP = 8             /* a HIP runtime call or launch failed */
 } scmp_status;
 
@@ -85,7 +86,7 @@ typedef struct {
   int Lmax;                  /* table length; must match the table */
   int D;                     /* contraction length */
   int chunk_d;               /* 0: one scale per row; >0: one scale per (row, chunk of chunk_d
-                                columns), the last chunk may be short; must be a multiple of 16 */
+                                columns), the last chunk may be short; must be a multiple of 32 */
   int n_rungs;               /* 1..SCMP_MAX_RUNGS; 1 = uniform length */
   const int* levels;         /* [n_rungs] stream lengths, strictly descending, >= 1 */
   const double* fractions;   /* [n_rungs] row fractions in the same order, sum 1; NULL = equal */
@@ -139,7 +140,7 @@ int scmp_table_export(scmp_table_t table, uint16_t* r_dev, uint32_t* K_dev, uint
  * equal column width.
  * Errors: ARG, CEILING (any length above the ceiling), ISO_COMPUTE
  * (sum_b D_b L[b][k] > D L_k), UNSUPPORTED (n_bands > 1 with op QK or AV;
- * range_mp with or without bands; chunk_d not a multiple of 16),
+ * range_mp with or without bands; chunk_d not a multiple of 32),
  * PLAN_MISMATCH (table_chunk_d / table_D differ from chunk_d / D). */
 int scmp_plan_create(const scmp_plan_desc* desc, scmp_plan_t* out);
 
@@ -196,6 +197,14 @@ int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const float* X_de
 int scmp_classify_rows(scmp_plan_t plan, const float* metric_dev, int G, int M, float* ghat_dev,
                        uint8_t* rung_dev, int32_t* perm_dev, float* thresholds_dev, void* stream);
 
+/* Workspace scmp_matmul needs for these sizes (0 for BITSERIAL).  The
+ * MFMA path keeps there, per call, the row side encoded at each row's
+ * length (signed half-window, int16 per (d, sorted position)), each row
+ * tile's largest half-window per d, the per-chunk n0 sums and the weight
+ * side's levels.  Errors: ARG, PLAN_MISMATCH. */
+int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                                size_t* bytes);
+
 /* The SC matmul C = A x B^T ([PAYN] Key designs 1 and 3; [KBAND] "How the
  * banding works").  Rows of A are taken bucket by bucket in sorted order
  * (rung k = sorted positions [cut_k, cut_(k+1)), all at one length), so
@@ -210,14 +219,17 @@ int scmp_classify_rows(scmp_plan_t plan, const float* metric_dev, int G, int M, 
  *   qB_dev int8 [G][N][D], sB_dev float [G][N][n_chunks],
  *   packedB_dev uint32 [G][N][D][ceil(Lmax/32)] (needed by BITSERIAL only),
  *   counts_dev int32 [G][M][N][n_bands] (nullable): per-band XNOR counts,
- *   C_dev float (nullable): decoded output at original row order.
+ *   C_dev float (nullable): decoded output at original row order,
+ *   workspace_dev / workspace_bytes: scratch of at least
+ *   scmp_matmul_workspace_bytes (ignored by BITSERIAL); calls that share a
+ *   workspace must be ordered on one stream.
  * At least one of counts_dev and C_dev must be given; ldc >= N.
- * Errors: ARG, PLAN_MISMATCH (table vs plan), HIP. */
+ * Errors: ARG, PLAN_MISMATCH (table vs plan), WORKSPACE (too small), HIP. */
 int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                 const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
                 const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
                 int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
-                void* stream);
+                void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* Decode counts produced without chunk scales ([PAYN] Key design 1, decode
  * equation): C_ij = s^A_i s^B_j q^2 (2 count_ij - L_i D) / L_i with

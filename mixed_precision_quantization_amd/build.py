@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libscmp.so")
 
-SOURCES = ["plan.cpp", "table.hip", "quantize.hip", "classify.hip", "matmul.hip"]
+SOURCES = ["plan.cpp", "table.hip", "quantize.hip", "classify.hip", "matmul.hip", "mfma.hip", "bitserial.hip"]
 
 ARCH = os.environ.get("SCMP_OFFLOAD_ARCH", "gfx950")
 

@@ -1,39 +1,16 @@
-// K3: the SC XNOR contraction with per-row stream lengths, K-band partial
-// sums and the fused float32 decode; plus the standalone decode.
+// The C-ABI entry points of the contraction (scmp_matmul and its workspace
+// query), the standalone decode, and the device error flags.
 //
-// "Precision As You Need" paper notes, Key design 1: A's stream for
-// contraction index d is the L-prefix of its table row, so it has n1 ones
-// and n0 = L - n1 zeros; B's stream is generated by two counters gated by
-// A's bits (C-BSG).  Position by position, the XNOR count of the pair is
-//   sum_c [ B_c T1_c + (1 - B_c) T0_c ],
-// where B_c = K[u_B][c] is B's counter-domain stream and T1 / T0 are the
-// prefix masks of n1 / n0 ones: where A emitted its c-th one, B emitted
-// K[u_B][c] and XNOR is that bit; where A emitted its c-th zero, XNOR is
-// the complement.  Two exact ways to evaluate it are provided:
-//
-//  BITSERIAL: popcount(bitselect(B_w, T1_w, T0_w)) per 32-position word w,
-//             one bit-select and one accumulating popcount per word
-//             (vector ALU).
-//  MFMA:      count = n0 + sum_c B_c (T1_c - T0_c).  T1 - T0 is +1 on
-//             [n0, n1) or -1 on [n1, n0), a window symmetric about L / 2.
-//             Folding the window at its centre turns it into a prefix of
-//             hh = ceil(|n1 - n0| / 2) paired positions with sign +-1, and B
-//             into pair sums B'_k in {0, 1, 2} (see table.hip).  The count is
-//             then an exact int8 x int8 contraction of length ceil(L/2)
-//             per d, run on v_mfma_i32_32x32x32_i8, and only the paired
-//             positions some row of the tile needs are visited.
-//
-// Key design 3: cost is proportional to each row's length; rows are
-// bucketed by rung (scmp_classify_rows) so a tile has one length.
-// K-band pull request, "How the banding works": band b of the contraction
-// axis runs rung k at L[b][k]; partial products of the bands are summed.
-// Decode per chunk c: s^A s^B q^2 (2 count_c - L_c |c|) / L_c.
+// "Precision As You Need" paper notes, Key design 1 (C-BSG, decode
+// equation) and Key design 3 (per-row early termination); K-band pull
+// request, "How the banding works".  The two contraction kernels live in
+// mfma.hip (matrix cores, default) and bitserial.hip (vector ALU).
 
 #include <hip/hip_runtime.h>
 
 #include <string>
 
-#include "internal.h"
+#include "matmul_common.h"
 #include "table.h"
 
 namespace scmp {
@@ -41,399 +18,47 @@ namespace scmp {
 int read_clear_quant_flags(hipStream_t st, int* flags);
 int read_clear_classify_flags(hipStream_t st, int* flags);
 
-struct MatmulArgs {
-  const int8_t* qA;
-  const float* sA;
-  const int32_t* perm;
-  const int8_t* qB;
-  const uint32_t* packedB;
-  const float* sB;
-  int32_t* counts;
-  float* C;
-  long long ldc, bsc;
-  const uint8_t* pair;
-  const uint16_t* cum;
-  int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
-  int cuts[SCMP_MAX_RUNGS + 1];
-  int tile_start[SCMP_MAX_RUNGS + 1];
-  int band_cols[SCMP_MAX_BANDS + 1];
-  int bandL[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
-  unsigned long long pair_off[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
-};
-
-// Level of a stored integer, clamped to [0, P] so that a corrupted input can
-// never index outside the tables.
-__device__ __forceinline__ int level_of(int x, int P, int q) {
-  const int u = (P * (x + q) + q) / (2 * q);
-  return u < 0 ? 0 : (u > P ? P : u);
+void fill_tiles(MatmulArgs& a, const Plan& P, int BM) {
+  row_cuts(P, a.M, a.cuts);
+  a.tile_start[0] = 0;
+  for (int k = 0; k < P.n_rungs; ++k)
+    a.tile_start[k + 1] = a.tile_start[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
 }
 
-// Rung and first sorted position of the block's row tile.
-__device__ __forceinline__ void locate_tile(const MatmulArgs& a, int y, int BM, int& k, int& pos0, int& nrows) {
-  k = 0;
-  while (k + 1 < a.n_rungs && y >= a.tile_start[k + 1]) ++k;
-  pos0 = a.cuts[k] + (y - a.tile_start[k]) * BM;
-  nrows = min(BM, a.cuts[k + 1] - pos0);
-}
-
-__device__ __forceinline__ int row_of(const MatmulArgs& a, int g, int pos) {
-  if (!a.perm) return pos;
-  int r = a.perm[(long long)g * a.M + pos];
-  return r < 0 ? 0 : (r >= a.M ? a.M - 1 : r);
-}
-
-// End of the chunk that contains column d.
-__device__ __forceinline__ int chunk_end(const MatmulArgs& a, int d) {
-  if (a.chunk_d <= 0) return a.D;
-  return min((d / a.chunk_d + 1) * a.chunk_d, a.D);
-}
-
-// ---------------------------------------------------------------- MFMA ----
-
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
-
-constexpr int MF_BM = 128, MF_BN = 128, MF_DC = 16;
-constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LDS (>= 128 + 16)
-constexpr int MAX_LEVELS = 257;
-
-template <bool COUNTS>
-__global__ void __launch_bounds__(256) k_matmul_mfma(MatmulArgs a) {
-  __shared__ __align__(16) uint8_t s_pt[MAX_LEVELS * PT_STRIDE];
-  __shared__ __align__(16) uint32_t s_pat[34 * 4];
-  __shared__ uint16_t s_ncum[MAX_LEVELS];
-  __shared__ int16_t s_h[MF_DC][MF_BM];
-  __shared__ uint16_t s_u[MF_DC][MF_BN];
-  __shared__ int s_maxh[MF_DC];
-  __shared__ int s_rowc[MF_BM];
-  __shared__ int s_rows[MF_BM];
-
-  const int tid = threadIdx.x;
-  const int g = blockIdx.z;
-  int k, pos0, nrows;
-  locate_tile(a, blockIdx.y, MF_BM, k, pos0, nrows);
-  const int col0 = blockIdx.x * MF_BN;
-
-  if (tid < MF_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
-  if (tid < 34 * 4) {
-    // Window pattern for n leading paired positions (n in [0, 16]) with
-    // sign + (byte 0x01) or - (byte 0xff): s_pat[(2 n + neg) * 4 + word].
-    const int pi = tid >> 2, wd = tid & 3, n = pi >> 1;
-    const uint32_t one = (pi & 1) ? 0xffu : 0x01u;
-    uint32_t v = 0;
-    for (int byte = 0; byte < 4; ++byte)
-      if (wd * 4 + byte < n) v |= one << (8 * byte);
-    s_pat[tid] = v;
-  }
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int qq = a.q * a.q;
-
-  v16i acc[2][2];
-  float cacc[2][2][16];
-  int bacc[2][2][16];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        acc[i][j][v] = 0;
-        cacc[i][j][v] = 0.0f;
-        bacc[i][j][v] = 0;
-      }
-
-  for (int b = 0; b < a.n_bands; ++b) {
-    const int L = a.bandL[b][k];
-    const int KL = (L + 1) >> 1;
-    const int KLpad = (KL + 31) & ~31;
-    const float scaleL = (float)qq / (float)L;
-    const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
-    __syncthreads();
-    {
-      const uint8_t* src = a.pair + a.pair_off[b][k];
-      const int vec_per_row = KLpad >> 4;
-      for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += 256) {
-        const int u = idx / vec_per_row, v = idx - u * vec_per_row;
-        *(uint4*)(s_pt + u * PT_STRIDE + v * 16) = *(const uint4*)(src + (long long)u * KLpad + v * 16);
-      }
-      for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
+// Validate the arguments and fill MatmulArgs (no device work).
+static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, MatmulArgs& a) {
+  if (!table || !plan) return set_error(SCMP_ERR_ARG, "table or plan is NULL");
+  const Plan& P = plan->plan;
+  if (table->p != P.p || table->Lmax != P.Lmax)
+    return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
+  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA) return set_error(SCMP_ERR_ARG, "unknown algo");
+  if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
+  if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
+  if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
+  a = MatmulArgs{};
+  a.pair = table->pair;
+  a.cum = table->cum;
+  a.G = G;
+  a.M = M;
+  a.N = N;
+  a.D = P.D;
+  a.chunk_d = P.chunk_d;
+  a.n_chunks = P.n_chunks;
+  a.n_rungs = P.n_rungs;
+  a.n_bands = P.n_bands;
+  a.q = qmax(P.p);
+  a.P = 1 << P.p;
+  a.Wl = table->Wl;
+  a.Lmax = table->Lmax;
+  const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
+  fill_tiles(a, P, bitserial ? 64 : 128);
+  for (int b = 0; b <= P.n_bands; ++b) a.band_cols[b] = P.band_cols[b];
+  for (int b = 0; b < P.n_bands; ++b)
+    for (int k = 0; k < P.n_rungs; ++k) {
+      a.bandL[b][k] = P.band_L[b][k];
+      a.pair_off[b][k] = table->pair_off[P.band_L[b][k]];
     }
-    for (int d0 = dbeg; d0 < dend; d0 += MF_DC) {
-      const int cend = chunk_end(a, d0);
-      const bool chunk_start = (a.chunk_d <= 0) ? (d0 == 0) : (d0 % a.chunk_d == 0);
-      const int dlim = min(d0 + MF_DC, dend);
-      __syncthreads();
-      // Stage A: half-window and sign per (d, row), n0 sum per row.
-      {
-        const int r = tid >> 1, part = tid & 1;
-        const int row = s_rows[r];
-        int n0sum = 0;
-        const int8_t* src = a.qA + ((long long)g * a.M + (row < 0 ? 0 : row)) * a.D;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int dd = part * 8 + i;
-          const int d = d0 + dd;
-          int hs = 0;
-          if (row >= 0 && d < dlim) {
-            const int u = level_of((int)src[d], a.P, a.q);
-            const int n1 = s_ncum[u];
-            const int diff = 2 * n1 - L;
-            const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
-            hs = diff > 0 ? hh : -hh;
-            n0sum += L - n1;
-          }
-          s_h[dd][r] = (int16_t)hs;
-        }
-        n0sum += __shfl_xor(n0sum, 1, 64);
-        if (part == 0) s_rowc[r] = (chunk_start ? 0 : s_rowc[r]) + n0sum;
-      }
-      // Stage B: levels per (d, col).
-      {
-        const int c = tid >> 1, part = tid & 1;
-        const int col = col0 + c;
-        const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int dd = part * 8 + i;
-          const int d = d0 + dd;
-          int u = a.P >> 1;
-          if (col < a.N && d < dlim) u = level_of((int)src[d], a.P, a.q);
-          s_u[dd][c] = (uint16_t)u;
-        }
-      }
-      __syncthreads();
-      // Largest half-window of the tile at each d: the paired positions
-      // beyond it are zero for every row of the tile.
-      {
-        const int dd = tid >> 4, seg = tid & 15;
-        int m = 0;
-#pragma unroll
-        for (int i = 0; i < MF_BM / 16; ++i) {
-          const int h = s_h[dd][seg * (MF_BM / 16) + i];
-          m = max(m, h < 0 ? -h : h);
-        }
-#pragma unroll
-        for (int off = 8; off > 0; off >>= 1) m = max(m, __shfl_xor(m, off, 64));
-        if (seg == 0) s_maxh[dd] = m;
-      }
-      __syncthreads();
-      for (int dd = 0; dd < MF_DC; ++dd) {
-        const int steps = (s_maxh[dd] + 31) >> 5;
-        if (steps == 0) continue;
-        int ha[2], ub[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ha[i] = s_h[dd][wr * 64 + i * 32 + l32];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) ub[j] = s_u[dd][wc * 64 + j * 32 + l32];
-        for (int s = 0; s < steps; ++s) {
-          const int kk = s * 32 + hf * 16;
-          v4i af[2], bf[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int h = ha[i] < 0 ? -ha[i] : ha[i];
-            int n = h - kk;
-            n = n < 0 ? 0 : (n > 16 ? 16 : n);
-            const int pi = 2 * n + (ha[i] < 0 ? 1 : 0);
-            af[i] = *(const v4i*)(s_pat + pi * 4);
-          }
-#pragma unroll
-          for (int j = 0; j < 2; ++j) bf[j] = *(const v4i*)(s_pt + ub[j] * PT_STRIDE + kk);
-#pragma unroll
-          for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-      }
-      if (dlim >= cend) {
-        // Chunk complete: add each row's n0 sum, decode, keep band counts.
-        const int ch = a.chunk_d > 0 ? (d0 / a.chunk_d) : 0;
-        const int cw = cend - (a.chunk_d > 0 ? ch * a.chunk_d : 0);
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = col0 + wc * 64 + j * 32 + l32;
-            const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
-              const int cnt = acc[i][j][v] + s_rowc[r];
-              const int row = s_rows[r];
-              const float sa = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
-              cacc[i][j][v] += (sa * sb) * (scaleL * (float)(2 * cnt - L * cw));
-              if (COUNTS) bacc[i][j][v] += cnt;
-              acc[i][j][v] = 0;
-            }
-          }
-      }
-    }
-    if (COUNTS) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int col = col0 + wc * 64 + j * 32 + l32;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
-            const int row = s_rows[r];
-            if (row >= 0 && col < a.N)
-              a.counts[(((long long)g * a.M + row) * a.N + col) * a.n_bands + b] = bacc[i][j][v];
-            bacc[i][j][v] = 0;
-          }
-        }
-    }
-  }
-  if (a.C) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = col0 + wc * 64 + j * 32 + l32;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
-          const int row = s_rows[r];
-          if (row >= 0 && col < a.N) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = cacc[i][j][v];
-        }
-      }
-  }
-}
-
-// ----------------------------------------------------------- bit-serial ----
-
-constexpr int BS_BM = 64, BS_BN = 64, BS_DC = 8, BS_WMAX = 8;
-
-// Prefix mask word: bits [0, n) of the stream restricted to word w.
-__device__ __forceinline__ uint32_t prefix_word(int n, int w) {
-  const int m = n - 32 * w;
-  return m <= 0 ? 0u : (m >= 32 ? 0xffffffffu : ((1u << m) - 1u));
-}
-
-template <bool COUNTS>
-__global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
-  __shared__ __align__(16) uint2 s_t[BS_DC][BS_WMAX][BS_BM];      // (T1, T0) words
-  __shared__ __align__(16) uint32_t s_b[BS_DC][BS_WMAX][BS_BN];   // B stream words
-  __shared__ uint16_t s_ncum[MAX_LEVELS];
-  __shared__ int s_rows[BS_BM];
-
-  const int tid = threadIdx.x;
-  const int g = blockIdx.z;
-  int k, pos0, nrows;
-  locate_tile(a, blockIdx.y, BS_BM, k, pos0, nrows);
-  const int col0 = blockIdx.x * BS_BN;
-  if (tid < BS_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
-  const int ty = tid >> 4, tx = tid & 15;
-  const int qq = a.q * a.q;
-
-  int cnt[4][4];
-  float cacc[4][4];
-  int bacc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      cnt[i][j] = 0;
-      cacc[i][j] = 0.0f;
-      bacc[i][j] = 0;
-    }
-
-  for (int b = 0; b < a.n_bands; ++b) {
-    const int L = a.bandL[b][k];
-    const int W = (L + 31) >> 5;
-    const float scaleL = (float)qq / (float)L;
-    const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
-    __syncthreads();
-    for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
-    for (int d0 = dbeg; d0 < dend; d0 += BS_DC) {
-      const int cend = chunk_end(a, d0);
-      const int dlim = min(d0 + BS_DC, dend);
-      __syncthreads();
-      {
-        // A masks: thread -> (row r, two d's).
-        const int r = tid >> 2, dp = (tid & 3) * 2;
-        const int row = s_rows[r];
-        const int8_t* src = a.qA + ((long long)g * a.M + (row < 0 ? 0 : row)) * a.D;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int dd = dp + i, d = d0 + dd;
-          int n1 = 0, n0 = 0;
-          if (row >= 0 && d < dlim) {
-            n1 = s_ncum[level_of((int)src[d], a.P, a.q)];
-            n0 = L - n1;
-          }
-          for (int w = 0; w < W; ++w) s_t[dd][w][r] = make_uint2(prefix_word(n1, w), prefix_word(n0, w));
-        }
-        // B words: thread -> (col c, two d's).
-        const int c = tid >> 2, col = col0 + c;
-        const uint32_t* bsrc = a.packedB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D * a.Wl;
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int dd = dp + i, d = d0 + dd;
-          for (int w = 0; w < W; ++w) s_b[dd][w][c] = (col < a.N && d < dlim) ? bsrc[(long long)d * a.Wl + w] : 0u;
-        }
-      }
-      __syncthreads();
-      for (int dd = 0; dd < BS_DC; ++dd) {
-        for (int w = 0; w < W; ++w) {
-          const uint4 t01 = *(const uint4*)&s_t[dd][w][ty * 4];
-          const uint4 t23 = *(const uint4*)&s_t[dd][w][ty * 4 + 2];
-          const uint4 bw = *(const uint4*)&s_b[dd][w][tx * 4];
-          const uint32_t T1[4] = {t01.x, t01.z, t23.x, t23.z};
-          const uint32_t T0[4] = {t01.y, t01.w, t23.y, t23.w};
-          const uint32_t B[4] = {bw.x, bw.y, bw.z, bw.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) cnt[i][j] += __popc((B[j] & T1[i]) | (~B[j] & T0[i]));
-        }
-      }
-      if (dlim >= cend) {
-        const int ch = a.chunk_d > 0 ? (d0 / a.chunk_d) : 0;
-        const int cw = cend - (a.chunk_d > 0 ? ch * a.chunk_d : 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = s_rows[ty * 4 + i];
-          const float sa = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int col = col0 + tx * 4 + j;
-            const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
-            cacc[i][j] += (sa * sb) * (scaleL * (float)(2 * cnt[i][j] - L * cw));
-            if (COUNTS) bacc[i][j] += cnt[i][j];
-            cnt[i][j] = 0;
-          }
-        }
-      }
-    }
-    if (COUNTS) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = s_rows[ty * 4 + i];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int col = col0 + tx * 4 + j;
-          if (row >= 0 && col < a.N)
-            a.counts[(((long long)g * a.M + row) * a.N + col) * a.n_bands + b] = bacc[i][j];
-          bacc[i][j] = 0;
-        }
-      }
-    }
-  }
-  if (a.C) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = s_rows[ty * 4 + i];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = col0 + tx * 4 + j;
-        if (row >= 0 && col < a.N) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = cacc[i][j];
-      }
-    }
-  }
+  return SCMP_OK;
 }
 
 // ---------------------------------------------------------------- decode ----
@@ -469,28 +94,35 @@ using scmp::set_error;
 
 extern "C" {
 
+int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                                size_t* bytes) {
+  scmp::clear_error();
+  if (!bytes) return set_error(SCMP_ERR_ARG, "bytes is NULL");
+  *bytes = 0;
+  scmp::MatmulArgs a;
+  int st = scmp::prepare(table, plan, algo, G, M, N, a);
+  if (st != SCMP_OK) return st;
+  if (algo == SCMP_ALGO_BITSERIAL || (long long)G * M * N == 0) return SCMP_OK;
+  *bytes = scmp::mfma_workspace_bytes(a);
+  return SCMP_OK;
+}
+
 int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
                 const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
                 const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
-                void* stream) {
+                void* workspace, size_t workspace_bytes, void* stream) {
   scmp::clear_error();
-  if (!table || !plan) return set_error(SCMP_ERR_ARG, "table or plan is NULL");
+  scmp::MatmulArgs a;
+  int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
+  if (st0 != SCMP_OK) return st0;
   const scmp::Plan& P = plan->plan;
-  if (table->p != P.p || table->Lmax != P.Lmax)
-    return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
-  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA) return set_error(SCMP_ERR_ARG, "unknown algo");
-  if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if ((long long)G * M * N == 0) return SCMP_OK;
-  if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (!qA || !sA || !qB || !sB) return set_error(SCMP_ERR_ARG, "qA, sA, qB and sB are required");
   if (!counts && !C) return set_error(SCMP_ERR_ARG, "at least one of counts and C is required");
   if (C && ldc < N) return set_error(SCMP_ERR_ARG, "ldc must be >= N");
   if (P.n_rungs > 1 && !permA) return set_error(SCMP_ERR_ARG, "mixed precision needs the row permutation");
   const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
   if (bitserial && !packedB) return set_error(SCMP_ERR_ARG, "the bit-serial kernel needs packed B streams");
-  if (table->P + 1 > scmp::MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
-
-  scmp::MatmulArgs a;
   a.qA = qA;
   a.sA = sA;
   a.perm = permA;
@@ -501,51 +133,8 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
   a.C = C;
   a.ldc = ldc;
   a.bsc = batch_stride_c;
-  a.pair = table->pair;
-  a.cum = table->cum;
-  a.G = G;
-  a.M = M;
-  a.N = N;
-  a.D = P.D;
-  a.chunk_d = P.chunk_d;
-  a.n_chunks = P.n_chunks;
-  a.n_rungs = P.n_rungs;
-  a.n_bands = P.n_bands;
-  a.q = scmp::qmax(P.p);
-  a.P = 1 << P.p;
-  a.Wl = table->Wl;
-  a.Lmax = table->Lmax;
-  scmp::row_cuts(P, M, a.cuts);
-  const int BM = bitserial ? scmp::BS_BM : scmp::MF_BM;
-  const int BN = bitserial ? scmp::BS_BN : scmp::MF_BN;
-  a.tile_start[0] = 0;
-  for (int k = 0; k < P.n_rungs; ++k)
-    a.tile_start[k + 1] = a.tile_start[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
-  for (int b = 0; b <= P.n_bands; ++b) a.band_cols[b] = P.band_cols[b];
-  for (int b = 0; b < P.n_bands; ++b)
-    for (int k = 0; k < P.n_rungs; ++k) {
-      a.bandL[b][k] = P.band_L[b][k];
-      a.pair_off[b][k] = table->pair_off[P.band_L[b][k]];
-    }
-  const int row_tiles = a.tile_start[P.n_rungs];
-  if (row_tiles == 0) return SCMP_OK;
-  if (row_tiles > 65535) return set_error(SCMP_ERR_ARG, "too many row tiles");
-  dim3 grid((N + BN - 1) / BN, row_tiles, G);
   hipStream_t st = (hipStream_t)stream;
-  if (bitserial) {
-    if (counts)
-      hipLaunchKernelGGL(scmp::k_matmul_bitserial<true>, grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(scmp::k_matmul_bitserial<false>, grid, dim3(256), 0, st, a);
-  } else {
-    if (counts)
-      hipLaunchKernelGGL(scmp::k_matmul_mfma<true>, grid, dim3(256), 0, st, a);
-    else
-      hipLaunchKernelGGL(scmp::k_matmul_mfma<false>, grid, dim3(256), 0, st, a);
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("matmul launch: ") + hipGetErrorString(e));
-  return SCMP_OK;
+  return bitserial ? scmp::launch_bitserial(a, st) : scmp::launch_mfma(a, workspace, workspace_bytes, st);
 }
 
 int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts, const float* sA, const float* sB,

@@ -1,0 +1,74 @@
+// Arguments and device helpers shared by the XNOR contraction kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "internal.h"
+
+namespace scmp {
+
+constexpr int MAX_LEVELS = 257;  // 2^p + 1 levels for p <= 8
+
+struct MatmulArgs {
+  const int8_t* qA;
+  const float* sA;
+  const int32_t* perm;
+  const int8_t* qB;
+  const uint32_t* packedB;
+  const float* sB;
+  int32_t* counts;
+  float* C;
+  long long ldc, bsc;
+  const uint8_t* pair;
+  const uint16_t* cum;
+  int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
+  int cuts[SCMP_MAX_RUNGS + 1];
+  int tile_start[SCMP_MAX_RUNGS + 1];
+  int band_cols[SCMP_MAX_BANDS + 1];
+  int bandL[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
+  unsigned long long pair_off[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
+};
+
+// Level of a stored integer, clamped to [0, P] so that a corrupted input can
+// never index outside the tables.
+__device__ __forceinline__ int level_of(int x, int P, int q) {
+  const int u = (P * (x + q) + q) / (2 * q);
+  return u < 0 ? 0 : (u > P ? P : u);
+}
+
+// Rung and first sorted position of a row tile (tiles are numbered bucket
+// after bucket).
+__device__ __forceinline__ void locate_tile(const MatmulArgs& a, int y, int BM, int& k, int& pos0, int& nrows) {
+  k = 0;
+  while (k + 1 < a.n_rungs && y >= a.tile_start[k + 1]) ++k;
+  pos0 = a.cuts[k] + (y - a.tile_start[k]) * BM;
+  nrows = min(BM, a.cuts[k + 1] - pos0);
+}
+
+// Original row of a sorted position (the identity without a permutation).
+__device__ __forceinline__ int row_of(const MatmulArgs& a, int g, int pos) {
+  if (!a.perm) return pos;
+  int r = a.perm[(long long)g * a.M + pos];
+  return r < 0 ? 0 : (r >= a.M ? a.M - 1 : r);
+}
+
+// End of the chunk that contains column d.
+__device__ __forceinline__ int chunk_end(const MatmulArgs& a, int d) {
+  if (a.chunk_d <= 0) return a.D;
+  return min((d / a.chunk_d + 1) * a.chunk_d, a.D);
+}
+
+// Host side: fill the tile table of the arguments for a row-tile height BM.
+void fill_tiles(MatmulArgs& a, const Plan& P, int BM);
+
+// Matrix-core path (mfma.hip).
+size_t mfma_workspace_bytes(const MatmulArgs& a);
+int launch_mfma(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
+
+// Vector-ALU bit-serial path (bitserial.hip).
+int launch_bitserial(const MatmulArgs& a, hipStream_t st);
+
+}  // namespace scmp

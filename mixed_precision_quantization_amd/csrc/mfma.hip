@@ -1,0 +1,427 @@
+// Matrix-core XNOR contraction (v_mfma_i32_32x32x32_i8).
+//
+// "Precision As You Need" paper notes, Key design 1 (C-BSG, decode
+// equation) and Key design 3 (early termination per row); K-band pull
+// request, "How the banding works" (band b of the contraction axis runs rung
+// k at L[b][k]; band partial products are summed).
+//
+// For contraction index d, A's L-prefix stream has n1 ones and n0 = L - n1
+// zeros, and the XNOR count against B's conditional stream is
+//   n0 + sum_c B_c (T1_c - T0_c)
+// with B_c = K[u_B][c] and T1, T0 the prefix masks of n1, n0 ones.
+// T1 - T0 is a run of +1 on [n0, n1) or -1 on [n1, n0), centred on L / 2.
+// Folded at the centre it becomes a prefix of hh = ceil(|n1 - n0| / 2)
+// paired positions k with sign s, and B becomes the pair sums
+// B'_k = B_lo(k) + B_hi(k) in {0, 1, 2} (table.hip), so
+//   count = n0 + s * sum_{k < hh} B'_k,
+// an exact int8 contraction over ceil(L/2) paired positions per d.
+//
+// Three kernels:
+//  k_prep_rows  per row tile: h = s * hh (int16) in bucket order, laid out
+//               [d][position], the tile's largest hh at each d, and the n0
+//               sum of every row over every chunk ("A side at the row's L").
+//  k_prep_cols  per column tile: B levels, laid out [d][column].
+//  k_mfma       per (row tile, column tile): stages 32 contraction indices
+//               at a time through double-buffered LDS (one barrier per
+//               stage), visits only the 32-position steps some row of the
+//               tile needs (the tile's largest hh), and decodes per chunk.
+// A row tile holds 128 consecutive sorted positions of one rung (one L per
+// band), so early termination costs no divergence.
+
+#include <hip/hip_runtime.h>
+
+#include <string>
+
+#include "matmul_common.h"
+
+namespace scmp {
+
+constexpr int MF_BM = 128, MF_BN = 128, MF_DC = 32;
+constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LDS
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v16i __attribute__((ext_vector_type(16)));
+
+struct MfmaWs {
+  int16_t* hs;      // [G][Dp][Mp]    signed half-window, bucket order
+  uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
+  int32_t* rowc;    // [G][n_chunks][Mp]  n0 summed over each chunk
+  uint16_t* ub;     // [G][Dp][Np]    B levels
+  long long Mp, Np, Dp;
+  int RT, CT;
+};
+
+static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
+  MfmaWs w{};
+  w.RT = a.tile_start[a.n_rungs];
+  w.CT = (a.N + MF_BN - 1) / MF_BN;
+  w.Mp = (long long)w.RT * MF_BM;
+  w.Np = (long long)w.CT * MF_BN;
+  w.Dp = ((long long)a.D + MF_DC - 1) / MF_DC * MF_DC;
+  auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
+  size_t off = 0;
+  const size_t hs_b = al((size_t)a.G * w.Dp * w.Mp * sizeof(int16_t));
+  const size_t mx_b = al((size_t)a.G * w.RT * w.Dp);
+  const size_t rc_b = al((size_t)a.G * a.n_chunks * w.Mp * sizeof(int32_t));
+  const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
+  char* p = (char*)base;
+  w.hs = (int16_t*)(p ? p + off : nullptr);
+  off += hs_b;
+  w.maxh = (uint8_t*)(p ? p + off : nullptr);
+  off += mx_b;
+  w.rowc = (int32_t*)(p ? p + off : nullptr);
+  off += rc_b;
+  w.ub = (uint16_t*)(p ? p + off : nullptr);
+  off += ub_b;
+  *total = off;
+  return w;
+}
+
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// Load 16 int8 values x[0..16) (bounds-checked, vectorised when aligned).
+__device__ __forceinline__ void load16(const int8_t* src, int valid, int8_t* out) {
+  if (valid >= 16 && (((uintptr_t)src) & 15) == 0) {
+    const int4 v = *(const int4*)src;
+    const int8_t* b = (const int8_t*)&v;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = b[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) out[i] = i < valid ? src[i] : (int8_t)0;
+  }
+}
+
+// ------------------------------------------------------------ prep A ----
+// grid (RT, G), block 256: thread -> (position p = tid % 128, half).
+__global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
+  __shared__ uint16_t s_ncum[MAX_LEVELS];
+  __shared__ int s_mx[2][MF_DC];
+  __shared__ int s_rc[MF_BM];
+  __shared__ int s_rows[MF_BM];
+  const int tid = threadIdx.x;
+  const int y = blockIdx.x, g = blockIdx.y;
+  int k, pos0, nrows;
+  locate_tile(a, y, MF_BM, k, pos0, nrows);
+  const int p = tid & (MF_BM - 1), half = tid >> 7;
+  const int wave = tid >> 6, lane = tid & 63;
+  if (tid < MF_BM) {
+    s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+    s_rc[tid] = 0;
+  }
+  const long long colbase = (long long)y * MF_BM + p;
+  for (int b = 0; b < a.n_bands; ++b) {
+    const int L = a.bandL[b][k];
+    __syncthreads();
+    for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
+    __syncthreads();
+    const int dend = a.band_cols[b + 1];
+    for (int d0 = a.band_cols[b]; d0 < dend; d0 += MF_DC) {
+      const int row = s_rows[p];
+      const int dfirst = d0 + 16 * half;
+      int8_t x[16];
+      const int valid = row >= 0 ? min(16, dend - dfirst) : 0;
+      load16(a.qA + ((long long)g * a.M + (row < 0 ? 0 : row)) * a.D + dfirst, valid, x);
+      int n0s = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        int h = 0;
+        if (i < valid) {
+          const int n1 = s_ncum[level_of((int)x[i], a.P, a.q)];
+          const int diff = 2 * n1 - L;
+          const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
+          h = diff > 0 ? hh : -hh;
+          n0s += L - n1;
+        }
+        const int d = dfirst + i;
+        if (d < w.Dp) w.hs[((long long)g * w.Dp + d) * w.Mp + colbase] = (int16_t)h;
+        const int m = wave_max_i(h < 0 ? -h : h);
+        if (lane == 0) s_mx[wave & 1][16 * half + i] = m;  // waves 0,1 -> half 0; 2,3 -> half 1
+      }
+      atomicAdd(&s_rc[p], n0s);
+      __syncthreads();
+      if (tid < MF_DC) {
+        const int d = d0 + tid;
+        const int m = max(s_mx[0][tid], s_mx[1][tid]);
+        if (d < w.Dp) w.maxh[((long long)g * w.RT + y) * w.Dp + d] = (uint8_t)m;
+      }
+      const bool chunk_done = (a.chunk_d > 0) ? ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)
+                                              : (d0 + MF_DC >= a.D);
+      if (chunk_done) {
+        const int ch = a.chunk_d > 0 ? d0 / a.chunk_d : 0;
+        if (tid < MF_BM) {
+          w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
+          s_rc[tid] = 0;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ------------------------------------------------------------ prep B ----
+// grid (CT, G), block 256: thread -> (column j = tid % 128, half).
+__global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
+  const int tid = threadIdx.x;
+  const int c0 = blockIdx.x * MF_BN, g = blockIdx.y;
+  const int j = tid & (MF_BN - 1), half = tid >> 7;
+  const int col = c0 + j;
+  const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
+  for (int d0 = 0; d0 < w.Dp; d0 += MF_DC) {
+    const int dfirst = d0 + 16 * half;
+    int8_t x[16];
+    const int valid = col < a.N ? max(0, min(16, a.D - dfirst)) : 0;
+    load16(src + dfirst, valid, x);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = i < valid ? level_of((int)x[i], a.P, a.q) : (a.P >> 1);
+      w.ub[((long long)g * w.Dp + dfirst + i) * w.Np + c0 + j] = (uint16_t)u;
+    }
+  }
+}
+
+// ------------------------------------------------------------- main ----
+
+// Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
+// that also write per-band counts keep a third accumulator set and run one.
+template <bool CHUNKED, bool COUNTS>
+__global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, MfmaWs w) {
+  __shared__ __align__(16) uint8_t s_pt[MAX_LEVELS * PT_STRIDE];
+  __shared__ __align__(16) uint32_t s_pat[34 * 4];
+  __shared__ __align__(16) int16_t s_h[2][MF_DC][MF_BM];
+  __shared__ __align__(16) uint16_t s_u[2][MF_DC][MF_BN];
+  __shared__ __align__(16) uint8_t s_mx[2][MF_DC];
+  __shared__ int s_rows[MF_BM];
+  __shared__ int s_rc[MF_BM];      // n0 sum of each row over the chunk being decoded
+  __shared__ float s_sa[MF_BM];    // row scale of that chunk
+
+  const int tid = threadIdx.x;
+  const int g = blockIdx.z, y = blockIdx.y;
+  int k, pos0, nrows;
+  locate_tile(a, y, MF_BM, k, pos0, nrows);
+  const int col0 = blockIdx.x * MF_BN;
+
+  if (tid < MF_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+  if (tid < 34 * 4) {
+    // Window pattern for n leading paired positions (n in [0, 16]) with
+    // sign + (bytes 0x01) or - (bytes 0xff): s_pat[(2 n + neg) * 4 + word].
+    const int pi = tid >> 2, wd = tid & 3, n = pi >> 1;
+    const uint32_t one = (pi & 1) ? 0xffu : 0x01u;
+    uint32_t v = 0;
+    for (int byte = 0; byte < 4; ++byte)
+      if (wd * 4 + byte < n) v |= one << (8 * byte);
+    s_pat[tid] = v;
+  }
+
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int qq = a.q * a.q;
+
+  // Stage loader: thread -> (d = tid / 8, 16 positions / columns).
+  const int ld_d = tid >> 3, ld_part = tid & 7;
+  const long long hs_base = (long long)g * w.Dp * w.Mp + (long long)y * MF_BM + ld_part * 16;
+  const long long ub_base = (long long)g * w.Dp * w.Np + col0 + ld_part * 16;
+  const long long mx_base = ((long long)g * w.RT + y) * w.Dp;
+  int4 rh0, rh1, ru0, ru1;
+  uint32_t rmx = 0;
+  auto fetch = [&](int d0) {
+    const int4* hp = (const int4*)(w.hs + hs_base + (long long)(d0 + ld_d) * w.Mp);
+    const int4* up = (const int4*)(w.ub + ub_base + (long long)(d0 + ld_d) * w.Np);
+    rh0 = hp[0];
+    rh1 = hp[1];
+    ru0 = up[0];
+    ru1 = up[1];
+    if (tid < MF_DC / 4) rmx = *(const uint32_t*)(w.maxh + mx_base + d0 + tid * 4);
+  };
+  auto store = [&](int buf) {
+    int4* hd = (int4*)&s_h[buf][ld_d][ld_part * 16];
+    int4* ud = (int4*)&s_u[buf][ld_d][ld_part * 16];
+    hd[0] = rh0;
+    hd[1] = rh1;
+    ud[0] = ru0;
+    ud[1] = ru1;
+    if (tid < MF_DC / 4) *(uint32_t*)&s_mx[buf][tid * 4] = rmx;
+  };
+
+  v16i acc[2][2];
+  float cacc[2][2][16];
+  int bacc[2][2][16];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        acc[i][j][v] = 0;
+        if (CHUNKED) cacc[i][j][v] = 0.0f;
+        if (COUNTS) bacc[i][j][v] = 0;
+      }
+
+  int buf = 0;
+  fetch(a.band_cols[0]);
+  for (int b = 0; b < a.n_bands; ++b) {
+    const int L = a.bandL[b][k];
+    const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
+    const float scaleL = (float)qq / (float)L;
+    const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
+    __syncthreads();  // every wave is done with the previous band's table
+    {
+      const uint8_t* src = a.pair + a.pair_off[b][k];
+      const int vec_per_row = KLpad >> 4;
+      for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += 256) {
+        const int u = idx / vec_per_row, v = idx - u * vec_per_row;
+        *(int4*)(s_pt + u * PT_STRIDE + v * 16) = *(const int4*)(src + (long long)u * KLpad + v * 16);
+      }
+    }
+    store(buf);
+    __syncthreads();
+    for (int d0 = dbeg; d0 < dend; d0 += MF_DC) {
+      const int dn = d0 + MF_DC;
+      if (dn < a.D) fetch(dn);  // next stage (possibly in the next band) into registers
+      for (int dd = 0; dd < MF_DC; ++dd) {
+        const int steps = (s_mx[buf][dd] + 31) >> 5;
+        if (steps == 0) continue;
+        int ha[2];
+        const uint8_t* bp[2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) ha[i] = s_h[buf][dd][wr * 64 + i * 32 + l32];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) bp[j] = s_pt + (int)s_u[buf][dd][wc * 64 + j * 32 + l32] * PT_STRIDE + hf * 16;
+        for (int s = 0; s < steps; ++s) {
+          const int kk = s * 32 + hf * 16;
+          v4i af[2], bf[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int h = ha[i];
+            int n = (h < 0 ? -h : h) - kk;
+            n = n < 0 ? 0 : (n > 16 ? 16 : n);
+            af[i] = *(const v4i*)(s_pat + ((2 * n + (h < 0 ? 1 : 0)) << 2));
+          }
+#pragma unroll
+          for (int j = 0; j < 2; ++j) bf[j] = *(const v4i*)(bp[j] + s * 32);
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+      }
+      const int cend = chunk_end(a, d0);
+      if (CHUNKED && min(dn, dend) >= cend) {
+        // Chunk complete: add each row's n0 sum, decode with the chunk scales.
+        const int ch = d0 / a.chunk_d;
+        const int cw = cend - ch * a.chunk_d;
+        if (tid < MF_BM) {
+          const int row = s_rows[tid];
+          s_rc[tid] = w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + (long long)y * MF_BM + tid];
+          s_sa[tid] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wc * 64 + j * 32 + l32;
+          const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
+#pragma unroll
+          for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+              const int cnt = acc[i][j][v] + s_rc[r];
+              cacc[i][j][v] += (s_sa[r] * sb) * (scaleL * (float)(2 * cnt - L * cw));
+              if (COUNTS) bacc[i][j][v] += cnt;
+              acc[i][j][v] = 0;
+            }
+        }
+        __syncthreads();  // s_rc / s_sa are rewritten at the next chunk
+      }
+      if (dn < dend) {
+        store(buf ^ 1);
+        __syncthreads();
+        buf ^= 1;
+      }
+    }
+    if (CHUNKED && COUNTS) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          const int col = col0 + wc * 64 + j * 32 + l32;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+            const int row = s_rows[r];
+            if (row >= 0 && col < a.N)
+              a.counts[(((long long)g * a.M + row) * a.N + col) * a.n_bands + b] = bacc[i][j][v];
+            bacc[i][j][v] = 0;
+          }
+        }
+    }
+    if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
+  }
+
+  // Output.
+  const int32_t* rc0 = w.rowc + (long long)g * a.n_chunks * w.Mp + (long long)y * MF_BM;
+  const int L0 = a.bandL[0][k];
+  const float scale0 = (float)qq / (float)L0;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int col = col0 + wc * 64 + j * 32 + l32;
+    const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+        const int row = s_rows[r];
+        if (row < 0 || col >= a.N) continue;
+        float out;
+        if (CHUNKED) {
+          out = cacc[i][j][v];
+        } else {
+          const int cnt = acc[i][j][v] + rc0[r];
+          if (COUNTS) a.counts[((long long)g * a.M + row) * a.N + col] = cnt;
+          const float sa = a.sA[(long long)g * a.M + row];
+          out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
+        }
+        if (a.C) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = out;
+      }
+  }
+}
+
+size_t mfma_workspace_bytes(const MatmulArgs& a) {
+  size_t total = 0;
+  ws_layout(a, nullptr, &total);
+  return total;
+}
+
+int launch_mfma(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+  size_t need = 0;
+  MfmaWs w = ws_layout(a, ws, &need);
+  if (!ws || ws_bytes < need)
+    return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
+  if (w.RT == 0) return SCMP_OK;
+  if (w.RT > 65535 || w.CT > 65535) return set_error(SCMP_ERR_ARG, "too many tiles");
+  hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, a.G), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, a.G), dim3(256), 0, st, a, w);
+  const dim3 grid(w.CT, w.RT, a.G);
+  const bool chunked = a.chunk_d > 0;
+  const bool counts = a.counts != nullptr;
+  if (chunked && counts)
+    hipLaunchKernelGGL((k_mfma<true, true>), grid, dim3(256), 0, st, a, w);
+  else if (chunked)
+    hipLaunchKernelGGL((k_mfma<true, false>), grid, dim3(256), 0, st, a, w);
+  else if (counts)
+    hipLaunchKernelGGL((k_mfma<false, true>), grid, dim3(256), 0, st, a, w);
+  else
+    hipLaunchKernelGGL((k_mfma<false, false>), grid, dim3(256), 0, st, a, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("mfma launch: ") + hipGetErrorString(e));
+  return SCMP_OK;
+}
+
+}  // namespace scmp

@@ -109,8 +109,8 @@ int build_plan(const scmp_plan_desc* d, Plan& P) {
   P.n_rungs = d->n_rungs;
   P.n_bands = d->n_bands;
   P.ceiling = ceiling;
-  if (d->chunk_d > 0 && d->chunk_d % 16 != 0)
-    return set_error(SCMP_ERR_UNSUPPORTED, fmt("chunk_d=%lld must be a multiple of 16", d->chunk_d));
+  if (d->chunk_d > 0 && d->chunk_d % 32 != 0)
+    return set_error(SCMP_ERR_UNSUPPORTED, fmt("chunk_d=%lld must be a multiple of 32", d->chunk_d));
 
   for (int k = 0; k < d->n_rungs; ++k) {
     int L = d->levels[k];

@@ -39,7 +39,8 @@ EXPORTED = [
     "scmp_status_string", "scmp_last_error", "scmp_build_sobol_table", "scmp_table_destroy",
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
-    "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul",
+    "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
+    "scmp_matmul",
     "scmp_decode", "scmp_error_flags",
 ]
 
@@ -97,7 +98,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_plan_row_cuts": (i, [vp, i, ctypes.POINTER(i)]),
         "scmp_quantize_encode": (i, [vp, vp, vp, i, i, i, i64, i64, i64, vp, vp, vp, vp, vp]),
         "scmp_classify_rows": (i, [vp, vp, i, i, vp, vp, vp, vp, vp]),
-        "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp]),
+        "scmp_matmul_workspace_bytes": (i, [vp, vp, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]),
+        "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
         "scmp_decode": (i, [vp, i, i, i, vp, vp, vp, vp, vp, i64, i64, vp]),
         "scmp_error_flags": (i, [vp, ctypes.POINTER(i)]),
     }
@@ -319,9 +321,19 @@ def scmp_classify_rows(plan: Plan, metric: torch.Tensor, ghat_out=None, rung_out
     return ghat_out, rung_out, perm_out, thresholds_out
 
 
+def scmp_matmul_workspace_bytes(table: Table, plan: Plan, G: int, M: int, N: int, algo: str = "auto") -> int:
+    out = ctypes.c_size_t(0)
+    _check("scmp_matmul_workspace_bytes",
+           load().scmp_matmul_workspace_bytes(table.handle, plan.handle, ALGOS[algo], G, M, N, ctypes.byref(out)))
+    return int(out.value)
+
+
 def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=None, algo: str = "auto",
-                counts_out=None, C_out=None, want_counts: bool = False, want_C: bool = True, stream=None):
+                counts_out=None, C_out=None, want_counts: bool = False, want_C: bool = True, workspace=None,
+                stream=None):
     """SC product of encoded operands.  qA int8 [G, M, D], qB int8 [G, N, D].
+    ``workspace``: uint8 device tensor of at least scmp_matmul_workspace_bytes
+    (allocated here when None).
 
     Returns (counts int32 [G, M, N, n_bands] or None, C float [G, M, N] or None).
     """
@@ -342,12 +354,16 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
     _need(packedB, G * N * D * table.words, "packedB")
     _need(counts_out, G * M * N * plan.n_bands, "counts_out")
     _need(C_out, G * M * N, "C_out")
+    ws_need = scmp_matmul_workspace_bytes(table, plan, G, M, N, algo)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, ws_need, "workspace")
     st = load().scmp_matmul(
         table.handle, plan.handle, ALGOS[algo], G, M, N,
         _ptr(qA3, torch.int8, "qA"), _ptr(sA, torch.float32, "sA"), _ptr(permA, torch.int32, "permA"),
         _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"), _ptr(sB, torch.float32, "sB"),
         _ptr(counts_out, torch.int32, "counts_out"), _ptr(C_out, torch.float32, "C_out"),
-        N, M * N, _stream(stream))
+        N, M * N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check("scmp_matmul", st)
     return counts_out, C_out
 

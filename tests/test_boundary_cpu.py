@@ -109,8 +109,9 @@ def test_plan_argument_errors(kw):
     _err(lambda: scmp.scmp_plan_create(**args), scmp.SCMP_ERR_ARG)
 
 
-def test_chunk_d_must_be_a_multiple_of_16():
+def test_chunk_d_must_be_a_multiple_of_32():
     _err(lambda: scmp.scmp_plan_create(D=256, chunk_d=24, levels=(128,)), scmp.SCMP_ERR_UNSUPPORTED)
+    _err(lambda: scmp.scmp_plan_create(D=256, chunk_d=48, levels=(128,)), scmp.SCMP_ERR_UNSUPPORTED)
 
 
 # ---------------------------------------------------- ladder and row cuts --
@@ -163,7 +164,7 @@ def test_uneven_bands_with_ragged_last_chunk():
 
 def test_device_entry_points_reject_null_handles_without_touching_the_device():
     lib = scmp.load()
-    assert lib.scmp_matmul(None, None, 0, 1, 1, 1, *([None] * 8), 1, 1, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_matmul(None, None, 0, 1, 1, 1, *([None] * 8), 1, 1, None, 0, None) == scmp.SCMP_ERR_ARG
     assert lib.scmp_quantize_encode(None, None, None, 1, 1, 1, 1, 1, 1, None, None, None, None,
                                     None) == scmp.SCMP_ERR_ARG
     assert lib.scmp_classify_rows(None, None, 1, 1, None, None, None, None, None) == scmp.SCMP_ERR_ARG
@@ -175,4 +176,6 @@ def test_device_entry_points_reject_null_handles_without_touching_the_device():
     plan = scmp.scmp_plan_create(D=64, chunk_d=0, levels=(128, 64))
     # shape checks before any launch: cols must equal D
     assert lib.scmp_decode(plan.handle, 1, 1, 1, None, None, None, None, None, 1, 1, None) == scmp.SCMP_ERR_ARG
-    assert lib.scmp_matmul(None, plan.handle, 0, 1, 1, 1, *([None] * 8), 1, 1, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_matmul(None, plan.handle, 0, 1, 1, 1, *([None] * 8), 1, 1, None, 0, None) == scmp.SCMP_ERR_ARG
+    size = ctypes.c_size_t(7)
+    assert lib.scmp_matmul_workspace_bytes(None, plan.handle, 0, 1, 1, 1, ctypes.byref(size)) == scmp.SCMP_ERR_ARG

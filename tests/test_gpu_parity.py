@@ -121,7 +121,7 @@ def test_quantise_bit_exact_rows_chunks_strides(table):
     X[3] = 0.0
     X[5, :64] = 0.0                                  # zero chunk
     X[7, 10] = 2.5 * np.float32(1.0)                 # a few exact ties after scaling
-    for chunk_d in (0, 64, 16):
+    for chunk_d in (0, 64, 32):
         plan = scmp.scmp_plan_create(D=150, chunk_d=chunk_d, levels=(64,))
         print(f"  quantise chunk_d={chunk_d}", flush=True)
         Xt = torch.from_numpy(X).cuda()
