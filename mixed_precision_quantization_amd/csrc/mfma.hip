@@ -31,6 +31,7 @@
 #include <hip/hip_runtime.h>
 
 #include <string>
+#include <vector>
 
 #include "matmul_common.h"
 
@@ -47,6 +48,7 @@ struct MfmaWs {
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_chunks][Mp]  n0 summed over each chunk
   uint16_t* ub;     // [G][Dp][Np]    B levels
+  int32_t* tsteps;  // [G][RT]        32-position steps the tile issues (sum over d)
   long long Mp, Np, Dp;
   int RT, CT;
 };
@@ -64,6 +66,7 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const size_t mx_b = al((size_t)a.G * w.RT * w.Dp);
   const size_t rc_b = al((size_t)a.G * a.n_chunks * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
+  const size_t ts_b = al((size_t)a.G * w.RT * sizeof(int32_t));
   char* p = (char*)base;
   w.hs = (int16_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -73,6 +76,8 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   off += rc_b;
   w.ub = (uint16_t*)(p ? p + off : nullptr);
   off += ub_b;
+  w.tsteps = (int32_t*)(p ? p + off : nullptr);
+  off += ts_b;
   *total = off;
   return w;
 }
@@ -103,6 +108,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ int s_mx[2][MF_DC];
   __shared__ int s_rc[MF_BM];
   __shared__ int s_rows[MF_BM];
+  __shared__ int s_steps;
   const int tid = threadIdx.x;
   const int y = blockIdx.x, g = blockIdx.y;
   int k, pos0, nrows;
@@ -113,6 +119,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
     s_rc[tid] = 0;
   }
+  if (tid == 0) s_steps = 0;
   const long long colbase = (long long)y * MF_BM + p;
   for (int b = 0; b < a.n_bands; ++b) {
     const int L = a.bandL[b][k];
@@ -148,6 +155,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
         const int d = d0 + tid;
         const int m = max(s_mx[0][tid], s_mx[1][tid]);
         if (d < w.Dp) w.maxh[((long long)g * w.RT + y) * w.Dp + d] = (uint8_t)m;
+        atomicAdd(&s_steps, (m + 31) >> 5);
       }
       const bool chunk_done = (a.chunk_d > 0) ? ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)
                                               : (d0 + MF_DC >= a.D);
@@ -161,6 +169,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
       __syncthreads();
     }
   }
+  if (tid == 0) w.tsteps[(long long)g * w.RT + y] = s_steps;
 }
 
 // ------------------------------------------------------------ prep B ----
@@ -185,6 +194,15 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
 }
 
 // ------------------------------------------------------------- main ----
+
+// A fragment for paired positions [kk, kk + 16) of a row whose signed
+// half-window is h: the first clamp(|h| - kk, 0, 16) bytes are the sign
+// (+1 = 0x01, -1 = 0xff), the rest 0; read from the 34-entry pattern table.
+__device__ __forceinline__ v4i a_frag(const uint32_t* pat, int h, int kk) {
+  int n = (h < 0 ? -h : h) - kk;
+  n = n < 0 ? 0 : (n > 16 ? 16 : n);
+  return *(const v4i*)(pat + ((2 * n + (h < 0 ? 1 : 0)) << 2));
+}
 
 // Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
 // that also write per-band counts keep a third accumulator set and run one.
@@ -283,32 +301,52 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     for (int d0 = dbeg; d0 < dend; d0 += MF_DC) {
       const int dn = d0 + MF_DC;
       if (dn < a.D) fetch(dn);  // next stage (possibly in the next band) into registers
-      for (int dd = 0; dd < MF_DC; ++dd) {
-        const int steps = (s_mx[buf][dd] + 31) >> 5;
-        if (steps == 0) continue;
-        int ha[2];
-        const uint8_t* bp[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) ha[i] = s_h[buf][dd][wr * 64 + i * 32 + l32];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bp[j] = s_pt + (int)s_u[buf][dd][wc * 64 + j * 32 + l32] * PT_STRIDE + hf * 16;
-        for (int s = 0; s < steps; ++s) {
-          const int kk = s * 32 + hf * 16;
+      {
+        // Step 0 (paired positions 0..31) of every index of the stage,
+        // branch-free so that LDS reads pipeline across indices; an index
+        // whose window is empty everywhere has all-zero A fragments.
+        const int16_t* hcol = &s_h[buf][0][wr * 64 + l32];
+        const uint16_t* ucol = &s_u[buf][0][wc * 64 + l32];
+#pragma unroll 4
+        for (int dd = 0; dd < MF_DC; ++dd) {
           v4i af[2], bf[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) {
-            const int h = ha[i];
-            int n = (h < 0 ? -h : h) - kk;
-            n = n < 0 ? 0 : (n > 16 ? 16 : n);
-            af[i] = *(const v4i*)(s_pat + ((2 * n + (h < 0 ? 1 : 0)) << 2));
-          }
+          for (int i = 0; i < 2; ++i) af[i] = a_frag(s_pat, hcol[dd * MF_BM + i * 32], hf * 16);
 #pragma unroll
-          for (int j = 0; j < 2; ++j) bf[j] = *(const v4i*)(bp[j] + s * 32);
+          for (int j = 0; j < 2; ++j)
+            bf[j] = *(const v4i*)(s_pt + (int)ucol[dd * MF_BN + j * 32] * PT_STRIDE + hf * 16);
 #pragma unroll
           for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
               acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        }
+        // Further steps only where some row of the tile needs them: a
+        // wave-uniform mask of the stage's indices with a window wider
+        // than 32 paired positions.
+        unsigned long long more = __ballot(s_mx[buf][lane & (MF_DC - 1)] > 32) & 0xffffffffull;
+        while (more) {
+          const int dd = __builtin_ctzll(more);
+          more &= more - 1;
+          const int steps = (s_mx[buf][dd] + 31) >> 5;
+          int ha[2];
+          const uint8_t* bp[2];
+#pragma unroll
+          for (int i = 0; i < 2; ++i) ha[i] = hcol[dd * MF_BM + i * 32];
+#pragma unroll
+          for (int j = 0; j < 2; ++j) bp[j] = s_pt + (int)ucol[dd * MF_BN + j * 32] * PT_STRIDE + hf * 16;
+          for (int st = 1; st < steps; ++st) {
+            v4i af[2], bf[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) af[i] = a_frag(s_pat, ha[i], st * 32 + hf * 16);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) bf[j] = *(const v4i*)(bp[j] + st * 32);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+              for (int j = 0; j < 2; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+          }
         }
       }
       const int cend = chunk_end(a, d0);
@@ -391,6 +429,25 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (a.C) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = out;
       }
   }
+}
+
+int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
+                     unsigned long long* macs) {
+  size_t need = 0;
+  MfmaWs w = ws_layout(a, (void*)ws, &need);
+  if (!ws || ws_bytes < need)
+    return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
+  std::vector<int32_t> steps((size_t)a.G * w.RT);
+  *macs = 0;
+  if (steps.empty()) return SCMP_OK;
+  hipError_t e = hipMemcpyAsync(steps.data(), w.tsteps, steps.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("work readback: ") + hipGetErrorString(e));
+  unsigned long long total = 0;
+  for (int32_t v : steps) total += (unsigned long long)v;
+  // Each step of a 128 x 128 tile is 16 MFMAs of 32 x 32 x 32.
+  *macs = total * (unsigned long long)w.CT * MF_BM * MF_BN * 32ull;
+  return SCMP_OK;
 }
 
 size_t mfma_workspace_bytes(const MatmulArgs& a) {

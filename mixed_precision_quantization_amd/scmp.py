@@ -40,8 +40,7 @@ EXPORTED = [
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
-    "scmp_matmul",
-    "scmp_decode", "scmp_error_flags",
+    "scmp_matmul", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
 ]
 
 
@@ -100,6 +99,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_classify_rows": (i, [vp, vp, i, i, vp, vp, vp, vp, vp]),
         "scmp_matmul_workspace_bytes": (i, [vp, vp, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]),
         "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
+        "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
+                                        ctypes.POINTER(ctypes.c_ulonglong), vp]),
         "scmp_decode": (i, [vp, i, i, i, vp, vp, vp, vp, vp, i64, i64, vp]),
         "scmp_error_flags": (i, [vp, ctypes.POINTER(i)]),
     }
@@ -366,6 +367,17 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
         N, M * N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
     _check("scmp_matmul", st)
     return counts_out, C_out
+
+
+def scmp_matmul_issued_macs(table: Table, plan: Plan, G: int, M: int, N: int, workspace, algo: str = "auto",
+                            stream=None) -> int:
+    """int8 MACs the last MFMA-path matmul with ``workspace`` issued (synchronises)."""
+    out = ctypes.c_ulonglong(0)
+    _check("scmp_matmul_issued_macs",
+           load().scmp_matmul_issued_macs(table.handle, plan.handle, ALGOS[algo], G, M, N,
+                                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                          ctypes.byref(out), _stream(stream)))
+    return int(out.value)
 
 
 def scmp_decode(plan: Plan, counts, sA, sB, rung=None, C_out=None, stream=None):
