@@ -33,68 +33,80 @@ struct ClassifyArgs {
 // Ranking key: the normalised metric, with NaN below every number.
 __device__ __forceinline__ float rank_key(float v) { return v == v ? v : -1.0f; }
 
-// One block per group: max of the metric, g_hat = g / max.
-__global__ void __launch_bounds__(256) k_normalise(ClassifyArgs a) {
-  const int g = blockIdx.x;
+constexpr int CL_ROWS = 64;     // rows ranked per block
+constexpr int CL_WAVES = 8;     // waves per block, each scans 1/8 of every key tile
+constexpr int CL_TILE = 8192;   // keys staged in LDS at a time
+
+// One block ranks 64 rows of one group.  Every block first reduces the
+// group's largest metric itself (so no separate pass is needed), then
+// stages tiles of normalised keys g_j / max in LDS; the 8 waves each count,
+// for their 64 rows, the keys that sort before the row:
+//   rank_i = #{j < i : key_j >= key_i} + #{j > i : key_j > key_i},
+// i.e. descending key, ties by row index.  The keys form a strict total
+// order, so the ranks are a permutation; perm[rank_i] = i and the rung
+// follows from the cuts.
+__global__ void __launch_bounds__(512) k_classify(ClassifyArgs a) {
+  __shared__ float keys[CL_TILE];
+  __shared__ float red[CL_WAVES];
+  __shared__ int part[CL_WAVES][CL_ROWS];
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const float* m = a.metric + (long long)g * a.M;
-  __shared__ float red[4];
+
   float mx = 0.0f;
   bool bad = false;
-  for (int i = threadIdx.x; i < a.M; i += 256) {
-    const float v = m[i];
+  for (int j = tid; j < a.M; j += 512) {
+    const float v = m[j];
     bad |= !__builtin_isfinite(v);
     mx = fmaxf(mx, v);
   }
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+  if (lane == 0) red[wave] = mx;
   __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  float* gh = a.ghat + (long long)g * a.M;
-  for (int i = threadIdx.x; i < a.M; i += 256) gh[i] = mx == 0.0f ? 0.0f : m[i] / mx;
-  if (a.thr && threadIdx.x < a.n_rungs - 1) a.thr[(long long)g * (a.n_rungs - 1) + threadIdx.x] = 1.0f;
-  if (bad) atomicOr(&g_classify_flags, 1);
-}
+  mx = red[0];
+#pragma unroll
+  for (int w = 1; w < CL_WAVES; ++w) mx = fmaxf(mx, red[w]);
+  if (bad && blockIdx.x == 0) atomicOr(&g_classify_flags, 1);
 
-// 64 rows per block, 4 threads per row each scanning a quarter of every
-// tile of keys staged in LDS.  rank_i = #{j : key_j > key_i} +
-// #{j < i : key_j == key_i}; then perm[rank_i] = i and the rung from the
-// cuts.  The keys form a strict total order, so ranks are a permutation.
-__global__ void __launch_bounds__(256) k_rank(ClassifyArgs a) {
-  constexpr int TILE = 4096;
-  __shared__ float keys[TILE];
-  __shared__ int part[4][64];
-  const int g = blockIdx.y;
-  const float* gh = a.ghat + (long long)g * a.M;
-  const int r = threadIdx.x & 63;
-  const int qt = threadIdx.x >> 6;
-  const int i = blockIdx.x * 64 + r;
-  const float ki = i < a.M ? rank_key(gh[i]) : 0.0f;
+  const int i = blockIdx.x * CL_ROWS + lane;
+  const float gi = i < a.M ? (mx == 0.0f ? 0.0f : m[i] / mx) : 0.0f;
+  const float ki = rank_key(gi);
   int rank = 0;
-  for (int t0 = 0; t0 < a.M; t0 += TILE) {
-    const int n = min(TILE, a.M - t0);
+  for (int t0 = 0; t0 < a.M; t0 += CL_TILE) {
+    const int n = min(CL_TILE, a.M - t0);
     __syncthreads();
-    for (int j = threadIdx.x; j < n; j += 256) keys[j] = rank_key(gh[t0 + j]);
+    for (int j = tid; j < n; j += 512) keys[j] = rank_key(mx == 0.0f ? 0.0f : m[t0 + j] / mx);
     __syncthreads();
-    const int per = (n + 3) / 4;
-    const int j0 = qt * per;
-    const int j1 = min(n, j0 + per);
-    for (int j = j0; j < j1; ++j) {
-      const float kj = keys[j];
-      rank += (kj > ki) || (kj == ki && (t0 + j) < i);
-    }
+    const int per = (n + CL_WAVES - 1) / CL_WAVES;
+    const int j0 = wave * per, j1 = min(n, j0 + per);
+    // Keys before row i count when >=, keys after it when >, the row itself
+    // never: [j0, lo_end) with >=, [hi_start, j1) with >.
+    const int li = i - t0;
+    const int lo_end = min(max(li, j0), j1);
+    const int hi_start = min(max(li + 1, j0), j1);
+#pragma unroll 8
+    for (int j = j0; j < lo_end; ++j) rank += keys[j] >= ki;
+#pragma unroll 8
+    for (int j = hi_start; j < j1; ++j) rank += keys[j] > ki;
   }
-  part[qt][r] = rank;
+  part[wave][lane] = rank;
   __syncthreads();
-  if (qt == 0 && i < a.M) {
-    rank = part[0][r] + part[1][r] + part[2][r] + part[3][r];
+  if (wave == 0 && i < a.M) {
+    rank = 0;
+#pragma unroll
+    for (int w = 0; w < CL_WAVES; ++w) rank += part[w][lane];
+    a.ghat[(long long)g * a.M + i] = gi;
     a.perm[(long long)g * a.M + rank] = i;
     int k = 0;
     while (k + 1 < a.n_rungs && rank >= a.cuts[k + 1]) ++k;
     if (a.rung) a.rung[(long long)g * a.M + i] = (uint8_t)k;
     if (a.thr) {
-      for (int kk = 1; kk < a.n_rungs; ++kk)
-        if (rank == a.cuts[kk] - 1) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = gh[i];
+      for (int kk = 1; kk < a.n_rungs; ++kk) {
+        if (rank == a.cuts[kk] - 1) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = gi;
+        if (a.cuts[kk] == 0 && i == 0) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = 1.0f;
+      }
     }
   }
 }
@@ -135,8 +147,7 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   a.n_rungs = P.n_rungs;
   scmp::row_cuts(P, M, a.cuts);
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(scmp::k_normalise, dim3(G), dim3(256), 0, st, a);
-  hipLaunchKernelGGL(scmp::k_rank, dim3((M + 63) / 64, G), dim3(256), 0, st, a);
+  hipLaunchKernelGGL(scmp::k_classify, dim3((M + scmp::CL_ROWS - 1) / scmp::CL_ROWS, G), dim3(512), 0, st, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("classify launch: ") + hipGetErrorString(e));
   return SCMP_OK;
