@@ -46,11 +46,15 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 struct MfmaWs {
   int16_t* hs;      // [G][Dp][Mp]    signed half-window, bucket order
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
-  int32_t* rowc;    // [G][n_chunks][Mp]  n0 summed over each chunk
+  int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
   uint16_t* ub;     // [G][Dp][Np]    B levels
-  int32_t* tsteps;  // [G][RT]        32-position steps the tile issues (sum over d)
+  int32_t* tsteps;  // [G][RT][n_parts] 32-position steps the tile issues (sum over the part)
   long long Mp, Np, Dp;
   int RT, CT;
+  // The encode kernels split the contraction axis into n_parts parts of
+  // part_len columns (whole chunks when chunk_d is set, so a part's n0 sums
+  // are the chunk sums; otherwise the decode adds the parts' partial sums).
+  int n_parts, part_len;
 };
 
 static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
@@ -60,13 +64,26 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   w.Mp = (long long)w.RT * MF_BM;
   w.Np = (long long)w.CT * MF_BN;
   w.Dp = ((long long)a.D + MF_DC - 1) / MF_DC * MF_DC;
+  {
+    // Enough blocks to cover the CUs several times over.
+    const long long tiles = (long long)w.RT * a.G;
+    const int unit = a.chunk_d > 0 ? a.chunk_d : MF_DC;
+    const int units = (a.D + unit - 1) / unit;
+    long long want = tiles > 0 ? (2048 + tiles - 1) / tiles : 1;
+    if (want < 1) want = 1;
+    if (want > units) want = units;
+    const int per = (int)((units + want - 1) / want);
+    w.part_len = per * unit;
+    w.n_parts = (a.D + w.part_len - 1) / w.part_len;
+  }
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   size_t off = 0;
   const size_t hs_b = al((size_t)a.G * w.Dp * w.Mp * sizeof(int16_t));
   const size_t mx_b = al((size_t)a.G * w.RT * w.Dp);
-  const size_t rc_b = al((size_t)a.G * a.n_chunks * w.Mp * sizeof(int32_t));
+  const int rc_parts = a.chunk_d > 0 ? a.n_chunks : w.n_parts;
+  const size_t rc_b = al((size_t)a.G * rc_parts * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
-  const size_t ts_b = al((size_t)a.G * w.RT * sizeof(int32_t));
+  const size_t ts_b = al((size_t)a.G * w.RT * w.n_parts * sizeof(int32_t));
   char* p = (char*)base;
   w.hs = (int16_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -102,7 +119,8 @@ __device__ __forceinline__ void load16(const int8_t* src, int valid, int8_t* out
 }
 
 // ------------------------------------------------------------ prep A ----
-// grid (RT, G), block 256: thread -> (position p = tid % 128, half).
+// grid (RT, n_parts, G), block 256: thread -> (position p = tid % 128, half);
+// the block encodes contraction indices [part * part_len, ...) of one tile.
 __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ uint16_t s_ncum[MAX_LEVELS];
   __shared__ int s_mx[2][MF_DC];
@@ -110,7 +128,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ int s_rows[MF_BM];
   __shared__ int s_steps;
   const int tid = threadIdx.x;
-  const int y = blockIdx.x, g = blockIdx.y;
+  const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, y, MF_BM, k, pos0, nrows);
   const int p = tid & (MF_BM - 1), half = tid >> 7;
@@ -120,14 +138,18 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     s_rc[tid] = 0;
   }
   if (tid == 0) s_steps = 0;
+  const int plo = part * w.part_len;
+  const int phi = min(plo + w.part_len, a.D);
   const long long colbase = (long long)y * MF_BM + p;
   for (int b = 0; b < a.n_bands; ++b) {
+    const int lo = max(a.band_cols[b], plo);
+    const int dend = min(a.band_cols[b + 1], phi);
+    if (lo >= dend) continue;  // uniform over the block
     const int L = a.bandL[b][k];
     __syncthreads();
     for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
     __syncthreads();
-    const int dend = a.band_cols[b + 1];
-    for (int d0 = a.band_cols[b]; d0 < dend; d0 += MF_DC) {
+    for (int d0 = lo; d0 < dend; d0 += MF_DC) {
       const int row = s_rows[p];
       const int dfirst = d0 + 16 * half;
       int8_t x[16];
@@ -157,10 +179,8 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
         if (d < w.Dp) w.maxh[((long long)g * w.RT + y) * w.Dp + d] = (uint8_t)m;
         atomicAdd(&s_steps, (m + 31) >> 5);
       }
-      const bool chunk_done = (a.chunk_d > 0) ? ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)
-                                              : (d0 + MF_DC >= a.D);
-      if (chunk_done) {
-        const int ch = a.chunk_d > 0 ? d0 / a.chunk_d : 0;
+      if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)) {
+        const int ch = d0 / a.chunk_d;
         if (tid < MF_BM) {
           w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
           s_rc[tid] = 0;
@@ -169,18 +189,22 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
       __syncthreads();
     }
   }
-  if (tid == 0) w.tsteps[(long long)g * w.RT + y] = s_steps;
+  if (a.chunk_d <= 0 && tid < MF_BM)
+    w.rowc[((long long)g * w.n_parts + part) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
+  if (tid == 0) w.tsteps[((long long)g * w.RT + y) * w.n_parts + part] = s_steps;
 }
 
 // ------------------------------------------------------------ prep B ----
-// grid (CT, G), block 256: thread -> (column j = tid % 128, half).
+// grid (CT, n_parts, G), block 256: thread -> (column j = tid % 128, half).
 __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int tid = threadIdx.x;
-  const int c0 = blockIdx.x * MF_BN, g = blockIdx.y;
+  const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
+  const int plo = blockIdx.y * w.part_len;
+  const int phi = (int)min((long long)plo + w.part_len, w.Dp);
   const int j = tid & (MF_BN - 1), half = tid >> 7;
   const int col = c0 + j;
   const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
-  for (int d0 = 0; d0 < w.Dp; d0 += MF_DC) {
+  for (int d0 = plo; d0 < phi; d0 += MF_DC) {
     const int dfirst = d0 + 16 * half;
     int8_t x[16];
     const int valid = col < a.N ? max(0, min(16, a.D - dfirst)) : 0;
@@ -403,7 +427,17 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   }
 
   // Output.
-  const int32_t* rc0 = w.rowc + (long long)g * a.n_chunks * w.Mp + (long long)y * MF_BM;
+  if (!CHUNKED) {
+    // Each row's n0 sum over the whole contraction axis: the parts' partial
+    // sums, added once per row into LDS.
+    if (tid < MF_BM) {
+      const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
+      int t = 0;
+      for (int pt = 0; pt < w.n_parts; ++pt) t += rc0[(long long)pt * w.Mp];
+      s_rc[tid] = t;
+    }
+    __syncthreads();
+  }
   const int L0 = a.bandL[0][k];
   const float scale0 = (float)qq / (float)L0;
 #pragma unroll
@@ -421,7 +455,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (CHUNKED) {
           out = cacc[i][j][v];
         } else {
-          const int cnt = acc[i][j][v] + rc0[r];
+          const int cnt = acc[i][j][v] + s_rc[r];
           if (COUNTS) a.counts[((long long)g * a.M + row) * a.N + col] = cnt;
           const float sa = a.sA[(long long)g * a.M + row];
           out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
@@ -437,7 +471,7 @@ int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipSt
   MfmaWs w = ws_layout(a, (void*)ws, &need);
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
-  std::vector<int32_t> steps((size_t)a.G * w.RT);
+  std::vector<int32_t> steps((size_t)a.G * w.RT * w.n_parts);
   *macs = 0;
   if (steps.empty()) return SCMP_OK;
   hipError_t e = hipMemcpyAsync(steps.data(), w.tsteps, steps.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
@@ -462,9 +496,9 @@ int launch_mfma(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st) 
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
   if (w.RT == 0) return SCMP_OK;
-  if (w.RT > 65535 || w.CT > 65535) return set_error(SCMP_ERR_ARG, "too many tiles");
-  hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, a.G), dim3(256), 0, st, a, w);
-  hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, a.G), dim3(256), 0, st, a, w);
+  if (w.RT > 65535 || w.CT > 65535 || w.n_parts > 65535) return set_error(SCMP_ERR_ARG, "too many tiles");
+  hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   const dim3 grid(w.CT, w.RT, a.G);
   const bool chunked = a.chunk_d > 0;
   const bool counts = a.counts != nullptr;
