@@ -26,7 +26,8 @@ struct MatmulArgs {
   const uint16_t* cum;
   int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
   int cuts[SCMP_MAX_RUNGS + 1];
-  int tile_start[SCMP_MAX_RUNGS + 1];
+  int tile_start[SCMP_MAX_RUNGS + 1];   // row tiles of the encode kernels (and bit-serial)
+  int tile_start2[SCMP_MAX_RUNGS + 1];  // row tiles of the matrix-core contraction
   int band_cols[SCMP_MAX_BANDS + 1];
   int bandL[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
   unsigned long long pair_off[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];

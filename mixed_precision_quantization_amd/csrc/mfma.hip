@@ -48,7 +48,7 @@ struct MfmaWs {
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
   uint16_t* ub;     // [G][Dp][Np]    B levels
-  int32_t* tsteps;  // [G][RT][n_parts] 32-position steps the tile issues (sum over the part)
+  unsigned long long* issued;  // 32-position steps the contraction issued, summed over row tiles
   long long Mp, Np, Dp;
   int RT, CT;
   // The encode kernels split the contraction axis into n_parts parts of
@@ -83,7 +83,7 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const int rc_parts = a.chunk_d > 0 ? a.n_chunks : w.n_parts;
   const size_t rc_b = al((size_t)a.G * rc_parts * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
-  const size_t ts_b = al((size_t)a.G * w.RT * w.n_parts * sizeof(int32_t));
+  const size_t ts_b = al(sizeof(unsigned long long));
   char* p = (char*)base;
   w.hs = (int16_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -93,7 +93,7 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   off += rc_b;
   w.ub = (uint16_t*)(p ? p + off : nullptr);
   off += ub_b;
-  w.tsteps = (int32_t*)(p ? p + off : nullptr);
+  w.issued = (unsigned long long*)(p ? p + off : nullptr);
   off += ts_b;
   *total = off;
   return w;
@@ -126,7 +126,6 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ int s_mx[2][MF_DC];
   __shared__ int s_rc[MF_BM];
   __shared__ int s_rows[MF_BM];
-  __shared__ int s_steps;
   const int tid = threadIdx.x;
   const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
@@ -137,7 +136,6 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
     s_rc[tid] = 0;
   }
-  if (tid == 0) s_steps = 0;
   const int plo = part * w.part_len;
   const int phi = min(plo + w.part_len, a.D);
   const long long colbase = (long long)y * MF_BM + p;
@@ -177,7 +175,6 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
         const int d = d0 + tid;
         const int m = max(s_mx[0][tid], s_mx[1][tid]);
         if (d < w.Dp) w.maxh[((long long)g * w.RT + y) * w.Dp + d] = (uint8_t)m;
-        atomicAdd(&s_steps, (m + 31) >> 5);
       }
       if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)) {
         const int ch = d0 / a.chunk_d;
@@ -191,7 +188,6 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   }
   if (a.chunk_d <= 0 && tid < MF_BM)
     w.rowc[((long long)g * w.n_parts + part) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
-  if (tid == 0) w.tsteps[((long long)g * w.RT + y) * w.n_parts + part] = s_steps;
 }
 
 // ------------------------------------------------------------ prep B ----
@@ -201,6 +197,9 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
+  // The contraction (launched after this kernel on the same stream) adds
+  // its issued steps to this counter.
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *w.issued = 0;
   const int j = tid & (MF_BN - 1), half = tid >> 7;
   const int col = c0 + j;
   const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
@@ -228,26 +227,51 @@ __device__ __forceinline__ v4i a_frag(const uint32_t* pat, int h, int kk) {
   return *(const v4i*)(pat + ((2 * n + (h < 0 ? 1 : 0)) << 2));
 }
 
+// Tile shape of the contraction: 4 waves as 2 x 2, each owning WR row
+// subtiles and 2 column subtiles of 32 x 32.  WR = 4 (256 x 128 blocks, 16
+// indices per LDS stage) reuses every gathered B fragment four times; the
+// chunked variants keep WR = 2 (128 x 128, 32 indices per stage) because
+// they also hold float accumulators.
+template <int WR>
+struct MfTile {
+  static constexpr int BM = 64 * WR;
+  static constexpr int BN = 128;
+  static constexpr int DC = WR == 2 ? 32 : 16;
+  static constexpr int SUB = BM / MF_BM;  // 128-row encode tiles per block
+};
+
 // Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
 // that also write per-band counts keep a third accumulator set and run one.
-template <bool CHUNKED, bool COUNTS>
+template <bool CHUNKED, bool COUNTS, int WR>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, MfmaWs w) {
+  using T = MfTile<WR>;
+  constexpr int BM = T::BM, BN = T::BN, DC = T::DC, SUB = T::SUB;
+  constexpr int H_PER = DC * BM / 8 / 256;  // 16-byte h chunks each thread stages
+  constexpr int U_PER = DC * BN / 8 / 256;  // 16-byte level chunks each thread stages
   __shared__ __align__(16) uint8_t s_pt[MAX_LEVELS * PT_STRIDE];
   __shared__ __align__(16) uint32_t s_pat[34 * 4];
-  __shared__ __align__(16) int16_t s_h[2][MF_DC][MF_BM];
-  __shared__ __align__(16) uint16_t s_u[2][MF_DC][MF_BN];
-  __shared__ __align__(16) uint8_t s_mx[2][MF_DC];
-  __shared__ int s_rows[MF_BM];
-  __shared__ int s_rc[MF_BM];      // n0 sum of each row over the chunk being decoded
-  __shared__ float s_sa[MF_BM];    // row scale of that chunk
+  __shared__ __align__(16) int16_t s_h[2][DC][BM];
+  __shared__ __align__(16) uint16_t s_u[2][DC][BN];
+  __shared__ __align__(16) uint8_t s_mx[2][DC];
+  __shared__ int s_rows[BM];
+  __shared__ int s_rc[BM];      // n0 sum of each row over the chunk (or axis) being decoded
+  __shared__ float s_sa[BM];    // row scale of that chunk
 
   const int tid = threadIdx.x;
   const int g = blockIdx.z, y = blockIdx.y;
-  int k, pos0, nrows;
-  locate_tile(a, y, MF_BM, k, pos0, nrows);
-  const int col0 = blockIdx.x * MF_BN;
+  // Row tile: BM consecutive sorted positions of one rung, covering the
+  // encode tiles T0 .. T0 + nsub - 1 (128 rows each).
+  int k = 0;
+  while (k + 1 < a.n_rungs && y >= a.tile_start2[k + 1]) ++k;
+  const int t = y - a.tile_start2[k];
+  const int pos0 = a.cuts[k] + t * BM;
+  const int nrows = min(BM, a.cuts[k + 1] - pos0);
+  const int T0 = a.tile_start[k] + t * SUB;
+  const int nsub = min(SUB, a.tile_start[k + 1] - T0);
+  const long long prow0 = (long long)T0 * MF_BM;
+  const int col0 = blockIdx.x * BN;
 
-  if (tid < MF_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+  for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
   if (tid < 34 * 4) {
     // Window pattern for n leading paired positions (n in [0, 16]) with
     // sign + (bytes 0x01) or - (bytes 0xff): s_pat[(2 n + neg) * 4 + word].
@@ -263,38 +287,49 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int wr = wave >> 1, wc = wave & 1;
   const int l32 = lane & 31, hf = lane >> 5;
   const int qq = a.q * a.q;
+  const int wrow0 = wr * 32 * WR;  // first row of this wave
+  const int wcol0 = wc * 64;       // first column of this wave
 
-  // Stage loader: thread -> (d = tid / 8, 16 positions / columns).
-  const int ld_d = tid >> 3, ld_part = tid & 7;
-  const long long hs_base = (long long)g * w.Dp * w.Mp + (long long)y * MF_BM + ld_part * 16;
-  const long long ub_base = (long long)g * w.Dp * w.Np + col0 + ld_part * 16;
-  const long long mx_base = ((long long)g * w.RT + y) * w.Dp;
-  int4 rh0, rh1, ru0, ru1;
-  uint32_t rmx = 0;
+  // Stage loader: 16-byte chunks of h ([d][position]) and levels ([d][column]),
+  // two h chunks and U_PER level chunks per thread (named registers, so
+  // they stay in VGPRs).
+  static_assert(H_PER == 2 && (U_PER == 1 || U_PER == 2), "stage loader shape");
+  int4 rh0, rh1, ru0, ru1 = int4{0, 0, 0, 0};
+  int rmx = 0;
+  auto h_src = [&](int d0, int e) -> int4 {
+    const int dd = e / (BM / 8), cp = (e % (BM / 8)) * 8;
+    return cp < nsub * MF_BM ? *(const int4*)(w.hs + ((long long)g * w.Dp + d0 + dd) * w.Mp + prow0 + cp)
+                             : int4{0, 0, 0, 0};
+  };
+  auto u_src = [&](int d0, int e) -> int4 {
+    const int dd = e / (BN / 8), cc = (e % (BN / 8)) * 8;
+    return *(const int4*)(w.ub + ((long long)g * w.Dp + d0 + dd) * w.Np + col0 + cc);
+  };
   auto fetch = [&](int d0) {
-    const int4* hp = (const int4*)(w.hs + hs_base + (long long)(d0 + ld_d) * w.Mp);
-    const int4* up = (const int4*)(w.ub + ub_base + (long long)(d0 + ld_d) * w.Np);
-    rh0 = hp[0];
-    rh1 = hp[1];
-    ru0 = up[0];
-    ru1 = up[1];
-    if (tid < MF_DC / 4) rmx = *(const uint32_t*)(w.maxh + mx_base + d0 + tid * 4);
+    rh0 = h_src(d0, tid);
+    rh1 = h_src(d0, tid + 256);
+    ru0 = u_src(d0, tid);
+    if constexpr (U_PER > 1) ru1 = u_src(d0, tid + 256);
+    if (tid < DC) {
+      const uint8_t* mp = w.maxh + ((long long)g * w.RT + T0) * w.Dp + d0 + tid;
+      int m = mp[0];
+      for (int sb = 1; sb < nsub; ++sb) m = max(m, (int)mp[(long long)sb * w.Dp]);
+      rmx = m;
+    }
   };
-  auto store = [&](int buf) {
-    int4* hd = (int4*)&s_h[buf][ld_d][ld_part * 16];
-    int4* ud = (int4*)&s_u[buf][ld_d][ld_part * 16];
-    hd[0] = rh0;
-    hd[1] = rh1;
-    ud[0] = ru0;
-    ud[1] = ru1;
-    if (tid < MF_DC / 4) *(uint32_t*)&s_mx[buf][tid * 4] = rmx;
+  auto store = [&](int bf) {
+    *(int4*)&s_h[bf][tid / (BM / 8)][(tid % (BM / 8)) * 8] = rh0;
+    *(int4*)&s_h[bf][(tid + 256) / (BM / 8)][((tid + 256) % (BM / 8)) * 8] = rh1;
+    *(int4*)&s_u[bf][tid / (BN / 8)][(tid % (BN / 8)) * 8] = ru0;
+    if constexpr (U_PER > 1) *(int4*)&s_u[bf][(tid + 256) / (BN / 8)][((tid + 256) % (BN / 8)) * 8] = ru1;
+    if (tid < DC) s_mx[bf][tid] = (uint8_t)rmx;
   };
 
-  v16i acc[2][2];
-  float cacc[2][2][16];
-  int bacc[2][2][16];
+  v16i acc[WR][2];
+  float cacc[WR][2][16];
+  int bacc[WR][2][16];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < WR; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -303,6 +338,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (CHUNKED) cacc[i][j][v] = 0.0f;
         if (COUNTS) bacc[i][j][v] = 0;
       }
+  unsigned long long issued = 0;  // MFMA steps this row tile issues (counted by the x == 0 blocks)
 
   int buf = 0;
   fetch(a.band_cols[0]);
@@ -322,77 +358,108 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     store(buf);
     __syncthreads();
-    for (int d0 = dbeg; d0 < dend; d0 += MF_DC) {
-      const int dn = d0 + MF_DC;
+    for (int d0 = dbeg; d0 < dend; d0 += DC) {
+      const int dn = d0 + DC;
       if (dn < a.D) fetch(dn);  // next stage (possibly in the next band) into registers
       {
-        // Step 0 (paired positions 0..31) of every index of the stage,
-        // branch-free so that LDS reads pipeline across indices; an index
-        // whose window is empty everywhere has all-zero A fragments.
-        const int16_t* hcol = &s_h[buf][0][wr * 64 + l32];
-        const uint16_t* ucol = &s_u[buf][0][wc * 64 + l32];
-#pragma unroll 4
-        for (int dd = 0; dd < MF_DC; ++dd) {
-          v4i af[2], bf[2];
+        // One MFMA step: each half of the wave (hf) contracts 16 paired
+        // positions [kk, kk + 16) of staged index dd; the A fragments are its
+        // rows' window bytes, the B fragments its columns' pair sums.  When
+        // the two halves take different indices the step covers the first
+        // 16 positions of two indices at once.
+        const int16_t* hcol = &s_h[buf][0][wrow0 + l32];
+        const uint16_t* ucol = &s_u[buf][0][wcol0 + l32];
+        unsigned steps = 0;  // wave-uniform count of MFMA steps
+        auto step = [&](int dd, int kk) __attribute__((always_inline)) {
+          v4i af[WR], bfr[2];
 #pragma unroll
-          for (int i = 0; i < 2; ++i) af[i] = a_frag(s_pat, hcol[dd * MF_BM + i * 32], hf * 16);
+          for (int i = 0; i < WR; ++i) af[i] = a_frag(s_pat, hcol[dd * BM + i * 32], kk);
 #pragma unroll
-          for (int j = 0; j < 2; ++j)
-            bf[j] = *(const v4i*)(s_pt + (int)ucol[dd * MF_BN + j * 32] * PT_STRIDE + hf * 16);
+          for (int jj = 0; jj < 2; ++jj)
+            bfr[jj] = *(const v4i*)(s_pt + (int)ucol[dd * BN + jj * 32] * PT_STRIDE + kk);
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < WR; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
-        }
-        // Further steps only where some row of the tile needs them: a
-        // wave-uniform mask of the stage's indices with a window wider
-        // than 32 paired positions.
-        unsigned long long more = __ballot(s_mx[buf][lane & (MF_DC - 1)] > 32) & 0xffffffffull;
-        while (more) {
-          const int dd = __builtin_ctzll(more);
-          more &= more - 1;
-          const int steps = (s_mx[buf][dd] + 31) >> 5;
-          int ha[2];
-          const uint8_t* bp[2];
-#pragma unroll
-          for (int i = 0; i < 2; ++i) ha[i] = hcol[dd * MF_BM + i * 32];
-#pragma unroll
-          for (int j = 0; j < 2; ++j) bp[j] = s_pt + (int)ucol[dd * MF_BN + j * 32] * PT_STRIDE + hf * 16;
-          for (int st = 1; st < steps; ++st) {
-            v4i af[2], bf[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) af[i] = a_frag(s_pat, ha[i], st * 32 + hf * 16);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) bf[j] = *(const v4i*)(bp[j] + st * 32);
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-              for (int j = 0; j < 2; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int jj = 0; jj < 2; ++jj)
+              acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+          ++steps;
+        };
+        const int mx_lane = s_mx[buf][lane & (DC - 1)];
+        const unsigned long long dmask = (1ull << DC) - 1;
+        constexpr int UNR = CHUNKED ? 1 : (WR > 2 ? 2 : 4);
+        // Narrow stage (most indices' tile windows within 16 positions):
+        // positions [0, 16) of indices 2m (lanes 0-31) and 2m + 1 (lanes
+        // 32-63) in one step, then 32-position steps from position 16 for
+        // the wider indices.  Wide stage: 32-position steps from position 0.
+        // Either way a band of positions is swept branch-free when most
+        // indices need it and one index at a time otherwise; windows nest,
+        // so the first empty band ends the stage.
+        if constexpr (CHUNKED) {
+          // The chunked variants also hold float accumulators; to stay within
+          // two waves' registers they keep the simplest schedule: steps of 32
+          // positions from position 0 (a branch-free sweep for the first),
+          // further steps one index at a time where the tile window needs them.
+#pragma unroll 1
+          for (int dd = 0; dd < DC; ++dd) step(dd, hf * 16);
+          for (int sb = 1; sb < 4; ++sb) {
+            unsigned long long need = __ballot(mx_lane > 32 * sb) & dmask;
+            if (need == 0) break;
+            while (need) {
+              const int dd = __builtin_ctzll(need);
+              need &= need - 1;
+              step(dd, 32 * sb + 16 * hf);
+            }
+          }
+        } else {
+          const unsigned long long wide16 = __ballot(mx_lane > 16) & dmask;
+          const bool narrow = 2 * __builtin_popcountll(wide16) <= DC;
+          int base;
+          if (narrow) {
+#pragma unroll UNR
+            for (int m = 0; m < DC / 2; ++m) step(2 * m + hf, 0);
+            base = 16;
+          } else {
+            base = 0;
+          }
+          for (int sb = 0; sb < 4; ++sb) {
+            const int lo = base + 32 * sb;
+            unsigned long long need = __ballot(mx_lane > lo) & dmask;
+            if (need == 0) break;
+            const int kk = lo + 16 * hf;
+            if (2 * __builtin_popcountll(need) >= DC) {
+#pragma unroll UNR
+              for (int dd = 0; dd < DC; ++dd) step(dd, kk);
+            } else {
+              while (need) {
+                const int dd = __builtin_ctzll(need);
+                need &= need - 1;
+                step(dd, kk);
+              }
+            }
           }
         }
+        if (blockIdx.x == 0 && tid == 0) issued += steps;
       }
       const int cend = chunk_end(a, d0);
       if (CHUNKED && min(dn, dend) >= cend) {
         // Chunk complete: add each row's n0 sum, decode with the chunk scales.
         const int ch = d0 / a.chunk_d;
         const int cw = cend - ch * a.chunk_d;
-        if (tid < MF_BM) {
-          const int row = s_rows[tid];
-          s_rc[tid] = w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + (long long)y * MF_BM + tid];
-          s_sa[tid] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
+        for (int r = tid; r < BM; r += 256) {
+          const int row = s_rows[r];
+          s_rc[r] = r < nsub * MF_BM ? w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + prow0 + r] : 0;
+          s_sa[r] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = col0 + wc * 64 + j * 32 + l32;
+          const int col = col0 + wcol0 + j * 32 + l32;
           const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
 #pragma unroll
-          for (int i = 0; i < 2; ++i)
+          for (int i = 0; i < WR; ++i)
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
-              const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+              const int r = wrow0 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
               const int cnt = acc[i][j][v] + s_rc[r];
               cacc[i][j][v] += (s_sa[r] * sb) * (scaleL * (float)(2 * cnt - L * cw));
               if (COUNTS) bacc[i][j][v] += cnt;
@@ -409,13 +476,13 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (CHUNKED && COUNTS) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < WR; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          const int col = col0 + wc * 64 + j * 32 + l32;
+          const int col = col0 + wcol0 + j * 32 + l32;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+            const int r = wrow0 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
             const int row = s_rows[r];
             if (row >= 0 && col < a.N)
               a.counts[(((long long)g * a.M + row) * a.N + col) * a.n_bands + b] = bacc[i][j][v];
@@ -425,16 +492,18 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
   }
+  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued, issued);
 
-  // Output.
   if (!CHUNKED) {
     // Each row's n0 sum over the whole contraction axis: the parts' partial
     // sums, added once per row into LDS.
-    if (tid < MF_BM) {
-      const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
-      int t = 0;
-      for (int pt = 0; pt < w.n_parts; ++pt) t += rc0[(long long)pt * w.Mp];
-      s_rc[tid] = t;
+    for (int r = tid; r < BM; r += 256) {
+      int tot = 0;
+      if (r < nsub * MF_BM) {
+        const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + prow0 + r;
+        for (int pt = 0; pt < w.n_parts; ++pt) tot += rc0[(long long)pt * w.Mp];
+      }
+      s_rc[r] = tot;
     }
     __syncthreads();
   }
@@ -442,13 +511,13 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const float scale0 = (float)qq / (float)L0;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    const int col = col0 + wc * 64 + j * 32 + l32;
+    const int col = col0 + wcol0 + j * 32 + l32;
     const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < WR; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int r = wr * 64 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
+        const int r = wrow0 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
         const int row = s_rows[r];
         if (row < 0 || col >= a.N) continue;
         float out;
@@ -465,22 +534,23 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   }
 }
 
+// Row subtiles per wave for a plan.
+static int mfma_wr(const MatmulArgs&) { return 2; }
+
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
                      unsigned long long* macs) {
   size_t need = 0;
   MfmaWs w = ws_layout(a, (void*)ws, &need);
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
-  std::vector<int32_t> steps((size_t)a.G * w.RT * w.n_parts);
-  *macs = 0;
-  if (steps.empty()) return SCMP_OK;
-  hipError_t e = hipMemcpyAsync(steps.data(), w.tsteps, steps.size() * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  unsigned long long steps = 0;
+  hipError_t e = hipMemcpyAsync(&steps, w.issued, sizeof steps, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("work readback: ") + hipGetErrorString(e));
-  unsigned long long total = 0;
-  for (int32_t v : steps) total += (unsigned long long)v;
-  // Each step of a 128 x 128 tile is 16 MFMAs of 32 x 32 x 32.
-  *macs = total * (unsigned long long)w.CT * MF_BM * MF_BN * 32ull;
+  // Every step of a BM x 128 tile is 2 WR MFMAs per wave, 4 waves, of
+  // 32 x 32 x 32 MACs: BM * 128 * 32 MACs, issued by each column tile.
+  const unsigned long long BM = 64ull * mfma_wr(a);
+  *macs = steps * (unsigned long long)w.CT * BM * 128ull * 32ull;
   return SCMP_OK;
 }
 
@@ -490,26 +560,39 @@ size_t mfma_workspace_bytes(const MatmulArgs& a) {
   return total;
 }
 
-int launch_mfma(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st) {
+static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStream_t st) {
+  const bool counts = a.counts != nullptr;
+  if (a.chunk_d > 0) {
+    if (counts)
+      hipLaunchKernelGGL((k_mfma<true, true, 2>), grid, dim3(256), 0, st, a, w);
+    else
+      hipLaunchKernelGGL((k_mfma<true, false, 2>), grid, dim3(256), 0, st, a, w);
+  } else {
+    if (counts)
+      hipLaunchKernelGGL((k_mfma<false, true, 2>), grid, dim3(256), 0, st, a, w);
+    else
+      hipLaunchKernelGGL((k_mfma<false, false, 2>), grid, dim3(256), 0, st, a, w);
+  }
+}
+
+int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st) {
   size_t need = 0;
+  MatmulArgs a = a0;
   MfmaWs w = ws_layout(a, ws, &need);
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
   if (w.RT == 0) return SCMP_OK;
-  if (w.RT > 65535 || w.CT > 65535 || w.n_parts > 65535) return set_error(SCMP_ERR_ARG, "too many tiles");
+  const int WR = mfma_wr(a);
+  const int BM = 64 * WR;
+  a.tile_start2[0] = 0;
+  for (int k = 0; k < a.n_rungs; ++k)
+    a.tile_start2[k + 1] = a.tile_start2[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
+  const int RT2 = a.tile_start2[a.n_rungs];
+  if (w.RT > 65535 || RT2 > 65535 || w.CT > 65535 || w.n_parts > 65535)
+    return set_error(SCMP_ERR_ARG, "too many tiles");
   hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
-  const dim3 grid(w.CT, w.RT, a.G);
-  const bool chunked = a.chunk_d > 0;
-  const bool counts = a.counts != nullptr;
-  if (chunked && counts)
-    hipLaunchKernelGGL((k_mfma<true, true>), grid, dim3(256), 0, st, a, w);
-  else if (chunked)
-    hipLaunchKernelGGL((k_mfma<true, false>), grid, dim3(256), 0, st, a, w);
-  else if (counts)
-    hipLaunchKernelGGL((k_mfma<false, true>), grid, dim3(256), 0, st, a, w);
-  else
-    hipLaunchKernelGGL((k_mfma<false, false>), grid, dim3(256), 0, st, a, w);
+  launch_main(a, w, dim3(w.CT, RT2, a.G), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("mfma launch: ") + hipGetErrorString(e));
   return SCMP_OK;
