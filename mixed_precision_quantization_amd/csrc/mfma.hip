@@ -17,10 +17,16 @@
 // an exact int8 contraction over ceil(L/2) paired positions per d.
 //
 // Three kernels:
-//  k_prep_rows  per row tile: h = s * hh (int16) in bucket order, laid out
-//               [d][position], the tile's largest hh at each d, and the n0
-//               sum of every row over every chunk ("A side at the row's L").
-//  k_prep_cols  per column tile: B levels, laid out [d][column].
+//  k_prep_rows  per row tile: the window code 16 (2 hh + (s < 0)) (uint16,
+//               the byte offset of the row's A fragment in the pattern table)
+//               in bucket order, laid out [d][position], the tile's largest
+//               hh at each d, and the n0 sum of every row over every chunk
+//               ("A side at the row's L").
+//  k_prep_cols  per column tile: the byte offset of each B level's row in
+//               the paired table (uint16), laid out [d][column].
+// Within every 64 positions (columns) the encode kernels store p and p + 32
+// side by side, so one 32-bit LDS read gives a lane both of its row
+// (column) subtiles.
 //  k_mfma       per (row tile, column tile): stages 32 contraction indices
 //               at a time through double-buffered LDS (one barrier per
 //               stage), visits only the 32-position steps some row of the
@@ -44,10 +50,10 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct MfmaWs {
-  int16_t* hs;      // [G][Dp][Mp]    signed half-window, bucket order
+  uint16_t* hs;     // [G][Dp][Mp]    window code 2 hh + neg, bucket order (interleaved)
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
-  uint16_t* ub;     // [G][Dp][Np]    B levels
+  uint16_t* ub;     // [G][Dp][Np]    paired-table row offset of each B level (interleaved)
   unsigned long long* issued;  // 32-position steps the contraction issued, summed over row tiles
   long long Mp, Np, Dp;
   int RT, CT;
@@ -78,14 +84,14 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   }
   auto al = [](size_t v) { return (v + 255) & ~(size_t)255; };
   size_t off = 0;
-  const size_t hs_b = al((size_t)a.G * w.Dp * w.Mp * sizeof(int16_t));
+  const size_t hs_b = al((size_t)a.G * w.Dp * w.Mp * sizeof(uint16_t));
   const size_t mx_b = al((size_t)a.G * w.RT * w.Dp);
   const int rc_parts = a.chunk_d > 0 ? a.n_chunks : w.n_parts;
   const size_t rc_b = al((size_t)a.G * rc_parts * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
   const size_t ts_b = al(sizeof(unsigned long long));
   char* p = (char*)base;
-  w.hs = (int16_t*)(p ? p + off : nullptr);
+  w.hs = (uint16_t*)(p ? p + off : nullptr);
   off += hs_b;
   w.maxh = (uint8_t*)(p ? p + off : nullptr);
   off += mx_b;
@@ -104,6 +110,10 @@ __device__ __forceinline__ int wave_max_i(int v) {
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
   return v;
 }
+
+// Storage slot of position p of a 128-wide tile: within each 64, p and
+// p + 32 are adjacent (slot 2 (p mod 32) + ((p / 32) mod 2)).
+__device__ __forceinline__ int interleave64(int p) { return (p & 64) | ((p & 31) << 1) | ((p >> 5) & 1); }
 
 // Load 16 int8 values x[0..16) (bounds-checked, vectorised when aligned).
 __device__ __forceinline__ void load16(const int8_t* src, int valid, int8_t* out) {
@@ -138,7 +148,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   }
   const int plo = part * w.part_len;
   const int phi = min(plo + w.part_len, a.D);
-  const long long colbase = (long long)y * MF_BM + p;
+  const long long colbase = (long long)y * MF_BM + interleave64(p);
   for (int b = 0; b < a.n_bands; ++b) {
     const int lo = max(a.band_cols[b], plo);
     const int dend = min(a.band_cols[b + 1], phi);
@@ -156,17 +166,17 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
       int n0s = 0;
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        int h = 0;
+        int hh = 0, code = 0;
         if (i < valid) {
           const int n1 = s_ncum[level_of((int)x[i], a.P, a.q)];
           const int diff = 2 * n1 - L;
-          const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
-          h = diff > 0 ? hh : -hh;
+          hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
+          code = 16 * (2 * hh + (diff < 0 ? 1 : 0));
           n0s += L - n1;
         }
         const int d = dfirst + i;
-        if (d < w.Dp) w.hs[((long long)g * w.Dp + d) * w.Mp + colbase] = (int16_t)h;
-        const int m = wave_max_i(h < 0 ? -h : h);
+        if (d < w.Dp) w.hs[((long long)g * w.Dp + d) * w.Mp + colbase] = (uint16_t)code;
+        const int m = wave_max_i(hh);
         if (lane == 0) s_mx[wave & 1][16 * half + i] = m;  // waves 0,1 -> half 0; 2,3 -> half 1
       }
       atomicAdd(&s_rc[p], n0s);
@@ -211,20 +221,23 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int u = i < valid ? level_of((int)x[i], a.P, a.q) : (a.P >> 1);
-      w.ub[((long long)g * w.Dp + dfirst + i) * w.Np + c0 + j] = (uint16_t)u;
+      w.ub[((long long)g * w.Dp + dfirst + i) * w.Np + c0 + interleave64(j)] = (uint16_t)(u * PT_STRIDE);
     }
   }
 }
 
 // ------------------------------------------------------------- main ----
 
-// A fragment for paired positions [kk, kk + 16) of a row whose signed
-// half-window is h: the first clamp(|h| - kk, 0, 16) bytes are the sign
-// (+1 = 0x01, -1 = 0xff), the rest 0; read from the 34-entry pattern table.
-__device__ __forceinline__ v4i a_frag(const uint32_t* pat, int h, int kk) {
-  int n = (h < 0 ? -h : h) - kk;
-  n = n < 0 ? 0 : (n > 16 ? 16 : n);
-  return *(const v4i*)(pat + ((2 * n + (h < 0 ? 1 : 0)) << 2));
+// A fragment for paired positions [kk, kk + 16) of a row whose window code
+// is c = 16 (2 hh + neg): the first clamp(hh - kk, 0, 16) bytes are the sign
+// (+1 = 0x01, -1 = 0xff), the rest 0.  Entry e of the pattern table holds
+// min(e / 2, 16) sign bytes of sign e mod 2, so the fragment is entry
+// max(2 (hh - kk) + neg, neg): a byte offset of max(c - 32 kk, c & 16).
+__device__ __forceinline__ v4i a_frag(const uint8_t* pat, int c, int kk) {
+  if (__builtin_constant_p(kk) && kk == 0) return *(const v4i*)(pat + c);
+  const int o = c - 32 * kk;
+  const int lo = c & 16;
+  return *(const v4i*)(pat + (o < lo ? lo : o));
 }
 
 // Tile shape of the contraction: 4 waves as 2 x 2, each owning WR row
@@ -249,8 +262,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   constexpr int H_PER = DC * BM / 8 / 256;  // 16-byte h chunks each thread stages
   constexpr int U_PER = DC * BN / 8 / 256;  // 16-byte level chunks each thread stages
   __shared__ __align__(16) uint8_t s_pt[MAX_LEVELS * PT_STRIDE];
-  __shared__ __align__(16) uint32_t s_pat[34 * 4];
-  __shared__ __align__(16) int16_t s_h[2][DC][BM];
+  __shared__ __align__(16) uint32_t s_pat[258 * 4];  // A fragment patterns by window code
+  __shared__ __align__(16) uint16_t s_h[2][DC][BM];
   __shared__ __align__(16) uint16_t s_u[2][DC][BN];
   __shared__ __align__(16) uint8_t s_mx[2][DC];
   __shared__ int s_rows[BM];
@@ -272,15 +285,15 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int col0 = blockIdx.x * BN;
 
   for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
-  if (tid < 34 * 4) {
-    // Window pattern for n leading paired positions (n in [0, 16]) with
-    // sign + (bytes 0x01) or - (bytes 0xff): s_pat[(2 n + neg) * 4 + word].
-    const int pi = tid >> 2, wd = tid & 3, n = pi >> 1;
-    const uint32_t one = (pi & 1) ? 0xffu : 0x01u;
-    uint32_t v = 0;
+  for (int e = tid; e < 258 * 4; e += 256) {
+    // Entry v (words 4 v .. 4 v + 3): n = min(v / 2, 16) leading sign bytes,
+    // 0xff when v is odd (negative window) and 0x01 otherwise.
+    const int v = e >> 2, wd = e & 3, n = min(v >> 1, 16);
+    const uint32_t one = (v & 1) ? 0xffu : 0x01u;
+    uint32_t x = 0;
     for (int byte = 0; byte < 4; ++byte)
-      if (wd * 4 + byte < n) v |= one << (8 * byte);
-    s_pat[tid] = v;
+      if (wd * 4 + byte < n) x |= one << (8 * byte);
+    s_pat[e] = x;
   }
 
   const int lane = tid & 63, wave = tid >> 6;
@@ -367,16 +380,20 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // rows' window bytes, the B fragments its columns' pair sums.  When
         // the two halves take different indices the step covers the first
         // 16 positions of two indices at once.
-        const int16_t* hcol = &s_h[buf][0][wrow0 + l32];
-        const uint16_t* ucol = &s_u[buf][0][wcol0 + l32];
+        static_assert(WR == 2, "the interleaved row codes serve two row subtiles per wave");
+        const uint32_t* hcol = (const uint32_t*)&s_h[buf][0][wrow0] + l32;
+        const uint32_t* ucol = (const uint32_t*)&s_u[buf][0][wcol0] + l32;
         unsigned steps = 0;  // wave-uniform count of MFMA steps
         auto step = [&](int dd, int kk) __attribute__((always_inline)) {
+          const uint32_t hw = hcol[dd * (BM / 2)];   // codes of rows l32 and l32 + 32
+          const uint32_t uw = ucol[dd * (BN / 2)];   // table offsets of columns l32, l32 + 32
+          const int hv[2] = {(int)(hw & 0xffffu), (int)(hw >> 16)};
+          const int uo[2] = {(int)(uw & 0xffffu), (int)(uw >> 16)};
           v4i af[WR], bfr[2];
 #pragma unroll
-          for (int i = 0; i < WR; ++i) af[i] = a_frag(s_pat, hcol[dd * BM + i * 32], kk);
+          for (int i = 0; i < WR; ++i) af[i] = a_frag((const uint8_t*)s_pat, hv[i], kk);
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
-            bfr[jj] = *(const v4i*)(s_pt + (int)ucol[dd * BN + jj * 32] * PT_STRIDE + kk);
+          for (int jj = 0; jj < 2; ++jj) bfr[jj] = *(const v4i*)(s_pt + uo[jj] + kk);
 #pragma unroll
           for (int i = 0; i < WR; ++i)
 #pragma unroll
