@@ -384,26 +384,55 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         const uint32_t* hcol = (const uint32_t*)&s_h[buf][0][wrow0] + l32;
         const uint32_t* ucol = (const uint32_t*)&s_u[buf][0][wcol0] + l32;
         unsigned steps = 0;  // wave-uniform count of MFMA steps
-        auto step = [&](int dd, int kk) __attribute__((always_inline)) {
-          const uint32_t hw = hcol[dd * (BM / 2)];   // codes of rows l32 and l32 + 32
-          const uint32_t uw = ucol[dd * (BN / 2)];   // table offsets of columns l32, l32 + 32
-          const int hv[2] = {(int)(hw & 0xffffu), (int)(hw >> 16)};
-          const int uo[2] = {(int)(uw & 0xffffu), (int)(uw >> 16)};
-          v4i af[WR], bfr[2];
+        struct Frag {
+          v4i a[WR], b[2];
+        };
+        // Codes of staged index dd: the window codes of rows l32 and l32 + 32
+        // (x) and the table offsets of columns l32 and l32 + 32 (y).
+        auto codes = [&](int dd) __attribute__((always_inline)) {
+          return uint2{hcol[dd * (BM / 2)], ucol[dd * (BN / 2)]};
+        };
+        auto frags = [&](uint2 c, int kk) __attribute__((always_inline)) {
+          const int hv[2] = {(int)(c.x & 0xffffu), (int)(c.x >> 16)};
+          const int uo[2] = {(int)(c.y & 0xffffu), (int)(c.y >> 16)};
+          Frag f;
 #pragma unroll
-          for (int i = 0; i < WR; ++i) af[i] = a_frag((const uint8_t*)s_pat, hv[i], kk);
+          for (int i = 0; i < WR; ++i) f.a[i] = a_frag((const uint8_t*)s_pat, hv[i], kk);
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj) bfr[jj] = *(const v4i*)(s_pt + uo[jj] + kk);
+          for (int jj = 0; jj < 2; ++jj) f.b[jj] = *(const v4i*)(s_pt + uo[jj] + kk);
+          return f;
+        };
+        auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
           for (int i = 0; i < WR; ++i)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
-              acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bfr[jj], acc[i][jj], 0, 0, 0);
+              acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
           ++steps;
+        };
+        auto step = [&](int dd, int kk) __attribute__((always_inline)) { mma(frags(codes(dd), kk)); };
+        // Software-pipelined sweep over n >= 1 steps (index of step i:
+        // idx(i), any in-range index past the end): while step i's MFMAs
+        // run, the fragments of step i + 1 and the codes of step i + 2 are
+        // already in flight.  LDS reads complete in order, so the codes are
+        // read one step ahead of the fragments they address.
+        auto sweep = [&](int n, int kk, auto&& idx) __attribute__((always_inline)) {
+          const uint2 c0 = codes(idx(0));  // idx is called in step order
+          uint2 c1 = codes(idx(1));
+          Frag f = frags(c0, kk);
+#pragma unroll 4
+          for (int i = 1; i < n; ++i) {
+            const uint2 c2 = codes(idx(i + 1));
+            const Frag nx = frags(c1, kk);
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+            mma(f);
+            f = nx;
+            c1 = c2;
+          }
+          mma(f);
         };
         const int mx_lane = s_mx[buf][lane & (DC - 1)];
         const unsigned long long dmask = (1ull << DC) - 1;
-        constexpr int UNR = CHUNKED ? 1 : (WR > 2 ? 2 : 4);
         // Narrow stage (most indices' tile windows within 16 positions):
         // positions [0, 16) of indices 2m (lanes 0-31) and 2m + 1 (lanes
         // 32-63) in one step, then 32-position steps from position 16 for
@@ -432,26 +461,30 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           const bool narrow = 2 * __builtin_popcountll(wide16) <= DC;
           int base;
           if (narrow) {
-#pragma unroll UNR
-            for (int m = 0; m < DC / 2; ++m) step(2 * m + hf, 0);
+            sweep(DC / 2, 0, [&](int m) { return (2 * m + hf) & (DC - 1); });
             base = 16;
           } else {
             base = 0;
           }
           for (int sb = 0; sb < 4; ++sb) {
             const int lo = base + 32 * sb;
-            unsigned long long need = __ballot(mx_lane > lo) & dmask;
+            const unsigned long long need = __ballot(mx_lane > lo) & dmask;
             if (need == 0) break;
             const int kk = lo + 16 * hf;
-            if (2 * __builtin_popcountll(need) >= DC) {
-#pragma unroll UNR
-              for (int dd = 0; dd < DC; ++dd) step(dd, kk);
+            const int cnt = __builtin_popcountll(need);
+            if (2 * cnt >= DC) {
+              sweep(DC, kk, [&](int i) { return i & (DC - 1); });
             } else {
-              while (need) {
-                const int dd = __builtin_ctzll(need);
-                need &= need - 1;
-                step(dd, kk);
-              }
+              // The i-th set index of the mask: peel set bits in step order.
+              unsigned long long rest = need;
+              int cur = __builtin_ctzll(rest);
+              sweep(cnt, kk, [&](int i) {
+                (void)i;
+                const int d = cur;
+                rest &= rest - 1;
+                cur = rest ? __builtin_ctzll(rest) : d;
+                return d;
+              });
             }
           }
         }
