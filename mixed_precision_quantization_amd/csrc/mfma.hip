@@ -231,13 +231,11 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
 // A fragment for paired positions [kk, kk + 16) of a row whose window code
 // is c = 16 (2 hh + neg): the first clamp(hh - kk, 0, 16) bytes are the sign
 // (+1 = 0x01, -1 = 0xff), the rest 0.  Entry e of the pattern table holds
-// min(e / 2, 16) sign bytes of sign e mod 2, so the fragment is entry
-// max(2 (hh - kk) + neg, neg): a byte offset of max(c - 32 kk, c & 16).
-__device__ __forceinline__ v4i a_frag(const uint8_t* pat, int c, int kk) {
-  if (__builtin_constant_p(kk) && kk == 0) return *(const v4i*)(pat + c);
-  const int o = c - 32 * kk;
-  const int lo = c & 16;
-  return *(const v4i*)(pat + (o < lo ? lo : o));
+// min(e / 2, 16) sign bytes of sign e mod 2 (entries 0 and 1 are zero), so
+// the fragment sits at byte offset max(c - 32 kk, 0) = 16 (2 (hh - kk) + neg)
+// when hh > kk, and at a zero entry otherwise.  kk32 = 32 kk.
+__device__ __forceinline__ v4i a_frag(const uint8_t* pat, unsigned c, unsigned kk32) {
+  return *(const v4i*)(pat + __builtin_elementwise_sub_sat(c, kk32));
 }
 
 // Tile shape of the contraction: 4 waves as 2 x 2, each owning WR row
@@ -261,14 +259,29 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   constexpr int BM = T::BM, BN = T::BN, DC = T::DC, SUB = T::SUB;
   constexpr int H_PER = DC * BM / 8 / 256;  // 16-byte h chunks each thread stages
   constexpr int U_PER = DC * BN / 8 / 256;  // 16-byte level chunks each thread stages
-  __shared__ __align__(16) uint8_t s_pt[MAX_LEVELS * PT_STRIDE];
-  __shared__ __align__(16) uint32_t s_pat[258 * 4];  // A fragment patterns by window code
+  // The two gather tables share one object (the largest, laid out first) so
+  // that both sit below 64 KB, where a constant base folds into the LDS
+  // instruction's offset: the paired table (one row per B level) and the A
+  // fragment patterns by window code.
+  struct __align__(16) GatherTables {
+    uint8_t pt[MAX_LEVELS * PT_STRIDE];
+    uint32_t pat[258 * 4];
+  };
+  __shared__ GatherTables s_tab;
+  uint8_t* const s_pt = s_tab.pt;
+  uint32_t* const s_pat = s_tab.pat;
   __shared__ __align__(16) uint16_t s_h[2][DC][BM];
   __shared__ __align__(16) uint16_t s_u[2][DC][BN];
-  __shared__ __align__(16) uint8_t s_mx[2][DC];
+  // Stage schedule: the half-blocks past the stage's full levels in order,
+  // then padding entries (a zero half-block), and the number of MFMA steps
+  // they take.
+  constexpr int SCHED_N = DC * 8 + 8;
+  __shared__ uint32_t s_sched[2][SCHED_N];
+  __shared__ int s_nsteps[2];
+  __shared__ int s_full[2];  // leading levels needed by every index of the stage
   __shared__ int s_rows[BM];
-  __shared__ int s_rc[BM];      // n0 sum of each row over the chunk (or axis) being decoded
-  __shared__ float s_sa[BM];    // row scale of that chunk
+  __shared__ __align__(16) int s_rc[BM];      // n0 sum of each row over the chunk (or axis) being decoded
+  __shared__ __align__(16) float s_sa[BM];    // row scale of that chunk
 
   const int tid = threadIdx.x;
   const int g = blockIdx.z, y = blockIdx.y;
@@ -335,7 +348,33 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     *(int4*)&s_h[bf][(tid + 256) / (BM / 8)][((tid + 256) % (BM / 8)) * 8] = rh1;
     *(int4*)&s_u[bf][tid / (BN / 8)][(tid % (BN / 8)) * 8] = ru0;
     if constexpr (U_PER > 1) *(int4*)&s_u[bf][(tid + 256) / (BN / 8)][((tid + 256) % (BN / 8)) * 8] = ru1;
-    if (tid < DC) s_mx[bf][tid] = (uint8_t)rmx;
+    if (tid < 64) {
+      // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
+      // tile maximum rmx) needs positions [16 j, 16 j + 16) for every
+      // j < ceil(rmx / 16); they are listed level by level (j-major),
+      // indices in order within a level.  Entry: low half d * 256 + kk (the
+      // byte offset of index d's codes in a stage row pair, and the first
+      // paired position kk = 16 j), high half 32 kk.
+      const int m = tid < DC ? rmx : 0;
+      // Leading levels that every index needs are swept without a list.
+      int full = 0;
+      while (full < 8 && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
+      int base = 0;
+      for (int j = full; j < 8; ++j) {
+        const unsigned long long bal = __ballot(m > 16 * j);
+        if (bal == 0) break;
+        if (m > 16 * j) {
+          const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
+          s_sched[bf][pos] = ((uint32_t)(512 * j) << 16) | (uint32_t)(tid * 256 + 16 * j);
+        }
+        base += __builtin_popcountll(bal);
+      }
+      // Padding: position 128 is past every window (A bytes all zero).
+      if (tid < 8) s_sched[bf][base + tid] = (4096u << 16) | 128u;
+      if (tid == 0) s_full[bf] = full;
+      if (tid == 0) s_nsteps[bf] = (base + 1) >> 1;
+    }
   };
 
   v16i acc[WR][2];
@@ -375,32 +414,45 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       const int dn = d0 + DC;
       if (dn < a.D) fetch(dn);  // next stage (possibly in the next band) into registers
       {
-        // One MFMA step: each half of the wave (hf) contracts 16 paired
-        // positions [kk, kk + 16) of staged index dd; the A fragments are its
-        // rows' window bytes, the B fragments its columns' pair sums.  When
-        // the two halves take different indices the step covers the first
-        // 16 positions of two indices at once.
+        // Work of a stage: for every staged index d, the 16-position blocks
+        // [16 j, 16 j + 16) of paired positions with j < ceil(mx_d / 16),
+        // mx_d being the largest half-window of the tile's rows at d (rows'
+        // windows nest inside it; past a row's own window its A bytes are 0).
+        // One MFMA step takes two such half-blocks: lanes 0-31 contract the
+        // first (its index's row codes and column levels, positions
+        // [kk, kk + 16)), lanes 32-63 the second; the MFMA sums both halves
+        // into the same accumulators, so any two half-blocks may share a
+        // step.  Step s takes schedule entries 2 s and 2 s + 1; a lone last
+        // half-block is paired with a padding entry.
         static_assert(WR == 2, "the interleaved row codes serve two row subtiles per wave");
-        const uint32_t* hcol = (const uint32_t*)&s_h[buf][0][wrow0] + l32;
-        const uint32_t* ucol = (const uint32_t*)&s_u[buf][0][wcol0] + l32;
-        unsigned steps = 0;  // wave-uniform count of MFMA steps
+        static_assert(DC == 32, "one index per lane of a half-wave");
+        const char* hbase = (const char*)((const uint32_t*)&s_h[buf][0][wrow0] + l32);
+        const char* ubase = (const char*)((const uint32_t*)&s_u[buf][0][wcol0] + l32);
+        const uint32_t* sched = &s_sched[buf][hf];
+        const int n = s_nsteps[buf];
         struct Frag {
           v4i a[WR], b[2];
         };
-        // Codes of staged index dd: the window codes of rows l32 and l32 + 32
-        // (x) and the table offsets of columns l32 and l32 + 32 (y).
-        auto codes = [&](int dd) __attribute__((always_inline)) {
-          return uint2{hcol[dd * (BM / 2)], ucol[dd * (BN / 2)]};
+        // A half-block as this lane sees it: the window codes of rows l32 and
+        // l32 + 32 (h), the table offsets of columns l32 and l32 + 32 (u),
+        // and its schedule entry (e).
+        struct Item {
+          uint32_t h, u, e;
         };
-        auto frags = [&](uint2 c, int kk) __attribute__((always_inline)) {
-          const int hv[2] = {(int)(c.x & 0xffffu), (int)(c.x >> 16)};
-          const int uo[2] = {(int)(c.y & 0xffffu), (int)(c.y >> 16)};
+        auto item = [&](uint32_t e) __attribute__((always_inline)) {
+          const uint32_t off = e & 0x1f00u;
+          return Item{*(const uint32_t*)(hbase + off), *(const uint32_t*)(ubase + off), e};
+        };
+        auto frags_at = [&](uint32_t h, uint32_t u, uint32_t kk, uint32_t kk32) __attribute__((always_inline)) {
           Frag f;
-#pragma unroll
-          for (int i = 0; i < WR; ++i) f.a[i] = a_frag((const uint8_t*)s_pat, hv[i], kk);
-#pragma unroll
-          for (int jj = 0; jj < 2; ++jj) f.b[jj] = *(const v4i*)(s_pt + uo[jj] + kk);
+          f.a[0] = a_frag((const uint8_t*)s_pat, h & 0xffffu, kk32);
+          f.a[1] = a_frag((const uint8_t*)s_pat, h >> 16, kk32);
+          f.b[0] = *(const v4i*)(s_pt + (u & 0xffffu) + kk);
+          f.b[1] = *(const v4i*)(s_pt + (u >> 16) + kk);
           return f;
+        };
+        auto frags = [&](const Item& c) __attribute__((always_inline)) {
+          return frags_at(c.h, c.u, c.e & 0xffu, c.e >> 16);
         };
         auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -408,86 +460,87 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
               acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
-          ++steps;
         };
-        auto step = [&](int dd, int kk) __attribute__((always_inline)) { mma(frags(codes(dd), kk)); };
-        // Software-pipelined sweep over n >= 1 steps (index of step i:
-        // idx(i), any in-range index past the end): while step i's MFMAs
-        // run, the fragments of step i + 1 and the codes of step i + 2 are
-        // already in flight.  LDS reads complete in order, so the codes are
-        // read one step ahead of the fragments they address.
-        auto sweep = [&](int n, int kk, auto&& idx) __attribute__((always_inline)) {
-          const uint2 c0 = codes(idx(0));  // idx is called in step order
-          uint2 c1 = codes(idx(1));
-          Frag f = frags(c0, kk);
-#pragma unroll 4
-          for (int i = 1; i < n; ++i) {
-            const uint2 c2 = codes(idx(i + 1));
-            const Frag nx = frags(c1, kk);
-            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
-            mma(f);
-            f = nx;
+        // Software-pipelined sweep over steps 0 .. cnt - 1, ent(s) giving the
+        // lane's schedule entry of step s (any entry past the end is a zero
+        // half-block): while step s's MFMAs run, the fragments of step s + 1,
+        // the codes of step s + 2 and the entry of step s + 3 are in flight
+        // (LDS reads complete in order, so each is read a step ahead of the
+        // reads it addresses).  Two fragment sets are used in turn.
+        auto sweep = [&](int cnt, auto&& ent) __attribute__((always_inline)) {
+          uint32_t e2 = ent(2);
+          const Item c0 = item(ent(0));
+          Item c1 = item(ent(1));
+          Frag fa = frags(c0), fb;
+          int st = 0;
+          for (; st + 2 < cnt; st += 2) {
+            uint32_t e3 = ent(st + 3);
+            Item c2 = item(e2);
+            fb = frags(c1);
+            e2 = e3;
             c1 = c2;
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+            mma(fa);
+            e3 = ent(st + 4);
+            c2 = item(e2);
+            fa = frags(c1);
+            e2 = e3;
+            c1 = c2;
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
           }
-          mma(f);
+          // Last one or two steps.
+          if (cnt - st == 2) fb = frags(c1);
+          __builtin_amdgcn_sched_barrier(0);
+          mma(fa);
+          if (cnt - st == 2) mma(fb);
         };
-        const int mx_lane = s_mx[buf][lane & (DC - 1)];
-        const unsigned long long dmask = (1ull << DC) - 1;
-        // Narrow stage (most indices' tile windows within 16 positions):
-        // positions [0, 16) of indices 2m (lanes 0-31) and 2m + 1 (lanes
-        // 32-63) in one step, then 32-position steps from position 16 for
-        // the wider indices.  Wide stage: 32-position steps from position 0.
-        // Either way a band of positions is swept branch-free when most
-        // indices need it and one index at a time otherwise; windows nest,
-        // so the first empty band ends the stage.
-        if constexpr (CHUNKED) {
-          // The chunked variants also hold float accumulators; to stay within
-          // two waves' registers they keep the simplest schedule: steps of 32
-          // positions from position 0 (a branch-free sweep for the first),
-          // further steps one index at a time where the tile window needs them.
-#pragma unroll 1
-          for (int dd = 0; dd < DC; ++dd) step(dd, hf * 16);
-          for (int sb = 1; sb < 4; ++sb) {
-            unsigned long long need = __ballot(mx_lane > 32 * sb) & dmask;
-            if (need == 0) break;
-            while (need) {
-              const int dd = __builtin_ctzll(need);
-              need &= need - 1;
-              step(dd, 32 * sb + 16 * hf);
+        // Full levels: step s = 16 j + m takes positions [16 j, 16 j + 16) of
+        // indices 2 m (lanes 0-31) and 2 m + 1 (lanes 32-63).
+        const int full = s_full[buf];
+        if constexpr (!CHUNKED) {
+          // The codes of these 16 index pairs serve every full level: read
+          // once into registers, so a step only forms its fragment addresses.
+          if (full > 0) {
+            uint32_t ch[16], cu[16];
+            const uint32_t* hq = (const uint32_t*)(hbase + 256 * hf);
+            const uint32_t* uq = (const uint32_t*)(ubase + 256 * hf);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) {
+              ch[m] = hq[128 * m];
+              cu[m] = uq[128 * m];
+            }
+            Frag fa = frags_at(ch[0], cu[0], 0u, 0u), fb;
+            for (int j = 0; j < full; ++j) {
+              const uint32_t kk = 16u * j, kk32 = 512u * j;
+#pragma unroll
+              for (int m = 0; m < 16; m += 2) {
+                fb = frags_at(ch[m + 1], cu[m + 1], kk, kk32);
+                __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+                mma(fa);
+                // Next: pair m + 2 of this level, or pair 0 of the next level
+                // (read but unused after the last level; position <= 128
+                // stays inside the table rows).
+                if (m + 2 < 16)
+                  fa = frags_at(ch[m + 2], cu[m + 2], kk, kk32);
+                else
+                  fa = frags_at(ch[0], cu[0], kk + 16u, kk32 + 512u);
+                __builtin_amdgcn_sched_barrier(0);
+                mma(fb);
+              }
             }
           }
         } else {
-          const unsigned long long wide16 = __ballot(mx_lane > 16) & dmask;
-          const bool narrow = 2 * __builtin_popcountll(wide16) <= DC;
-          int base;
-          if (narrow) {
-            sweep(DC / 2, 0, [&](int m) { return (2 * m + hf) & (DC - 1); });
-            base = 16;
-          } else {
-            base = 0;
-          }
-          for (int sb = 0; sb < 4; ++sb) {
-            const int lo = base + 32 * sb;
-            const unsigned long long need = __ballot(mx_lane > lo) & dmask;
-            if (need == 0) break;
-            const int kk = lo + 16 * hf;
-            const int cnt = __builtin_popcountll(need);
-            if (2 * cnt >= DC) {
-              sweep(DC, kk, [&](int i) { return i & (DC - 1); });
-            } else {
-              // The i-th set index of the mask: peel set bits in step order.
-              unsigned long long rest = need;
-              int cur = __builtin_ctzll(rest);
-              sweep(cnt, kk, [&](int i) {
-                (void)i;
-                const int d = cur;
-                rest &= rest - 1;
-                cur = rest ? __builtin_ctzll(rest) : d;
-                return d;
-              });
-            }
-          }
+          // Chunked variants (short of registers for the resident codes).
+          if (full > 0)
+            sweep(16 * full, [&](int st) {
+              const uint32_t j = (uint32_t)(st >> 4) & 7u, d = (uint32_t)(2 * (st & 15) + hf);
+              return ((512u * j) << 16) | (d * 256u + 16u * j);
+            });
         }
+        // The rest from the stage's list.
+        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; });
+        const unsigned steps = n + 16 * full;
         if (blockIdx.x == 0 && tid == 0) issued += steps;
       }
       const int cend = chunk_end(a, d0);
@@ -501,21 +554,34 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           s_sa[r] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
         }
         __syncthreads();
+        float sb[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = col0 + wcol0 + j * 32 + l32;
-          const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
-#pragma unroll
-          for (int i = 0; i < WR; ++i)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-              const int r = wrow0 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
-              const int cnt = acc[i][j][v] + s_rc[r];
-              cacc[i][j][v] += (s_sa[r] * sb) * (scaleL * (float)(2 * cnt - L * cw));
-              if (COUNTS) bacc[i][j][v] += cnt;
-              acc[i][j][v] = 0;
-            }
+          sb[j] = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
         }
+        // Rows four at a time (accumulator entries v = 4 q .. 4 q + 3 are
+        // consecutive rows), used by both column subtiles at once.
+#pragma unroll
+        for (int i = 0; i < WR; ++i)
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
+            const int4 rc = *(const int4*)&s_rc[r0];
+            const float4 sa = *(const float4*)&s_sa[r0];
+            const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
+            const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+              for (int j = 0; j < 2; ++j) {
+                const int v = q4 * 4 + e;
+                const int cnt = acc[i][j][v] + rcv[e];
+                cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * (float)(2 * cnt - L * cw));
+                if (COUNTS) bacc[i][j][v] += cnt;
+                acc[i][j][v] = 0;
+              }
+          }
         __syncthreads();  // s_rc / s_sa are rewritten at the next chunk
       }
       if (dn < dend) {
