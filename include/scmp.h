@@ -65,12 +65,25 @@ typedef enum {
 
 typedef enum { SCMP_OP_LINEAR = 0, SCMP_OP_QK = 1, SCMP_OP_AV = 2 } scmp_op;
 
-/* Contraction kernel.  Both give bit-identical counts.
+/* Contraction kernel.  All give bit-identical counts.
  *  AUTO/MFMA: windowed ternary x paired-binary contraction on the int8
- *             matrix cores (v_mfma_i32_32x32x32_i8).
+ *             matrix cores (v_mfma_i32_32x32x32_i8); the launch form is
+ *             chosen by size (persistent when the plan allows it and there
+ *             are several output tiles per block, one block per tile
+ *             otherwise).
+ *  MFMA_PERSISTENT: the matrix-core path as a persistent grid taking
+ *             output tiles from a work counter; plans without chunk scales
+ *             and with one band only (UNSUPPORTED otherwise).
+ *  MFMA_ONEPASS: the matrix-core path with one block per output tile.
  *  BITSERIAL: one bit-select + popcount per 32 stream positions on the
  *             vector ALU; needs the packed weight-side streams. */
-typedef enum { SCMP_ALGO_AUTO = 0, SCMP_ALGO_BITSERIAL = 1, SCMP_ALGO_MFMA = 2 } scmp_algo;
+typedef enum {
+  SCMP_ALGO_AUTO = 0,
+  SCMP_ALGO_BITSERIAL = 1,
+  SCMP_ALGO_MFMA = 2,
+  SCMP_ALGO_MFMA_PERSISTENT = 3,
+  SCMP_ALGO_MFMA_ONEPASS = 4
+} scmp_algo;
 
 typedef struct scmp_table_s* scmp_table_t; /* opaque, library-owned */
 typedef struct scmp_plan_s* scmp_plan_t;   /* opaque, library-owned, host only */

@@ -31,7 +31,7 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M,
   const Plan& P = plan->plan;
   if (table->p != P.p || table->Lmax != P.Lmax)
     return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
-  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA) return set_error(SCMP_ERR_ARG, "unknown algo");
+  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA_ONEPASS) return set_error(SCMP_ERR_ARG, "unknown algo");
   if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
@@ -50,6 +50,7 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M,
   a.P = 1 << P.p;
   a.Wl = table->Wl;
   a.Lmax = table->Lmax;
+  a.launch = algo == SCMP_ALGO_MFMA_PERSISTENT ? 1 : (algo == SCMP_ALGO_MFMA_ONEPASS ? 2 : 0);
   const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
   fill_tiles(a, P, bitserial ? 64 : 128);
   for (int b = 0; b <= P.n_bands; ++b) a.band_cols[b] = P.band_cols[b];

@@ -25,6 +25,7 @@ struct MatmulArgs {
   const uint8_t* pair;
   const uint16_t* cum;
   int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
+  int launch;  // matrix-core launch form: 0 by size, 1 persistent, 2 one block per tile
   int cuts[SCMP_MAX_RUNGS + 1];
   int tile_start[SCMP_MAX_RUNGS + 1];   // row tiles of the encode kernels (and bit-serial)
   int tile_start2[SCMP_MAX_RUNGS + 1];  // row tiles of the matrix-core contraction

@@ -36,6 +36,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <string>
 #include <vector>
 
@@ -54,7 +55,10 @@ struct MfmaWs {
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
   uint16_t* ub;     // [G][Dp][Np]    paired-table row offset of each B level (interleaved)
+  int32_t* rowid;   // [G][Mp]       original row of each sorted position (-1: none)
+  float* sas;       // [G][Mp]       row scale of each sorted position (single-segment plans)
   unsigned long long* issued;  // 32-position steps the contraction issued, summed over row tiles
+  unsigned int* work;          // work counter of the persistent contraction
   long long Mp, Np, Dp;
   int RT, CT;
   // The encode kernels split the contraction axis into n_parts parts of
@@ -89,7 +93,9 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const int rc_parts = a.chunk_d > 0 ? a.n_chunks : w.n_parts;
   const size_t rc_b = al((size_t)a.G * rc_parts * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
-  const size_t ts_b = al(sizeof(unsigned long long));
+  const size_t ri_b = al((size_t)a.G * w.Mp * sizeof(int32_t));
+  const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
+  const size_t ts_b = al(sizeof(unsigned long long) + sizeof(unsigned int));
   char* p = (char*)base;
   w.hs = (uint16_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -99,7 +105,12 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   off += rc_b;
   w.ub = (uint16_t*)(p ? p + off : nullptr);
   off += ub_b;
+  w.rowid = (int32_t*)(p ? p + off : nullptr);
+  off += ri_b;
+  w.sas = (float*)(p ? p + off : nullptr);
+  off += sa_b;
   w.issued = (unsigned long long*)(p ? p + off : nullptr);
+  w.work = (unsigned int*)(p ? p + off + sizeof(unsigned long long) : nullptr);
   off += ts_b;
   *total = off;
   return w;
@@ -198,6 +209,12 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   }
   if (a.chunk_d <= 0 && tid < MF_BM)
     w.rowc[((long long)g * w.n_parts + part) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
+  if (part == 0 && tid < MF_BM) {
+    const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
+    const int row = s_rows[tid];
+    w.rowid[pos] = row;
+    w.sas[pos] = (a.chunk_d <= 0 && row >= 0) ? a.sA[(long long)g * a.M + row] : 0.0f;
+  }
 }
 
 // ------------------------------------------------------------ prep B ----
@@ -209,7 +226,10 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
   // The contraction (launched after this kernel on the same stream) adds
   // its issued steps to this counter.
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) *w.issued = 0;
+  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
+    *w.issued = 0;
+    *w.work = 0;
+  }
   const int j = tid & (MF_BN - 1), half = tid >> 7;
   const int col = c0 + j;
   const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
@@ -233,9 +253,36 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
 // (+1 = 0x01, -1 = 0xff), the rest 0.  Entry e of the pattern table holds
 // min(e / 2, 16) sign bytes of sign e mod 2 (entries 0 and 1 are zero), so
 // the fragment sits at byte offset max(c - 32 kk, 0) = 16 (2 (hh - kk) + neg)
-// when hh > kk, and at a zero entry otherwise.  kk32 = 32 kk.
+// when hh > kk, and at a zero entry otherwise.  Rows with equal fragments
+// read one address (an LDS broadcast).  kk32 = 32 kk.
+constexpr int PAT_WORDS = 258 * 4;
 __device__ __forceinline__ v4i a_frag(const uint8_t* pat, unsigned c, unsigned kk32) {
   return *(const v4i*)(pat + __builtin_elementwise_sub_sat(c, kk32));
+}
+
+// A fragment patterns: entry v (words 4 v .. 4 v + 3) holds min(v / 2, 16)
+// leading sign bytes, 0xff when v is odd (negative window), 0x01 otherwise.
+__device__ __forceinline__ void init_patterns(uint32_t* pat, int tid, int nthreads) {
+  for (int e = tid; e < PAT_WORDS; e += nthreads) {
+    const int v = e >> 2, wd = e & 3, n = min(v >> 1, 16);
+    const uint32_t one = (v & 1) ? 0xffu : 0x01u;
+    uint32_t x = 0;
+    for (int byte = 0; byte < 4; ++byte)
+      if (wd * 4 + byte < n) x |= one << (8 * byte);
+    pat[e] = x;
+  }
+}
+
+// Copy the paired table of band b, rung k (rows of KLpad bytes, one per B
+// level) into LDS rows of PT_STRIDE bytes.
+__device__ __forceinline__ void stage_pair_table(uint8_t* pt, const MatmulArgs& a, int b, int k, int KLpad, int tid,
+                                                 int nthreads) {
+  const uint8_t* src = a.pair + a.pair_off[b][k];
+  const int vec_per_row = KLpad >> 4;
+  for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += nthreads) {
+    const int u = idx / vec_per_row, v = idx - u * vec_per_row;
+    *(int4*)(pt + u * PT_STRIDE + v * 16) = *(const int4*)(src + (long long)u * KLpad + v * 16);
+  }
 }
 
 // Tile shape of the contraction: 4 waves as 2 x 2, each owning WR row
@@ -265,7 +312,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   // fragment patterns by window code.
   struct __align__(16) GatherTables {
     uint8_t pt[MAX_LEVELS * PT_STRIDE];
-    uint32_t pat[258 * 4];
+    uint32_t pat[PAT_WORDS];
   };
   __shared__ GatherTables s_tab;
   uint8_t* const s_pt = s_tab.pt;
@@ -276,7 +323,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   // then padding entries (a zero half-block), and the number of MFMA steps
   // they take.
   constexpr int SCHED_N = DC * 8 + 8;
-  __shared__ uint32_t s_sched[2][SCHED_N];
+  __shared__ uint16_t s_sched[2][SCHED_N];
   __shared__ int s_nsteps[2];
   __shared__ int s_full[2];  // leading levels needed by every index of the stage
   __shared__ int s_rows[BM];
@@ -298,16 +345,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int col0 = blockIdx.x * BN;
 
   for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
-  for (int e = tid; e < 258 * 4; e += 256) {
-    // Entry v (words 4 v .. 4 v + 3): n = min(v / 2, 16) leading sign bytes,
-    // 0xff when v is odd (negative window) and 0x01 otherwise.
-    const int v = e >> 2, wd = e & 3, n = min(v >> 1, 16);
-    const uint32_t one = (v & 1) ? 0xffu : 0x01u;
-    uint32_t x = 0;
-    for (int byte = 0; byte < 4; ++byte)
-      if (wd * 4 + byte < n) x |= one << (8 * byte);
-    s_pat[e] = x;
-  }
+  init_patterns(s_pat, tid, 256);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
@@ -352,9 +390,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
       // tile maximum rmx) needs positions [16 j, 16 j + 16) for every
       // j < ceil(rmx / 16); they are listed level by level (j-major),
-      // indices in order within a level.  Entry: low half d * 256 + kk (the
-      // byte offset of index d's codes in a stage row pair, and the first
-      // paired position kk = 16 j), high half 32 kk.
+      // indices in order within a level.  Entry: d * 256 + kk (the byte
+      // offset of index d's codes in a stage row pair, and the first paired
+      // position kk = 16 j).
       const int m = tid < DC ? rmx : 0;
       // Leading levels that every index needs are swept without a list.
       int full = 0;
@@ -366,12 +404,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (m > 16 * j) {
           const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-          s_sched[bf][pos] = ((uint32_t)(512 * j) << 16) | (uint32_t)(tid * 256 + 16 * j);
+          s_sched[bf][pos] = (uint16_t)(tid * 256 + 16 * j);
         }
         base += __builtin_popcountll(bal);
       }
       // Padding: position 128 is past every window (A bytes all zero).
-      if (tid < 8) s_sched[bf][base + tid] = (4096u << 16) | 128u;
+      if (tid < 8) s_sched[bf][base + tid] = (uint16_t)128u;
       if (tid == 0) s_full[bf] = full;
       if (tid == 0) s_nsteps[bf] = (base + 1) >> 1;
     }
@@ -400,14 +438,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     const float scaleL = (float)qq / (float)L;
     const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
     __syncthreads();  // every wave is done with the previous band's table
-    {
-      const uint8_t* src = a.pair + a.pair_off[b][k];
-      const int vec_per_row = KLpad >> 4;
-      for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += 256) {
-        const int u = idx / vec_per_row, v = idx - u * vec_per_row;
-        *(int4*)(s_pt + u * PT_STRIDE + v * 16) = *(const int4*)(src + (long long)u * KLpad + v * 16);
-      }
-    }
+    stage_pair_table(s_pt, a, b, k, KLpad, tid, 256);
     store(buf);
     __syncthreads();
     for (int d0 = dbeg; d0 < dend; d0 += DC) {
@@ -428,7 +459,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         static_assert(DC == 32, "one index per lane of a half-wave");
         const char* hbase = (const char*)((const uint32_t*)&s_h[buf][0][wrow0] + l32);
         const char* ubase = (const char*)((const uint32_t*)&s_u[buf][0][wcol0] + l32);
-        const uint32_t* sched = &s_sched[buf][hf];
+        const uint16_t* sched = &s_sched[buf][hf];
         const int n = s_nsteps[buf];
         struct Frag {
           v4i a[WR], b[2];
@@ -452,7 +483,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           return f;
         };
         auto frags = [&](const Item& c) __attribute__((always_inline)) {
-          return frags_at(c.h, c.u, c.e & 0xffu, c.e >> 16);
+          const uint32_t kk = c.e & 0xffu;
+          return frags_at(c.h, c.u, kk, 32u * kk);
         };
         auto mma = [&](const Frag& f) __attribute__((always_inline)) {
 #pragma unroll
@@ -535,11 +567,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           if (full > 0)
             sweep(16 * full, [&](int st) {
               const uint32_t j = (uint32_t)(st >> 4) & 7u, d = (uint32_t)(2 * (st & 15) + hf);
-              return ((512u * j) << 16) | (d * 256u + 16u * j);
+              return d * 256u + 16u * j;
             });
         }
         // The rest from the stage's list.
-        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; });
+        if (n > 0) sweep(n, [&](int st) { return (uint32_t)sched[2 * st]; });
         const unsigned steps = n + 16 * full;
         if (blockIdx.x == 0 && tid == 0) issued += steps;
       }
@@ -650,6 +682,344 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   }
 }
 
+// ------------------------------------------------ persistent variant ----
+// The single-segment contraction (no chunk scales, one band) as a
+// persistent kernel: each block takes 128 x 128 output tiles from a work
+// counter, in rung order, so the paired table is staged again only when the
+// rung changes, and the next tile's row data are read while the current
+// tile is contracted (its output stores then drain behind the next tile's
+// contraction).  Within a tile every wave reads its own row and column
+// codes straight from the encode buffers into registers, one group of 32
+// contraction indices ahead, with no block-wide synchronisation.  Per
+// group, the levels every index needs (16-position half-blocks, as in
+// k_mfma) are swept from those registers; the remaining half-blocks go to a
+// list in this wave's own part of LDS and are contracted, two per step,
+// when the list fills and at the end, with their codes read from the encode
+// buffers a few steps ahead.
+constexpr int FL_LIST = 512;  // list capacity per wave (half-blocks)
+constexpr int FL_RING = 4;    // list steps whose codes are in flight
+constexpr int FL_PAD = 4 * FL_RING + 4;  // padding entries past a list's end
+
+// Work item -> (rung k, group g, encode tile y, column tile x); items run
+// rung by rung, then group, row tile, column tile.
+struct PersItem {
+  int k, g, y, x;
+};
+__device__ __forceinline__ PersItem pers_item(const MatmulArgs& a, int CT, int item) {
+  PersItem it;
+  int k = 0, base = 0;
+  while (k + 1 < a.n_rungs) {
+    const int n = (a.tile_start[k + 1] - a.tile_start[k]) * a.G * CT;
+    if (item < base + n) break;
+    base += n;
+    ++k;
+  }
+  int r = item - base;
+  const int tiles = a.tile_start[k + 1] - a.tile_start[k];
+  it.k = k;
+  it.x = r % CT;
+  r /= CT;
+  it.y = a.tile_start[k] + r % tiles;
+  it.g = r / tiles;
+  return it;
+}
+
+template <bool COUNTS>
+__global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a, MfmaWs w, int n_items) {
+  struct __align__(16) GatherTables {
+    uint8_t pt[MAX_LEVELS * PT_STRIDE];
+    uint32_t pat[PAT_WORDS];
+  };
+  __shared__ GatherTables s_tab;
+  __shared__ uint32_t s_list[4][FL_LIST];
+  __shared__ __align__(16) int s_rows[2][MF_BM];    // original row of each position (-1: none)
+  __shared__ __align__(16) int s_rc[2][MF_BM];      // each row's n0 sum over the contraction axis
+  __shared__ __align__(16) float s_sa[2][MF_BM];    // each row's scale
+  __shared__ int s_item[2];
+  uint8_t* const s_pt = s_tab.pt;
+  uint32_t* const s_pat = s_tab.pat;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int wrow0 = wr * 64, wcol0 = wc * 64;
+  uint32_t* const list = s_list[wave];
+  const int qq = a.q * a.q;
+
+
+  // Row data of tile y in group g for position tid (< 128): original row,
+  // n0 summed over the encode parts, row scale.
+  auto row_data = [&](int g, int y, int& row, int& rc, float& sa) __attribute__((always_inline)) {
+    const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
+    row = w.rowid[pos];
+    sa = w.sas[pos];
+    rc = 0;
+    const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
+    for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
+  };
+
+  init_patterns(s_pat, tid, 256);
+  if (tid == 0) {
+    s_item[0] = (int)atomicAdd(w.work, 1u);
+    s_item[1] = (int)atomicAdd(w.work, 1u);
+  }
+  __syncthreads();
+  int item = s_item[0];
+  if (item >= n_items) return;
+  if (tid < MF_BM) {
+    const PersItem it = pers_item(a, w.CT, item);
+    int row, rc;
+    float sa;
+    row_data(it.g, it.y, row, rc, sa);
+    s_rows[0][tid] = row;
+    s_rc[0][tid] = rc;
+    s_sa[0][tid] = sa;
+  }
+
+  struct Frag {
+    v4i a[2], b[2];
+  };
+  auto frags_at = [&](uint32_t h, uint32_t u, uint32_t kk, uint32_t kk32) __attribute__((always_inline)) {
+    Frag f;
+    f.a[0] = a_frag((const uint8_t*)s_pat, h & 0xffffu, kk32);
+    f.a[1] = a_frag((const uint8_t*)s_pat, h >> 16, kk32);
+    f.b[0] = *(const v4i*)(s_pt + (u & 0xffffu) + kk);
+    f.b[1] = *(const v4i*)(s_pt + (u >> 16) + kk);
+    return f;
+  };
+  // A list entry is (index << 4) | level; level 8 (position 128, past every
+  // window) is the zero half-block used as padding.
+  auto frags_e = [&](uint32_t h, uint32_t u, uint32_t e) __attribute__((always_inline)) {
+    const uint32_t j = e & 15u;
+    return frags_at(h, u, 16u * j, 512u * j);
+  };
+  v16i acc[2][2];
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
+  };
+  unsigned long long issued = 0;  // MFMA steps of the column-0 tiles
+  int staged_k = -1;
+  int cur = 0;
+
+  while (true) {
+    const PersItem it = pers_item(a, w.CT, item);
+    const int k = it.k, g = it.g, y = it.y;
+    const int col0 = it.x * MF_BN;
+    const long long prow0 = (long long)y * MF_BM;
+    const bool count_steps = it.x == 0;
+    const int next = s_item[cur ^ 1];
+    // The next tile's row data, read now and stored after this tile.
+    int nrow = -1, nrc = 0;
+    float nsa = 0.0f;
+    if (next < n_items && tid < MF_BM) {
+      const PersItem nt = pers_item(a, w.CT, next);
+      row_data(nt.g, nt.y, nrow, nrc, nsa);
+    }
+    const int L = a.bandL[0][k];
+    if (k != staged_k) {
+      // Every wave finished the previous tile (the loop ends on a barrier).
+      const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
+      stage_pair_table(s_pt, a, 0, k, KLpad, tid, 256);
+      __syncthreads();
+      staged_k = k;
+    }
+
+    // Uniform bases (the group's part of the buffers at the wave's first
+    // row / column) and 32-bit per-lane word offsets: the host checks that
+    // an index's words stay below 2^31 bytes from the base.
+    const uint32_t hs32 = (uint32_t)(w.Mp / 2), us32 = (uint32_t)(w.Np / 2);  // words per index
+    const uint32_t* hbase = (const uint32_t*)(w.hs + (long long)g * w.Dp * w.Mp + prow0 + wrow0);
+    const uint32_t* ubase = (const uint32_t*)(w.ub + (long long)g * w.Dp * w.Np + col0 + wcol0);
+    const uint8_t* mq = w.maxh + ((long long)g * w.RT + y) * w.Dp;
+    auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hbase[d * hs32 + (uint32_t)l32]; };
+    auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ubase[d * us32 + (uint32_t)l32]; };
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
+
+    // Contract the wave's list of cnt half-blocks, two per step (lanes 0-31
+    // take entry 2 s, lanes 32-63 entry 2 s + 1).  Slot r of the ring holds
+    // the entry and codes of a step FL_RING steps ahead; its fragments are
+    // read one step ahead of its MFMAs.  dpad: any index of the band, for
+    // the padding entries' (unused) codes.
+    auto list_sweep = [&](int cnt, int dpad) __attribute__((always_inline)) {
+      if (lane < FL_PAD) list[cnt + lane] = ((uint32_t)dpad << 4) | 8u;
+      const int nsteps = (cnt + 1) >> 1;
+      uint32_t re[FL_RING], rh[FL_RING], ru[FL_RING];
+#pragma unroll
+      for (int r = 0; r < FL_RING; ++r) {
+        re[r] = list[2 * r + hf];
+        rh[r] = hword(re[r] >> 4);
+        ru[r] = uword(re[r] >> 4);
+      }
+      uint32_t enext = list[2 * FL_RING + hf];
+      Frag fr[2];
+      fr[0] = frags_e(rh[0], ru[0], re[0]);
+      for (int s0 = 0; s0 < nsteps; s0 += FL_RING) {
+#pragma unroll
+        for (int r = 0; r < FL_RING; ++r) {
+          const int rn = (r + 1) % FL_RING;
+          fr[(r + 1) & 1] = frags_e(rh[rn], ru[rn], re[rn]);
+          // Slot r now serves step s0 + r + FL_RING.
+          re[r] = enext;
+          rh[r] = hword(enext >> 4);
+          ru[r] = uword(enext >> 4);
+          enext = list[2 * (s0 + r + FL_RING + 1) + hf];
+          __builtin_amdgcn_sched_barrier(0);
+          if (s0 + r < nsteps) mma(fr[r & 1]);
+        }
+      }
+      if (count_steps) issued += nsteps;
+    };
+
+    const int dbeg = a.band_cols[0], dend = a.band_cols[1];
+    const int ngrp = (dend - dbeg + 31) / 32;
+    // A group's loads: index d0 + 2 mm + hf for this lane's codes (uniform
+    // base of the pair plus the lane's half), and this lane's index maximum
+    // (raw: the band's bound is applied where it is used, so that nothing
+    // waits for the loads here).
+    const uint32_t hlane = (uint32_t)l32 + (uint32_t)hf * hs32, ulane = (uint32_t)l32 + (uint32_t)hf * us32;
+    auto load_group = [&](int d0, uint32_t* h, uint32_t* u, int& m) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mm = 0; mm < 16; ++mm) {
+        const uint32_t* hp = hbase + (size_t)(uint32_t)(d0 + 2 * mm) * hs32;
+        const uint32_t* up = ubase + (size_t)(uint32_t)(d0 + 2 * mm) * us32;
+        h[mm] = hp[hlane];
+        u[mm] = up[ulane];
+      }
+      m = mq[d0 + l32];  // d0 + l32 < Dp
+    };
+    int cnt = 0;  // entries in this wave's list
+    // fa: the fragments of the group's first step (level 0, pair 0), read
+    // at the end of the previous group.
+    Frag fa;
+    // One group: its codes (ch, cu) and this lane's index maximum (mx) are
+    // in registers; nh, nu: the next group's codes.
+    auto group = [&](int grp, const uint32_t* ch, const uint32_t* cu, int mx, const uint32_t* nh,
+                     const uint32_t* nu) __attribute__((always_inline)) {
+      const int d0 = dbeg + 32 * grp;
+      // Index d0 + l32 needs nl half-blocks; the leading levels every index
+      // needs are swept here, the rest listed (level-major).
+      const int nl = d0 + l32 < dend ? (mx + 15) >> 4 : 0;
+      int full = 0;
+      for (int j = 0; j < 8; ++j) {
+        const unsigned bal = (unsigned)__ballot(nl > j);
+        if (bal == 0) break;
+        if (bal == 0xffffffffu && j == full) {
+          ++full;
+          continue;
+        }
+        if (hf == 0 && nl > j)
+          list[cnt + (int)__builtin_amdgcn_mbcnt_lo(bal, 0u)] = ((uint32_t)(d0 + l32) << 4) | (uint32_t)j;
+        cnt += __builtin_popcount(bal);
+      }
+      if (full > 0) {
+        Frag fb;
+        for (int j = 0; j < full; ++j) {
+          const uint32_t kk = 16u * j, kk32 = 512u * j;
+#pragma unroll
+          for (int m = 0; m < 16; m += 2) {
+            fb = frags_at(ch[m + 1], cu[m + 1], kk, kk32);
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+            mma(fa);
+            // Next: pair m + 2 of this level or pair 0 of the next level
+            // (after the last level: read, unused; position <= 128 stays
+            // inside the table rows).
+            if (m + 2 < 16)
+              fa = frags_at(ch[m + 2], cu[m + 2], kk, kk32);
+            else
+              fa = frags_at(ch[0], cu[0], kk + 16u, kk32 + 512u);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
+          }
+        }
+        if (count_steps) issued += 16 * full;
+      }
+      // The next group adds at most 256 entries.
+      if (cnt > FL_LIST - 256 - FL_PAD || (grp == ngrp - 1 && cnt > 0)) {
+        list_sweep(cnt, d0);
+        cnt = 0;
+      }
+      // The next group's first step, read while this group's last MFMAs
+      // run and the next group's levels are counted.
+      fa = frags_at(nh[0], nu[0], 0u, 0u);
+    };
+    // Two register sets in turn: the next group's codes load while this
+    // group is contracted.  The look-ahead loads are unconditional (past the
+    // last group they repeat it), so every path issues the same loads and
+    // the waits for a set count only the loads issued after it.
+    if (ngrp > 0) {
+      uint32_t ha[16], ua[16], hb[16], ub[16];
+      int ma, mb = 0;
+      load_group(dbeg, ha, ua, ma);
+      fa = frags_at(ha[0], ua[0], 0u, 0u);
+      for (int grp = 0; grp < ngrp; grp += 2) {
+        load_group(dbeg + 32 * min(grp + 1, ngrp - 1), hb, ub, mb);
+        group(grp, ha, ua, ma, hb, ub);
+        if (grp + 1 >= ngrp) break;
+        load_group(dbeg + 32 * min(grp + 2, ngrp - 1), ha, ua, ma);
+        group(grp + 1, hb, ub, mb, ha, ua);
+      }
+    }
+
+    // The next tile's row data into the other buffer; the tile after it.
+    if (tid < MF_BM) {
+      s_rows[cur ^ 1][tid] = nrow;
+      s_rc[cur ^ 1][tid] = nrc;
+      s_sa[cur ^ 1][tid] = nsa;
+    }
+    if (tid == 0) s_item[cur] = next < n_items ? (int)atomicAdd(w.work, 1u) : n_items;
+
+    // Decode: rows four at a time (accumulator entries v = 4 q .. 4 q + 3
+    // are consecutive rows), each used by both column subtiles.
+    const float scale0 = (float)qq / (float)L;
+    float sb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wcol0 + j * 32 + l32;
+      sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
+        const int4 rw = *(const int4*)&s_rows[cur][r0];
+        const int4 rc = *(const int4*)&s_rc[cur][r0];
+        const float4 sa = *(const float4*)&s_sa[cur][r0];
+        const int rowv[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
+        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = col0 + wcol0 + j * 32 + l32;
+            if (rowv[e] < 0 || col >= a.N) continue;
+            const int cnt2 = acc[i][j][q4 * 4 + e] + rcv[e];
+            if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
+            if (a.C)
+              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + col] =
+                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D));
+          }
+      }
+    __syncthreads();  // publishes the next tile's row data and item
+    if (next >= n_items) break;
+    item = next;
+    cur ^= 1;
+  }
+  if (tid == 0 && issued) atomicAdd(w.issued, issued);
+}
+
 // Row subtiles per wave for a plan.
 static int mfma_wr(const MatmulArgs&) { return 2; }
 
@@ -676,6 +1046,28 @@ size_t mfma_workspace_bytes(const MatmulArgs& a) {
   return total;
 }
 
+// The persistent kernel handles one band starting on a 32-index boundary,
+// with 32-bit word offsets into the encode buffers and an int item count.
+static bool pers_ok(const MatmulArgs& a, const MfmaWs& w) {
+  if (a.chunk_d > 0 || a.n_bands != 1 || a.band_cols[0] % MF_DC != 0) return false;
+  if ((double)w.Dp * (double)w.Mp * 2.0 >= 2147483648.0) return false;
+  if ((double)w.Dp * (double)w.Np * 2.0 >= 2147483648.0) return false;
+  return (double)a.tile_start[a.n_rungs] * a.G * w.CT < 2147483647.0;
+}
+
+// Compute units of the current device (cached per device).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
 static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStream_t st) {
   const bool counts = a.counts != nullptr;
   if (a.chunk_d > 0) {
@@ -683,6 +1075,17 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
       hipLaunchKernelGGL((k_mfma<true, true, 2>), grid, dim3(256), 0, st, a, w);
     else
       hipLaunchKernelGGL((k_mfma<true, false, 2>), grid, dim3(256), 0, st, a, w);
+  } else if (a.launch == 1 ||
+             (a.launch == 0 && pers_ok(a, w) &&
+              a.tile_start[a.n_rungs] * a.G * w.CT >= 3 * (counts ? 1 : 2) * device_cus())) {
+    // Persistent when every block gets several tiles; a one-pass grid
+    // otherwise (its blocks then need no work counter or table reuse).
+    const int n_items = a.tile_start[a.n_rungs] * a.G * w.CT;
+    const int blocks = std::max(1, std::min(n_items, (counts ? 1 : 2) * device_cus()));
+    if (counts)
+      hipLaunchKernelGGL((k_mfma_pers<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+    else
+      hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
   } else {
     if (counts)
       hipLaunchKernelGGL((k_mfma<false, true, 2>), grid, dim3(256), 0, st, a, w);
@@ -706,6 +1109,9 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
   const int RT2 = a.tile_start2[a.n_rungs];
   if (w.RT > 65535 || RT2 > 65535 || w.CT > 65535 || w.n_parts > 65535)
     return set_error(SCMP_ERR_ARG, "too many tiles");
+  if (a.launch == 1 && !pers_ok(a, w))
+    return set_error(SCMP_ERR_UNSUPPORTED,
+                     "the persistent launch needs a plan without chunk scales, one band and 32-bit buffer offsets");
   hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   launch_main(a, w, dim3(w.CT, RT2, a.G), st);

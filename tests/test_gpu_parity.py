@@ -20,7 +20,15 @@ from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, sample_r
 pytestmark = pytest.mark.gpu
 
 RTOL = 1e-5
-ALGOS = ("mfma", "bitserial")
+# Contraction kernels: the matrix-core path by size, forced persistent or
+# one block per tile, and the bit-serial path.
+ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass")
+
+
+def _skip_unsupported(algo, chunk_d=0, n_bands=1):
+    """The persistent launch takes plans without chunk scales and one band."""
+    if algo == "mfma_persistent" and ((chunk_d or 0) > 0 or n_bands > 1):
+        pytest.skip("the persistent launch needs a single-segment plan (checked in test_persistent_rejects_chunks)")
 
 
 @pytest.fixture(scope="module")
@@ -209,6 +217,7 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_workload_parity(table, name, algo):
     w = shrink(WORKLOADS[name], **SMALL[name]) if SMALL[name] else WORKLOADS[name]
+    _skip_unsupported(algo, w.chunk_d, w.n_bands)
     A, B = _groups(*draw(w))
     plan, okw = _plans(w)
     print(f"  {w.name} G={A.shape[0]} M={w.M} N={w.N} D={w.D}", flush=True)
@@ -220,6 +229,7 @@ def test_small_workload_parity(table, name, algo):
 
 @pytest.mark.parametrize("algo", ALGOS)
 def test_ragged_chunks_and_uneven_bands(table, algo):
+    _skip_unsupported(algo, chunk_d=64, n_bands=2)
     rng = np.random.default_rng(23)
     M, N, D = 150, 90, 150
     A = rng.standard_normal((M, D)).astype(np.float32)
@@ -265,6 +275,17 @@ def test_single_row_and_column_and_empty(table, algo):
     q, s, m, _ = scmp.scmp_quantize_encode(table, plan, e)
     c, C = scmp.scmp_matmul(table, plan, q, s, q, s, algo=algo, want_counts=True)
     assert c.numel() == 0 and C.numel() == 0
+
+
+def test_persistent_rejects_chunks(table):
+    """The forced persistent launch reports UNSUPPORTED for chunk scales."""
+    rng = np.random.default_rng(26)
+    A = torch.from_numpy(rng.standard_normal((40, 128)).astype(np.float32)).cuda()
+    plan = scmp.scmp_plan_create(D=128, chunk_d=64, levels=(64,))
+    q, s, m, _ = scmp.scmp_quantize_encode(table, plan, A)
+    with pytest.raises(scmp.ScmpError) as ei:
+        scmp.scmp_matmul(table, plan, q, s, q, s, algo="mfma_persistent", want_counts=True)
+    assert ei.value.status == scmp.SCMP_ERR_UNSUPPORTED
 
 
 def test_standalone_decode_matches_fused(table):
