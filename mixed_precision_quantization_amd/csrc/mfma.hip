@@ -51,10 +51,14 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct MfmaWs {
-  uint16_t* hs;     // [G][Dp][Mp]    window code 2 hh + neg, bucket order (interleaved)
+  uint32_t* hs;     // [G][Mp/2][Dp]  window codes 16 (2 hh + neg) of a row pair, by index
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
-  uint16_t* ub;     // [G][Dp][Np]    paired-table row offset of each B level (interleaved)
+  uint32_t* ub;     // [G][Np/2][Dp]  paired-table row offsets of a column pair, by index
+  // Single-segment plans also keep the codes index-major (the persistent
+  // contraction's list steps read one index for every pair); else null.
+  uint32_t* hsi;    // [G][Dp][Mp/2]  window code words, by index then row pair
+  uint32_t* ubi;    // [G][Dp][Np/2]  table offset words, by index then column pair
   int32_t* rowid;   // [G][Mp]       original row of each sorted position (-1: none)
   float* sas;       // [G][Mp]       row scale of each sorted position (single-segment plans)
   unsigned long long* issued;  // 32-position steps the contraction issued, summed over row tiles
@@ -93,18 +97,25 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const int rc_parts = a.chunk_d > 0 ? a.n_chunks : w.n_parts;
   const size_t rc_b = al((size_t)a.G * rc_parts * w.Mp * sizeof(int32_t));
   const size_t ub_b = al((size_t)a.G * w.Dp * w.Np * sizeof(uint16_t));
+  const bool index_major = a.chunk_d <= 0 && a.n_bands == 1;
+  const size_t hsi_b = index_major ? hs_b : 0;
+  const size_t ubi_b = index_major ? ub_b : 0;
   const size_t ri_b = al((size_t)a.G * w.Mp * sizeof(int32_t));
   const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
   const size_t ts_b = al(sizeof(unsigned long long) + sizeof(unsigned int));
   char* p = (char*)base;
-  w.hs = (uint16_t*)(p ? p + off : nullptr);
+  w.hs = (uint32_t*)(p ? p + off : nullptr);
   off += hs_b;
   w.maxh = (uint8_t*)(p ? p + off : nullptr);
   off += mx_b;
   w.rowc = (int32_t*)(p ? p + off : nullptr);
   off += rc_b;
-  w.ub = (uint16_t*)(p ? p + off : nullptr);
+  w.ub = (uint32_t*)(p ? p + off : nullptr);
   off += ub_b;
+  w.hsi = (index_major && p) ? (uint32_t*)(p + off) : nullptr;
+  off += hsi_b;
+  w.ubi = (index_major && p) ? (uint32_t*)(p + off) : nullptr;
+  off += ubi_b;
   w.rowid = (int32_t*)(p ? p + off : nullptr);
   off += ri_b;
   w.sas = (float*)(p ? p + off : nullptr);
@@ -122,44 +133,63 @@ __device__ __forceinline__ int wave_max_i(int v) {
   return v;
 }
 
-// Storage slot of position p of a 128-wide tile: within each 64, p and
-// p + 32 are adjacent (slot 2 (p mod 32) + ((p / 32) mod 2)).
-__device__ __forceinline__ int interleave64(int p) { return (p & 64) | ((p & 31) << 1) | ((p >> 5) & 1); }
+// Row (column) pairs.  A 128-wide tile has 64 pairs; pair pr holds
+// positions lo(pr) and lo(pr) + 32 with lo(pr) = 64 (pr / 32) + pr mod 32,
+// the two rows (columns) one lane supplies to the two 32-wide subtiles of a
+// 64-wide wave tile.  The encode buffers keep, per pair, one 32-bit word per
+// contraction index: the low half for position lo, the high half for lo + 32.
+__device__ __forceinline__ int pair_lo(int pr) { return ((pr & 32) << 1) | (pr & 31); }
 
-// Load 16 int8 values x[0..16) (bounds-checked, vectorised when aligned).
-__device__ __forceinline__ void load16(const int8_t* src, int valid, int8_t* out) {
-  if (valid >= 16 && (((uintptr_t)src) & 15) == 0) {
-    const int4 v = *(const int4*)src;
+// Load 8 int8 values x[0..8) (bounds-checked, vectorised when aligned).
+__device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out) {
+  if (valid >= 8 && (((uintptr_t)src) & 7) == 0) {
+    const int2 v = *(const int2*)src;
     const int8_t* b = (const int8_t*)&v;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = b[i];
+    for (int i = 0; i < 8; ++i) out[i] = b[i];
   } else {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) out[i] = i < valid ? src[i] : (int8_t)0;
+    for (int i = 0; i < 8; ++i) out[i] = i < valid ? src[i] : (int8_t)0;
   }
 }
 
 // ------------------------------------------------------------ prep A ----
-// grid (RT, n_parts, G), block 256: thread -> (position p = tid % 128, half);
-// the block encodes contraction indices [part * part_len, ...) of one tile.
+// grid (RT, n_parts, G), block 256: thread -> (row pair pr = tid / 4,
+// quarter q = tid % 4); per group of 32 contraction indices a thread
+// encodes indices [d0 + 8 q, d0 + 8 q + 8) of both rows of its pair.  The
+// block covers indices [part * part_len, ...) of one tile.
 __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ uint16_t s_ncum[MAX_LEVELS];
-  __shared__ int s_mx[2][MF_DC];
-  __shared__ int s_rc[MF_BM];
+  __shared__ int s_mx[4][MF_DC];
   __shared__ int s_rows[MF_BM];
   const int tid = threadIdx.x;
   const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, y, MF_BM, k, pos0, nrows);
-  const int p = tid & (MF_BM - 1), half = tid >> 7;
   const int wave = tid >> 6, lane = tid & 63;
-  if (tid < MF_BM) {
-    s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
-    s_rc[tid] = 0;
-  }
+  const int pr = tid >> 2, q = tid & 3;
+  const int p_lo = pair_lo(pr), p_hi = p_lo + 32;
+  if (tid < MF_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+  __syncthreads();
+  const int row_lo = s_rows[p_lo], row_hi = s_rows[p_hi];
+  const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
+  const int8_t* src_hi = a.qA + ((long long)g * a.M + (row_hi < 0 ? 0 : row_hi)) * a.D;
+  uint32_t* dst = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + pr) * w.Dp;
   const int plo = part * w.part_len;
   const int phi = min(plo + w.part_len, a.D);
-  const long long colbase = (long long)y * MF_BM + interleave64(p);
+  int rc_lo = 0, rc_hi = 0;  // n0 sums of this thread's indices
+  // n0 sums of both rows over the four quarters, written by quarter 0.
+  auto flush_rc = [&](long long slot) {
+    rc_lo += __shfl_xor(rc_lo, 1, 64);
+    rc_lo += __shfl_xor(rc_lo, 2, 64);
+    rc_hi += __shfl_xor(rc_hi, 1, 64);
+    rc_hi += __shfl_xor(rc_hi, 2, 64);
+    if (q == 0) {
+      w.rowc[slot * w.Mp + (long long)y * MF_BM + p_lo] = rc_lo;
+      w.rowc[slot * w.Mp + (long long)y * MF_BM + p_hi] = rc_hi;
+    }
+    rc_lo = rc_hi = 0;
+  };
   for (int b = 0; b < a.n_bands; ++b) {
     const int lo = max(a.band_cols[b], plo);
     const int dend = min(a.band_cols[b + 1], phi);
@@ -169,46 +199,61 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
     __syncthreads();
     for (int d0 = lo; d0 < dend; d0 += MF_DC) {
-      const int row = s_rows[p];
-      const int dfirst = d0 + 16 * half;
-      int8_t x[16];
-      const int valid = row >= 0 ? min(16, dend - dfirst) : 0;
-      load16(a.qA + ((long long)g * a.M + (row < 0 ? 0 : row)) * a.D + dfirst, valid, x);
-      int n0s = 0;
+      const int dfirst = d0 + 8 * q;
+      const int span = max(0, min(8, dend - dfirst));
+      int8_t x_lo[8], x_hi[8];
+      load8(src_lo + dfirst, row_lo >= 0 ? span : 0, x_lo);
+      load8(src_hi + dfirst, row_hi >= 0 ? span : 0, x_hi);
+      uint32_t word[8];
+      int mh[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        int hh = 0, code = 0;
-        if (i < valid) {
-          const int n1 = s_ncum[level_of((int)x[i], a.P, a.q)];
-          const int diff = 2 * n1 - L;
-          hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
-          code = 16 * (2 * hh + (diff < 0 ? 1 : 0));
-          n0s += L - n1;
+      for (int i = 0; i < 8; ++i) {
+        int code[2] = {0, 0}, hh[2] = {0, 0};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const bool ok = i < span && (h == 0 ? row_lo : row_hi) >= 0;
+          if (ok) {
+            const int n1 = s_ncum[level_of((int)(h == 0 ? x_lo[i] : x_hi[i]), a.P, a.q)];
+            const int diff = 2 * n1 - L;
+            hh[h] = ((diff < 0 ? -diff : diff) + 1) >> 1;
+            code[h] = 16 * (2 * hh[h] + (diff < 0 ? 1 : 0));
+            (h == 0 ? rc_lo : rc_hi) += L - n1;
+          }
         }
-        const int d = dfirst + i;
-        if (d < w.Dp) w.hs[((long long)g * w.Dp + d) * w.Mp + colbase] = (uint16_t)code;
-        const int m = wave_max_i(hh);
-        if (lane == 0) s_mx[wave & 1][16 * half + i] = m;  // waves 0,1 -> half 0; 2,3 -> half 1
+        word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
+        mh[i] = max(hh[0], hh[1]);
       }
-      atomicAdd(&s_rc[p], n0s);
+      // d0 + 32 <= Dp: the whole group is inside the buffer row (indices past
+      // the band or D get code 0).
+      *(uint4*)(dst + dfirst) = uint4{word[0], word[1], word[2], word[3]};
+      *(uint4*)(dst + dfirst + 4) = uint4{word[4], word[5], word[6], word[7]};
+      if (w.hsi) {
+        uint32_t* di = w.hsi + ((long long)g * w.Dp + dfirst) * (w.Mp / 2) + (long long)y * 64 + pr;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) di[(long long)i * (w.Mp / 2)] = word[i];
+      }
+      // Tile maximum per index: over the 16 pairs of this wave (lanes with
+      // the same quarter), then over the four waves.
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        int m = mh[i];
+        m = max(m, __shfl_xor(m, 4, 64));
+        m = max(m, __shfl_xor(m, 8, 64));
+        m = max(m, __shfl_xor(m, 16, 64));
+        m = max(m, __shfl_xor(m, 32, 64));
+        if (lane < 4) s_mx[wave][8 * lane + i] = m;
+      }
       __syncthreads();
       if (tid < MF_DC) {
-        const int d = d0 + tid;
-        const int m = max(s_mx[0][tid], s_mx[1][tid]);
-        if (d < w.Dp) w.maxh[((long long)g * w.RT + y) * w.Dp + d] = (uint8_t)m;
+        const int m = max(max(s_mx[0][tid], s_mx[1][tid]), max(s_mx[2][tid], s_mx[3][tid]));
+        w.maxh[((long long)g * w.RT + y) * w.Dp + d0 + tid] = (uint8_t)m;
       }
-      if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D)) {
-        const int ch = d0 / a.chunk_d;
-        if (tid < MF_BM) {
-          w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
-          s_rc[tid] = 0;
-        }
-      }
-      __syncthreads();
+      if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D))
+        flush_rc((long long)g * a.n_chunks + d0 / a.chunk_d);
+      __syncthreads();  // s_mx is rewritten by the next group
     }
   }
-  if (a.chunk_d <= 0 && tid < MF_BM)
-    w.rowc[((long long)g * w.n_parts + part) * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
+  if (a.chunk_d <= 0) flush_rc((long long)g * w.n_parts + part);
   if (part == 0 && tid < MF_BM) {
     const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
     const int row = s_rows[tid];
@@ -218,7 +263,9 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
 }
 
 // ------------------------------------------------------------ prep B ----
-// grid (CT, n_parts, G), block 256: thread -> (column j = tid % 128, half).
+// grid (CT, n_parts, G), block 256: thread -> (column pair cp = tid / 4,
+// quarter q = tid % 4), indices [d0 + 8 q, d0 + 8 q + 8) of each group of
+// 32 in the block's part of the contraction axis.
 __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int tid = threadIdx.x;
   const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
@@ -230,18 +277,30 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
     *w.issued = 0;
     *w.work = 0;
   }
-  const int j = tid & (MF_BN - 1), half = tid >> 7;
-  const int col = c0 + j;
-  const int8_t* src = a.qB + ((long long)g * a.N + (col < a.N ? col : 0)) * a.D;
+  const int cp = tid >> 2, q = tid & 3;
+  const int col_lo = c0 + pair_lo(cp), col_hi = col_lo + 32;
+  const int8_t* src_lo = a.qB + ((long long)g * a.N + (col_lo < a.N ? col_lo : 0)) * a.D;
+  const int8_t* src_hi = a.qB + ((long long)g * a.N + (col_hi < a.N ? col_hi : 0)) * a.D;
+  uint32_t* dst = w.ub + ((long long)g * (w.Np / 2) + (long long)blockIdx.x * 64 + cp) * w.Dp;
   for (int d0 = plo; d0 < phi; d0 += MF_DC) {
-    const int dfirst = d0 + 16 * half;
-    int8_t x[16];
-    const int valid = col < a.N ? max(0, min(16, a.D - dfirst)) : 0;
-    load16(src + dfirst, valid, x);
+    const int dfirst = d0 + 8 * q;
+    const int span = max(0, min(8, a.D - dfirst));
+    int8_t x_lo[8], x_hi[8];
+    load8(src_lo + dfirst, col_lo < a.N ? span : 0, x_lo);
+    load8(src_hi + dfirst, col_hi < a.N ? span : 0, x_hi);
+    uint32_t word[8];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int u = i < valid ? level_of((int)x[i], a.P, a.q) : (a.P >> 1);
-      w.ub[((long long)g * w.Dp + dfirst + i) * w.Np + c0 + interleave64(j)] = (uint16_t)(u * PT_STRIDE);
+    for (int i = 0; i < 8; ++i) {
+      const int u_lo = (i < span && col_lo < a.N) ? level_of((int)x_lo[i], a.P, a.q) : (a.P >> 1);
+      const int u_hi = (i < span && col_hi < a.N) ? level_of((int)x_hi[i], a.P, a.q) : (a.P >> 1);
+      word[i] = (uint32_t)(u_lo * PT_STRIDE) | ((uint32_t)(u_hi * PT_STRIDE) << 16);
+    }
+    *(uint4*)(dst + dfirst) = uint4{word[0], word[1], word[2], word[3]};
+    *(uint4*)(dst + dfirst + 4) = uint4{word[4], word[5], word[6], word[7]};
+    if (w.ubi) {
+      uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)blockIdx.x * 64 + cp;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) di[(long long)i * (w.Np / 2)] = word[i];
     }
   }
 }
@@ -304,8 +363,6 @@ template <bool CHUNKED, bool COUNTS, int WR>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, MfmaWs w) {
   using T = MfTile<WR>;
   constexpr int BM = T::BM, BN = T::BN, DC = T::DC, SUB = T::SUB;
-  constexpr int H_PER = DC * BM / 8 / 256;  // 16-byte h chunks each thread stages
-  constexpr int U_PER = DC * BN / 8 / 256;  // 16-byte level chunks each thread stages
   // The two gather tables share one object (the largest, laid out first) so
   // that both sit below 64 KB, where a constant base folds into the LDS
   // instruction's offset: the paired table (one row per B level) and the A
@@ -354,38 +411,33 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int wrow0 = wr * 32 * WR;  // first row of this wave
   const int wcol0 = wc * 64;       // first column of this wave
 
-  // Stage loader: 16-byte chunks of h ([d][position]) and levels ([d][column]),
-  // two h chunks and U_PER level chunks per thread (named registers, so
-  // they stay in VGPRs).
-  static_assert(H_PER == 2 && (U_PER == 1 || U_PER == 2), "stage loader shape");
-  int4 rh0, rh1, ru0, ru1 = int4{0, 0, 0, 0};
+  // Stage loader: thread (pair pr = tid / 4, quarter q = tid % 4) reads the
+  // code words of indices [d0 + 8 q, d0 + 8 q + 8) of row pair pr and of
+  // column pair pr (two 16-byte loads each, into named registers so they
+  // stay in VGPRs) and stores them as the stage's [index][pair] words.
+  static_assert(SUB == 1 && BM == 128 && BN == 128 && DC == 32, "stage loader shape");
+  int4 rh0, rh1, ru0, ru1;
   int rmx = 0;
-  auto h_src = [&](int d0, int e) -> int4 {
-    const int dd = e / (BM / 8), cp = (e % (BM / 8)) * 8;
-    return cp < nsub * MF_BM ? *(const int4*)(w.hs + ((long long)g * w.Dp + d0 + dd) * w.Mp + prow0 + cp)
-                             : int4{0, 0, 0, 0};
-  };
-  auto u_src = [&](int d0, int e) -> int4 {
-    const int dd = e / (BN / 8), cc = (e % (BN / 8)) * 8;
-    return *(const int4*)(w.ub + ((long long)g * w.Dp + d0 + dd) * w.Np + col0 + cc);
-  };
+  const int lpr = tid >> 2, lq = tid & 3;
+  const uint32_t* hrow_g = w.hs + ((long long)g * (w.Mp / 2) + (long long)T0 * 64 + lpr) * w.Dp + 8 * lq;
+  const uint32_t* urow_g = w.ub + ((long long)g * (w.Np / 2) + (long long)(col0 / 2) + lpr) * w.Dp + 8 * lq;
   auto fetch = [&](int d0) {
-    rh0 = h_src(d0, tid);
-    rh1 = h_src(d0, tid + 256);
-    ru0 = u_src(d0, tid);
-    if constexpr (U_PER > 1) ru1 = u_src(d0, tid + 256);
-    if (tid < DC) {
-      const uint8_t* mp = w.maxh + ((long long)g * w.RT + T0) * w.Dp + d0 + tid;
-      int m = mp[0];
-      for (int sb = 1; sb < nsub; ++sb) m = max(m, (int)mp[(long long)sb * w.Dp]);
-      rmx = m;
-    }
+    rh0 = *(const int4*)(hrow_g + d0);
+    rh1 = *(const int4*)(hrow_g + d0 + 4);
+    ru0 = *(const int4*)(urow_g + d0);
+    ru1 = *(const int4*)(urow_g + d0 + 4);
+    if (tid < DC) rmx = w.maxh[((long long)g * w.RT + T0) * w.Dp + d0 + tid];
   };
   auto store = [&](int bf) {
-    *(int4*)&s_h[bf][tid / (BM / 8)][(tid % (BM / 8)) * 8] = rh0;
-    *(int4*)&s_h[bf][(tid + 256) / (BM / 8)][((tid + 256) % (BM / 8)) * 8] = rh1;
-    *(int4*)&s_u[bf][tid / (BN / 8)][(tid % (BN / 8)) * 8] = ru0;
-    if constexpr (U_PER > 1) *(int4*)&s_u[bf][(tid + 256) / (BN / 8)][((tid + 256) % (BN / 8)) * 8] = ru1;
+    uint32_t* sh = (uint32_t*)&s_h[bf][0][0];  // [DC][64] words
+    uint32_t* su = (uint32_t*)&s_u[bf][0][0];
+    const int hv[8] = {rh0.x, rh0.y, rh0.z, rh0.w, rh1.x, rh1.y, rh1.z, rh1.w};
+    const int uv[8] = {ru0.x, ru0.y, ru0.z, ru0.w, ru1.x, ru1.y, ru1.z, ru1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      sh[(8 * lq + i) * 64 + lpr] = (uint32_t)hv[i];
+      su[(8 * lq + i) * 64 + lpr] = (uint32_t)uv[i];
+    }
     if (tid < 64) {
       // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
       // tile maximum rmx) needs positions [16 j, 16 j + 16) for every
@@ -829,15 +881,18 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
       staged_k = k;
     }
 
-    // Uniform bases (the group's part of the buffers at the wave's first
-    // row / column) and 32-bit per-lane word offsets: the host checks that
-    // an index's words stay below 2^31 bytes from the base.
-    const uint32_t hs32 = (uint32_t)(w.Mp / 2), us32 = (uint32_t)(w.Np / 2);  // words per index
-    const uint32_t* hbase = (const uint32_t*)(w.hs + (long long)g * w.Dp * w.Mp + prow0 + wrow0);
-    const uint32_t* ubase = (const uint32_t*)(w.ub + (long long)g * w.Dp * w.Np + col0 + wcol0);
+    // This lane's rows of the encode buffers: row pair wr * 32 + l32 of tile
+    // y (rows wrow0 + l32 and wrow0 + l32 + 32) and column pair
+    // wc * 32 + l32 of column tile x, one code word per contraction index.
+    const uint32_t* hrow = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32) * w.Dp;
+    const uint32_t* urow = w.ub + ((long long)g * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32) * w.Dp;
     const uint8_t* mq = w.maxh + ((long long)g * w.RT + y) * w.Dp;
-    auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hbase[d * hs32 + (uint32_t)l32]; };
-    auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ubase[d * us32 + (uint32_t)l32]; };
+    // List steps read one index for all pairs: the index-major copies.
+    const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
+    const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
+    const long long hstr = w.Mp / 2, ustr = w.Np / 2;
+    auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hcol[(long long)d * hstr]; };
+    auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ucol[(long long)d * ustr]; };
 
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -883,18 +938,25 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
 
     const int dbeg = a.band_cols[0], dend = a.band_cols[1];
     const int ngrp = (dend - dbeg + 31) / 32;
-    // A group's loads: index d0 + 2 mm + hf for this lane's codes (uniform
-    // base of the pair plus the lane's half), and this lane's index maximum
+    // A group's loads: the codes of indices d0 + 16 hf + m, m < 16 (four
+    // 16-byte loads per buffer), so pair step m takes index d0 + m in lanes
+    // 0-31 and d0 + 16 + m in lanes 32-63; and this lane's index maximum
     // (raw: the band's bound is applied where it is used, so that nothing
     // waits for the loads here).
-    const uint32_t hlane = (uint32_t)l32 + (uint32_t)hf * hs32, ulane = (uint32_t)l32 + (uint32_t)hf * us32;
     auto load_group = [&](int d0, uint32_t* h, uint32_t* u, int& m) __attribute__((always_inline)) {
+      const uint4* hp = (const uint4*)(hrow + d0 + 16 * hf);
+      const uint4* up = (const uint4*)(urow + d0 + 16 * hf);
 #pragma unroll
-      for (int mm = 0; mm < 16; ++mm) {
-        const uint32_t* hp = hbase + (size_t)(uint32_t)(d0 + 2 * mm) * hs32;
-        const uint32_t* up = ubase + (size_t)(uint32_t)(d0 + 2 * mm) * us32;
-        h[mm] = hp[hlane];
-        u[mm] = up[ulane];
+      for (int i = 0; i < 4; ++i) {
+        const uint4 th = hp[i], tu = up[i];
+        h[4 * i] = th.x;
+        h[4 * i + 1] = th.y;
+        h[4 * i + 2] = th.z;
+        h[4 * i + 3] = th.w;
+        u[4 * i] = tu.x;
+        u[4 * i + 1] = tu.y;
+        u[4 * i + 2] = tu.z;
+        u[4 * i + 3] = tu.w;
       }
       m = mq[d0 + l32];  // d0 + l32 < Dp
     };
@@ -1046,12 +1108,10 @@ size_t mfma_workspace_bytes(const MatmulArgs& a) {
   return total;
 }
 
-// The persistent kernel handles one band starting on a 32-index boundary,
-// with 32-bit word offsets into the encode buffers and an int item count.
+// The persistent kernel handles one band starting on a 32-index boundary
+// and an int item count.
 static bool pers_ok(const MatmulArgs& a, const MfmaWs& w) {
   if (a.chunk_d > 0 || a.n_bands != 1 || a.band_cols[0] % MF_DC != 0) return false;
-  if ((double)w.Dp * (double)w.Mp * 2.0 >= 2147483648.0) return false;
-  if ((double)w.Dp * (double)w.Np * 2.0 >= 2147483648.0) return false;
   return (double)a.tile_start[a.n_rungs] * a.G * w.CT < 2147483647.0;
 }
 
@@ -1111,7 +1171,7 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
     return set_error(SCMP_ERR_ARG, "too many tiles");
   if (a.launch == 1 && !pers_ok(a, w))
     return set_error(SCMP_ERR_UNSUPPORTED,
-                     "the persistent launch needs a plan without chunk scales, one band and 32-bit buffer offsets");
+                     "the persistent launch needs a plan without chunk scales and one band");
   hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   launch_main(a, w, dim3(w.CT, RT2, a.G), st);
