@@ -30,6 +30,7 @@ DEFAULT_WORKLOAD = "vitl_fc1_mp"
 
 # MI355X published peaks used for the roofline fractions.
 PEAK_INT8_TOPS = 5000.0          # dense int8 MFMA, 5.0 POP/s
+PEAK_FP4_TOPS = 10100.0          # dense fp4 MFMA, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0            # HBM3E, 8 TB/s
 # Vector-ALU bit-serial bound: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz int32
 # ops, two ops (bit-select, popcount) per 32 stream positions.
@@ -42,7 +43,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
-    ap.add_argument("--algo", default="auto", choices=["auto", "mfma", "bitserial"])
+    ap.add_argument("--algo", default="auto",
+                    choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle sample (0 = 2 per worker)")
     return ap.parse_args()
@@ -199,15 +201,23 @@ def main():
                 "work": "bit-MACs (D * L per output element), two VALU ops per 32"}
     else:
         # The windowed contraction issues, per 128 x 128 tile and contraction
-        # index, only the 32-position steps some row of the tile needs; the
-        # library counts them exactly.  achieved = issued int8 ops / time.
-        issued = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo, stream=stream)
+        # index, only the steps some row of the tile needs, on the int8 or
+        # the fp4 matrix cores; the library counts both exactly.  The peak is
+        # the mix's: the time both parts take at their dense peaks.
+        issued, issued_fp4 = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo,
+                                                          stream=stream, split=True)
+        issued_i8 = issued - issued_fp4
+        t_peak = 2.0 * issued_i8 / (PEAK_INT8_TOPS * 1e12) + 2.0 * issued_fp4 / (PEAK_FP4_TOPS * 1e12)
         achieved = 2.0 * issued / (kern_ms / 1e3) / 1e12
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_INT8_TOPS, "unit": "TOP/s",
-                "frac": achieved / PEAK_INT8_TOPS, "traffic": None,
-                "work": "int8 MACs issued per launch x 2 (v_mfma_i32_32x32x32_i8 steps the data needs)",
-                "issued_macs": issued, "dense_paired_macs": paired,
-                "dense_paired_frac": 2.0 * paired / (kern_ms / 1e3) / 1e12 / PEAK_INT8_TOPS}
+        peak = 2.0 * issued / t_peak / 1e12 if t_peak > 0 else PEAK_INT8_TOPS
+        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TOP/s",
+                "frac": achieved / peak, "traffic": None,
+                "work": "MACs issued per launch x 2: int8 (v_mfma_i32_32x32x32_i8) and fp4 "
+                        "(v_mfma_scale_f32_32x32x64_f8f6f4) steps the data needs; peak = the mix at the "
+                        "dense int8 5.0 and fp4 10.1 POP/s peaks",
+                "issued_macs": issued, "issued_macs_int8": issued_i8, "issued_macs_fp4": issued_fp4,
+                "dense_paired_macs": paired,
+                "dense_paired_frac_of_int8_peak": 2.0 * paired / (kern_ms / 1e3) / 1e12 / PEAK_INT8_TOPS}
     # The events bracket one scmp_matmul call: the contraction kernel plus, on
     # the matrix-core path, its two small encode kernels (k_prep_rows,
     # k_prep_cols), which run first on the same stream.
@@ -217,6 +227,13 @@ def main():
     roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
     roof["valu_bitserial_frac"] = bitmacs / (kern_ms / 1e3) / PEAK_VALU_BITMACS
 
+    # Arithmetic of the contraction: integer stream counts from int8 codes,
+    # on int8 or e2m1 (fp4, exact for these operands) matrix-core operands.
+    if args.algo == "bitserial":
+        dtype = "u32 bit-ops"
+    else:
+        dtype = {(True, False): "i8", (False, True): "fp4(e2m1)", (True, True): "i8+fp4(e2m1)"}.get(
+            (roof["issued_macs_int8"] > 0, roof["issued_macs_fp4"] > 0), "i8")
     out = {
         "metric": METRIC,
         "value": value,
@@ -228,7 +245,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "i8",
+        "dtype": dtype,
         "data": "synthetic",
         "config": {
             "workload": w.name, "G": G, "M": M, "N": N, "D": D, "levels": list(w.levels),

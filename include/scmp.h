@@ -244,15 +244,16 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
                 void* workspace_dev, size_t workspace_bytes, void* stream);
 
-/* Diagnostic: synchronise `stream` and return the int8 multiply-accumulates
- * the last MFMA-path scmp_matmul with this workspace issued on the matrix
- * cores (every 32-position step of every 128 x 128 tile, 32 x 32 x 32 MACs
- * per MFMA).  The count follows from the data: a step is issued when some
- * row of the tile needs it.  Errors: ARG, UNSUPPORTED (BITSERIAL),
- * WORKSPACE, HIP. */
+/* Diagnostic: synchronise `stream` and return the multiply-accumulates the
+ * last MFMA-path scmp_matmul with this workspace issued on the matrix cores
+ * (every step of every 128 x 128 tile: four MFMAs per wave, 32 x 32 x 32
+ * int8 or 32 x 32 x 64 fp4 MACs each).  The count follows from the data: a
+ * step is issued when some row of the tile needs it.  *macs receives all of
+ * them; fp4_macs (may be NULL) receives the fp4 part.  Errors: ARG,
+ * UNSUPPORTED (BITSERIAL), WORKSPACE, HIP. */
 int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                             const void* workspace_dev, size_t workspace_bytes, unsigned long long* macs,
-                            void* stream);
+                            unsigned long long* fp4_macs, void* stream);
 
 /* Decode counts produced without chunk scales ([PAYN] Key design 1, decode
  * equation): C_ij = s^A_i s^B_j q^2 (2 count_ij - L_i D) / L_i with

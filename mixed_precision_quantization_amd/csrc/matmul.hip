@@ -140,16 +140,17 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
 
 int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                             const void* workspace, size_t workspace_bytes, unsigned long long* macs,
-                            void* stream) {
+                            unsigned long long* fp4_macs, void* stream) {
   scmp::clear_error();
   if (!macs) return set_error(SCMP_ERR_ARG, "macs is NULL");
   *macs = 0;
+  if (fp4_macs) *fp4_macs = 0;
   scmp::MatmulArgs a;
   int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
   if (st0 != SCMP_OK) return st0;
   if (algo == SCMP_ALGO_BITSERIAL) return set_error(SCMP_ERR_UNSUPPORTED, "only the MFMA path counts its steps");
   if ((long long)G * M * N == 0) return SCMP_OK;
-  return scmp::mfma_issued_macs(a, workspace, workspace_bytes, (hipStream_t)stream, macs);
+  return scmp::mfma_issued_macs(a, workspace, workspace_bytes, (hipStream_t)stream, macs, fp4_macs);
 }
 
 int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts, const float* sA, const float* sB,

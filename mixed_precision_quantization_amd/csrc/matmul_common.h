@@ -70,7 +70,7 @@ void fill_tiles(MatmulArgs& a, const Plan& P, int BM);
 size_t mfma_workspace_bytes(const MatmulArgs& a);
 int launch_mfma(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
-                     unsigned long long* macs);
+                     unsigned long long* macs, unsigned long long* fp4_macs);
 
 // Vector-ALU bit-serial path (bitserial.hip).
 int launch_bitserial(const MatmulArgs& a, hipStream_t st);

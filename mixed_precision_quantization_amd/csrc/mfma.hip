@@ -61,7 +61,7 @@ struct MfmaWs {
   uint32_t* ubi;    // [G][Dp][Np/2]  table offset words, by index then column pair
   int32_t* rowid;   // [G][Mp]       original row of each sorted position (-1: none)
   float* sas;       // [G][Mp]       row scale of each sorted position (single-segment plans)
-  unsigned long long* issued;  // 32-position steps the contraction issued, summed over row tiles
+  unsigned long long* issued;  // [2] MFMA steps issued over the row tiles: int8 steps, fp4 steps
   unsigned int* work;          // work counter of the persistent contraction
   long long Mp, Np, Dp;
   int RT, CT;
@@ -102,7 +102,7 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const size_t ubi_b = index_major ? ub_b : 0;
   const size_t ri_b = al((size_t)a.G * w.Mp * sizeof(int32_t));
   const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
-  const size_t ts_b = al(sizeof(unsigned long long) + sizeof(unsigned int));
+  const size_t ts_b = al(2 * sizeof(unsigned long long) + sizeof(unsigned int));
   char* p = (char*)base;
   w.hs = (uint32_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -121,7 +121,7 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   w.sas = (float*)(p ? p + off : nullptr);
   off += sa_b;
   w.issued = (unsigned long long*)(p ? p + off : nullptr);
-  w.work = (unsigned int*)(p ? p + off + sizeof(unsigned long long) : nullptr);
+  w.work = (unsigned int*)(p ? p + off + 2 * sizeof(unsigned long long) : nullptr);
   off += ts_b;
   *total = off;
   return w;
@@ -274,7 +274,8 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   // The contraction (launched after this kernel on the same stream) adds
   // its issued steps to this counter.
   if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
-    *w.issued = 0;
+    w.issued[0] = 0;
+    w.issued[1] = 0;
     *w.work = 0;
   }
   const int cp = tid >> 2, q = tid & 3;
@@ -692,7 +693,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
   }
-  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued, issued);
+  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued, issued);  // int8 steps
 
   if (!CHUNKED) {
     // Each row's n0 sum over the whole contraction axis: the parts' partial
@@ -1079,26 +1080,382 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     item = next;
     cur ^= 1;
   }
-  if (tid == 0 && issued) atomicAdd(w.issued, issued);
+  if (tid == 0 && issued) atomicAdd(w.issued, issued);  // int8 steps
+}
+
+// ------------------------------------------- persistent variant, fp4 ----
+// The persistent contraction on the fp4 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 operands, unit scales): the
+// A bytes {-1, 0, +1} and the pair sums {0, 1, 2} are exact in e2m1 and the
+// fp32 accumulators hold the integer counts exactly (below 2^24).  One lane
+// half of an MFMA covers 32 nibbles, so it takes two 16-position
+// half-blocks (X in nibbles 0-15, Y in 16-31): four half-blocks per MFMA
+// step, twice the int8 step, with the same bytes read per half-block.
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+
+// fp4 A patterns: entry e (16-byte stride, first 8 bytes used) holds
+// min(e / 2, 16) leading sign nibbles, 0xA (-1) when e is odd, 0x2 (+1)
+// otherwise, then zero nibbles (low nibble first).
+__device__ __forceinline__ void init_patterns4(uint32_t* pat, int tid, int nthreads) {
+  for (int w = tid; w < PAT_WORDS; w += nthreads) {
+    const int e = w >> 2, wd = w & 3, n = min(e >> 1, 16);
+    const uint32_t one = (e & 1) ? 0xAu : 0x2u;
+    uint32_t x = 0;
+    if (wd < 2)
+      for (int nib = 0; nib < 8; ++nib)
+        if (wd * 8 + nib < n) x |= one << (4 * nib);
+    pat[w] = x;
+  }
+}
+
+// The paired table of band b, rung k as e2m1 nibbles (value v -> code 2 v,
+// position p in nibble p mod 2 of byte p / 2), rows of PT_STRIDE bytes.
+__device__ __forceinline__ void stage_pair_table4(uint8_t* pt, const MatmulArgs& a, int b, int k, int KLpad, int tid,
+                                                  int nthreads) {
+  const uint8_t* src = a.pair + a.pair_off[b][k];
+  const int vec_per_row = KLpad >> 4;
+  for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += nthreads) {
+    const int u = idx / vec_per_row, v = idx - u * vec_per_row;
+    const uint4 x = *(const uint4*)(src + (long long)u * KLpad + v * 16);
+    auto pack = [](uint32_t wd) {
+      const uint32_t t = wd << 1;  // bytes <= 2: doubling never carries
+      return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
+    };
+    *(uint2*)(pt + u * PT_STRIDE + v * 8) = uint2{pack(x.x) | (pack(x.y) << 16), pack(x.z) | (pack(x.w) << 16)};
+  }
+}
+
+template <bool COUNTS>
+__global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers4(MatmulArgs a, MfmaWs w, int n_items) {
+  struct __align__(16) GatherTables {
+    uint8_t pt[MAX_LEVELS * PT_STRIDE];
+    uint32_t pat[PAT_WORDS];
+  };
+  __shared__ GatherTables s_tab;
+  __shared__ __align__(8) uint32_t s_list[4][FL_LIST];
+  __shared__ __align__(16) int s_rows[2][MF_BM];    // original row of each position (-1: none)
+  __shared__ __align__(16) int s_rc[2][MF_BM];      // each row's n0 sum over the contraction axis
+  __shared__ __align__(16) float s_sa[2][MF_BM];    // each row's scale
+  __shared__ int s_item[2];
+  uint8_t* const s_pt = s_tab.pt;
+  uint32_t* const s_pat = s_tab.pat;
+  constexpr int PAD4 = 8 * FL_RING + 4;  // padding entries past a list's end
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int wrow0 = wr * 64, wcol0 = wc * 64;
+  uint32_t* const list = s_list[wave];
+  const int qq = a.q * a.q;
+
+  // Row data of tile y in group g for position tid (< 128): original row,
+  // n0 summed over the encode parts, row scale.
+  auto row_data = [&](int g, int y, int& row, int& rc, float& sa) __attribute__((always_inline)) {
+    const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
+    row = w.rowid[pos];
+    sa = w.sas[pos];
+    rc = 0;
+    const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
+    for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
+  };
+
+  init_patterns4(s_pat, tid, 256);
+  if (tid == 0) {
+    s_item[0] = (int)atomicAdd(w.work, 1u);
+    s_item[1] = (int)atomicAdd(w.work, 1u);
+  }
+  __syncthreads();
+  int item = s_item[0];
+  if (item >= n_items) return;
+  if (tid < MF_BM) {
+    const PersItem it = pers_item(a, w.CT, item);
+    int row, rc;
+    float sa;
+    row_data(it.g, it.y, row, rc, sa);
+    s_rows[0][tid] = row;
+    s_rc[0][tid] = rc;
+    s_sa[0][tid] = sa;
+  }
+
+  struct Frag {
+    v8i a[2], b[2];
+  };
+  // Fragments of half-blocks X (codes hx, ux, first position kx) and Y for
+  // this lane half: A from the pattern table at max(c - 32 k, 0), B from the
+  // nibble table at row offset + k / 2.
+  auto frags_at = [&](uint32_t hx, uint32_t ux, uint32_t kx, uint32_t hy, uint32_t uy, uint32_t ky)
+                      __attribute__((always_inline)) {
+    Frag f;
+    const uint8_t* pat = (const uint8_t*)s_pat;
+    const v2i ax0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx & 0xffffu, 32u * kx));
+    const v2i ax1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx >> 16, 32u * kx));
+    const v2i ay0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy & 0xffffu, 32u * ky));
+    const v2i ay1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy >> 16, 32u * ky));
+    const v2i bx0 = *(const v2i*)(s_pt + (ux & 0xffffu) + (kx >> 1));
+    const v2i bx1 = *(const v2i*)(s_pt + (ux >> 16) + (kx >> 1));
+    const v2i by0 = *(const v2i*)(s_pt + (uy & 0xffffu) + (ky >> 1));
+    const v2i by1 = *(const v2i*)(s_pt + (uy >> 16) + (ky >> 1));
+    f.a[0] = v8i{ax0.x, ax0.y, ay0.x, ay0.y, 0, 0, 0, 0};
+    f.a[1] = v8i{ax1.x, ax1.y, ay1.x, ay1.y, 0, 0, 0, 0};
+    f.b[0] = v8i{bx0.x, bx0.y, by0.x, by0.y, 0, 0, 0, 0};
+    f.b[1] = v8i{bx1.x, bx1.y, by1.x, by1.y, 0, 0, 0, 0};
+    return f;
+  };
+  v16f acc[2][2];
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[jj], acc[i][jj], 4, 4, 0, 127, 0, 127);
+  };
+  unsigned long long issued = 0;  // fp4 MFMA steps of the column-0 tiles
+  int staged_k = -1;
+  int cur = 0;
+
+  while (true) {
+    const PersItem it = pers_item(a, w.CT, item);
+    const int k = it.k, g = it.g, y = it.y;
+    const int col0 = it.x * MF_BN;
+    const bool count_steps = it.x == 0;
+    const int next = s_item[cur ^ 1];
+    // The next tile's row data, read now and stored after this tile.
+    int nrow = -1, nrc = 0;
+    float nsa = 0.0f;
+    if (next < n_items && tid < MF_BM) {
+      const PersItem nt = pers_item(a, w.CT, next);
+      row_data(nt.g, nt.y, nrow, nrc, nsa);
+    }
+    const int L = a.bandL[0][k];
+    if (k != staged_k) {
+      // Every wave finished the previous tile (the loop ends on a barrier).
+      const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
+      stage_pair_table4(s_pt, a, 0, k, KLpad, tid, 256);
+      __syncthreads();
+      staged_k = k;
+    }
+
+    // This lane's rows of the encode buffers (row pair wr * 32 + l32 of
+    // tile y, column pair wc * 32 + l32 of column tile x), and the
+    // index-major copies for list steps.
+    const uint32_t* hrow = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32) * w.Dp;
+    const uint32_t* urow = w.ub + ((long long)g * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32) * w.Dp;
+    const uint8_t* mq = w.maxh + ((long long)g * w.RT + y) * w.Dp;
+    const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
+    const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
+    const long long hstr = w.Mp / 2, ustr = w.Np / 2;
+    auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hcol[(long long)d * hstr]; };
+    auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ucol[(long long)d * ustr]; };
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    // Contract the wave's list of cnt half-blocks, four per step (lanes 0-31
+    // take entries 4 s and 4 s + 1, lanes 32-63 entries 4 s + 2 and
+    // 4 s + 3).  Slot r of the ring holds the entries and codes of a step
+    // FL_RING steps ahead; its fragments are read one step ahead of its
+    // MFMAs.  A list entry is (index << 4) | level; level 8 (position 128,
+    // past every window) is the zero half-block used as padding, with dpad
+    // (any index of the band) for its unused codes.
+    auto list_sweep = [&](int cnt, int dpad) __attribute__((always_inline)) {
+      if (lane < PAD4) list[cnt + lane] = ((uint32_t)dpad << 4) | 8u;
+      const int nsteps = (cnt + 3) >> 2;
+      uint2 re[FL_RING];
+      uint32_t rhx[FL_RING], rux[FL_RING], rhy[FL_RING], ruy[FL_RING];
+      auto fill = [&](int r, uint2 e) __attribute__((always_inline)) {
+        re[r] = e;
+        rhx[r] = hword(e.x >> 4);
+        rux[r] = uword(e.x >> 4);
+        rhy[r] = hword(e.y >> 4);
+        ruy[r] = uword(e.y >> 4);
+      };
+      auto frags_r = [&](int r) __attribute__((always_inline)) {
+        return frags_at(rhx[r], rux[r], 16u * (re[r].x & 15u), rhy[r], ruy[r], 16u * (re[r].y & 15u));
+      };
+      const uint2* lst = (const uint2*)list;  // entry pairs
+#pragma unroll
+      for (int r = 0; r < FL_RING; ++r) fill(r, lst[2 * r + hf]);
+      uint2 enext = lst[2 * FL_RING + hf];
+      Frag fr[2];
+      fr[0] = frags_r(0);
+      for (int s0 = 0; s0 < nsteps; s0 += FL_RING) {
+#pragma unroll
+        for (int r = 0; r < FL_RING; ++r) {
+          fr[(r + 1) & 1] = frags_r((r + 1) % FL_RING);
+          fill(r, enext);  // slot r now serves step s0 + r + FL_RING
+          enext = lst[2 * (s0 + r + FL_RING + 1) + hf];
+          __builtin_amdgcn_sched_barrier(0);
+          if (s0 + r < nsteps) mma(fr[r & 1]);
+        }
+      }
+      if (count_steps) issued += nsteps;
+    };
+
+    const int dbeg = a.band_cols[0], dend = a.band_cols[1];
+    const int ngrp = (dend - dbeg + 31) / 32;
+    // A group's loads: the codes of indices d0 + 16 hf + m, m < 16 (four
+    // 16-byte loads per buffer), and this lane's index maximum (raw: the
+    // band's bound is applied where it is used).
+    auto load_group = [&](int d0, uint32_t* h, uint32_t* u, int& m) __attribute__((always_inline)) {
+      const uint4* hp = (const uint4*)(hrow + d0 + 16 * hf);
+      const uint4* up = (const uint4*)(urow + d0 + 16 * hf);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint4 th = hp[i], tu = up[i];
+        h[4 * i] = th.x;
+        h[4 * i + 1] = th.y;
+        h[4 * i + 2] = th.z;
+        h[4 * i + 3] = th.w;
+        u[4 * i] = tu.x;
+        u[4 * i + 1] = tu.y;
+        u[4 * i + 2] = tu.z;
+        u[4 * i + 3] = tu.w;
+      }
+      m = mq[d0 + l32];  // d0 + l32 < Dp
+    };
+    int cnt = 0;  // entries in this wave's list
+    // fa: the fragments of the group's first step, read at the end of the
+    // previous group.
+    Frag fa;
+    // One group: its codes (ch, cu) and this lane's index maximum (mx) are
+    // in registers; nh, nu: the next group's codes.  A full level takes 8
+    // steps: step m pairs indices d0 + 16 hf + m (X) and d0 + 16 hf + 8 + m
+    // (Y) in lane half hf.
+    auto group = [&](int grp, const uint32_t* ch, const uint32_t* cu, int mx, const uint32_t* nh,
+                     const uint32_t* nu) __attribute__((always_inline)) {
+      const int d0 = dbeg + 32 * grp;
+      const int nl = d0 + l32 < dend ? (mx + 15) >> 4 : 0;
+      int full = 0;
+      for (int j = 0; j < 8; ++j) {
+        const unsigned bal = (unsigned)__ballot(nl > j);
+        if (bal == 0) break;
+        if (bal == 0xffffffffu && j == full) {
+          ++full;
+          continue;
+        }
+        if (hf == 0 && nl > j)
+          list[cnt + (int)__builtin_amdgcn_mbcnt_lo(bal, 0u)] = ((uint32_t)(d0 + l32) << 4) | (uint32_t)j;
+        cnt += __builtin_popcount(bal);
+      }
+      if (full > 0) {
+        Frag fb;
+        for (int j = 0; j < full; ++j) {
+          const uint32_t kk = 16u * j;
+#pragma unroll
+          for (int m = 0; m < 8; m += 2) {
+            fb = frags_at(ch[m + 1], cu[m + 1], kk, ch[m + 9], cu[m + 9], kk);
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+            mma(fa);
+            // Next: step m + 2 of this level or step 0 of the next level
+            // (after the last level: read, unused; position <= 128 stays
+            // inside the table rows).
+            if (m + 2 < 8)
+              fa = frags_at(ch[m + 2], cu[m + 2], kk, ch[m + 10], cu[m + 10], kk);
+            else
+              fa = frags_at(ch[0], cu[0], kk + 16u, ch[8], cu[8], kk + 16u);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
+          }
+        }
+        if (count_steps) issued += 8 * full;
+      }
+      // The next group adds at most 256 entries.
+      if (cnt > FL_LIST - 256 - PAD4 || (grp == ngrp - 1 && cnt > 0)) {
+        list_sweep(cnt, d0);
+        cnt = 0;
+      }
+      // The next group's first step.
+      fa = frags_at(nh[0], nu[0], 0u, nh[8], nu[8], 0u);
+    };
+    if (ngrp > 0) {
+      uint32_t ha[16], ua[16], hb[16], ub[16];
+      int ma, mb = 0;
+      load_group(dbeg, ha, ua, ma);
+      fa = frags_at(ha[0], ua[0], 0u, ha[8], ua[8], 0u);
+      for (int grp = 0; grp < ngrp; grp += 2) {
+        load_group(dbeg + 32 * min(grp + 1, ngrp - 1), hb, ub, mb);
+        group(grp, ha, ua, ma, hb, ub);
+        if (grp + 1 >= ngrp) break;
+        load_group(dbeg + 32 * min(grp + 2, ngrp - 1), ha, ua, ma);
+        group(grp + 1, hb, ub, mb, ha, ua);
+      }
+    }
+
+    // The next tile's row data into the other buffer; the tile after it.
+    if (tid < MF_BM) {
+      s_rows[cur ^ 1][tid] = nrow;
+      s_rc[cur ^ 1][tid] = nrc;
+      s_sa[cur ^ 1][tid] = nsa;
+    }
+    if (tid == 0) s_item[cur] = next < n_items ? (int)atomicAdd(w.work, 1u) : n_items;
+
+    // Decode: rows four at a time (accumulator entries v = 4 q .. 4 q + 3
+    // are consecutive rows), each used by both column subtiles.
+    const float scale0 = (float)qq / (float)L;
+    float sb[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wcol0 + j * 32 + l32;
+      sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
+        const int4 rw = *(const int4*)&s_rows[cur][r0];
+        const int4 rc = *(const int4*)&s_rc[cur][r0];
+        const float4 sa = *(const float4*)&s_sa[cur][r0];
+        const int rowv[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
+        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = col0 + wcol0 + j * 32 + l32;
+            if (rowv[e] < 0 || col >= a.N) continue;
+            const int cnt2 = (int)acc[i][j][q4 * 4 + e] + rcv[e];
+            if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
+            if (a.C)
+              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + col] =
+                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D));
+          }
+      }
+    __syncthreads();  // publishes the next tile's row data and item
+    if (next >= n_items) break;
+    item = next;
+    cur ^= 1;
+  }
+  if (tid == 0 && issued) atomicAdd(w.issued + 1, issued);
 }
 
 // Row subtiles per wave for a plan.
 static int mfma_wr(const MatmulArgs&) { return 2; }
 
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
-                     unsigned long long* macs) {
+                     unsigned long long* macs, unsigned long long* fp4_macs) {
   size_t need = 0;
   MfmaWs w = ws_layout(a, (void*)ws, &need);
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
-  unsigned long long steps = 0;
-  hipError_t e = hipMemcpyAsync(&steps, w.issued, sizeof steps, hipMemcpyDeviceToHost, st);
+  unsigned long long steps[2] = {0, 0};
+  hipError_t e = hipMemcpyAsync(steps, w.issued, sizeof steps, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("work readback: ") + hipGetErrorString(e));
-  // Every step of a BM x 128 tile is 2 WR MFMAs per wave, 4 waves, of
-  // 32 x 32 x 32 MACs: BM * 128 * 32 MACs, issued by each column tile.
-  const unsigned long long BM = 64ull * mfma_wr(a);
-  *macs = steps * (unsigned long long)w.CT * BM * 128ull * 32ull;
+  // A step of a 128 x 128 tile is four MFMAs per wave (2 x 2 subtiles of
+  // 32 x 32), four waves: 128 * 128 * K MACs with K = 32 (int8) or 64
+  // (fp4), issued by each column tile.
+  const unsigned long long per8 = (unsigned long long)w.CT * 128ull * 128ull * 32ull;
+  *macs = steps[0] * per8 + steps[1] * 2 * per8;
+  if (fp4_macs) *fp4_macs = steps[1] * 2 * per8;
   return SCMP_OK;
 }
 
@@ -1143,9 +1500,9 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
     const int n_items = a.tile_start[a.n_rungs] * a.G * w.CT;
     const int blocks = std::max(1, std::min(n_items, (counts ? 1 : 2) * device_cus()));
     if (counts)
-      hipLaunchKernelGGL((k_mfma_pers<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers4<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
     else
-      hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers4<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
   } else {
     if (counts)
       hipLaunchKernelGGL((k_mfma<false, true, 2>), grid, dim3(256), 0, st, a, w);

@@ -102,7 +102,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_matmul_workspace_bytes": (i, [vp, vp, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]),
         "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
         "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
-                                        ctypes.POINTER(ctypes.c_ulonglong), vp]),
+                                        ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_ulonglong),
+                                        vp]),
         "scmp_decode": (i, [vp, i, i, i, vp, vp, vp, vp, vp, i64, i64, vp]),
         "scmp_error_flags": (i, [vp, ctypes.POINTER(i)]),
     }
@@ -372,14 +373,16 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
 
 
 def scmp_matmul_issued_macs(table: Table, plan: Plan, G: int, M: int, N: int, workspace, algo: str = "auto",
-                            stream=None) -> int:
-    """int8 MACs the last MFMA-path matmul with ``workspace`` issued (synchronises)."""
+                            stream=None, split: bool = False):
+    """MACs the last MFMA-path matmul with ``workspace`` issued on the matrix
+    cores (synchronises); with ``split`` the pair (all, fp4 part)."""
     out = ctypes.c_ulonglong(0)
+    fp4 = ctypes.c_ulonglong(0)
     _check("scmp_matmul_issued_macs",
            load().scmp_matmul_issued_macs(table.handle, plan.handle, ALGOS[algo], G, M, N,
                                           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
-                                          ctypes.byref(out), _stream(stream)))
-    return int(out.value)
+                                          ctypes.byref(out), ctypes.byref(fp4), _stream(stream)))
+    return (int(out.value), int(fp4.value)) if split else int(out.value)
 
 
 def scmp_decode(plan: Plan, counts, sA, sB, rung=None, C_out=None, stream=None):
