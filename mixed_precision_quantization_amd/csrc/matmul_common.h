@@ -27,8 +27,7 @@ struct MatmulArgs {
   int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
   int launch;  // matrix-core launch form: 0 by size, 1 persistent, 2 one block per tile
   int cuts[SCMP_MAX_RUNGS + 1];
-  int tile_start[SCMP_MAX_RUNGS + 1];   // row tiles of the encode kernels (and bit-serial)
-  int tile_start2[SCMP_MAX_RUNGS + 1];  // row tiles of the matrix-core contraction
+  int tile_start[SCMP_MAX_RUNGS + 1];  // first row tile of each rung (128 rows; 64 for bit-serial)
   int band_cols[SCMP_MAX_BANDS + 1];
   int bandL[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];
   unsigned long long pair_off[SCMP_MAX_BANDS][SCMP_MAX_RUNGS];

@@ -47,8 +47,6 @@ namespace scmp {
 constexpr int MF_BM = 128, MF_BN = 128, MF_DC = 32;
 constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LDS
 
-typedef int v4i __attribute__((ext_vector_type(4)));
-typedef int v16i __attribute__((ext_vector_type(16)));
 
 struct MfmaWs {
   uint32_t* hs;     // [G][Mp/2][Dp]  window codes 16 (2 hh + neg) of a row pair, by index
@@ -307,147 +305,172 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
 }
 
 // ------------------------------------------------------------- main ----
+// The contraction runs on the fp4 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 A and B operands at unit
+// scales): the A bytes {-1, 0, +1} and the pair sums {0, 1, 2} are exact in
+// e2m1, and the fp32 accumulators hold the integer counts exactly (every
+// count is below 2^24).  Lane l of a 32 x 32 x 64 MFMA supplies row
+// (column) l mod 32 and positions [32 (l / 32), 32 (l / 32) + 32) as 32
+// nibbles, low nibble first; each lane half takes two 16-position
+// half-blocks of the windowed contraction, X in nibbles 0-15 and Y in
+// nibbles 16-31 (the MFMA sums both), so one step of four MFMAs per wave
+// covers four half-blocks of its 64 x 64 tile.
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v16f __attribute__((ext_vector_type(16)));
 
-// A fragment for paired positions [kk, kk + 16) of a row whose window code
-// is c = 16 (2 hh + neg): the first clamp(hh - kk, 0, 16) bytes are the sign
-// (+1 = 0x01, -1 = 0xff), the rest 0.  Entry e of the pattern table holds
-// min(e / 2, 16) sign bytes of sign e mod 2 (entries 0 and 1 are zero), so
-// the fragment sits at byte offset max(c - 32 kk, 0) = 16 (2 (hh - kk) + neg)
-// when hh > kk, and at a zero entry otherwise.  Rows with equal fragments
-// read one address (an LDS broadcast).  kk32 = 32 kk.
+// A patterns: entry e (16-byte stride, first 8 bytes used) holds
+// min(e / 2, 16) leading sign nibbles, 0xA (-1) when e is odd and 0x2 (+1)
+// otherwise, then zero nibbles.  A row whose window code is
+// c = 16 (2 hh + neg) finds its fragment for positions [kk, kk + 16) at byte
+// offset max(c - 32 kk, 0): entry 2 (hh - kk) + neg when hh > kk (the first
+// clamp(hh - kk, 0, 16) positions), a zero entry (0 or 1) otherwise.  Rows
+// with equal fragments read one address (an LDS broadcast).
 constexpr int PAT_WORDS = 258 * 4;
-__device__ __forceinline__ v4i a_frag(const uint8_t* pat, unsigned c, unsigned kk32) {
-  return *(const v4i*)(pat + __builtin_elementwise_sub_sat(c, kk32));
-}
-
-// A fragment patterns: entry v (words 4 v .. 4 v + 3) holds min(v / 2, 16)
-// leading sign bytes, 0xff when v is odd (negative window), 0x01 otherwise.
 __device__ __forceinline__ void init_patterns(uint32_t* pat, int tid, int nthreads) {
-  for (int e = tid; e < PAT_WORDS; e += nthreads) {
-    const int v = e >> 2, wd = e & 3, n = min(v >> 1, 16);
-    const uint32_t one = (v & 1) ? 0xffu : 0x01u;
+  for (int w = tid; w < PAT_WORDS; w += nthreads) {
+    const int e = w >> 2, wd = w & 3, n = min(e >> 1, 16);
+    const uint32_t one = (e & 1) ? 0xAu : 0x2u;
     uint32_t x = 0;
-    for (int byte = 0; byte < 4; ++byte)
-      if (wd * 4 + byte < n) x |= one << (8 * byte);
-    pat[e] = x;
+    if (wd < 2)
+      for (int nib = 0; nib < 8; ++nib)
+        if (wd * 8 + nib < n) x |= one << (4 * nib);
+    pat[w] = x;
   }
 }
 
-// Copy the paired table of band b, rung k (rows of KLpad bytes, one per B
-// level) into LDS rows of PT_STRIDE bytes.
+// The paired table of band b, rung k as e2m1 nibbles (value v -> code 2 v,
+// position p in nibble p mod 2 of byte p / 2), one LDS row of PT_STRIDE
+// bytes per B level.
 __device__ __forceinline__ void stage_pair_table(uint8_t* pt, const MatmulArgs& a, int b, int k, int KLpad, int tid,
                                                  int nthreads) {
   const uint8_t* src = a.pair + a.pair_off[b][k];
   const int vec_per_row = KLpad >> 4;
   for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += nthreads) {
     const int u = idx / vec_per_row, v = idx - u * vec_per_row;
-    *(int4*)(pt + u * PT_STRIDE + v * 16) = *(const int4*)(src + (long long)u * KLpad + v * 16);
+    const uint4 x = *(const uint4*)(src + (long long)u * KLpad + v * 16);
+    auto pack = [](uint32_t wd) {
+      const uint32_t t = wd << 1;  // bytes <= 2: doubling never carries
+      return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
+    };
+    *(uint2*)(pt + u * PT_STRIDE + v * 8) = uint2{pack(x.x) | (pack(x.y) << 16), pack(x.z) | (pack(x.w) << 16)};
   }
 }
 
-// Tile shape of the contraction: 4 waves as 2 x 2, each owning WR row
-// subtiles and 2 column subtiles of 32 x 32.  WR = 4 (256 x 128 blocks, 16
-// indices per LDS stage) reuses every gathered B fragment four times; the
-// chunked variants keep WR = 2 (128 x 128, 32 indices per stage) because
-// they also hold float accumulators.
-template <int WR>
-struct MfTile {
-  static constexpr int BM = 64 * WR;
-  static constexpr int BN = 128;
-  static constexpr int DC = WR == 2 ? 32 : 16;
-  static constexpr int SUB = BM / MF_BM;  // 128-row encode tiles per block
+// Operands of one step for this lane half: half-blocks X (row codes hx of
+// rows l32 and l32 + 32, column table offsets ux of columns l32 and l32 + 32,
+// first position kx) and Y.  A from the pattern table, B from the nibble
+// table at row offset + k / 2.
+struct Frag {
+  v8i a[2], b[2];
 };
+__device__ __forceinline__ Frag frags_at(const uint8_t* pat, const uint8_t* pt, uint32_t hx, uint32_t ux, uint32_t kx,
+                                         uint32_t hy, uint32_t uy, uint32_t ky) {
+  Frag f;
+  const v2i ax0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx & 0xffffu, 32u * kx));
+  const v2i ax1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx >> 16, 32u * kx));
+  const v2i ay0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy & 0xffffu, 32u * ky));
+  const v2i ay1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy >> 16, 32u * ky));
+  const v2i bx0 = *(const v2i*)(pt + (ux & 0xffffu) + (kx >> 1));
+  const v2i bx1 = *(const v2i*)(pt + (ux >> 16) + (kx >> 1));
+  const v2i by0 = *(const v2i*)(pt + (uy & 0xffffu) + (ky >> 1));
+  const v2i by1 = *(const v2i*)(pt + (uy >> 16) + (ky >> 1));
+  f.a[0] = v8i{ax0.x, ax0.y, ay0.x, ay0.y, 0, 0, 0, 0};
+  f.a[1] = v8i{ax1.x, ax1.y, ay1.x, ay1.y, 0, 0, 0, 0};
+  f.b[0] = v8i{bx0.x, bx0.y, by0.x, by0.y, 0, 0, 0, 0};
+  f.b[1] = v8i{bx1.x, bx1.y, by1.x, by1.y, 0, 0, 0, 0};
+  return f;
+}
 
+// One step: the wave's 2 x 2 subtiles of 32 x 32.
+__device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Frag& f) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+      acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[jj], acc[i][jj], 4, 4, 0, 127, 0, 127);
+}
+
+// ------------------------------------------------------------ staged ----
+// One block per 128 x 128 output tile (grid: column tiles, row tiles,
+// groups); handles chunk scales and K-bands.  The tile's row and column
+// codes pass through LDS 32 contraction indices (a stage) at a time, double
+// buffered; one wave lists the stage's work while the stage is stored.
 // Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
 // that also write per-band counts keep a third accumulator set and run one.
-template <bool CHUNKED, bool COUNTS, int WR>
+template <bool CHUNKED, bool COUNTS>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, MfmaWs w) {
-  using T = MfTile<WR>;
-  constexpr int BM = T::BM, BN = T::BN, DC = T::DC, SUB = T::SUB;
+  constexpr int BM = MF_BM, BN = MF_BN, DC = MF_DC;
   // The two gather tables share one object (the largest, laid out first) so
   // that both sit below 64 KB, where a constant base folds into the LDS
-  // instruction's offset: the paired table (one row per B level) and the A
-  // fragment patterns by window code.
+  // instruction's offset.
   struct __align__(16) GatherTables {
     uint8_t pt[MAX_LEVELS * PT_STRIDE];
     uint32_t pat[PAT_WORDS];
   };
   __shared__ GatherTables s_tab;
-  uint8_t* const s_pt = s_tab.pt;
-  uint32_t* const s_pat = s_tab.pat;
-  __shared__ __align__(16) uint16_t s_h[2][DC][BM];
-  __shared__ __align__(16) uint16_t s_u[2][DC][BN];
+  const uint8_t* const s_pt = s_tab.pt;
+  const uint8_t* const s_pat = (const uint8_t*)s_tab.pat;
+  __shared__ __align__(16) uint32_t s_h[2][DC][BM / 2];  // stage code words, [index][row pair]
+  __shared__ __align__(16) uint32_t s_u[2][DC][BN / 2];  // [index][column pair]
   // Stage schedule: the half-blocks past the stage's full levels in order,
-  // then padding entries (a zero half-block), and the number of MFMA steps
-  // they take.
-  constexpr int SCHED_N = DC * 8 + 8;
-  __shared__ uint16_t s_sched[2][SCHED_N];
+  // then padding entries (a zero half-block), and the steps they take.
+  constexpr int SCHED_N = DC * 8 + 16;
+  __shared__ __align__(4) uint16_t s_sched[2][SCHED_N];
   __shared__ int s_nsteps[2];
   __shared__ int s_full[2];  // leading levels needed by every index of the stage
-  __shared__ int s_rows[BM];
+  __shared__ __align__(16) int s_rows[BM];
   __shared__ __align__(16) int s_rc[BM];      // n0 sum of each row over the chunk (or axis) being decoded
   __shared__ __align__(16) float s_sa[BM];    // row scale of that chunk
 
   const int tid = threadIdx.x;
-  const int g = blockIdx.z, y = blockIdx.y;
-  // Row tile: BM consecutive sorted positions of one rung, covering the
-  // encode tiles T0 .. T0 + nsub - 1 (128 rows each).
-  int k = 0;
-  while (k + 1 < a.n_rungs && y >= a.tile_start2[k + 1]) ++k;
-  const int t = y - a.tile_start2[k];
-  const int pos0 = a.cuts[k] + t * BM;
-  const int nrows = min(BM, a.cuts[k + 1] - pos0);
-  const int T0 = a.tile_start[k] + t * SUB;
-  const int nsub = min(SUB, a.tile_start[k + 1] - T0);
-  const long long prow0 = (long long)T0 * MF_BM;
+  const int g = blockIdx.z, y = blockIdx.y;  // y: encode tile (128 rows of one rung)
+  int k, pos0, nrows;
+  locate_tile(a, y, BM, k, pos0, nrows);
+  const long long prow0 = (long long)y * BM;
   const int col0 = blockIdx.x * BN;
-
   for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
-  init_patterns(s_pat, tid, 256);
+  init_patterns(s_tab.pat, tid, 256);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wr = wave >> 1, wc = wave & 1;
   const int l32 = lane & 31, hf = lane >> 5;
   const int qq = a.q * a.q;
-  const int wrow0 = wr * 32 * WR;  // first row of this wave
-  const int wcol0 = wc * 64;       // first column of this wave
+  const int wrow0 = wr * 64;  // first row of this wave
+  const int wcol0 = wc * 64;  // first column of this wave
 
   // Stage loader: thread (pair pr = tid / 4, quarter q = tid % 4) reads the
   // code words of indices [d0 + 8 q, d0 + 8 q + 8) of row pair pr and of
   // column pair pr (two 16-byte loads each, into named registers so they
   // stay in VGPRs) and stores them as the stage's [index][pair] words.
-  static_assert(SUB == 1 && BM == 128 && BN == 128 && DC == 32, "stage loader shape");
   int4 rh0, rh1, ru0, ru1;
   int rmx = 0;
   const int lpr = tid >> 2, lq = tid & 3;
-  const uint32_t* hrow_g = w.hs + ((long long)g * (w.Mp / 2) + (long long)T0 * 64 + lpr) * w.Dp + 8 * lq;
+  const uint32_t* hrow_g = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + lpr) * w.Dp + 8 * lq;
   const uint32_t* urow_g = w.ub + ((long long)g * (w.Np / 2) + (long long)(col0 / 2) + lpr) * w.Dp + 8 * lq;
   auto fetch = [&](int d0) {
     rh0 = *(const int4*)(hrow_g + d0);
     rh1 = *(const int4*)(hrow_g + d0 + 4);
     ru0 = *(const int4*)(urow_g + d0);
     ru1 = *(const int4*)(urow_g + d0 + 4);
-    if (tid < DC) rmx = w.maxh[((long long)g * w.RT + T0) * w.Dp + d0 + tid];
+    if (tid < DC) rmx = w.maxh[((long long)g * w.RT + y) * w.Dp + d0 + tid];
   };
   auto store = [&](int bf) {
-    uint32_t* sh = (uint32_t*)&s_h[bf][0][0];  // [DC][64] words
-    uint32_t* su = (uint32_t*)&s_u[bf][0][0];
     const int hv[8] = {rh0.x, rh0.y, rh0.z, rh0.w, rh1.x, rh1.y, rh1.z, rh1.w};
     const int uv[8] = {ru0.x, ru0.y, ru0.z, ru0.w, ru1.x, ru1.y, ru1.z, ru1.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      sh[(8 * lq + i) * 64 + lpr] = (uint32_t)hv[i];
-      su[(8 * lq + i) * 64 + lpr] = (uint32_t)uv[i];
+      s_h[bf][8 * lq + i][lpr] = (uint32_t)hv[i];
+      s_u[bf][8 * lq + i][lpr] = (uint32_t)uv[i];
     }
     if (tid < 64) {
       // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
       // tile maximum rmx) needs positions [16 j, 16 j + 16) for every
-      // j < ceil(rmx / 16); they are listed level by level (j-major),
-      // indices in order within a level.  Entry: d * 256 + kk (the byte
-      // offset of index d's codes in a stage row pair, and the first paired
-      // position kk = 16 j).
+      // j < ceil(rmx / 16); the leading levels every index needs are swept
+      // without a list, the rest are listed level by level, indices in
+      // order within a level.  Entry: d * 256 + kk (the byte offset of index
+      // d's words in a stage row, and the first paired position kk = 16 j).
       const int m = tid < DC ? rmx : 0;
-      // Leading levels that every index needs are swept without a list.
       int full = 0;
       while (full < 8 && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
       int base = 0;
@@ -461,27 +484,27 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         }
         base += __builtin_popcountll(bal);
       }
-      // Padding: position 128 is past every window (A bytes all zero).
-      if (tid < 8) s_sched[bf][base + tid] = (uint16_t)128u;
+      // Padding: position 128 is past every window (A nibbles all zero).
+      if (tid < 16) s_sched[bf][base + tid] = (uint16_t)128u;
       if (tid == 0) s_full[bf] = full;
-      if (tid == 0) s_nsteps[bf] = (base + 1) >> 1;
+      if (tid == 0) s_nsteps[bf] = (base + 3) >> 2;
     }
   };
 
-  v16i acc[WR][2];
-  float cacc[WR][2][16];
-  int bacc[WR][2][16];
+  v16f acc[2][2];
+  float cacc[2][2][16];
+  int bacc[2][2][16];
 #pragma unroll
-  for (int i = 0; i < WR; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        acc[i][j][v] = 0;
+        acc[i][j][v] = 0.0f;
         if (CHUNKED) cacc[i][j][v] = 0.0f;
         if (COUNTS) bacc[i][j][v] = 0;
       }
-  unsigned long long issued = 0;  // MFMA steps this row tile issues (counted by the x == 0 blocks)
+  unsigned long long issued = 0;  // fp4 MFMA steps of this row tile (counted by the x == 0 blocks)
 
   int buf = 0;
   fetch(a.band_cols[0]);
@@ -491,7 +514,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     const float scaleL = (float)qq / (float)L;
     const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
     __syncthreads();  // every wave is done with the previous band's table
-    stage_pair_table(s_pt, a, b, k, KLpad, tid, 256);
+    stage_pair_table(s_tab.pt, a, b, k, KLpad, tid, 256);
     store(buf);
     __syncthreads();
     for (int d0 = dbeg; d0 < dend; d0 += DC) {
@@ -501,55 +524,31 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // Work of a stage: for every staged index d, the 16-position blocks
         // [16 j, 16 j + 16) of paired positions with j < ceil(mx_d / 16),
         // mx_d being the largest half-window of the tile's rows at d (rows'
-        // windows nest inside it; past a row's own window its A bytes are 0).
-        // One MFMA step takes two such half-blocks: lanes 0-31 contract the
-        // first (its index's row codes and column levels, positions
-        // [kk, kk + 16)), lanes 32-63 the second; the MFMA sums both halves
-        // into the same accumulators, so any two half-blocks may share a
-        // step.  Step s takes schedule entries 2 s and 2 s + 1; a lone last
-        // half-block is paired with a padding entry.
-        static_assert(WR == 2, "the interleaved row codes serve two row subtiles per wave");
-        static_assert(DC == 32, "one index per lane of a half-wave");
-        const char* hbase = (const char*)((const uint32_t*)&s_h[buf][0][wrow0] + l32);
-        const char* ubase = (const char*)((const uint32_t*)&s_u[buf][0][wcol0] + l32);
-        const uint16_t* sched = &s_sched[buf][hf];
+        // windows nest inside it; past a row's own window its A nibbles are
+        // zero).  Any four half-blocks may share a step: lanes 0-31 take
+        // the first two (X, Y), lanes 32-63 the other two.
+        const char* hbase = (const char*)&s_h[buf][0][wr * 32 + l32];
+        const char* ubase = (const char*)&s_u[buf][0][wc * 32 + l32];
+        const uint32_t* sched = (const uint32_t*)&s_sched[buf][0] + hf;  // entry pairs
         const int n = s_nsteps[buf];
-        struct Frag {
-          v4i a[WR], b[2];
-        };
-        // A half-block as this lane sees it: the window codes of rows l32 and
-        // l32 + 32 (h), the table offsets of columns l32 and l32 + 32 (u),
-        // and its schedule entry (e).
+        const int full = s_full[buf];
+        // Two half-blocks as this lane sees them: the row and column words
+        // of X and Y and their schedule entries (X low, Y high half of e).
         struct Item {
-          uint32_t h, u, e;
+          uint32_t hx, ux, hy, uy, e;
         };
         auto item = [&](uint32_t e) __attribute__((always_inline)) {
-          const uint32_t off = e & 0x1f00u;
-          return Item{*(const uint32_t*)(hbase + off), *(const uint32_t*)(ubase + off), e};
-        };
-        auto frags_at = [&](uint32_t h, uint32_t u, uint32_t kk, uint32_t kk32) __attribute__((always_inline)) {
-          Frag f;
-          f.a[0] = a_frag((const uint8_t*)s_pat, h & 0xffffu, kk32);
-          f.a[1] = a_frag((const uint8_t*)s_pat, h >> 16, kk32);
-          f.b[0] = *(const v4i*)(s_pt + (u & 0xffffu) + kk);
-          f.b[1] = *(const v4i*)(s_pt + (u >> 16) + kk);
-          return f;
+          const uint32_t ox = e & 0x1f00u, oy = (e >> 16) & 0x1f00u;
+          return Item{*(const uint32_t*)(hbase + ox), *(const uint32_t*)(ubase + ox),
+                      *(const uint32_t*)(hbase + oy), *(const uint32_t*)(ubase + oy), e};
         };
         auto frags = [&](const Item& c) __attribute__((always_inline)) {
-          const uint32_t kk = c.e & 0xffu;
-          return frags_at(c.h, c.u, kk, 32u * kk);
-        };
-        auto mma = [&](const Frag& f) __attribute__((always_inline)) {
-#pragma unroll
-          for (int i = 0; i < WR; ++i)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-              acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
+          return frags_at(s_pat, s_pt, c.hx, c.ux, c.e & 0xffu, c.hy, c.uy, (c.e >> 16) & 0xffu);
         };
         // Software-pipelined sweep over steps 0 .. cnt - 1, ent(s) giving the
-        // lane's schedule entry of step s (any entry past the end is a zero
+        // lane's entry pair of step s (any entry past the end is a zero
         // half-block): while step s's MFMAs run, the fragments of step s + 1,
-        // the codes of step s + 2 and the entry of step s + 3 are in flight
+        // the codes of step s + 2 and the entries of step s + 3 are in flight
         // (LDS reads complete in order, so each is read a step ahead of the
         // reads it addresses).  Two fragment sets are used in turn.
         auto sweep = [&](int cnt, auto&& ent) __attribute__((always_inline)) {
@@ -565,68 +564,34 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
             e2 = e3;
             c1 = c2;
             __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
-            mma(fa);
+            mma_step(acc, fa);
             e3 = ent(st + 4);
             c2 = item(e2);
             fa = frags(c1);
             e2 = e3;
             c1 = c2;
             __builtin_amdgcn_sched_barrier(0);
-            mma(fb);
+            mma_step(acc, fb);
           }
           // Last one or two steps.
           if (cnt - st == 2) fb = frags(c1);
           __builtin_amdgcn_sched_barrier(0);
-          mma(fa);
-          if (cnt - st == 2) mma(fb);
+          mma_step(acc, fa);
+          if (cnt - st == 2) mma_step(acc, fb);
         };
-        // Full levels: step s = 16 j + m takes positions [16 j, 16 j + 16) of
-        // indices 2 m (lanes 0-31) and 2 m + 1 (lanes 32-63).
-        const int full = s_full[buf];
-        if constexpr (!CHUNKED) {
-          // The codes of these 16 index pairs serve every full level: read
-          // once into registers, so a step only forms its fragment addresses.
-          if (full > 0) {
-            uint32_t ch[16], cu[16];
-            const uint32_t* hq = (const uint32_t*)(hbase + 256 * hf);
-            const uint32_t* uq = (const uint32_t*)(ubase + 256 * hf);
-#pragma unroll
-            for (int m = 0; m < 16; ++m) {
-              ch[m] = hq[128 * m];
-              cu[m] = uq[128 * m];
-            }
-            Frag fa = frags_at(ch[0], cu[0], 0u, 0u), fb;
-            for (int j = 0; j < full; ++j) {
-              const uint32_t kk = 16u * j, kk32 = 512u * j;
-#pragma unroll
-              for (int m = 0; m < 16; m += 2) {
-                fb = frags_at(ch[m + 1], cu[m + 1], kk, kk32);
-                __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
-                mma(fa);
-                // Next: pair m + 2 of this level, or pair 0 of the next level
-                // (read but unused after the last level; position <= 128
-                // stays inside the table rows).
-                if (m + 2 < 16)
-                  fa = frags_at(ch[m + 2], cu[m + 2], kk, kk32);
-                else
-                  fa = frags_at(ch[0], cu[0], kk + 16u, kk32 + 512u);
-                __builtin_amdgcn_sched_barrier(0);
-                mma(fb);
-              }
-            }
-          }
-        } else {
-          // Chunked variants (short of registers for the resident codes).
-          if (full > 0)
-            sweep(16 * full, [&](int st) {
-              const uint32_t j = (uint32_t)(st >> 4) & 7u, d = (uint32_t)(2 * (st & 15) + hf);
-              return d * 256u + 16u * j;
-            });
-        }
+        // Full levels: step 8 j + m takes level j of indices 16 hf + m (X)
+        // and 16 hf + 8 + m (Y).  Past the last level the entries fall on
+        // level full <= 8 (position <= 128, inside the table rows): read,
+        // never used.
+        if (full > 0)
+          sweep(8 * full, [&](int st) {
+            const uint32_t j = (uint32_t)(st >> 3) & 15u, m = (uint32_t)(st & 7);
+            const uint32_t dx = 16u * hf + m, dy = dx + 8u;
+            return (dx * 256u + 16u * j) | ((dy * 256u + 16u * j) << 16);
+          });
         // The rest from the stage's list.
-        if (n > 0) sweep(n, [&](int st) { return (uint32_t)sched[2 * st]; });
-        const unsigned steps = n + 16 * full;
-        if (blockIdx.x == 0 && tid == 0) issued += steps;
+        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; });
+        if (blockIdx.x == 0 && tid == 0) issued += n + 8 * full;
       }
       const int cend = chunk_end(a, d0);
       if (CHUNKED && min(dn, dend) >= cend) {
@@ -635,7 +600,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         const int cw = cend - ch * a.chunk_d;
         for (int r = tid; r < BM; r += 256) {
           const int row = s_rows[r];
-          s_rc[r] = r < nsub * MF_BM ? w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + prow0 + r] : 0;
+          s_rc[r] = w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + prow0 + r];
           s_sa[r] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
         }
         __syncthreads();
@@ -648,7 +613,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // Rows four at a time (accumulator entries v = 4 q .. 4 q + 3 are
         // consecutive rows), used by both column subtiles at once.
 #pragma unroll
-        for (int i = 0; i < WR; ++i)
+        for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
@@ -661,10 +626,10 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
 #pragma unroll
               for (int j = 0; j < 2; ++j) {
                 const int v = q4 * 4 + e;
-                const int cnt = acc[i][j][v] + rcv[e];
+                const int cnt = (int)acc[i][j][v] + rcv[e];
                 cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * (float)(2 * cnt - L * cw));
                 if (COUNTS) bacc[i][j][v] += cnt;
-                acc[i][j][v] = 0;
+                acc[i][j][v] = 0.0f;
               }
           }
         __syncthreads();  // s_rc / s_sa are rewritten at the next chunk
@@ -677,7 +642,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (CHUNKED && COUNTS) {
 #pragma unroll
-      for (int i = 0; i < WR; ++i)
+      for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int col = col0 + wcol0 + j * 32 + l32;
@@ -693,17 +658,15 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
   }
-  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued, issued);  // int8 steps
+  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued + 1, issued);  // fp4 steps
 
   if (!CHUNKED) {
     // Each row's n0 sum over the whole contraction axis: the parts' partial
     // sums, added once per row into LDS.
     for (int r = tid; r < BM; r += 256) {
       int tot = 0;
-      if (r < nsub * MF_BM) {
-        const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + prow0 + r;
-        for (int pt = 0; pt < w.n_parts; ++pt) tot += rc0[(long long)pt * w.Mp];
-      }
+      const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + prow0 + r;
+      for (int pt = 0; pt < w.n_parts; ++pt) tot += rc0[(long long)pt * w.Mp];
       s_rc[r] = tot;
     }
     __syncthreads();
@@ -715,7 +678,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     const int col = col0 + wcol0 + j * 32 + l32;
     const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < WR; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int r = wrow0 + i * 32 + (v >> 2) * 8 + hf * 4 + (v & 3);
@@ -725,7 +688,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (CHUNKED) {
           out = cacc[i][j][v];
         } else {
-          const int cnt = acc[i][j][v] + s_rc[r];
+          const int cnt = (int)acc[i][j][v] + s_rc[r];
           if (COUNTS) a.counts[((long long)g * a.M + row) * a.N + col] = cnt;
           const float sa = a.sA[(long long)g * a.M + row];
           out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
@@ -735,20 +698,20 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   }
 }
 
-// ------------------------------------------------ persistent variant ----
+// ------------------------------------------------------- persistent ----
 // The single-segment contraction (no chunk scales, one band) as a
 // persistent kernel: each block takes 128 x 128 output tiles from a work
-// counter, in rung order, so the paired table is staged again only when the
-// rung changes, and the next tile's row data are read while the current
-// tile is contracted (its output stores then drain behind the next tile's
-// contraction).  Within a tile every wave reads its own row and column
-// codes straight from the encode buffers into registers, one group of 32
-// contraction indices ahead, with no block-wide synchronisation.  Per
-// group, the levels every index needs (16-position half-blocks, as in
-// k_mfma) are swept from those registers; the remaining half-blocks go to a
-// list in this wave's own part of LDS and are contracted, two per step,
-// when the list fills and at the end, with their codes read from the encode
-// buffers a few steps ahead.
+// counter, in rung order (which balances the rungs' different tile costs),
+// so the paired table is staged again only when the rung changes, and the
+// next tile's row data are read while the current tile is contracted (its
+// output stores then drain behind the next tile's contraction).  Within a
+// tile every wave reads its own row and column codes straight from the
+// encode buffers into registers, one group of 32 contraction indices ahead,
+// with no block-wide synchronisation.  Per group, the levels every index
+// needs are swept from those registers; the remaining half-blocks go to a
+// list in this wave's own part of LDS and are contracted, four per step,
+// when the list fills and at the end, with their codes read from the
+// index-major copies of the encode buffers a few steps ahead.
 constexpr int FL_LIST = 512;  // list capacity per wave (half-blocks)
 constexpr int FL_RING = 4;    // list steps whose codes are in flight
 constexpr int FL_PAD = 4 * FL_RING + 4;  // padding entries past a list's end
@@ -784,13 +747,14 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     uint32_t pat[PAT_WORDS];
   };
   __shared__ GatherTables s_tab;
-  __shared__ uint32_t s_list[4][FL_LIST];
+  __shared__ __align__(8) uint32_t s_list[4][FL_LIST];
   __shared__ __align__(16) int s_rows[2][MF_BM];    // original row of each position (-1: none)
   __shared__ __align__(16) int s_rc[2][MF_BM];      // each row's n0 sum over the contraction axis
   __shared__ __align__(16) float s_sa[2][MF_BM];    // each row's scale
   __shared__ int s_item[2];
   uint8_t* const s_pt = s_tab.pt;
   uint32_t* const s_pat = s_tab.pat;
+  constexpr int PAD4 = 8 * FL_RING + 4;  // padding entries past a list's end
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -799,7 +763,6 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
   const int wrow0 = wr * 64, wcol0 = wc * 64;
   uint32_t* const list = s_list[wave];
   const int qq = a.q * a.q;
-
 
   // Row data of tile y in group g for position tid (< 128): original row,
   // n0 summed over the encode parts, row scale.
@@ -830,388 +793,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     s_sa[0][tid] = sa;
   }
 
-  struct Frag {
-    v4i a[2], b[2];
-  };
-  auto frags_at = [&](uint32_t h, uint32_t u, uint32_t kk, uint32_t kk32) __attribute__((always_inline)) {
-    Frag f;
-    f.a[0] = a_frag((const uint8_t*)s_pat, h & 0xffffu, kk32);
-    f.a[1] = a_frag((const uint8_t*)s_pat, h >> 16, kk32);
-    f.b[0] = *(const v4i*)(s_pt + (u & 0xffffu) + kk);
-    f.b[1] = *(const v4i*)(s_pt + (u >> 16) + kk);
-    return f;
-  };
-  // A list entry is (index << 4) | level; level 8 (position 128, past every
-  // window) is the zero half-block used as padding.
-  auto frags_e = [&](uint32_t h, uint32_t u, uint32_t e) __attribute__((always_inline)) {
-    const uint32_t j = e & 15u;
-    return frags_at(h, u, 16u * j, 512u * j);
-  };
-  v16i acc[2][2];
-  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        acc[i][jj] = __builtin_amdgcn_mfma_i32_32x32x32_i8(f.a[i], f.b[jj], acc[i][jj], 0, 0, 0);
-  };
-  unsigned long long issued = 0;  // MFMA steps of the column-0 tiles
-  int staged_k = -1;
-  int cur = 0;
-
-  while (true) {
-    const PersItem it = pers_item(a, w.CT, item);
-    const int k = it.k, g = it.g, y = it.y;
-    const int col0 = it.x * MF_BN;
-    const long long prow0 = (long long)y * MF_BM;
-    const bool count_steps = it.x == 0;
-    const int next = s_item[cur ^ 1];
-    // The next tile's row data, read now and stored after this tile.
-    int nrow = -1, nrc = 0;
-    float nsa = 0.0f;
-    if (next < n_items && tid < MF_BM) {
-      const PersItem nt = pers_item(a, w.CT, next);
-      row_data(nt.g, nt.y, nrow, nrc, nsa);
-    }
-    const int L = a.bandL[0][k];
-    if (k != staged_k) {
-      // Every wave finished the previous tile (the loop ends on a barrier).
-      const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
-      stage_pair_table(s_pt, a, 0, k, KLpad, tid, 256);
-      __syncthreads();
-      staged_k = k;
-    }
-
-    // This lane's rows of the encode buffers: row pair wr * 32 + l32 of tile
-    // y (rows wrow0 + l32 and wrow0 + l32 + 32) and column pair
-    // wc * 32 + l32 of column tile x, one code word per contraction index.
-    const uint32_t* hrow = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32) * w.Dp;
-    const uint32_t* urow = w.ub + ((long long)g * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32) * w.Dp;
-    const uint8_t* mq = w.maxh + ((long long)g * w.RT + y) * w.Dp;
-    // List steps read one index for all pairs: the index-major copies.
-    const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
-    const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
-    const long long hstr = w.Mp / 2, ustr = w.Np / 2;
-    auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hcol[(long long)d * hstr]; };
-    auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ucol[(long long)d * ustr]; };
-
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0;
-
-    // Contract the wave's list of cnt half-blocks, two per step (lanes 0-31
-    // take entry 2 s, lanes 32-63 entry 2 s + 1).  Slot r of the ring holds
-    // the entry and codes of a step FL_RING steps ahead; its fragments are
-    // read one step ahead of its MFMAs.  dpad: any index of the band, for
-    // the padding entries' (unused) codes.
-    auto list_sweep = [&](int cnt, int dpad) __attribute__((always_inline)) {
-      if (lane < FL_PAD) list[cnt + lane] = ((uint32_t)dpad << 4) | 8u;
-      const int nsteps = (cnt + 1) >> 1;
-      uint32_t re[FL_RING], rh[FL_RING], ru[FL_RING];
-#pragma unroll
-      for (int r = 0; r < FL_RING; ++r) {
-        re[r] = list[2 * r + hf];
-        rh[r] = hword(re[r] >> 4);
-        ru[r] = uword(re[r] >> 4);
-      }
-      uint32_t enext = list[2 * FL_RING + hf];
-      Frag fr[2];
-      fr[0] = frags_e(rh[0], ru[0], re[0]);
-      for (int s0 = 0; s0 < nsteps; s0 += FL_RING) {
-#pragma unroll
-        for (int r = 0; r < FL_RING; ++r) {
-          const int rn = (r + 1) % FL_RING;
-          fr[(r + 1) & 1] = frags_e(rh[rn], ru[rn], re[rn]);
-          // Slot r now serves step s0 + r + FL_RING.
-          re[r] = enext;
-          rh[r] = hword(enext >> 4);
-          ru[r] = uword(enext >> 4);
-          enext = list[2 * (s0 + r + FL_RING + 1) + hf];
-          __builtin_amdgcn_sched_barrier(0);
-          if (s0 + r < nsteps) mma(fr[r & 1]);
-        }
-      }
-      if (count_steps) issued += nsteps;
-    };
-
-    const int dbeg = a.band_cols[0], dend = a.band_cols[1];
-    const int ngrp = (dend - dbeg + 31) / 32;
-    // A group's loads: the codes of indices d0 + 16 hf + m, m < 16 (four
-    // 16-byte loads per buffer), so pair step m takes index d0 + m in lanes
-    // 0-31 and d0 + 16 + m in lanes 32-63; and this lane's index maximum
-    // (raw: the band's bound is applied where it is used, so that nothing
-    // waits for the loads here).
-    auto load_group = [&](int d0, uint32_t* h, uint32_t* u, int& m) __attribute__((always_inline)) {
-      const uint4* hp = (const uint4*)(hrow + d0 + 16 * hf);
-      const uint4* up = (const uint4*)(urow + d0 + 16 * hf);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint4 th = hp[i], tu = up[i];
-        h[4 * i] = th.x;
-        h[4 * i + 1] = th.y;
-        h[4 * i + 2] = th.z;
-        h[4 * i + 3] = th.w;
-        u[4 * i] = tu.x;
-        u[4 * i + 1] = tu.y;
-        u[4 * i + 2] = tu.z;
-        u[4 * i + 3] = tu.w;
-      }
-      m = mq[d0 + l32];  // d0 + l32 < Dp
-    };
-    int cnt = 0;  // entries in this wave's list
-    // fa: the fragments of the group's first step (level 0, pair 0), read
-    // at the end of the previous group.
-    Frag fa;
-    // One group: its codes (ch, cu) and this lane's index maximum (mx) are
-    // in registers; nh, nu: the next group's codes.
-    auto group = [&](int grp, const uint32_t* ch, const uint32_t* cu, int mx, const uint32_t* nh,
-                     const uint32_t* nu) __attribute__((always_inline)) {
-      const int d0 = dbeg + 32 * grp;
-      // Index d0 + l32 needs nl half-blocks; the leading levels every index
-      // needs are swept here, the rest listed (level-major).
-      const int nl = d0 + l32 < dend ? (mx + 15) >> 4 : 0;
-      int full = 0;
-      for (int j = 0; j < 8; ++j) {
-        const unsigned bal = (unsigned)__ballot(nl > j);
-        if (bal == 0) break;
-        if (bal == 0xffffffffu && j == full) {
-          ++full;
-          continue;
-        }
-        if (hf == 0 && nl > j)
-          list[cnt + (int)__builtin_amdgcn_mbcnt_lo(bal, 0u)] = ((uint32_t)(d0 + l32) << 4) | (uint32_t)j;
-        cnt += __builtin_popcount(bal);
-      }
-      if (full > 0) {
-        Frag fb;
-        for (int j = 0; j < full; ++j) {
-          const uint32_t kk = 16u * j, kk32 = 512u * j;
-#pragma unroll
-          for (int m = 0; m < 16; m += 2) {
-            fb = frags_at(ch[m + 1], cu[m + 1], kk, kk32);
-            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
-            mma(fa);
-            // Next: pair m + 2 of this level or pair 0 of the next level
-            // (after the last level: read, unused; position <= 128 stays
-            // inside the table rows).
-            if (m + 2 < 16)
-              fa = frags_at(ch[m + 2], cu[m + 2], kk, kk32);
-            else
-              fa = frags_at(ch[0], cu[0], kk + 16u, kk32 + 512u);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fb);
-          }
-        }
-        if (count_steps) issued += 16 * full;
-      }
-      // The next group adds at most 256 entries.
-      if (cnt > FL_LIST - 256 - FL_PAD || (grp == ngrp - 1 && cnt > 0)) {
-        list_sweep(cnt, d0);
-        cnt = 0;
-      }
-      // The next group's first step, read while this group's last MFMAs
-      // run and the next group's levels are counted.
-      fa = frags_at(nh[0], nu[0], 0u, 0u);
-    };
-    // Two register sets in turn: the next group's codes load while this
-    // group is contracted.  The look-ahead loads are unconditional (past the
-    // last group they repeat it), so every path issues the same loads and
-    // the waits for a set count only the loads issued after it.
-    if (ngrp > 0) {
-      uint32_t ha[16], ua[16], hb[16], ub[16];
-      int ma, mb = 0;
-      load_group(dbeg, ha, ua, ma);
-      fa = frags_at(ha[0], ua[0], 0u, 0u);
-      for (int grp = 0; grp < ngrp; grp += 2) {
-        load_group(dbeg + 32 * min(grp + 1, ngrp - 1), hb, ub, mb);
-        group(grp, ha, ua, ma, hb, ub);
-        if (grp + 1 >= ngrp) break;
-        load_group(dbeg + 32 * min(grp + 2, ngrp - 1), ha, ua, ma);
-        group(grp + 1, hb, ub, mb, ha, ua);
-      }
-    }
-
-    // The next tile's row data into the other buffer; the tile after it.
-    if (tid < MF_BM) {
-      s_rows[cur ^ 1][tid] = nrow;
-      s_rc[cur ^ 1][tid] = nrc;
-      s_sa[cur ^ 1][tid] = nsa;
-    }
-    if (tid == 0) s_item[cur] = next < n_items ? (int)atomicAdd(w.work, 1u) : n_items;
-
-    // Decode: rows four at a time (accumulator entries v = 4 q .. 4 q + 3
-    // are consecutive rows), each used by both column subtiles.
-    const float scale0 = (float)qq / (float)L;
-    float sb[2];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = col0 + wcol0 + j * 32 + l32;
-      sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
-    }
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
-        const int4 rw = *(const int4*)&s_rows[cur][r0];
-        const int4 rc = *(const int4*)&s_rc[cur][r0];
-        const float4 sa = *(const float4*)&s_sa[cur][r0];
-        const int rowv[4] = {rw.x, rw.y, rw.z, rw.w};
-        const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
-        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            const int col = col0 + wcol0 + j * 32 + l32;
-            if (rowv[e] < 0 || col >= a.N) continue;
-            const int cnt2 = acc[i][j][q4 * 4 + e] + rcv[e];
-            if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
-            if (a.C)
-              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + col] =
-                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D));
-          }
-      }
-    __syncthreads();  // publishes the next tile's row data and item
-    if (next >= n_items) break;
-    item = next;
-    cur ^= 1;
-  }
-  if (tid == 0 && issued) atomicAdd(w.issued, issued);  // int8 steps
-}
-
-// ------------------------------------------- persistent variant, fp4 ----
-// The persistent contraction on the fp4 matrix cores
-// (v_mfma_scale_f32_32x32x64_f8f6f4 with e2m1 operands, unit scales): the
-// A bytes {-1, 0, +1} and the pair sums {0, 1, 2} are exact in e2m1 and the
-// fp32 accumulators hold the integer counts exactly (below 2^24).  One lane
-// half of an MFMA covers 32 nibbles, so it takes two 16-position
-// half-blocks (X in nibbles 0-15, Y in 16-31): four half-blocks per MFMA
-// step, twice the int8 step, with the same bytes read per half-block.
-typedef int v2i __attribute__((ext_vector_type(2)));
-typedef int v8i __attribute__((ext_vector_type(8)));
-typedef float v16f __attribute__((ext_vector_type(16)));
-
-// fp4 A patterns: entry e (16-byte stride, first 8 bytes used) holds
-// min(e / 2, 16) leading sign nibbles, 0xA (-1) when e is odd, 0x2 (+1)
-// otherwise, then zero nibbles (low nibble first).
-__device__ __forceinline__ void init_patterns4(uint32_t* pat, int tid, int nthreads) {
-  for (int w = tid; w < PAT_WORDS; w += nthreads) {
-    const int e = w >> 2, wd = w & 3, n = min(e >> 1, 16);
-    const uint32_t one = (e & 1) ? 0xAu : 0x2u;
-    uint32_t x = 0;
-    if (wd < 2)
-      for (int nib = 0; nib < 8; ++nib)
-        if (wd * 8 + nib < n) x |= one << (4 * nib);
-    pat[w] = x;
-  }
-}
-
-// The paired table of band b, rung k as e2m1 nibbles (value v -> code 2 v,
-// position p in nibble p mod 2 of byte p / 2), rows of PT_STRIDE bytes.
-__device__ __forceinline__ void stage_pair_table4(uint8_t* pt, const MatmulArgs& a, int b, int k, int KLpad, int tid,
-                                                  int nthreads) {
-  const uint8_t* src = a.pair + a.pair_off[b][k];
-  const int vec_per_row = KLpad >> 4;
-  for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += nthreads) {
-    const int u = idx / vec_per_row, v = idx - u * vec_per_row;
-    const uint4 x = *(const uint4*)(src + (long long)u * KLpad + v * 16);
-    auto pack = [](uint32_t wd) {
-      const uint32_t t = wd << 1;  // bytes <= 2: doubling never carries
-      return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
-    };
-    *(uint2*)(pt + u * PT_STRIDE + v * 8) = uint2{pack(x.x) | (pack(x.y) << 16), pack(x.z) | (pack(x.w) << 16)};
-  }
-}
-
-template <bool COUNTS>
-__global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers4(MatmulArgs a, MfmaWs w, int n_items) {
-  struct __align__(16) GatherTables {
-    uint8_t pt[MAX_LEVELS * PT_STRIDE];
-    uint32_t pat[PAT_WORDS];
-  };
-  __shared__ GatherTables s_tab;
-  __shared__ __align__(8) uint32_t s_list[4][FL_LIST];
-  __shared__ __align__(16) int s_rows[2][MF_BM];    // original row of each position (-1: none)
-  __shared__ __align__(16) int s_rc[2][MF_BM];      // each row's n0 sum over the contraction axis
-  __shared__ __align__(16) float s_sa[2][MF_BM];    // each row's scale
-  __shared__ int s_item[2];
-  uint8_t* const s_pt = s_tab.pt;
-  uint32_t* const s_pat = s_tab.pat;
-  constexpr int PAD4 = 8 * FL_RING + 4;  // padding entries past a list's end
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wr = wave >> 1, wc = wave & 1;
-  const int l32 = lane & 31, hf = lane >> 5;
-  const int wrow0 = wr * 64, wcol0 = wc * 64;
-  uint32_t* const list = s_list[wave];
-  const int qq = a.q * a.q;
-
-  // Row data of tile y in group g for position tid (< 128): original row,
-  // n0 summed over the encode parts, row scale.
-  auto row_data = [&](int g, int y, int& row, int& rc, float& sa) __attribute__((always_inline)) {
-    const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
-    row = w.rowid[pos];
-    sa = w.sas[pos];
-    rc = 0;
-    const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
-    for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
-  };
-
-  init_patterns4(s_pat, tid, 256);
-  if (tid == 0) {
-    s_item[0] = (int)atomicAdd(w.work, 1u);
-    s_item[1] = (int)atomicAdd(w.work, 1u);
-  }
-  __syncthreads();
-  int item = s_item[0];
-  if (item >= n_items) return;
-  if (tid < MF_BM) {
-    const PersItem it = pers_item(a, w.CT, item);
-    int row, rc;
-    float sa;
-    row_data(it.g, it.y, row, rc, sa);
-    s_rows[0][tid] = row;
-    s_rc[0][tid] = rc;
-    s_sa[0][tid] = sa;
-  }
-
-  struct Frag {
-    v8i a[2], b[2];
-  };
-  // Fragments of half-blocks X (codes hx, ux, first position kx) and Y for
-  // this lane half: A from the pattern table at max(c - 32 k, 0), B from the
-  // nibble table at row offset + k / 2.
+  const uint8_t* const pat = (const uint8_t*)s_pat;
   auto frags_at = [&](uint32_t hx, uint32_t ux, uint32_t kx, uint32_t hy, uint32_t uy, uint32_t ky)
-                      __attribute__((always_inline)) {
-    Frag f;
-    const uint8_t* pat = (const uint8_t*)s_pat;
-    const v2i ax0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx & 0xffffu, 32u * kx));
-    const v2i ax1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hx >> 16, 32u * kx));
-    const v2i ay0 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy & 0xffffu, 32u * ky));
-    const v2i ay1 = *(const v2i*)(pat + __builtin_elementwise_sub_sat(hy >> 16, 32u * ky));
-    const v2i bx0 = *(const v2i*)(s_pt + (ux & 0xffffu) + (kx >> 1));
-    const v2i bx1 = *(const v2i*)(s_pt + (ux >> 16) + (kx >> 1));
-    const v2i by0 = *(const v2i*)(s_pt + (uy & 0xffffu) + (ky >> 1));
-    const v2i by1 = *(const v2i*)(s_pt + (uy >> 16) + (ky >> 1));
-    f.a[0] = v8i{ax0.x, ax0.y, ay0.x, ay0.y, 0, 0, 0, 0};
-    f.a[1] = v8i{ax1.x, ax1.y, ay1.x, ay1.y, 0, 0, 0, 0};
-    f.b[0] = v8i{bx0.x, bx0.y, by0.x, by0.y, 0, 0, 0, 0};
-    f.b[1] = v8i{bx1.x, bx1.y, by1.x, by1.y, 0, 0, 0, 0};
-    return f;
-  };
+                      __attribute__((always_inline)) { return scmp::frags_at(pat, s_pt, hx, ux, kx, hy, uy, ky); };
   v16f acc[2][2];
-  auto mma = [&](const Frag& f) __attribute__((always_inline)) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
-        acc[i][jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.a[i], f.b[jj], acc[i][jj], 4, 4, 0, 127, 0, 127);
-  };
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) { mma_step(acc, f); };
   unsigned long long issued = 0;  // fp4 MFMA steps of the column-0 tiles
   int staged_k = -1;
   int cur = 0;
@@ -1233,7 +819,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers4(MatmulArgs a
     if (k != staged_k) {
       // Every wave finished the previous tile (the loop ends on a barrier).
       const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
-      stage_pair_table4(s_pt, a, 0, k, KLpad, tid, 256);
+      stage_pair_table(s_pt, a, 0, k, KLpad, tid, 256);
       __syncthreads();
       staged_k = k;
     }
@@ -1437,9 +1023,6 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers4(MatmulArgs a
   if (tid == 0 && issued) atomicAdd(w.issued + 1, issued);
 }
 
-// Row subtiles per wave for a plan.
-static int mfma_wr(const MatmulArgs&) { return 2; }
-
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
                      unsigned long long* macs, unsigned long long* fp4_macs) {
   size_t need = 0;
@@ -1489,9 +1072,9 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
   const bool counts = a.counts != nullptr;
   if (a.chunk_d > 0) {
     if (counts)
-      hipLaunchKernelGGL((k_mfma<true, true, 2>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<true, true>), grid, dim3(256), 0, st, a, w);
     else
-      hipLaunchKernelGGL((k_mfma<true, false, 2>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<true, false>), grid, dim3(256), 0, st, a, w);
   } else if (a.launch == 1 ||
              (a.launch == 0 && pers_ok(a, w) &&
               a.tile_start[a.n_rungs] * a.G * w.CT >= 3 * (counts ? 1 : 2) * device_cus())) {
@@ -1500,14 +1083,14 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
     const int n_items = a.tile_start[a.n_rungs] * a.G * w.CT;
     const int blocks = std::max(1, std::min(n_items, (counts ? 1 : 2) * device_cus()));
     if (counts)
-      hipLaunchKernelGGL((k_mfma_pers4<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
     else
-      hipLaunchKernelGGL((k_mfma_pers4<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
   } else {
     if (counts)
-      hipLaunchKernelGGL((k_mfma<false, true, 2>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<false, true>), grid, dim3(256), 0, st, a, w);
     else
-      hipLaunchKernelGGL((k_mfma<false, false, 2>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<false, false>), grid, dim3(256), 0, st, a, w);
   }
 }
 
@@ -1518,20 +1101,14 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
   if (!ws || ws_bytes < need)
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
   if (w.RT == 0) return SCMP_OK;
-  const int WR = mfma_wr(a);
-  const int BM = 64 * WR;
-  a.tile_start2[0] = 0;
-  for (int k = 0; k < a.n_rungs; ++k)
-    a.tile_start2[k + 1] = a.tile_start2[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
-  const int RT2 = a.tile_start2[a.n_rungs];
-  if (w.RT > 65535 || RT2 > 65535 || w.CT > 65535 || w.n_parts > 65535)
+  if (w.RT > 65535 || w.CT > 65535 || w.n_parts > 65535)
     return set_error(SCMP_ERR_ARG, "too many tiles");
   if (a.launch == 1 && !pers_ok(a, w))
     return set_error(SCMP_ERR_UNSUPPORTED,
                      "the persistent launch needs a plan without chunk scales and one band");
   hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
-  launch_main(a, w, dim3(w.CT, RT2, a.G), st);
+  launch_main(a, w, dim3(w.CT, w.RT, a.G), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("mfma launch: ") + hipGetErrorString(e));
   return SCMP_OK;
