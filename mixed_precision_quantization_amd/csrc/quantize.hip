@@ -116,6 +116,72 @@ __global__ void __launch_bounds__(256) k_quantize(QuantArgs a) {
   }
 }
 
+// Fast path for unit column stride and 16-byte aligned rows: one wave per
+// row (four rows per block), float4 loads kept in registers between the max
+// and the quantisation, four integers packed per 32-bit store.  Per-chunk
+// scales need chunk_d a power of two in [4, 256]: the chunk of a float4 at
+// column c is c / chunk_d, and the lanes sharing it are chunk_d / 4
+// consecutive lanes (an xor-shuffle group).  R: float4 loads per lane
+// (cols <= 256 R).
+template <int R>
+__global__ void __launch_bounds__(256) k_quantize_vec(QuantArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  const int g = blockIdx.y;
+  if (row >= a.rows) return;
+  const float* x = a.X + (long long)g * a.bs + (long long)row * a.rs;
+  const long long orow = (long long)g * a.rows + row;
+  int8_t* qrow = a.qout + orow * a.cols;
+  const float qf = (float)a.q;
+  float4 v[R];
+  bool bad = false;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = 256 * r + 4 * lane;
+    v[r] = c < a.cols ? *(const float4*)(x + c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    bad |= !(__builtin_isfinite(v[r].x) && __builtin_isfinite(v[r].y) && __builtin_isfinite(v[r].z) &&
+             __builtin_isfinite(v[r].w));
+  }
+  auto amax4 = [](float4 t) { return fmaxf(fmaxf(fabsf(t.x), fabsf(t.y)), fmaxf(fabsf(t.z), fabsf(t.w))); };
+  auto pack = [&](float4 t, float sc) {
+    const uint32_t b0 = (uint8_t)quant_one(t.x, sc, qf), b1 = (uint8_t)quant_one(t.y, sc, qf);
+    const uint32_t b2 = (uint8_t)quant_one(t.z, sc, qf), b3 = (uint8_t)quant_one(t.w, sc, qf);
+    return b0 | (b1 << 8) | (b2 << 16) | (b3 << 24);
+  };
+  float rowmax = 0.0f;
+  if (a.chunk_d <= 0) {
+    float m = 0.0f;
+#pragma unroll
+    for (int r = 0; r < R; ++r) m = fmaxf(m, amax4(v[r]));
+    m = wave_max(m);
+    const float s = m == 0.0f ? 0.0f : m / qf;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int c = 256 * r + 4 * lane;
+      if (c < a.cols) *(uint32_t*)(qrow + c) = pack(v[r], s);
+    }
+    if (lane == 0) a.scales[orow] = s;
+    rowmax = m;
+  } else {
+    const int group = a.chunk_d >> 2;  // lanes per chunk (power of two, <= 64)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      float m = amax4(v[r]);
+      for (int off = 1; off < group; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+      const float s = m == 0.0f ? 0.0f : m / qf;
+      const int c = 256 * r + 4 * lane;
+      if (c < a.cols) {
+        *(uint32_t*)(qrow + c) = pack(v[r], s);
+        if ((lane & (group - 1)) == 0) a.scales[orow * a.n_chunks + c / a.chunk_d] = s;
+      }
+      rowmax = fmaxf(rowmax, m);
+    }
+    rowmax = wave_max(rowmax);
+  }
+  if (a.metric && lane == 0) a.metric[orow] = rowmax;
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(&g_quant_flags, 1);
+}
+
 int read_clear_quant_flags(hipStream_t st, int* flags) {
   int v = 0, zero = 0;
   hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_quant_flags), sizeof(int), 0, hipMemcpyDeviceToHost, st);
@@ -163,7 +229,25 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
   a.metric = metric_out;
   a.packed = packed_out;
   a.K = table->K;
-  hipLaunchKernelGGL(scmp::k_quantize, dim3(rows, G), dim3(256), 0, (hipStream_t)stream, a);
+  // Fast path: unit column stride, 16-byte aligned rows, no packed streams,
+  // cols a multiple of 4 up to 4096, chunk_d 0 or a power of two in [4, 256].
+  const bool cd_ok = P.chunk_d <= 0 || (P.chunk_d >= 4 && P.chunk_d <= 256 && (P.chunk_d & (P.chunk_d - 1)) == 0);
+  const bool vec = col_stride == 1 && !packed_out && cols % 4 == 0 && cols <= 4096 && cd_ok &&
+                   ((uintptr_t)X % 16) == 0 && row_stride % 4 == 0 && batch_stride % 4 == 0 &&
+                   ((uintptr_t)q_out % 4) == 0;
+  hipStream_t st = (hipStream_t)stream;
+  if (vec) {
+    const dim3 grid((rows + 3) / 4, G);
+    const int R = (cols + 255) / 256;
+    if (R <= 4)
+      hipLaunchKernelGGL(scmp::k_quantize_vec<4>, grid, dim3(256), 0, st, a);
+    else if (R <= 8)
+      hipLaunchKernelGGL(scmp::k_quantize_vec<8>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(scmp::k_quantize_vec<16>, grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(scmp::k_quantize, dim3(rows, G), dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("quantize launch: ") + hipGetErrorString(e));
   return SCMP_OK;
