@@ -49,10 +49,10 @@ constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LD
 
 
 struct MfmaWs {
-  uint32_t* hs;     // [G][Mp/2][Dp]  window codes 16 (2 hh + neg) of a row pair, by index
+  uint32_t* hs;     // [G][RT][Dp/32] blocks: window codes 16 (2 hh + neg) of a row pair, by index
   uint8_t* maxh;    // [G][RT][Dp]    largest |h| of each row tile at each d
   int32_t* rowc;    // [G][n_parts][Mp]   n0 summed over each part of the contraction axis
-  uint32_t* ub;     // [G][Np/2][Dp]  paired-table row offsets of a column pair, by index
+  uint32_t* ub;     // [G][CT][Dp/32] blocks: paired-table row offsets of a column pair, by index
   // Single-segment plans also keep the codes index-major (the persistent
   // contraction's list steps read one index for every pair); else null.
   uint32_t* hsi;    // [G][Dp][Mp/2]  window code words, by index then row pair
@@ -138,6 +138,20 @@ __device__ __forceinline__ int wave_max_i(int v) {
 // contraction index: the low half for position lo, the high half for lo + 32.
 __device__ __forceinline__ int pair_lo(int pr) { return ((pr & 32) << 1) | (pr & 31); }
 
+// The encode buffers hs and ub are blocked by groups of 32 contraction
+// indices: the 64 pairs x 32 indices of one (tile, group) are 2048
+// consecutive words, ordered [p / 32][(e % 16) / 4][e / 16][p % 32][e % 4]
+// for pair p and index e of the group.  A wave lane that supplies pair
+// 32 s + l and the index half h of a group then finds indices
+// 16 h + 4 i + [0, 4) at word (8 s + h) 128 + 4 l + 256 i of the block, so
+// each of the wave's four 16-byte loads per group reads one contiguous
+// kilobyte (a lane per pair with the index axis contiguous would touch 64
+// cache lines per load).
+__device__ __forceinline__ long long enc_word(long long tile, int ngrp, int d, int p) {
+  const int e = d & 31;
+  return ((tile * ngrp + (d >> 5)) << 11) + (long long)(((((p >> 5) * 4 + ((e & 15) >> 2)) * 2 + (e >> 4)) * 32 + (p & 31)) * 4 + (e & 3));
+}
+
 // Load 8 int8 values x[0..8) (bounds-checked, vectorised when aligned).
 __device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out) {
   if (valid >= 8 && (((uintptr_t)src) & 7) == 0) {
@@ -172,7 +186,8 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   const int row_lo = s_rows[p_lo], row_hi = s_rows[p_hi];
   const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
   const int8_t* src_hi = a.qA + ((long long)g * a.M + (row_hi < 0 ? 0 : row_hi)) * a.D;
-  uint32_t* dst = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + pr) * w.Dp;
+  const long long tile = (long long)g * w.RT + y;
+  const int ngrp = (int)(w.Dp / MF_DC);
   const int plo = part * w.part_len;
   const int phi = min(plo + w.part_len, a.D);
   int rc_lo = 0, rc_hi = 0;  // n0 sums of this thread's indices
@@ -221,10 +236,10 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
         word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
         mh[i] = max(hh[0], hh[1]);
       }
-      // d0 + 32 <= Dp: the whole group is inside the buffer row (indices past
-      // the band or D get code 0).
-      *(uint4*)(dst + dfirst) = uint4{word[0], word[1], word[2], word[3]};
-      *(uint4*)(dst + dfirst + 4) = uint4{word[4], word[5], word[6], word[7]};
+      // d0 + 32 <= Dp: the whole group is inside the buffer (indices past
+      // the band or D get code 0); dfirst is a multiple of 8.
+      *(uint4*)(w.hs + enc_word(tile, ngrp, dfirst, pr)) = uint4{word[0], word[1], word[2], word[3]};
+      *(uint4*)(w.hs + enc_word(tile, ngrp, dfirst + 4, pr)) = uint4{word[4], word[5], word[6], word[7]};
       if (w.hsi) {
         uint32_t* di = w.hsi + ((long long)g * w.Dp + dfirst) * (w.Mp / 2) + (long long)y * 64 + pr;
 #pragma unroll
@@ -280,7 +295,8 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int col_lo = c0 + pair_lo(cp), col_hi = col_lo + 32;
   const int8_t* src_lo = a.qB + ((long long)g * a.N + (col_lo < a.N ? col_lo : 0)) * a.D;
   const int8_t* src_hi = a.qB + ((long long)g * a.N + (col_hi < a.N ? col_hi : 0)) * a.D;
-  uint32_t* dst = w.ub + ((long long)g * (w.Np / 2) + (long long)blockIdx.x * 64 + cp) * w.Dp;
+  const long long tile = (long long)g * w.CT + blockIdx.x;
+  const int ngrp = (int)(w.Dp / MF_DC);
   for (int d0 = plo; d0 < phi; d0 += MF_DC) {
     const int dfirst = d0 + 8 * q;
     const int span = max(0, min(8, a.D - dfirst));
@@ -294,8 +310,8 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
       const int u_hi = (i < span && col_hi < a.N) ? level_of((int)x_hi[i], a.P, a.q) : (a.P >> 1);
       word[i] = (uint32_t)(u_lo * PT_STRIDE) | ((uint32_t)(u_hi * PT_STRIDE) << 16);
     }
-    *(uint4*)(dst + dfirst) = uint4{word[0], word[1], word[2], word[3]};
-    *(uint4*)(dst + dfirst + 4) = uint4{word[4], word[5], word[6], word[7]};
+    *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst, cp)) = uint4{word[0], word[1], word[2], word[3]};
+    *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst + 4, cp)) = uint4{word[4], word[5], word[6], word[7]};
     if (w.ubi) {
       uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)blockIdx.x * 64 + cp;
 #pragma unroll
@@ -439,29 +455,35 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int wrow0 = wr * 64;  // first row of this wave
   const int wcol0 = wc * 64;  // first column of this wave
 
-  // Stage loader: thread (pair pr = tid / 4, quarter q = tid % 4) reads the
-  // code words of indices [d0 + 8 q, d0 + 8 q + 8) of row pair pr and of
-  // column pair pr (two 16-byte loads each, into named registers so they
-  // stay in VGPRs) and stores them as the stage's [index][pair] words.
+  // Stage loader: thread t reads 16-byte pieces t and t + 256 of the
+  // stage's blocks of row and column code words (one contiguous 4 KB per
+  // wave and buffer; pieces t and t + 256 hold indices
+  // 16 ((t / 32) % 2) + 4 ((t / 64) % 4) + [0, 4) of pairs t % 32 and
+  // t % 32 + 32, into named registers so they stay in VGPRs) and stores them
+  // as the stage's [index][pair] words.
   int4 rh0, rh1, ru0, ru1;
   int rmx = 0;
-  const int lpr = tid >> 2, lq = tid & 3;
-  const uint32_t* hrow_g = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + lpr) * w.Dp + 8 * lq;
-  const uint32_t* urow_g = w.ub + ((long long)g * (w.Np / 2) + (long long)(col0 / 2) + lpr) * w.Dp + 8 * lq;
+  const int ngrp = (int)(w.Dp / MF_DC);
+  const uint32_t* hblk = w.hs + enc_word((long long)g * w.RT + y, ngrp, 0, 0) + 4 * tid;
+  const uint32_t* ublk = w.ub + enc_word((long long)g * w.CT + blockIdx.x, ngrp, 0, 0) + 4 * tid;
+  const int sp = tid & 31, se = 16 * ((tid >> 5) & 1) + 4 * ((tid >> 6) & 3);
   auto fetch = [&](int d0) {
-    rh0 = *(const int4*)(hrow_g + d0);
-    rh1 = *(const int4*)(hrow_g + d0 + 4);
-    ru0 = *(const int4*)(urow_g + d0);
-    ru1 = *(const int4*)(urow_g + d0 + 4);
+    const long long gb = (long long)(d0 >> 5) << 11;
+    rh0 = *(const int4*)(hblk + gb);
+    rh1 = *(const int4*)(hblk + gb + 1024);
+    ru0 = *(const int4*)(ublk + gb);
+    ru1 = *(const int4*)(ublk + gb + 1024);
     if (tid < DC) rmx = w.maxh[((long long)g * w.RT + y) * w.Dp + d0 + tid];
   };
   auto store = [&](int bf) {
-    const int hv[8] = {rh0.x, rh0.y, rh0.z, rh0.w, rh1.x, rh1.y, rh1.z, rh1.w};
-    const int uv[8] = {ru0.x, ru0.y, ru0.z, ru0.w, ru1.x, ru1.y, ru1.z, ru1.w};
+    const int h0[4] = {rh0.x, rh0.y, rh0.z, rh0.w}, h1[4] = {rh1.x, rh1.y, rh1.z, rh1.w};
+    const int u0[4] = {ru0.x, ru0.y, ru0.z, ru0.w}, u1[4] = {ru1.x, ru1.y, ru1.z, ru1.w};
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s_h[bf][8 * lq + i][lpr] = (uint32_t)hv[i];
-      s_u[bf][8 * lq + i][lpr] = (uint32_t)uv[i];
+    for (int i = 0; i < 4; ++i) {
+      s_h[bf][se + i][sp] = (uint32_t)h0[i];
+      s_h[bf][se + i][sp + 32] = (uint32_t)h1[i];
+      s_u[bf][se + i][sp] = (uint32_t)u0[i];
+      s_u[bf][se + i][sp + 32] = (uint32_t)u1[i];
     }
     if (tid < 64) {
       // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
@@ -827,8 +849,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     // This lane's rows of the encode buffers (row pair wr * 32 + l32 of
     // tile y, column pair wc * 32 + l32 of column tile x), and the
     // index-major copies for list steps.
-    const uint32_t* hrow = w.hs + ((long long)g * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32) * w.Dp;
-    const uint32_t* urow = w.ub + ((long long)g * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32) * w.Dp;
+    const int ngrp_all = (int)(w.Dp / MF_DC);
+    const uint32_t* hrow = w.hs + enc_word((long long)g * w.RT + y, ngrp_all, 0, 0) + (8 * wr + hf) * 128 + 4 * l32;
+    const uint32_t* urow = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0) + (8 * wc + hf) * 128 + 4 * l32;
     const uint8_t* mq = w.maxh + ((long long)g * w.RT + y) * w.Dp;
     const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
     const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
@@ -890,11 +913,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     // 16-byte loads per buffer), and this lane's index maximum (raw: the
     // band's bound is applied where it is used).
     auto load_group = [&](int d0, uint32_t* h, uint32_t* u, int& m) __attribute__((always_inline)) {
-      const uint4* hp = (const uint4*)(hrow + d0 + 16 * hf);
-      const uint4* up = (const uint4*)(urow + d0 + 16 * hf);
+      const uint4* hp = (const uint4*)(hrow + ((long long)(d0 >> 5) << 11));
+      const uint4* up = (const uint4*)(urow + ((long long)(d0 >> 5) << 11));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const uint4 th = hp[i], tu = up[i];
+        const uint4 th = hp[64 * i], tu = up[64 * i];
         h[4 * i] = th.x;
         h[4 * i + 1] = th.y;
         h[4 * i + 2] = th.z;
