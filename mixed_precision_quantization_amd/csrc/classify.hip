@@ -111,6 +111,156 @@ __global__ void __launch_bounds__(512) k_classify(ClassifyArgs a) {
   }
 }
 
+// Groups of at most CB_MAXM rows take a bucket form with O(M) work per
+// block instead of O(M^2): every block buckets all of its group's keys by
+// value in LDS (a monotone map, so every key of a higher bucket sorts
+// before every key of a lower one), scans the bucket counts from the top
+// and lists each bucket's rows; a row's rank is then the count of rows in
+// higher buckets plus the rows of its own bucket that sort before it.
+// Equal keys share a bucket, so ties (row index order) are decided by the
+// same direct comparison as above; with every key equal the members are
+// the whole group and the block does M comparisons per row, spread over
+// its eight waves.  A block ranks CL_ROWS x sets rows; the metric is read
+// once, into registers, with all of a thread's loads in flight together.
+constexpr int CB_MAXM = 18432;
+constexpr int CB_PER = CB_MAXM / 512;  // metric values per thread
+constexpr int CB_NB = 2048;            // buckets: 0 for negative (and NaN) keys, 1..2047 over [0, 1]
+
+__device__ __forceinline__ int key_bucket(float k) {
+  return k < 0.0f ? 0 : min(CB_NB - 1, 1 + (int)(k * (float)(CB_NB - 2)));
+}
+
+// Dynamic LDS: s_cnt, s_start [CB_NB] ints, s_key [M] floats, s_mem [M]
+// u16 (bytes: 8 CB_NB + 6 M, rounded).
+size_t classify_bucket_lds(int M) { return (size_t)8 * CB_NB + (size_t)4 * M + (size_t)2 * ((M + 1) & ~1); }
+
+__global__ void __launch_bounds__(512) k_classify_bucket(ClassifyArgs a, int sets) {
+  extern __shared__ __align__(16) unsigned char s_dyn[];
+  __shared__ int s_part[CL_WAVES][CL_ROWS];
+  __shared__ float s_red[CL_WAVES];
+  __shared__ int s_wsum[CL_WAVES];
+  const int M = a.M;
+  int* const s_cnt = (int*)s_dyn;                       // rows per bucket, then fill counters
+  int* const s_start = s_cnt + CB_NB;                   // first list position of each bucket
+  float* const s_key = (float*)(s_start + CB_NB);       // rank key of each row
+  uint16_t* const s_mem = (uint16_t*)(s_key + M);       // rows listed bucket by bucket, top first
+  const int g = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const float* m = a.metric + (long long)g * M;
+
+  float v[CB_PER];
+  float mx = 0.0f;
+  bool bad = false;
+#pragma unroll
+  for (int u = 0; u < CB_PER; ++u) {
+    const int j = tid + 512 * u;
+    v[u] = j < M ? m[j] : 0.0f;
+  }
+#pragma unroll
+  for (int u = 0; u < CB_PER; ++u)
+    if (tid + 512 * u < M) {
+      bad |= !__builtin_isfinite(v[u]);
+      mx = fmaxf(mx, v[u]);
+    }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) s_red[wave] = mx;
+  for (int b = tid; b < CB_NB; b += 512) s_cnt[b] = 0;
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < CL_WAVES; ++w) mx = fmaxf(mx, s_red[w]);
+  if (bad && blockIdx.x == 0) atomicOr(&g_classify_flags, 1);
+
+#pragma unroll
+  for (int u = 0; u < CB_PER; ++u) {
+    const int j = tid + 512 * u;
+    if (j < M) {
+      const float k = rank_key(mx == 0.0f ? 0.0f : v[u] / mx);
+      s_key[j] = k;
+      atomicAdd(&s_cnt[key_bucket(k)], 1);
+    }
+  }
+  __syncthreads();
+  // Exclusive scan from the top bucket down: thread t takes buckets
+  // 2047 - 4 t - [0, 4).
+  {
+    int c[4], sum = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c[q] = s_cnt[CB_NB - 1 - (4 * tid + q)];
+      sum += c[q];
+    }
+    int incl = sum;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int t = __shfl_up(incl, off, 64);
+      if (lane >= off) incl += t;
+    }
+    if (lane == 63) s_wsum[wave] = incl;
+    __syncthreads();
+    int run = incl - sum;
+    for (int w = 0; w < wave; ++w) run += s_wsum[w];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      s_start[CB_NB - 1 - (4 * tid + q)] = run;
+      run += c[q];
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < CB_NB; b += 512) s_cnt[b] = 0;
+  __syncthreads();
+#pragma unroll
+  for (int u = 0; u < CB_PER; ++u) {
+    const int j = tid + 512 * u;
+    if (j < M) {
+      const int b = key_bucket(s_key[j]);
+      s_mem[s_start[b] + atomicAdd(&s_cnt[b], 1)] = (uint16_t)j;
+    }
+  }
+  __syncthreads();
+
+  // Ranks of the block's rows: every wave scans an eighth of each row's
+  // bucket (the bucket's rows w, w + 8, ...).
+  for (int set = 0; set < sets; ++set) {
+    const int i = (blockIdx.x * sets + set) * CL_ROWS + lane;
+    int n = 0;
+    float ki = 0.0f;
+    int bi = 0;
+    if (i < M) {
+      ki = s_key[i];
+      bi = key_bucket(ki);
+      const int e = s_start[bi] + s_cnt[bi];
+      for (int q = s_start[bi] + wave; q < e; q += CL_WAVES) {
+        const int j = s_mem[q];
+        const float kj = s_key[j];
+        n += (kj > ki) || (kj == ki && j < i);
+      }
+    }
+    s_part[wave][lane] = n;
+    __syncthreads();
+    if (wave == 0 && i < M) {
+      int rank = s_start[bi];
+#pragma unroll
+      for (int w = 0; w < CL_WAVES; ++w) rank += s_part[w][lane];
+      const float gi = mx == 0.0f ? 0.0f : m[i] / mx;
+      a.ghat[(long long)g * M + i] = gi;
+      a.perm[(long long)g * M + rank] = i;
+      int k = 0;
+      while (k + 1 < a.n_rungs && rank >= a.cuts[k + 1]) ++k;
+      if (a.rung) a.rung[(long long)g * M + i] = (uint8_t)k;
+      if (a.thr) {
+        for (int kk = 1; kk < a.n_rungs; ++kk) {
+          if (rank == a.cuts[kk] - 1) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = gi;
+          if (a.cuts[kk] == 0 && i == 0) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = 1.0f;
+        }
+      }
+    }
+    __syncthreads();  // s_part is rewritten by the next set
+  }
+}
+
 int read_clear_classify_flags(hipStream_t st, int* flags) {
   int v = 0, zero = 0;
   hipError_t e =
@@ -147,7 +297,19 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   a.n_rungs = P.n_rungs;
   scmp::row_cuts(P, M, a.cuts);
   hipStream_t st = (hipStream_t)stream;
-  hipLaunchKernelGGL(scmp::k_classify, dim3((M + scmp::CL_ROWS - 1) / scmp::CL_ROWS, G), dim3(512), 0, st, a);
+  const int tiles = (M + scmp::CL_ROWS - 1) / scmp::CL_ROWS;
+  if (M <= scmp::CB_MAXM) {
+    // Large groups rank two sets of rows per block: every block repeats the
+    // group's O(M) bucketing, so fewer, fuller blocks cost less.
+    const int sets = M > 8192 ? 2 : 1;
+    const size_t lds = scmp::classify_bucket_lds(M);
+    hipError_t e = hipFuncSetAttribute((const void*)scmp::k_classify_bucket,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("classify LDS: ") + hipGetErrorString(e));
+    hipLaunchKernelGGL(scmp::k_classify_bucket, dim3((tiles + sets - 1) / sets, G), dim3(512), lds, st, a, sets);
+  } else {
+    hipLaunchKernelGGL(scmp::k_classify, dim3(tiles, G), dim3(512), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("classify launch: ") + hipGetErrorString(e));
   return SCMP_OK;

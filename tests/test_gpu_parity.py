@@ -201,6 +201,29 @@ def test_classify_matches_oracle_with_ties(table):
     assert torch.all(gh == 0) and perm[0].cpu().tolist() == list(range(50))
 
 
+@pytest.mark.parametrize("case", ["equal_keys", "above_bucket_limit"])
+def test_classify_large_groups(table, case):
+    # One bucket holding every row (all keys equal but a few), and a group
+    # past the bucket form's row limit (the all-pairs form).
+    rng = np.random.default_rng(23)
+    if case == "equal_keys":
+        g = np.full((1, 6000), 0.5, np.float32)
+        g[0, ::997] = rng.uniform(0, 1, g[0, ::997].shape).astype(np.float32)
+    else:
+        g = rng.uniform(0, 3, (1, 20000)).astype(np.float32)
+        g[0, 5000:5100] = g[0, 7]
+    levels, fr = (256, 192, 128, 96, 64), (0.1, 0.15, 0.2, 0.25, 0.3)
+    plan = scmp.scmp_plan_create(D=64, levels=levels, fractions=fr)
+    print("  classify", case, g.shape, flush=True)
+    gh, rung, perm, thr = scmp.scmp_classify_rows(plan, torch.from_numpy(g).cuda())
+    gho = o.normalise_metric(g[0])
+    ro, order = o.assign_rungs(gho, 5, fr)
+    assert np.array_equal(gh[0].cpu().numpy(), gho)
+    assert np.array_equal(rung[0].cpu().numpy().astype(np.int64), ro)
+    assert np.array_equal(perm[0].cpu().numpy().astype(np.int64), order)
+    assert np.array_equal(thr[0].cpu().numpy(), o.thresholds(gho, order, o.rung_cuts(g.shape[1], 5, fr)))
+
+
 # ------------------------------------------------------- small workloads --
 
 SMALL = {
