@@ -46,6 +46,7 @@ namespace scmp {
 
 constexpr int MF_BM = 128, MF_BN = 128, MF_DC = 32;
 constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LDS
+constexpr int PREP_BLOCKS = 1024;  // encode blocks aimed for (tiles x parts of the contraction axis)
 
 
 struct MfmaWs {
@@ -77,11 +78,12 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   w.Np = (long long)w.CT * MF_BN;
   w.Dp = ((long long)a.D + MF_DC - 1) / MF_DC * MF_DC;
   {
-    // Enough blocks to cover the CUs several times over.
+    // Enough encode blocks to cover the CUs several times over, each with
+    // a run of groups long enough to hide its fixed costs.
     const long long tiles = (long long)w.RT * a.G;
     const int unit = a.chunk_d > 0 ? a.chunk_d : MF_DC;
     const int units = (a.D + unit - 1) / unit;
-    long long want = tiles > 0 ? (2048 + tiles - 1) / tiles : 1;
+    long long want = tiles > 0 ? (PREP_BLOCKS + tiles - 1) / tiles : 1;
     if (want < 1) want = 1;
     if (want > units) want = units;
     const int per = (int)((units + want - 1) / want);
@@ -171,7 +173,7 @@ __device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out)
 // encodes indices [d0 + 8 q, d0 + 8 q + 8) of both rows of its pair.  The
 // block covers indices [part * part_len, ...) of one tile.
 __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
-  __shared__ uint16_t s_ncum[MAX_LEVELS];
+  __shared__ uint32_t s_lut[256];
   __shared__ int s_mx[4][MF_DC];
   __shared__ int s_rows[MF_BM];
   const int tid = threadIdx.x;
@@ -209,14 +211,39 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     if (lo >= dend) continue;  // uniform over the block
     const int L = a.bandL[b][k];
     __syncthreads();
-    for (int u = tid; u <= a.P; u += 256) s_ncum[u] = a.cum[(long long)u * (a.Lmax + 1) + L];
+    // Everything an element needs at this L, per stored value x (entry
+    // x + 128): window code (13 bits), hh (8 bits) and its n0 = L - n1
+    // (9 bits), so the per-element work is one table read.
+    {
+      const int x = tid - 128;
+      const int n1 = a.cum[(long long)level_of(x, a.P, a.q) * (a.Lmax + 1) + L];
+      const int diff = 2 * n1 - L;
+      const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
+      const int code = 16 * (2 * hh + (diff < 0 ? 1 : 0));
+      s_lut[tid] = (uint32_t)code | ((uint32_t)hh << 13) | ((uint32_t)(L - n1) << 21);
+    }
     __syncthreads();
+    // The next group's values are read while this group is encoded.
+    int8_t nx_lo[8], nx_hi[8];
+    {
+      const int span = max(0, min(8, dend - (lo + 8 * q)));
+      load8(src_lo + lo + 8 * q, row_lo >= 0 ? span : 0, nx_lo);
+      load8(src_hi + lo + 8 * q, row_hi >= 0 ? span : 0, nx_hi);
+    }
     for (int d0 = lo; d0 < dend; d0 += MF_DC) {
       const int dfirst = d0 + 8 * q;
       const int span = max(0, min(8, dend - dfirst));
       int8_t x_lo[8], x_hi[8];
-      load8(src_lo + dfirst, row_lo >= 0 ? span : 0, x_lo);
-      load8(src_hi + dfirst, row_hi >= 0 ? span : 0, x_hi);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        x_lo[i] = nx_lo[i];
+        x_hi[i] = nx_hi[i];
+      }
+      if (d0 + MF_DC < dend) {
+        const int nspan = max(0, min(8, dend - (dfirst + MF_DC)));
+        load8(src_lo + dfirst + MF_DC, row_lo >= 0 ? nspan : 0, nx_lo);
+        load8(src_hi + dfirst + MF_DC, row_hi >= 0 ? nspan : 0, nx_hi);
+      }
       uint32_t word[8];
       int mh[8];
 #pragma unroll
@@ -226,11 +253,10 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
         for (int h = 0; h < 2; ++h) {
           const bool ok = i < span && (h == 0 ? row_lo : row_hi) >= 0;
           if (ok) {
-            const int n1 = s_ncum[level_of((int)(h == 0 ? x_lo[i] : x_hi[i]), a.P, a.q)];
-            const int diff = 2 * n1 - L;
-            hh[h] = ((diff < 0 ? -diff : diff) + 1) >> 1;
-            code[h] = 16 * (2 * hh[h] + (diff < 0 ? 1 : 0));
-            (h == 0 ? rc_lo : rc_hi) += L - n1;
+            const uint32_t e = s_lut[(int)(h == 0 ? x_lo[i] : x_hi[i]) + 128];
+            code[h] = (int)(e & 0x1FFFu);
+            hh[h] = (int)((e >> 13) & 0xFFu);
+            (h == 0 ? rc_lo : rc_hi) += (int)(e >> 21);
           }
         }
         word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
@@ -280,7 +306,10 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
 // quarter q = tid % 4), indices [d0 + 8 q, d0 + 8 q + 8) of each group of
 // 32 in the block's part of the contraction axis.
 __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
+  // Table row offset of each stored value x (entry x + 128).
+  __shared__ uint32_t s_off[256];
   const int tid = threadIdx.x;
+  s_off[tid] = (uint32_t)(level_of(tid - 128, a.P, a.q) * PT_STRIDE);
   const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
@@ -297,6 +326,8 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int8_t* src_hi = a.qB + ((long long)g * a.N + (col_hi < a.N ? col_hi : 0)) * a.D;
   const long long tile = (long long)g * w.CT + blockIdx.x;
   const int ngrp = (int)(w.Dp / MF_DC);
+  const uint32_t pad = (uint32_t)((a.P >> 1) * PT_STRIDE);
+  __syncthreads();
   for (int d0 = plo; d0 < phi; d0 += MF_DC) {
     const int dfirst = d0 + 8 * q;
     const int span = max(0, min(8, a.D - dfirst));
@@ -306,9 +337,9 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
     uint32_t word[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const int u_lo = (i < span && col_lo < a.N) ? level_of((int)x_lo[i], a.P, a.q) : (a.P >> 1);
-      const int u_hi = (i < span && col_hi < a.N) ? level_of((int)x_hi[i], a.P, a.q) : (a.P >> 1);
-      word[i] = (uint32_t)(u_lo * PT_STRIDE) | ((uint32_t)(u_hi * PT_STRIDE) << 16);
+      const uint32_t o_lo = (i < span && col_lo < a.N) ? s_off[(int)x_lo[i] + 128] : pad;
+      const uint32_t o_hi = (i < span && col_hi < a.N) ? s_off[(int)x_hi[i] + 128] : pad;
+      word[i] = o_lo | (o_hi << 16);
     }
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst, cp)) = uint4{word[0], word[1], word[2], word[3]};
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst + 4, cp)) = uint4{word[4], word[5], word[6], word[7]};
