@@ -41,7 +41,8 @@ class Workload:
         return "av" if self.kind == "av" else "linear"
 
 
-# The five workloads (the fifth has two parts: fc2 with K-bands, and AV).
+# The five workloads (the fifth has two parts: fc2 with K-bands, and AV),
+# and per-query-row mixed precision on QK^T.
 WORKLOADS = {
     "single_64": Workload(
         "single_64", "linear", 1, 64, 64, 64, (64,), seed=1001,
@@ -64,6 +65,13 @@ WORKLOADS = {
         "vitl_av_mp", "av", 128, 257, 64, 257,
         (256, 128, 64), (0.333, 0.334, 0.333), seed=1006,
         a_dist="softmax", b_dist="normal"),
+    # Per-query-row mixed precision on QK^T: each query row's length from
+    # its ||Q_i||_inf within its head (the QK metric of "Precision As You
+    # Need", Key design 2), on the same ladder and split as AV.
+    "vitl_qk_mp": Workload(
+        "vitl_qk_mp", "qk", 128, 257, 257, 64,
+        (256, 128, 64), (0.333, 0.334, 0.333), seed=1007,
+        a_dist="normal", b_dist="normal"),
 }
 
 

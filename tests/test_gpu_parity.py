@@ -233,6 +233,7 @@ SMALL = {
     "vitl_fc1_mp": dict(M=300, N=200, D=160),
     "vitl_fc2_kband": dict(M=300, N=130, D=512),
     "vitl_av_mp": dict(G=4),
+    "vitl_qk_mp": dict(G=4),
 }
 
 
@@ -324,7 +325,7 @@ def test_standalone_decode_matches_fused(table):
 
 # ----------------------------------------------- full sizes, bench launch --
 
-FULL_GROUPS = {"vitl_qk": (0, 77, 127), "vitl_av_mp": (0, 64, 127)}
+FULL_GROUPS = {"vitl_qk": (0, 77, 127), "vitl_av_mp": (0, 64, 127), "vitl_qk_mp": (0, 77, 127)}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
