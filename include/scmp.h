@@ -7,10 +7,12 @@
  *          Quantizer" (paper notes): Key design 1 (Sobol-8 cumulative
  *          indicator table, conditional bitstream generator C-BSG, bipolar
  *          XNOR decode equation), Key design 2 (row metrics, threshold
- *          ladder), Key design 3 (early termination per row).
+ *          ladder), Key design 3 (early termination per row), Key design 4
+ *          (the compensation layer W_b x + b_b run as an SC linear).
  *  [VIT]   scmp_vit README: "Why it works" (per-row bipolar quantisation,
- *          scale = row abs-max / 127), the mixed-precision flag table, and
- *          the SC early-termination note for non-power-of-two lengths.
+ *          scale = row abs-max / 127), the mixed-precision flag table, the
+ *          SC early-termination note for non-power-of-two lengths, and the
+ *          head-aligned SC compensator (16 per-head D = 64 SC linears).
  *  [KBAND] pull request "feat(mp): per-group (K-band) stream lengths on the
  *          contraction axis": "How the banding works", "Guards", "Tooling".
  *
@@ -212,9 +214,11 @@ int scmp_classify_rows(scmp_plan_t plan, const float* metric_dev, int G, int M, 
 
 /* Workspace scmp_matmul needs for these sizes (0 for BITSERIAL).  The
  * MFMA path keeps there, per call, the row side encoded at each row's
- * length (signed half-window, int16 per (d, sorted position)), each row
- * tile's largest half-window per d, the per-chunk n0 sums and the weight
- * side's levels.  Errors: ARG, PLAN_MISMATCH. */
+ * length (two 16-bit window codes per row pair and index), each row tile's
+ * largest half-window per index, the per-part or per-chunk n0 sums, the
+ * weight side's table offsets (two per column pair and index), index-major
+ * copies of both for single-segment plans, sorted-row ids and scales, and
+ * a work counter.  Errors: ARG, PLAN_MISMATCH. */
 int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                                 size_t* bytes);
 
@@ -243,6 +247,21 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
                 int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
                 void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* scmp_matmul with a bias added to every row of C: C_ij = (decode as
+ * above) + bias_j.  With chunk_d = 64 and one length L this is the
+ * head-aligned SC compensator of [VIT] (its head-aligned compensator
+ * section): x split into heads of 64 columns, one SC linear per head
+ * (per-row scales over the head's columns on both operands, the same Sobol
+ * table), the heads' outputs summed and the bias added ([PAYN] Key design
+ * 4, the compensation layer W_b x + b_b as an SC linear).
+ *   bias_dev float [G][N] (required); other arguments as scmp_matmul.
+ * Errors: as scmp_matmul; ARG when bias_dev is NULL. */
+int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                     const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
+                     const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
+                     const float* bias_dev, int32_t* counts_dev, float* C_dev, int64_t ldc,
+                     int64_t batch_stride_c, void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* Diagnostic: synchronise `stream` and return the multiply-accumulates the
  * last MFMA-path scmp_matmul with this workspace issued on the matrix cores

@@ -144,7 +144,9 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = col0 + tx * 4 + j;
-        if (row >= 0 && col < a.N) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = cacc[i][j];
+        if (row >= 0 && col < a.N)
+          a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] =
+              cacc[i][j] + (a.bias ? a.bias[(long long)g * a.N + col] : 0.0f);
       }
     }
   }

@@ -108,10 +108,12 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
   return SCMP_OK;
 }
 
-int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
-                const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
-                const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
-                void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+static int matmul_impl(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
+                       const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
+                       const float* sB, const float* bias, int32_t* counts, float* C, int64_t ldc,
+                       int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
   scmp::clear_error();
   scmp::MatmulArgs a;
   int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
@@ -132,10 +134,33 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
   a.sB = sB;
   a.counts = counts;
   a.C = C;
+  a.bias = bias;
   a.ldc = ldc;
   a.bsc = batch_stride_c;
   hipStream_t st = (hipStream_t)stream;
   return bitserial ? scmp::launch_bitserial(a, st) : scmp::launch_mfma(a, workspace, workspace_bytes, st);
+}
+
+extern "C" {
+
+int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
+                const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
+                const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
+                void* workspace, size_t workspace_bytes, void* stream) {
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, nullptr, counts, C, ldc,
+                     batch_stride_c, workspace, workspace_bytes, stream);
+}
+
+int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
+                     const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
+                     const float* sB, const float* bias, int32_t* counts, float* C, int64_t ldc,
+                     int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!bias) {
+    scmp::clear_error();
+    return set_error(SCMP_ERR_ARG, "bias is NULL (use scmp_matmul)");
+  }
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, bias, counts, C, ldc,
+                     batch_stride_c, workspace, workspace_bytes, stream);
 }
 
 int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,

@@ -21,6 +21,7 @@ struct MatmulArgs {
   const float* sB;
   int32_t* counts;
   float* C;
+  const float* bias;  // [G][N] added to every row of C (nullable)
   long long ldc, bsc;
   const uint8_t* pair;
   const uint16_t* cum;

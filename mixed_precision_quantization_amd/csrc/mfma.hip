@@ -730,6 +730,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   for (int j = 0; j < 2; ++j) {
     const int col = col0 + wcol0 + j * 32 + l32;
     const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
+    const float bj = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -746,7 +747,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           const float sa = a.sA[(long long)g * a.M + row];
           out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
         }
-        if (a.C) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = out;
+        if (a.C) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = out + bj;
       }
   }
 }
@@ -1039,11 +1040,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     // Decode: rows four at a time (accumulator entries v = 4 q .. 4 q + 3
     // are consecutive rows), each used by both column subtiles.
     const float scale0 = (float)qq / (float)L;
-    float sb[2];
+    float sb[2], bj[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = col0 + wcol0 + j * 32 + l32;
       sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
+      bj[j] = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1066,7 +1068,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
             if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
             if (a.C)
               a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + col] =
-                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D));
+                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D)) + bj[j];
           }
       }
     __syncthreads();  // publishes the next tile's row data and item

@@ -42,7 +42,7 @@ EXPORTED = [
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
-    "scmp_matmul", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
+    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
 ]
 
 
@@ -101,6 +101,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_classify_rows": (i, [vp, vp, i, i, vp, vp, vp, vp, vp]),
         "scmp_matmul_workspace_bytes": (i, [vp, vp, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]),
         "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
+        "scmp_matmul_bias": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t,
+                                 vp]),
         "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
                                         ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_ulonglong),
                                         vp]),
@@ -334,10 +336,11 @@ def scmp_matmul_workspace_bytes(table: Table, plan: Plan, G: int, M: int, N: int
 
 def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=None, algo: str = "auto",
                 counts_out=None, C_out=None, want_counts: bool = False, want_C: bool = True, workspace=None,
-                stream=None):
+                bias=None, stream=None):
     """SC product of encoded operands.  qA int8 [G, M, D], qB int8 [G, N, D].
     ``workspace``: uint8 device tensor of at least scmp_matmul_workspace_bytes
-    (allocated here when None).
+    (allocated here when None).  ``bias``: float [G, N] added to every row
+    of C (scmp_matmul_bias), or None.
 
     Returns (counts int32 [G, M, N, n_bands] or None, C float [G, M, N] or None).
     """
@@ -362,13 +365,16 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
     if workspace is None:
         workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=dev)
     _need(workspace, ws_need, "workspace")
-    st = load().scmp_matmul(
-        table.handle, plan.handle, ALGOS[algo], G, M, N,
-        _ptr(qA3, torch.int8, "qA"), _ptr(sA, torch.float32, "sA"), _ptr(permA, torch.int32, "permA"),
-        _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"), _ptr(sB, torch.float32, "sB"),
-        _ptr(counts_out, torch.int32, "counts_out"), _ptr(C_out, torch.float32, "C_out"),
-        N, M * N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
-    _check("scmp_matmul", st)
+    head = (table.handle, plan.handle, ALGOS[algo], G, M, N,
+            _ptr(qA3, torch.int8, "qA"), _ptr(sA, torch.float32, "sA"), _ptr(permA, torch.int32, "permA"),
+            _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"), _ptr(sB, torch.float32, "sB"))
+    tail = (_ptr(counts_out, torch.int32, "counts_out"), _ptr(C_out, torch.float32, "C_out"),
+            N, M * N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
+    if bias is None:
+        _check("scmp_matmul", load().scmp_matmul(*head, *tail))
+    else:
+        _need(bias, G * N, "bias")
+        _check("scmp_matmul_bias", load().scmp_matmul_bias(*head, _ptr(bias, torch.float32, "bias"), *tail))
     return counts_out, C_out
 
 
@@ -411,9 +417,10 @@ def scmp_error_flags(stream=None) -> int:
 # --------------------------------------------------------------- pipeline --
 
 def sc_linear(table: Table, plan: Plan, A: torch.Tensor, B: torch.Tensor, algo: str = "auto",
-              want_counts: bool = False, stream=None):
+              want_counts: bool = False, bias=None, stream=None):
     """The whole path for one product: encode both operands, classify rows,
-    contract and decode.  Returns a dict of every intermediate (device)."""
+    contract and decode (plus ``bias`` [G, N] when given).  Returns a dict of
+    every intermediate (device)."""
     qA, sA, mA, _ = scmp_quantize_encode(table, plan, A, stream=stream)
     qB, sB, _, pB = scmp_quantize_encode(table, plan, B, want_metric=False,
                                          want_packed=(algo == "bitserial"), stream=stream)
@@ -421,6 +428,6 @@ def sc_linear(table: Table, plan: Plan, A: torch.Tensor, B: torch.Tensor, algo: 
     if plan.n_rungs > 1:
         ghat, rung, perm, thr = scmp_classify_rows(plan, mA, stream=stream)
     counts, C = scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, packedB=pB, algo=algo,
-                            want_counts=want_counts, stream=stream)
+                            want_counts=want_counts, bias=bias, stream=stream)
     return {"qA": qA, "sA": sA, "metric": mA, "qB": qB, "sB": sB, "packedB": pB, "ghat": ghat,
             "rung": rung, "perm": perm, "thresholds": thr, "counts": counts, "C": C}

@@ -42,7 +42,7 @@ class Workload:
 
 
 # The five workloads (the fifth has two parts: fc2 with K-bands, and AV),
-# and per-query-row mixed precision on QK^T.
+# per-query-row mixed precision on QK^T, and the head-aligned compensator.
 WORKLOADS = {
     "single_64": Workload(
         "single_64", "linear", 1, 64, 64, 64, (64,), seed=1001,
@@ -72,6 +72,14 @@ WORKLOADS = {
         "vitl_qk_mp", "qk", 128, 257, 257, 64,
         (256, 128, 64), (0.333, 0.334, 0.333), seed=1007,
         a_dist="normal", b_dist="normal"),
+    # The head-aligned SC compensator of one block (scmp_vit README): the
+    # block's 64 x 257 tokens x (16 heads x 64), a 1024 x 1024 W_b and a
+    # bias, every head at L = 256 (chunk_d = 64 gives each head its own
+    # per-row scales on both operands).
+    "vitl_comp_head_aligned": Workload(
+        "vitl_comp_head_aligned", "linear", 1, 64 * 257, 1024, 1024,
+        (256,), None, chunk_d=64, seed=1008,
+        a_dist="outlier", b_dist="weight", extra={"bias": True}),
 }
 
 
@@ -134,6 +142,15 @@ def draw(w: Workload):
     A = _draw(rng, w.a_dist, lead, w.M, w.D)
     B = _draw(rng, w.b_dist, lead, w.N, w.D)
     return A.astype(np.float32), B.astype(np.float32)
+
+
+def draw_bias(w: Workload) -> np.ndarray:
+    """The bias of a workload with ``extra["bias"]``: float32 [G, N] (or [N]
+    when G == 1), drawn as 0.02 N(0, 1) from its own seed (seed + 50000) so
+    that A and B are the same draws as without it."""
+    rng = np.random.default_rng(w.seed + 50000)
+    shape = (w.N,) if w.G == 1 else (w.G, w.N)
+    return (0.02 * rng.standard_normal(shape)).astype(np.float32)
 
 
 def draw_v(w: Workload):

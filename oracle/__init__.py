@@ -55,7 +55,7 @@ from .mp import (
     check_band_ladder,
 )
 from .decode import decode_terms, decode
-from .matmul import OraclePlan, classify, rows_product, sc_matmul_rows
+from .matmul import OraclePlan, classify, head_aligned_rows, rows_product, sc_matmul_rows
 
 __all__ = [
     "sobol_points",
@@ -85,4 +85,5 @@ __all__ = [
     "classify",
     "rows_product",
     "sc_matmul_rows",
+    "head_aligned_rows",
 ]

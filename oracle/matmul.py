@@ -170,3 +170,29 @@ def sc_matmul_rows(A, B, plan: OraclePlan, rows=None, metric=None):
     out.update(cls)
     out["rows"] = rows
     return out
+
+
+def head_aligned_rows(X, W, bias, head_dim: int = 64, L: int = 256, p: int = 8, rows=None):
+    """The head-aligned SC compensator (scmp_vit README, its head-aligned
+    compensator section; "Precision As You Need" Key design 4 runs the
+    compensation layer W_b x + b_b as an SC linear): x (M x D) is split into
+    heads of ``head_dim`` columns, head h is an SC linear of its own on
+    columns [h head_dim, (h + 1) head_dim) of x and W (its own per-row
+    scales on both operands, the one Sobol table, stream length L), the
+    heads' outputs are summed and the bias is added.  Float64; restricted to
+    the output rows ``rows`` (all when None).  Returns ``C`` and ``C_abs``
+    (the sum of the absolute decode terms plus |bias|, for tolerances)."""
+    X = np.asarray(X, dtype=np.float32)
+    W = np.asarray(W, dtype=np.float32)
+    bias = np.asarray(bias, dtype=np.float64)
+    D = X.shape[1]
+    rows = np.arange(X.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    C = np.zeros((len(rows), W.shape[0]), dtype=np.float64)
+    C_abs = np.zeros_like(C)
+    for h0 in range(0, D, head_dim):
+        cols = slice(h0, min(D, h0 + head_dim))
+        plan_h = OraclePlan(p=p, Lmax=2 ** p, D=cols.stop - cols.start, levels=(L,))
+        r = rows_product(X[rows][:, cols], np.zeros(len(rows), dtype=np.int64), W[:, cols], plan_h)
+        C += r["C"]
+        C_abs += r["C_abs"]
+    return {"C": C + bias[None, :], "C_abs": C_abs + np.abs(bias)[None, :]}

@@ -15,7 +15,7 @@ import torch
 import oracle as o
 from _oracle_pool import pooled_rows_product
 from mixed_precision_quantization_amd import scmp
-from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, sample_rows, shrink
+from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, draw_bias, sample_rows, shrink
 
 pytestmark = pytest.mark.gpu
 
@@ -357,3 +357,46 @@ def test_full_size_sampled_rows(table, name):
         pos = sample_rows(w.M, cls["cuts"], per_rung=3 if w.G == 1 else 2, seed=g)
         rows = cls["order"][pos]
         _check_group(full, g, A[g], B[g], okw, rows=rows)
+
+
+# --------------------------------------------- head-aligned compensator --
+
+def _head_aligned_check(table, X, W, b, algo, rows=None):
+    """GPU scmp_matmul_bias (chunk_d = 64, L = 256) against the oracle's
+    head-aligned compensator (heads summed, bias added); counts bit-exact
+    against the oracle's per-head counts."""
+    D = X.shape[1]
+    plan = scmp.scmp_plan_create(D=D, chunk_d=64, levels=(256,))
+    res = _to_np(scmp.sc_linear(table, plan, torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda(), algo=algo,
+                                want_counts=True, bias=torch.from_numpy(b).cuda().reshape(1, -1)))
+    torch.cuda.synchronize()
+    rows = np.arange(X.shape[0]) if rows is None else np.asarray(rows)
+    orc = o.head_aligned_rows(X, W, b, head_dim=64, L=256, rows=rows)
+    C = res["C"][0][rows].astype(np.float64)
+    err = np.abs(C - orc["C"])
+    lim = RTOL * orc["C_abs"]
+    assert np.all(err <= lim), f"max err/limit {np.max(err / np.maximum(lim, 1e-300)):.3g}"
+    okw = dict(p=8, Lmax=256, D=D, chunk_d=64, levels=(256,))
+    cnt = pooled_rows_product(X[rows], np.zeros(len(rows), np.int64), W, okw)
+    assert np.array_equal(res["counts"][0][rows].astype(np.int64), cnt["band_counts"]), "counts"
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_head_aligned_compensator_small(table, algo):
+    _skip_unsupported(algo, chunk_d=64)
+    rng = np.random.default_rng(41)
+    X = rng.standard_normal((96, 256)).astype(np.float32)
+    X[:, 7] *= 20.0
+    W = (0.02 * rng.standard_normal((80, 256))).astype(np.float32)
+    b = (0.02 * rng.standard_normal(80)).astype(np.float32)
+    print(f"  head-aligned small {algo}", flush=True)
+    _head_aligned_check(table, X, W, b, algo)
+
+
+def test_head_aligned_compensator_full_size(table):
+    w = WORKLOADS["vitl_comp_head_aligned"]
+    X, W = draw(w)
+    b = draw_bias(w)
+    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], np.random.default_rng(5).choice(w.M, 6)]))
+    print("  head-aligned full size", flush=True)
+    _head_aligned_check(table, X, W, b, "auto", rows=rows)

@@ -393,6 +393,51 @@ def test_sc_error_falls_with_stream_length_and_norm_ratio_is_near_one():
     assert errs[2] < 0.1
 
 
+# ------------------------------------------- head-aligned compensator ----
+
+def test_head_aligned_zero_weights_give_the_bias():
+    # W = 0 quantises to zero scales, so every head's decode term is 0.
+    rng = np.random.default_rng(31)
+    X = rng.standard_normal((5, 192)).astype(np.float32)
+    b = rng.standard_normal(7)
+    out = o.head_aligned_rows(X, np.zeros((7, 192), np.float32), b, head_dim=64, L=256)
+    assert np.array_equal(out["C"], np.broadcast_to(b, (5, 7)))
+
+
+def test_head_aligned_full_scale_heads_are_exact():
+    # Each head of each x row holds one positive value (a different one per
+    # head), so x quantises to +127 on every column with that head's own
+    # scale, and at L = 256 every term is (2 u_B / 256 - 1) exactly: the
+    # output is the sum over heads of s^A_h s^B_jh 127^2 sum_d (2 u_B / 256 - 1)
+    # with W quantised per row over each head's columns, plus the bias.
+    rng = np.random.default_rng(32)
+    hd, H, N = 16, 3, 6
+    X = np.repeat(np.array([[1.0, 5.0, 0.25], [2.0, 0.5, 3.0]], np.float32), hd, axis=1)
+    W = rng.standard_normal((N, H * hd)).astype(np.float32)
+    b = rng.standard_normal(N)
+    out = o.head_aligned_rows(X, W, b, head_dim=hd, L=256)
+    want = np.tile(b, (2, 1)).astype(np.float64)
+    for h in range(H):
+        cols = slice(h * hd, (h + 1) * hd)
+        xa, sa = o.quantize(X[:, cols], 8)
+        xb, sb = o.quantize(W[:, cols], 8)
+        assert np.all(xa == 127)
+        ub = o.bipolar_level(xb, 8)
+        term = (2.0 * ub / 256 - 1).sum(axis=1)
+        want += np.float64(sa[:, :1]) * sb[:, 0].astype(np.float64)[None, :] * 127 ** 2 * term[None, :]
+    assert np.allclose(out["C"], want, rtol=1e-12, atol=1e-12)
+
+
+def test_head_aligned_tracks_the_float_product():
+    rng = np.random.default_rng(33)
+    X = rng.standard_normal((4, 256)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((24, 256))).astype(np.float32)
+    b = 0.02 * rng.standard_normal(24)
+    ref = X.astype(np.float64) @ W.astype(np.float64).T + b
+    out = o.head_aligned_rows(X, W, b, head_dim=64, L=256)
+    assert np.linalg.norm(out["C"] - ref) / np.linalg.norm(ref) < 0.1
+
+
 # ---------------------------------------------------- mixed precision ----
 
 def test_rung_cuts_workload_fractions():
