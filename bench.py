@@ -58,10 +58,17 @@ def git_sha():
         return None
 
 
-def work_per_step(plan, M, N, G):
+def work_per_step(plan, M, N, G, heads=0):
     """Algorithmic work of one product: bit-MACs sum_i N * sum_b D_b L[b][rung_i],
-    and the paired int8 MACs sum_i N * sum_b D_b ceil(L/2) of the matrix-core form."""
-    cuts = plan.row_cuts(M)
+    and the paired int8 MACs sum_i N * sum_b D_b ceil(L/2) of the matrix-core form.
+    With ``heads`` the rungs are per head: per image, the plan's cuts split
+    the heads, and every row of a head runs its head's length."""
+    if heads:
+        hc = plan.row_cuts(heads)
+        cuts = [c * M for c in hc]
+        G = G // heads
+    else:
+        cuts = plan.row_cuts(M)
     cols = plan.band_columns()
     L = plan.band_lengths()
     bitmacs = 0
@@ -86,10 +93,39 @@ def cpu_baseline(w, A, B, n_rows_req):
 
     okw = dict(p=8, Lmax=256, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
                n_bands=w.n_bands, tilt=w.tilt, metric=w.metric)
+    nw = workers()
+    heads = w.extra.get("heads", 0)
+    if heads:
+        # Per-head rungs: rank the first image's heads, then, per rung, take
+        # query rows of its heads in rank order against each head's keys
+        # (rows here are several hundred times cheaper than fc1 rows).
+        want = n_rows_req or 400 * nw
+        t0 = time.perf_counter()
+        hr = o.head_rungs(A[:heads], o.OraclePlan(**okw))
+        per = max(1, -(-want // len(w.levels)))
+        rows_done = 0
+        bitmacs = 0
+        for k in range(len(w.levels)):
+            left = per
+            for h in [int(h) for h in hr["order"] if hr["rung"][h] == k]:
+                rows = np.arange(min(left, w.M))
+                out = pooled_rows_product(A[h][rows], np.full(len(rows), k), B[h], okw, n_workers=nw)
+                bitmacs += int(np.sum(out["L"])) * w.D * B.shape[1]
+                rows_done += len(rows)
+                left -= len(rows)
+                if left <= 0:
+                    break
+        dt = time.perf_counter() - t0
+        return {
+            "value": bitmacs / dt, "unit": "bit-MAC/s", "cores": nw, "kind": "oracle",
+            "sample": f"{rows_done} query rows (up to {per} per rung, heads of image 0 in rank order) x all "
+                      f"{B.shape[1]} keys x all D={w.D}, materialised C-BSG streams, {bitmacs:.3e} bit-MACs in "
+                      f"{dt:.1f} s wall incl. head ranking and quantisation",
+            "seconds": dt,
+        }
+    want = n_rows_req or 2 * nw
     A0 = A[0] if A.ndim == 3 else A
     B0 = B[0] if B.ndim == 3 else B
-    nw = workers()
-    want = n_rows_req or 2 * nw
     t0 = time.perf_counter()
     cls = o.classify(A0, o.OraclePlan(**okw))
     per = max(1, -(-want // len(w.levels)))
@@ -158,6 +194,14 @@ def main():
     rg = torch.empty((G, M), dtype=torch.uint8, device=dev)
     pm = torch.empty((G, M), dtype=torch.int32, device=dev)
     th = torch.empty((G, max(plan.n_rungs - 1, 1)), dtype=torch.float32, device=dev)
+    heads = w.extra.get("heads", 0)
+    if heads:
+        # Per-head rungs: one metric, rung and rank per (image, head).
+        hm = torch.empty(G, dtype=torch.float32, device=dev)
+        gh = torch.empty((G // heads, heads), dtype=torch.float32, device=dev)
+        rg = torch.empty((G // heads, heads), dtype=torch.uint8, device=dev)
+        pm = torch.empty((G // heads, heads), dtype=torch.int32, device=dev)
+        th = torch.empty((G // heads, max(plan.n_rungs - 1, 1)), dtype=torch.float32, device=dev)
     C = torch.empty((G, M, N), dtype=torch.float32, device=dev)
     ws_bytes = scmp.scmp_matmul_workspace_bytes(table, plan, G, M, N, args.algo)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
@@ -168,8 +212,13 @@ def main():
         scmp.scmp_quantize_encode(table, plan, A, q_out=qA, scales_out=sA, metric_out=mA, stream=stream)
         scmp.scmp_quantize_encode(table, plan, B, q_out=qB, scales_out=sB, packed_out=pB, want_metric=False,
                                   stream=stream)
-        perm = None
-        if plan.n_rungs > 1:
+        perm = group_rung = None
+        if heads:
+            scmp.scmp_group_max(mA, out=hm, stream=stream)
+            scmp.scmp_classify_rows(plan, hm.view(G // heads, heads), ghat_out=gh, rung_out=rg, perm_out=pm,
+                                    thresholds_out=th, stream=stream)
+            group_rung = rg.view(G)
+        elif plan.n_rungs > 1:
             scmp.scmp_classify_rows(plan, mA, ghat_out=gh, rung_out=rg, perm_out=pm, thresholds_out=th,
                                     stream=stream)
             perm = pm
@@ -178,7 +227,7 @@ def main():
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
         scmp.scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, packedB=pB, algo=args.algo, C_out=C,
-                         want_C=True, workspace=ws, bias=bias, stream=stream)
+                         want_C=True, workspace=ws, bias=bias, group_rung=group_rung, stream=stream)
         if timed:
             e1.record(stream)
             ev.append((e0, e1))
@@ -193,7 +242,7 @@ def main():
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    bitmacs, paired = work_per_step(plan, M, N, G)
+    bitmacs, paired = work_per_step(plan, M, N, G, heads)
     value = bitmacs / (ms_per_step / 1e3)
     L_eff = bitmacs / (G * M * N * D)
 

@@ -263,8 +263,37 @@ int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int 
                      const float* bias_dev, int32_t* counts_dev, float* C_dev, int64_t ldc,
                      int64_t batch_stride_c, void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/* scmp_matmul with one stream length per group instead of per row: every
+ * row of group g runs rung group_rung[g] of the plan's ladder (values past
+ * the last rung clamp to it), in original row order.  This is the per-head
+ * fixed mixed precision on QK of [VIT] (mixed-precision flag table: QK
+ * levels and head fractions, head metric |Q_h|.amax): with G = images x
+ * heads, each head's scores Q_h K_h^T all run at the head's length ([PAYN]
+ * Key design 3, one L per output row).  The plan's row cuts and fractions
+ * are not used here (they rank the heads, see scmp_group_max).  The
+ * workspace size is scmp_matmul_workspace_bytes for the same plan, algo
+ * and sizes (it covers both row orders).
+ *   group_rung_dev uint8 [G] (required); no row permutation; other
+ *   arguments as scmp_matmul.
+ * Errors: as scmp_matmul; ARG when group_rung_dev is NULL. */
+int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                            const int8_t* qA_dev, const float* sA_dev, const int8_t* qB_dev,
+                            const uint32_t* packedB_dev, const float* sB_dev, const uint8_t* group_rung_dev,
+                            int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
+                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* Largest value of each group: out_dev[g] = max_i in_dev[g][i] (float32;
+ * NaN values are skipped; -inf when all are NaN).  Applied to the row metrics
+ * of scmp_quantize_encode over a head's rows it gives the per-head QK
+ * metric |Q_h|.amax of [VIT] (mixed-precision flag table); ranking those
+ * per image with scmp_classify_rows (M = heads) gives the head rungs.
+ *   in_dev float [G][M], out_dev float [G]; M >= 1 when G > 0.
+ * Errors: ARG, HIP. */
+int scmp_group_max(const float* in_dev, int G, int M, float* out_dev, void* stream);
+
 /* Diagnostic: synchronise `stream` and return the multiply-accumulates the
- * last MFMA-path scmp_matmul with this workspace issued on the matrix cores
+ * last MFMA-path contraction with this workspace (scmp_matmul or one of
+ * its variants above) issued on the matrix cores
  * (every step of every 128 x 128 tile: four MFMAs per wave, 32 x 32 x 32
  * int8 or 32 x 32 x 64 fp4 MACs each).  The count follows from the data: a
  * step is issued when some row of the tile needs it.  *macs receives all of

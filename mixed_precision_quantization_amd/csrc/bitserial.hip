@@ -38,6 +38,7 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
   const int g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, blockIdx.y, BS_BM, k, pos0, nrows);
+  k = tile_rung(a, g, k);
   const int col0 = blockIdx.x * BS_BN;
   if (tid < BS_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
   const int ty = tid >> 4, tx = tid & 15;

@@ -261,6 +261,22 @@ __global__ void __launch_bounds__(512) k_classify_bucket(ClassifyArgs a, int set
   }
 }
 
+// Largest value of each group: the per-head metric |Q_h|.amax as the
+// maximum of the head's row metrics ([VIT] mixed-precision flag table,
+// per-head fixed MP on QK).  One block per group.
+__global__ void __launch_bounds__(256) k_group_max(const float* in, int M, float* out) {
+  __shared__ float red[4];
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const float* x = in + (long long)g * M;
+  float m = -__builtin_inff();
+  for (int j = tid; j < M; j += 256) m = fmaxf(m, x[j]);
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  if (tid == 0) out[g] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
 int read_clear_classify_flags(hipStream_t st, int* flags) {
   int v = 0, zero = 0;
   hipError_t e =
@@ -312,5 +328,17 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("classify launch: ") + hipGetErrorString(e));
+  return SCMP_OK;
+}
+
+extern "C" int scmp_group_max(const float* in_dev, int G, int M, float* out_dev, void* stream) {
+  scmp::clear_error();
+  if (G < 0 || M < 0) return set_error(SCMP_ERR_ARG, "negative size");
+  if (G == 0) return SCMP_OK;
+  if (M == 0) return set_error(SCMP_ERR_ARG, "a group needs at least one value");
+  if (!in_dev || !out_dev) return set_error(SCMP_ERR_ARG, "in and out are required");
+  hipLaunchKernelGGL(scmp::k_group_max, dim3(G), dim3(256), 0, (hipStream_t)stream, in_dev, M, out_dev);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("group max launch: ") + hipGetErrorString(e));
   return SCMP_OK;
 }

@@ -45,6 +45,7 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M,
   a.chunk_d = P.chunk_d;
   a.n_chunks = P.n_chunks;
   a.n_rungs = P.n_rungs;
+  a.n_ladder = P.n_rungs;
   a.n_bands = P.n_bands;
   a.q = qmax(P.p);
   a.P = 1 << P.p;
@@ -60,6 +61,17 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M,
       a.pair_off[b][k] = table->pair_off[P.band_L[b][k]];
     }
   return SCMP_OK;
+}
+
+// One tiling rung over every group's rows in original order, for per-group
+// lengths (the rung of each tile comes from group_rung).
+static void group_tiling(MatmulArgs& a, int algo) {
+  const int BM = algo == SCMP_ALGO_BITSERIAL ? 64 : 128;
+  a.n_rungs = 1;
+  a.cuts[0] = 0;
+  a.cuts[1] = a.M;
+  a.tile_start[0] = 0;
+  a.tile_start[1] = (a.M + BM - 1) / BM;
 }
 
 // ---------------------------------------------------------------- decode ----
@@ -104,7 +116,12 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
   int st = scmp::prepare(table, plan, algo, G, M, N, a);
   if (st != SCMP_OK) return st;
   if (algo == SCMP_ALGO_BITSERIAL || (long long)G * M * N == 0) return SCMP_OK;
-  *bytes = scmp::mfma_workspace_bytes(a);
+  // Enough for both tilings: rows bucketed by rung, or each group's rows in
+  // order (scmp_matmul_group_rungs).
+  const size_t by_rung = scmp::mfma_workspace_bytes(a);
+  scmp::group_tiling(a, algo);
+  const size_t by_group = scmp::mfma_workspace_bytes(a);
+  *bytes = by_rung > by_group ? by_rung : by_group;
   return SCMP_OK;
 }
 
@@ -112,8 +129,9 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
 
 static int matmul_impl(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
                        const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
-                       const float* sB, const float* bias, int32_t* counts, float* C, int64_t ldc,
-                       int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
+                       const float* sB, const float* bias, const uint8_t* group_rung, int32_t* counts, float* C,
+                       int64_t ldc, int64_t batch_stride_c, void* workspace, size_t workspace_bytes,
+                       void* stream) {
   scmp::clear_error();
   scmp::MatmulArgs a;
   int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
@@ -123,7 +141,13 @@ static int matmul_impl(scmp_table_t table, scmp_plan_t plan, int algo, int G, in
   if (!qA || !sA || !qB || !sB) return set_error(SCMP_ERR_ARG, "qA, sA, qB and sB are required");
   if (!counts && !C) return set_error(SCMP_ERR_ARG, "at least one of counts and C is required");
   if (C && ldc < N) return set_error(SCMP_ERR_ARG, "ldc must be >= N");
-  if (P.n_rungs > 1 && !permA) return set_error(SCMP_ERR_ARG, "mixed precision needs the row permutation");
+  if (group_rung) {
+    a.group_rung = group_rung;
+    scmp::group_tiling(a, algo);
+    permA = nullptr;
+  } else if (P.n_rungs > 1 && !permA) {
+    return set_error(SCMP_ERR_ARG, "mixed precision needs the row permutation");
+  }
   const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
   if (bitserial && !packedB) return set_error(SCMP_ERR_ARG, "the bit-serial kernel needs packed B streams");
   a.qA = qA;
@@ -147,8 +171,20 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
                 const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, nullptr, counts, C, ldc,
-                     batch_stride_c, workspace, workspace_bytes, stream);
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, nullptr, nullptr, counts, C,
+                     ldc, batch_stride_c, workspace, workspace_bytes, stream);
+}
+
+int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                            const int8_t* qA, const float* sA, const int8_t* qB, const uint32_t* packedB,
+                            const float* sB, const uint8_t* group_rung, int32_t* counts, float* C, int64_t ldc,
+                            int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!group_rung) {
+    scmp::clear_error();
+    return set_error(SCMP_ERR_ARG, "group_rung is NULL (use scmp_matmul)");
+  }
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, nullptr, qB, packedB, sB, nullptr, group_rung, counts, C,
+                     ldc, batch_stride_c, workspace, workspace_bytes, stream);
 }
 
 int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
@@ -159,7 +195,7 @@ int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int 
     scmp::clear_error();
     return set_error(SCMP_ERR_ARG, "bias is NULL (use scmp_matmul)");
   }
-  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, bias, counts, C, ldc,
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, bias, nullptr, counts, C, ldc,
                      batch_stride_c, workspace, workspace_bytes, stream);
 }
 

@@ -22,6 +22,11 @@ struct MatmulArgs {
   int32_t* counts;
   float* C;
   const float* bias;  // [G][N] added to every row of C (nullable)
+  // Per-group lengths: every row of group g runs rung group_rung[g] of the
+  // ladder (nullable).  Tiles then take each group's rows in order (one
+  // tiling rung, no permutation); n_ladder is the ladder's rung count.
+  const uint8_t* group_rung;
+  int n_ladder;
   long long ldc, bsc;
   const uint8_t* pair;
   const uint16_t* cum;
@@ -48,6 +53,14 @@ __device__ __forceinline__ void locate_tile(const MatmulArgs& a, int y, int BM, 
   while (k + 1 < a.n_rungs && y >= a.tile_start[k + 1]) ++k;
   pos0 = a.cuts[k] + (y - a.tile_start[k]) * BM;
   nrows = min(BM, a.cuts[k + 1] - pos0);
+}
+
+// The rung a tile runs: its group's rung with per-group lengths, else the
+// tiling rung k (clamped so a corrupted input never indexes past the ladder).
+__device__ __forceinline__ int tile_rung(const MatmulArgs& a, int g, int k) {
+  if (!a.group_rung) return k;
+  const int r = a.group_rung[g];
+  return r < a.n_ladder ? r : a.n_ladder - 1;
 }
 
 // Original row of a sorted position (the identity without a permutation).

@@ -104,6 +104,10 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
   const size_t ts_b = al(2 * sizeof(unsigned long long) + sizeof(unsigned int));
   char* p = (char*)base;
+  // The step counters first, at an offset that does not depend on the sizes.
+  w.issued = (unsigned long long*)(p ? p + off : nullptr);
+  w.work = (unsigned int*)(p ? p + off + 2 * sizeof(unsigned long long) : nullptr);
+  off += ts_b;
   w.hs = (uint32_t*)(p ? p + off : nullptr);
   off += hs_b;
   w.maxh = (uint8_t*)(p ? p + off : nullptr);
@@ -120,9 +124,6 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   off += ri_b;
   w.sas = (float*)(p ? p + off : nullptr);
   off += sa_b;
-  w.issued = (unsigned long long*)(p ? p + off : nullptr);
-  w.work = (unsigned int*)(p ? p + off + 2 * sizeof(unsigned long long) : nullptr);
-  off += ts_b;
   *total = off;
   return w;
 }
@@ -180,6 +181,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, y, MF_BM, k, pos0, nrows);
+  k = tile_rung(a, g, k);
   const int wave = tid >> 6, lane = tid & 63;
   const int pr = tid >> 2, q = tid & 3;
   const int p_lo = pair_lo(pr), p_hi = p_lo + 32;
@@ -474,6 +476,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int g = blockIdx.z, y = blockIdx.y;  // y: encode tile (128 rows of one rung)
   int k, pos0, nrows;
   locate_tile(a, y, BM, k, pos0, nrows);
+  k = tile_rung(a, g, k);
   const long long prow0 = (long long)y * BM;
   const int col0 = blockIdx.x * BN;
   for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
@@ -768,7 +771,6 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
 // index-major copies of the encode buffers a few steps ahead.
 constexpr int FL_LIST = 512;  // list capacity per wave (half-blocks)
 constexpr int FL_RING = 4;    // list steps whose codes are in flight
-constexpr int FL_PAD = 4 * FL_RING + 4;  // padding entries past a list's end
 
 // Work item -> (rung k, group g, encode tile y, column tile x); items run
 // rung by rung, then group, row tile, column tile.
@@ -858,7 +860,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
 
   while (true) {
     const PersItem it = pers_item(a, w.CT, item);
-    const int k = it.k, g = it.g, y = it.y;
+    const int k = tile_rung(a, it.g, it.k), g = it.g, y = it.y;
     const int col0 = it.x * MF_BN;
     const bool count_steps = it.x == 0;
     const int next = s_item[cur ^ 1];

@@ -42,7 +42,7 @@ EXPORTED = [
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
-    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
+    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
 ]
 
 
@@ -103,6 +103,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
         "scmp_matmul_bias": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t,
                                  vp]),
+        "scmp_matmul_group_rungs": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
+                                        ctypes.c_size_t, vp]),
+        "scmp_group_max": (i, [vp, i, i, vp, vp]),
         "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
                                         ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_ulonglong),
                                         vp]),
@@ -336,11 +339,12 @@ def scmp_matmul_workspace_bytes(table: Table, plan: Plan, G: int, M: int, N: int
 
 def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=None, algo: str = "auto",
                 counts_out=None, C_out=None, want_counts: bool = False, want_C: bool = True, workspace=None,
-                bias=None, stream=None):
+                bias=None, group_rung=None, stream=None):
     """SC product of encoded operands.  qA int8 [G, M, D], qB int8 [G, N, D].
     ``workspace``: uint8 device tensor of at least scmp_matmul_workspace_bytes
     (allocated here when None).  ``bias``: float [G, N] added to every row
-    of C (scmp_matmul_bias), or None.
+    of C (scmp_matmul_bias), or None.  ``group_rung``: uint8 [G], one rung
+    per group for all its rows (scmp_matmul_group_rungs; no permA), or None.
 
     Returns (counts int32 [G, M, N, n_bands] or None, C float [G, M, N] or None).
     """
@@ -370,7 +374,13 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
             _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"), _ptr(sB, torch.float32, "sB"))
     tail = (_ptr(counts_out, torch.int32, "counts_out"), _ptr(C_out, torch.float32, "C_out"),
             N, M * N, _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream))
-    if bias is None:
+    if group_rung is not None:
+        if bias is not None or permA is not None:
+            raise ValueError("group_rung excludes bias and permA")
+        _need(group_rung, G, "group_rung")
+        head = head[:8] + head[9:] + (_ptr(group_rung, torch.uint8, "group_rung"),)
+        _check("scmp_matmul_group_rungs", load().scmp_matmul_group_rungs(*head, *tail))
+    elif bias is None:
         _check("scmp_matmul", load().scmp_matmul(*head, *tail))
     else:
         _need(bias, G * N, "bias")
@@ -405,6 +415,19 @@ def scmp_decode(plan: Plan, counts, sA, sB, rung=None, C_out=None, stream=None):
     return C_out
 
 
+def scmp_group_max(values: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """out[g] = max of values[g, :] (float [G, M] -> float [G])."""
+    v2 = values if values.dim() == 2 else values.unsqueeze(0)
+    v2 = v2.contiguous()
+    G, M = v2.shape
+    if out is None:
+        out = torch.empty(G, dtype=torch.float32, device=values.device)
+    _need(out, G, "out")
+    _check("scmp_group_max", load().scmp_group_max(_ptr(v2, torch.float32, "values"), G, M,
+                                                    _ptr(out, torch.float32, "out"), _stream(stream)))
+    return out
+
+
 def scmp_error_flags(stream=None) -> int:
     """Synchronise and return (then clear) the device error flags; raises on NONFINITE."""
     flags = ctypes.c_int(0)
@@ -431,3 +454,29 @@ def sc_linear(table: Table, plan: Plan, A: torch.Tensor, B: torch.Tensor, algo: 
                             want_counts=want_counts, bias=bias, stream=stream)
     return {"qA": qA, "sA": sA, "metric": mA, "qB": qB, "sB": sB, "packedB": pB, "ghat": ghat,
             "rung": rung, "perm": perm, "thresholds": thr, "counts": counts, "C": C}
+
+
+def sc_qk_head_mp(table: Table, plan: Plan, Q: torch.Tensor, K: torch.Tensor, heads: int, algo: str = "auto",
+                  want_counts: bool = False, stream=None):
+    """Scores Q K^T with one stream length per head: Q [B*heads, M, D] and
+    K [B*heads, N, D] (group g = image g // heads, head g % heads).  Each
+    head's metric is |Q_h|.amax (the largest of its row metrics); per image
+    the heads are ranked by it with the plan's levels and fractions (read as
+    head fractions), and every score of a head runs at its rung."""
+    qA, sA, mA, _ = scmp_quantize_encode(table, plan, Q, stream=stream)
+    qB, sB, _, pB = scmp_quantize_encode(table, plan, K, want_metric=False,
+                                         want_packed=(algo == "bitserial"), stream=stream)
+    G = qA.shape[0] if qA.dim() == 3 else 1
+    if G % heads:
+        raise ValueError("G must be a multiple of heads")
+    head_metric = scmp_group_max(mA.reshape(G, -1), stream=stream)
+    ghat = rung = perm = thr = None
+    if plan.n_rungs > 1:
+        ghat, rung, perm, thr = scmp_classify_rows(plan, head_metric.view(G // heads, heads), stream=stream)
+        group_rung = rung.view(G)
+    else:
+        group_rung = torch.zeros(G, dtype=torch.uint8, device=qA.device)
+    counts, C = scmp_matmul(table, plan, qA, sA, qB, sB, packedB=pB, algo=algo, want_counts=want_counts,
+                            group_rung=group_rung, stream=stream)
+    return {"qA": qA, "sA": sA, "metric": mA, "head_metric": head_metric, "qB": qB, "sB": sB, "packedB": pB,
+            "ghat": ghat, "head_rung": group_rung, "perm": perm, "thresholds": thr, "counts": counts, "C": C}

@@ -42,7 +42,8 @@ class Workload:
 
 
 # The five workloads (the fifth has two parts: fc2 with K-bands, and AV),
-# per-query-row mixed precision on QK^T, and the head-aligned compensator.
+# per-query-row and per-head mixed precision on QK^T, and the head-aligned
+# compensator.
 WORKLOADS = {
     "single_64": Workload(
         "single_64", "linear", 1, 64, 64, 64, (64,), seed=1001,
@@ -80,6 +81,14 @@ WORKLOADS = {
         "vitl_comp_head_aligned", "linear", 1, 64 * 257, 1024, 1024,
         (256,), None, chunk_d=64, seed=1008,
         a_dist="outlier", b_dist="weight", extra={"bias": True}),
+    # Per-head fixed mixed precision on QK^T (scmp_vit README, the
+    # mixed-precision flag table): 8 images x 16 heads, each head's scores
+    # at one length from its |Q_h|.amax rank within the image, on the same
+    # ladder, with head fractions 1/4, 1/2, 1/4 (4, 8 and 4 heads).
+    "vitl_qk_head_mp": Workload(
+        "vitl_qk_head_mp", "qk", 128, 257, 257, 64,
+        (256, 128, 64), (0.25, 0.5, 0.25), seed=1009,
+        a_dist="head_scaled", b_dist="normal", extra={"heads": 16}),
 }
 
 
@@ -116,6 +125,12 @@ def _draw(rng, dist: str, lead: tuple, rows: int, cols: int) -> np.ndarray:
         chans = rng.choice(cols, size=n_out, replace=False)
         x[..., chans] *= 20.0
         return x
+    if dist == "head_scaled":
+        # Gaussian rows, each group (one image's head) scaled by its own
+        # log-normal amplitude exp(0.5 z), so that heads differ in |Q|.amax.
+        x = rng.standard_normal(shape)
+        amp = np.exp(0.5 * rng.standard_normal(lead + (1, 1)))
+        return x * amp
     if dist == "gelu":
         return _gelu(rng.standard_normal(shape))
     if dist == "softmax":

@@ -55,7 +55,15 @@ from .mp import (
     check_band_ladder,
 )
 from .decode import decode_terms, decode
-from .matmul import OraclePlan, classify, head_aligned_rows, rows_product, sc_matmul_rows
+from .matmul import (
+    OraclePlan,
+    classify,
+    head_aligned_rows,
+    head_mp_rows,
+    head_rungs,
+    rows_product,
+    sc_matmul_rows,
+)
 
 __all__ = [
     "sobol_points",
@@ -86,4 +94,6 @@ __all__ = [
     "rows_product",
     "sc_matmul_rows",
     "head_aligned_rows",
+    "head_mp_rows",
+    "head_rungs",
 ]

@@ -196,3 +196,41 @@ def head_aligned_rows(X, W, bias, head_dim: int = 64, L: int = 256, p: int = 8, 
         C += r["C"]
         C_abs += r["C_abs"]
     return {"C": C + bias[None, :], "C_abs": C_abs + np.abs(bias)[None, :]}
+
+
+def head_rungs(Q_heads, plan: OraclePlan):
+    """Per-head fixed mixed precision on QK (scmp_vit README, the
+    mixed-precision flag table: QK levels, head fractions, head metric
+    |Q_h|.amax) for one image: ``Q_heads`` (H, M, D).  The metric of head h
+    is the largest |Q| over all of its rows and columns (float32); the heads
+    are ranked by its normalised value exactly as rows are ranked in
+    "Precision As You Need" Key design 2 (descending, ties by head index),
+    and the plan's fractions, read as head fractions, cut that ranking into
+    the ladder's rungs.  Returns ``metric`` (H,), ``g_hat``, ``rung`` (H,)
+    and ``order``."""
+    Q = np.asarray(Q_heads, dtype=np.float32)
+    H = Q.shape[0]
+    metric = np.abs(Q).reshape(H, -1).max(axis=1).astype(np.float32)
+    g_hat = normalise_metric(metric)
+    if plan.n_rungs > 1:
+        rung, order = assign_rungs(g_hat, plan.n_rungs, plan.fractions)
+    else:
+        rung = np.zeros(H, dtype=np.int64)
+        order = np.arange(H, dtype=np.int64)
+    return {"metric": metric, "g_hat": g_hat, "rung": np.asarray(rung, dtype=np.int64), "order": order}
+
+
+def head_mp_rows(Q_heads, K_heads, plan: OraclePlan, head: int, rows=None):
+    """Scores Q_h K_h^T of head ``head`` of one image under per-head fixed
+    mixed precision: every row of the head runs the head's rung from
+    ``head_rungs`` ("Precision As You Need" Key design 3 with one length per
+    head).  Restricted to the query rows ``rows`` (all when None).  Returns
+    ``rows_product``'s dict plus ``head_rung`` and ``rows``."""
+    Q = np.asarray(Q_heads, dtype=np.float32)
+    cls = head_rungs(Q, plan)
+    k = int(cls["rung"][head])
+    rows = np.arange(Q.shape[1]) if rows is None else np.asarray(rows, dtype=np.int64)
+    out = rows_product(Q[head][rows], np.full(len(rows), k, dtype=np.int64), np.asarray(K_heads)[head], plan)
+    out["head_rung"] = k
+    out["rows"] = rows
+    return out

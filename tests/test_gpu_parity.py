@@ -334,6 +334,8 @@ def test_full_size_sampled_rows(table, name):
     (MFMA path, fused decode, no counts), checked on sampled rows of every
     rung; the counts variant is checked bit-exact on the same rows."""
     w = WORKLOADS[name]
+    if w.extra.get("heads"):
+        pytest.skip("per-head rungs: test_head_mp_full_size")
     A, B = _groups(*draw(w))
     plan, okw = _plans(w)
     print(f"  full {name}", flush=True)
@@ -400,3 +402,97 @@ def test_head_aligned_compensator_full_size(table):
     rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], np.random.default_rng(5).choice(w.M, 6)]))
     print("  head-aligned full size", flush=True)
     _head_aligned_check(table, X, W, b, "auto", rows=rows)
+
+
+# ------------------------------------------------- per-head MP on QK^T --
+
+def _head_mp_check(table, w, Q, K, algo, images, rows_of=None):
+    """GPU sc_qk_head_mp against the oracle: per image, the head metric
+    |Q_h|.amax, its normalised value and the head rungs bit-exact; per
+    checked head, the integers, scales and counts of its rows bit-exact at
+    the head's length and C within the decode tolerance."""
+    heads = w.extra["heads"]
+    plan, okw = _plans(w)
+    res = _to_np(scmp.sc_qk_head_mp(table, plan, torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda(), heads,
+                                    algo=algo, want_counts=True))
+    torch.cuda.synchronize()
+    oplan = o.OraclePlan(**okw)
+    for img in images:
+        hs = slice(img * heads, (img + 1) * heads)
+        cls = o.head_rungs(Q[hs], oplan)
+        assert np.array_equal(res["head_metric"][hs], cls["metric"]), "head metric"
+        assert np.array_equal(res["ghat"][img], cls["g_hat"]), "normalised head metric"
+        assert np.array_equal(res["head_rung"][hs].astype(np.int64), cls["rung"]), "head rungs"
+        assert np.array_equal(res["perm"][img].astype(np.int64), cls["order"]), "head order"
+        for h in range(heads):
+            g = img * heads + h
+            rows = np.arange(w.M) if rows_of is None else rows_of(g)
+            k = int(cls["rung"][h])
+            orc = pooled_rows_product(Q[g][rows], np.full(len(rows), k, np.int64), K[g], okw)
+            assert np.array_equal(res["qA"][g][rows].astype(np.int64), orc["x_a"]), "Q integers"
+            assert np.array_equal(res["sA"][g][rows], orc["s_a"]), "Q scales"
+            assert np.array_equal(res["qB"][g].astype(np.int64), orc["x_b"]), "K integers"
+            got = res["counts"][g][rows].astype(np.int64)
+            bad = np.argwhere(got != orc["band_counts"])
+            assert bad.size == 0, f"head {g}: {len(bad)} count mismatches, first {bad[:3].tolist()}"
+            err = np.abs(res["C"][g][rows].astype(np.float64) - orc["C"])
+            lim = RTOL * orc["C_abs"]
+            assert np.all(err <= lim), f"head {g}: max err/limit {np.max(err / np.maximum(lim, 1e-300)):.3g}"
+    return res
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_head_mp_small(table, algo):
+    w = shrink(WORKLOADS["vitl_qk_head_mp"], G=32, M=70, N=66)
+    Q, K = draw(w)
+    print(f"  head mp small {algo} G={w.G} M={w.M} N={w.N}", flush=True)
+    # Image 0: every row of every head; image 1: three rows per head.
+    _head_mp_check(table, w, Q, K, algo, images=(0,),)
+    _head_mp_check(table, w, Q, K, algo, images=(1,), rows_of=lambda g: np.array([0, 33, w.M - 1]))
+
+
+def test_head_mp_full_size(table):
+    """The benchmark's launch (AUTO, fused decode), checked on two sampled
+    rows of every head of images 0 and 7; the C of the counts-free launch
+    equals the counted one."""
+    w = WORKLOADS["vitl_qk_head_mp"]
+    Q, K = draw(w)
+    heads = w.extra["heads"]
+    plan, _ = _plans(w)
+    print("  head mp full size", flush=True)
+    bench = _to_np(scmp.sc_qk_head_mp(table, plan, torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda(), heads,
+                                      algo="auto", want_counts=False))
+    res = _head_mp_check(table, w, Q, K, "auto", images=(0, 7),
+                         rows_of=lambda g: np.array([(g * 37) % w.M, w.M - 1 - g % 5]))
+    assert np.array_equal(bench["C"], res["C"])
+    sizes = np.bincount(res["head_rung"].reshape(-1, heads)[0], minlength=plan.n_rungs)
+    assert sizes.tolist() == np.diff(plan.row_cuts(heads)).tolist()
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_group_rungs_clamp_and_match_fixed_length(table, algo):
+    """scmp_matmul_group_rungs with hand-set rungs: every group equals the
+    single-length product at its rung's level (rungs past the ladder clamp
+    to its last rung)."""
+    rng = np.random.default_rng(51)
+    G, M, N, D = 5, 150, 40, 64
+    Q = rng.standard_normal((G, M, D)).astype(np.float32)
+    K = rng.standard_normal((G, N, D)).astype(np.float32)
+    levels = (256, 96, 33)
+    plan = scmp.scmp_plan_create(op="qk", D=D, levels=levels, fractions=(0.2, 0.3, 0.5))
+    Qt, Kt = torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda()
+    qA, sA, _, _ = scmp.scmp_quantize_encode(table, plan, Qt)
+    qB, sB, _, pB = scmp.scmp_quantize_encode(table, plan, Kt, want_metric=False,
+                                              want_packed=(algo == "bitserial"))
+    gr = torch.tensor([2, 0, 1, 9, 1], dtype=torch.uint8, device="cuda")
+    print(f"  group rungs {algo}", flush=True)
+    counts, C = scmp.scmp_matmul(table, plan, qA, sA, qB, sB, packedB=pB, algo=algo, want_counts=True,
+                                 group_rung=gr)
+    torch.cuda.synchronize()
+    counts, C = counts.cpu().numpy(), C.cpu().numpy()
+    for g, k in enumerate([2, 0, 1, 2, 1]):
+        okw = dict(p=8, Lmax=256, D=D, levels=(levels[k],))
+        orc = pooled_rows_product(Q[g], np.zeros(M, np.int64), K[g], okw)
+        assert np.array_equal(counts[g].astype(np.int64), orc["band_counts"]), f"group {g}"
+        err = np.abs(C[g].astype(np.float64) - orc["C"])
+        assert np.all(err <= RTOL * orc["C_abs"]), f"group {g}"

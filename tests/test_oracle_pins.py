@@ -438,6 +438,55 @@ def test_head_aligned_tracks_the_float_product():
     assert np.linalg.norm(out["C"] - ref) / np.linalg.norm(ref) < 0.1
 
 
+def test_head_rungs_follow_head_amplitude_and_fractions():
+    # Head h of the image is a unit-variance block scaled by amp[h]; with
+    # the amplitudes far apart the |Q_h|.amax ranking is the amplitude
+    # ranking, and fractions (0.25, 0.5, 0.25) of 8 heads give 2 / 4 / 2.
+    rng = np.random.default_rng(41)
+    amp = np.array([3.0, 0.1, 9.0, 1.0, 0.3, 27.0, 0.03, 0.9], np.float32)
+    Q = (rng.uniform(-1, 1, (8, 5, 16)) * amp[:, None, None]).astype(np.float32)
+    Q[:, 0, 0] = amp                                 # pin each head's amax
+    plan = o.OraclePlan(D=16, levels=(256, 128, 64), fractions=(0.25, 0.5, 0.25))
+    cls = o.head_rungs(Q, plan)
+    assert np.array_equal(cls["metric"], amp)
+    assert cls["order"].tolist() == [5, 2, 0, 3, 7, 4, 1, 6]
+    want = np.empty(8, np.int64)
+    want[[5, 2]] = 0
+    want[[0, 3, 7, 4]] = 1
+    want[[1, 6]] = 2
+    assert np.array_equal(cls["rung"], want)
+
+
+def test_head_rungs_ties_go_to_the_lower_head_index():
+    Q = np.ones((4, 3, 8), np.float32)
+    plan = o.OraclePlan(D=8, levels=(256, 64), fractions=(0.5, 0.5))
+    assert o.head_rungs(Q, plan)["rung"].tolist() == [0, 0, 1, 1]
+
+
+def test_head_mp_rows_is_the_fixed_length_product_at_the_head_rung():
+    # Every row of a head runs the head's length: the same counts as the
+    # single-length plan at that level, and the counts of a head at L = 64
+    # stay within 64 D while differing from the L = 256 product.
+    rng = np.random.default_rng(42)
+    H, M, N, D = 4, 6, 5, 32
+    amp = np.array([1.0, 4.0, 0.25, 2.0], np.float32)
+    Q = (rng.standard_normal((H, M, D)) * amp[:, None, None]).astype(np.float32)
+    Kt = rng.standard_normal((H, N, D)).astype(np.float32)
+    plan = o.OraclePlan(D=D, levels=(256, 64), fractions=(0.5, 0.5))
+    rungs = o.head_rungs(Q, plan)["rung"]
+    assert rungs.tolist() == [1, 0, 1, 0]
+    for h in range(H):
+        L = plan.levels[rungs[h]]
+        got = o.head_mp_rows(Q, Kt, plan, h)
+        ref = o.rows_product(Q[h], np.zeros(M, np.int64), Kt[h], o.OraclePlan(D=D, levels=(L,)))
+        assert got["head_rung"] == rungs[h]
+        assert np.array_equal(got["counts"], ref["counts"])
+        assert np.array_equal(got["C"], ref["C"])
+        assert got["counts"].max() <= L * D
+    long = o.rows_product(Q[0], np.zeros(M, np.int64), Kt[0], o.OraclePlan(D=D, levels=(256,)))
+    assert not np.array_equal(o.head_mp_rows(Q, Kt, plan, 0)["counts"], long["counts"])
+
+
 # ---------------------------------------------------- mixed precision ----
 
 def test_rung_cuts_workload_fractions():
