@@ -21,7 +21,10 @@ It is plain, slow and written to be checked by eye against the pages:
   with scale = row abs-max / 127) and the mixed-precision flag table;
 * the pull request "feat(mp): per-group (K-band) stream lengths on the
   contraction axis", sections "How the banding works", "Guards" and
-  "Tooling".
+  "Tooling";
+* for the unipolar (AND) mode, "Precision As You Need" "Research background
+  and motivation" and Key design 3, and the scmp_vit README's SC
+  compensation driver flags (``unipolar.py``).
 
 Every stream is materialised bit by bit and every XNOR is counted; counts are
 int64 and the decode is float64.  Floating point that decides an integer (the
@@ -55,6 +58,7 @@ from .mp import (
     check_band_ladder,
 )
 from .decode import decode_terms, decode
+from .unipolar import and_count, and_count_row, decode_unipolar, sign_of, unipolar_level
 from .matmul import (
     OraclePlan,
     classify,
@@ -96,4 +100,9 @@ __all__ = [
     "head_aligned_rows",
     "head_mp_rows",
     "head_rungs",
+    "unipolar_level",
+    "and_count",
+    "and_count_row",
+    "sign_of",
+    "decode_unipolar",
 ]

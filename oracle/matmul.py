@@ -30,6 +30,7 @@ from .mp import (
 from .quant import QMAX, bipolar_level, quantize
 from .sobol import sobol_points
 from .table import indicator_table
+from .unipolar import and_count_row, decode_unipolar, sign_of, unipolar_level
 
 
 @dataclass
@@ -48,6 +49,7 @@ class OraclePlan:
     band_L: Optional[np.ndarray] = None
     ceiling: int = 0
     metric: str = "linear"  # "linear": max |X_i|; "av": max_j A_ij
+    mode: str = "bipolar"   # "bipolar" (XNOR) or "unipolar" (AND, sign-magnitude)
     _cache: dict = field(default_factory=dict, repr=False)
 
     @property
@@ -98,6 +100,8 @@ def rows_product(A_rows, rung_rows, B, plan: OraclePlan):
     ``B``: (N, D).  Returns a dict with ``x_a``, ``s_a`` (of these rows),
     ``x_b``, ``s_b``, ``counts`` (R, N, n_chunks), ``band_counts``
     (R, N, n_bands), ``L`` (R, n_chunks), ``C`` and ``C_abs`` (R, N).
+    In the unipolar mode the counts are the signed sums of
+    sign_A sign_B AND-count over each chunk's indices.
     """
     A_rows = np.asarray(A_rows, dtype=np.float32)
     B = np.asarray(B, dtype=np.float32)
@@ -109,8 +113,16 @@ def rows_product(A_rows, rung_rows, B, plan: OraclePlan):
     K = plan.table()
     x_a, s_a = quantize(A_rows, plan.p, plan.chunk_d)
     x_b, s_b = quantize(B, plan.p, plan.chunk_d)
-    u_a = bipolar_level(x_a, plan.p)
-    u_b = bipolar_level(x_b, plan.p)
+    unipolar = plan.mode == "unipolar"
+    if unipolar:
+        u_a = unipolar_level(x_a, plan.p)
+        u_b = unipolar_level(x_b, plan.p)
+        sg_b = sign_of(x_b)
+    elif plan.mode == "bipolar":
+        u_a = bipolar_level(x_a, plan.p)
+        u_b = bipolar_level(x_b, plan.p)
+    else:
+        raise ValueError("mode must be bipolar or unipolar")
 
     ladder = plan.ladder()
     band_cols, chunk_band = plan.bands()
@@ -125,7 +137,10 @@ def rows_product(A_rows, rung_rows, B, plan: OraclePlan):
     for t in range(R):
         k = int(rung_rows[t])
         L_per_d = ladder[band_of_d, k]
-        per_d = xnor_count_row(K, u_a[t], u_b, L_per_d)
+        if unipolar:
+            per_d = and_count_row(K, u_a[t], u_b, L_per_d) * sign_of(x_a[t])[None, :] * sg_b
+        else:
+            per_d = xnor_count_row(K, u_a[t], u_b, L_per_d)
         for c, (c0, c1) in enumerate(bounds):
             counts[t, :, c] = per_d[:, c0:c1].sum(axis=1)
             Lrc[t, c] = ladder[chunk_band[c], k]
@@ -134,7 +149,10 @@ def rows_product(A_rows, rung_rows, B, plan: OraclePlan):
     for c in range(len(bounds)):
         band_counts[:, :, chunk_band[c]] += counts[:, :, c]
 
-    C, C_abs = decode(counts, s_a, s_b, Lrc, widths, q)
+    if unipolar:
+        C, C_abs = decode_unipolar(counts, s_a, s_b, Lrc, q)
+    else:
+        C, C_abs = decode(counts, s_a, s_b, Lrc, widths, q)
     return {"x_a": x_a, "s_a": s_a, "x_b": x_b, "s_b": s_b, "counts": counts,
             "band_counts": band_counts, "L": Lrc, "C": C, "C_abs": C_abs, "ladder": ladder}
 

@@ -487,6 +487,134 @@ def test_head_mp_rows_is_the_fixed_length_product_at_the_head_rung():
     assert not np.array_equal(o.head_mp_rows(Q, Kt, plan, 0)["counts"], long["counts"])
 
 
+# --------------------------------------------------- unipolar (AND) mode --
+
+def test_unipolar_level_values_and_symmetry():
+    # round(256 |x| / 127): 0 -> 0, 1 -> 2 (2.016), 63 -> 127 (126.99),
+    # 64 -> 129 (129.01), 127 -> 256; magnitude only; monotone in |x|.
+    x = np.array([0, 1, -1, 63, 64, -64, 127, -127])
+    assert o.unipolar_level(x, 8).tolist() == [0, 2, 2, 127, 129, 129, 256, 256]
+    allx = np.arange(0, 128)
+    u = o.unipolar_level(allx, 8)
+    assert np.all(np.diff(u) >= 2) and np.all(np.diff(u) <= 3)
+    # No ties: 2 P |x| is never an odd multiple of q, and u is the nearest level.
+    assert np.all(np.abs(256 * allx - 127 * u) * 2 < 127)
+    for p in (2, 3, 4, 8):
+        q, P = o.QMAX(p), 1 << p
+        assert o.unipolar_level(q, p) == P and o.unipolar_level(-q, p) == P and o.unipolar_level(0, p) == 0
+
+
+def _and_closed_form(cum, ua, ub, L):
+    # Under AND only A's ones count, and there B emits K[u_B][0..n1).
+    return int(cum[ub, int(cum[ua, L])])
+
+
+@pytest.mark.parametrize("p", [2, 3, 4])
+def test_and_count_equals_closed_form_exhaustive(p):
+    P = 1 << p
+    _, K, cum = _table(p)
+    for L in range(1, P + 1):
+        for ua in range(P + 1):
+            for ub in range(P + 1):
+                assert o.and_count(K, K, ua, ub, L) == _and_closed_form(cum, ua, ub, L)
+
+
+def test_and_count_special_levels_p8():
+    # Level 0 emits no ones (count 0 on either side); level P emits all ones,
+    # so A at P makes the count B's ones in its L-prefix and B at P makes it
+    # A's ones; the count never exceeds either operand's ones.
+    rng = np.random.default_rng(61)
+    _, K, cum = _table(8)
+    for L in (1, 33, 64, 97, 128, 200, 256):
+        for u in rng.integers(0, 257, 12):
+            u = int(u)
+            assert o.and_count(K, K, 0, u, L) == 0 and o.and_count(K, K, u, 0, L) == 0
+            assert o.and_count(K, K, 256, u, L) == cum[u, L]
+            assert o.and_count(K, K, u, 256, L) == cum[u, L]
+        for ua, ub in rng.integers(0, 257, (20, 2)):
+            c = o.and_count(K, K, int(ua), int(ub), L)
+            assert c <= min(cum[int(ua), L], cum[int(ub), L])
+
+
+def test_and_count_full_period_power_of_two_is_within_one_of_the_product():
+    # At L = P the row at level 2^k emits exactly 2^k ones, and B's prefix
+    # of 2^k Sobol points is stratified: count = ceil(u_B 2^k / P), within 1
+    # of the exact product u_A u_B / P.
+    _, K, _ = _table(8)
+    for k in range(9):
+        ua = 1 << k
+        for ub in range(257):
+            c = o.and_count(K, K, ua, ub, 256)
+            assert c == -(-ub * ua // 256)
+            assert 0 <= c - ua * ub / 256 < 1
+
+
+def test_vectorised_and_row_count_matches_per_triple_count():
+    rng = np.random.default_rng(62)
+    _, K, _ = _table(8)
+    D, N = 9, 5
+    ua = rng.integers(0, 257, D)
+    ub = rng.integers(0, 257, (N, D))
+    Ls = rng.integers(1, 257, D)
+    got = o.and_count_row(K, ua, ub, Ls)
+    for j in range(N):
+        for d in range(D):
+            assert got[j, d] == o.and_count(K, K, int(ua[d]), int(ub[j, d]), int(Ls[d]))
+
+
+def test_unipolar_full_scale_rows_are_exact_products():
+    # Entries in {0, +-127} are levels 0 and P, whose streams are all zeros
+    # or all ones, so every count is exact and the decode equals the float
+    # product up to the float32 rounding of the two scales (3/127, 0.5/127).
+    rng = np.random.default_rng(63)
+    vals = np.array([0.0, 1.0, -1.0], np.float32)
+    A = vals[rng.integers(0, 3, (4, 40))] * np.float32(3.0)
+    B = vals[rng.integers(0, 3, (6, 40))] * np.float32(0.5)
+    A[:, 0], B[:, 0] = 3.0, 0.5                       # every row has full scale
+    for L in (64, 97, 256):
+        plan = o.OraclePlan(D=40, levels=(L,), mode="unipolar")
+        out = o.rows_product(A, np.zeros(4, np.int64), B, plan)
+        want = A.astype(np.float64) @ B.astype(np.float64).T
+        assert np.allclose(out["C"], want, rtol=3e-7, atol=1e-12)
+        assert np.all(out["counts"] % L == 0)          # each index adds 0 or +-L
+
+
+def test_unipolar_signs_and_zero_rows():
+    rng = np.random.default_rng(64)
+    A = rng.standard_normal((5, 48)).astype(np.float32)
+    B = rng.standard_normal((7, 48)).astype(np.float32)
+    plan = o.OraclePlan(D=48, levels=(128,), mode="unipolar")
+    r = o.rows_product(A, np.zeros(5, np.int64), B, plan)
+    neg = o.rows_product(-A, np.zeros(5, np.int64), B, plan)
+    assert np.array_equal(neg["counts"], -r["counts"])
+    assert np.array_equal(neg["C"], -r["C"])
+    Bn = B.copy()
+    Bn[2] = -Bn[2]
+    flip = o.rows_product(A, np.zeros(5, np.int64), Bn, plan)
+    assert np.array_equal(flip["counts"][:, 2], -r["counts"][:, 2])
+    assert np.array_equal(np.delete(flip["counts"], 2, axis=1), np.delete(r["counts"], 2, axis=1))
+    zero = o.rows_product(np.zeros((2, 48), np.float32), np.zeros(2, np.int64), B, plan)
+    assert not zero["counts"].any() and not zero["C"].any()
+    # The bipolar mode on the same inputs counts differently.
+    bip = o.rows_product(A, np.zeros(5, np.int64), B, o.OraclePlan(D=48, levels=(128,)))
+    assert not np.array_equal(bip["counts"], r["counts"])
+
+
+def test_unipolar_nonnegative_rows_track_the_float_product():
+    # Softmax rows times Gaussian columns: the error falls as L grows.
+    rng = np.random.default_rng(65)
+    z = 3.0 * rng.standard_normal((6, 64))
+    A = (np.exp(z - z.max(1, keepdims=True)) / np.exp(z - z.max(1, keepdims=True)).sum(1, keepdims=True))
+    A = A.astype(np.float32)
+    B = rng.standard_normal((20, 64)).astype(np.float32)
+    ref = A.astype(np.float64) @ B.astype(np.float64).T
+    errs = []
+    for L in (32, 256):
+        out = o.rows_product(A, np.zeros(6, np.int64), B, o.OraclePlan(D=64, levels=(L,), mode="unipolar"))
+        errs.append(np.linalg.norm(out["C"] - ref) / np.linalg.norm(ref))
+    assert errs[1] < errs[0] and errs[1] < 0.1
+
+
 # ---------------------------------------------------- mixed precision ----
 
 def test_rung_cuts_workload_fractions():
