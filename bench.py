@@ -82,66 +82,75 @@ def work_per_step(plan, M, N, G, heads=0):
     return bitmacs * N * G, paired * N * G
 
 
-def cpu_baseline(w, A, B, n_rows_req):
+def cpu_baseline(w, A, B, n_rows_req, seconds=12.0):
     """Time the CPU oracle, as it stands, on a bounded sample of output rows
-    of the same workload (all columns, all of D), one worker process per core."""
+    of the same workload (all columns, all of D), one worker process per
+    core.  Rows are taken batch by batch (per-row rungs: sampled rows of
+    every rung; per-group workloads: whole groups in order; per-head rungs:
+    whole images) until about ``seconds`` of wall time have been spent, or
+    ``n_rows_req`` rows when that is given."""
     import numpy as np
     sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as o
-    from _oracle_pool import pooled_rows_product, workers
+    from _oracle_pool import OraclePool, workers
     from mixed_precision_quantization_amd.workloads import sample_rows
 
     okw = dict(p=8, Lmax=256, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
-               n_bands=w.n_bands, tilt=w.tilt, metric=w.metric)
+               n_bands=w.n_bands, tilt=w.tilt, metric=w.metric, mode=w.mode)
+    oplan = o.OraclePlan(**okw)
+    widths = np.diff(oplan.chunk_bounds(), axis=1).T          # (1, n_chunks)
     nw = workers()
     heads = w.extra.get("heads", 0)
-    if heads:
-        # Per-head rungs: rank the first image's heads, then, per rung, take
-        # query rows of its heads in rank order against each head's keys
-        # (rows here are several hundred times cheaper than fc1 rows).
-        want = n_rows_req or 400 * nw
-        t0 = time.perf_counter()
-        hr = o.head_rungs(A[:heads], o.OraclePlan(**okw))
-        per = max(1, -(-want // len(w.levels)))
-        rows_done = 0
-        bitmacs = 0
-        for k in range(len(w.levels)):
-            left = per
-            for h in [int(h) for h in hr["order"] if hr["rung"][h] == k]:
-                rows = np.arange(min(left, w.M))
-                out = pooled_rows_product(A[h][rows], np.full(len(rows), k), B[h], okw, n_workers=nw)
-                bitmacs += int(np.sum(out["L"])) * w.D * B.shape[1]
-                rows_done += len(rows)
-                left -= len(rows)
-                if left <= 0:
-                    break
-        dt = time.perf_counter() - t0
-        return {
-            "value": bitmacs / dt, "unit": "bit-MAC/s", "cores": nw, "kind": "oracle",
-            "sample": f"{rows_done} query rows (up to {per} per rung, heads of image 0 in rank order) x all "
-                      f"{B.shape[1]} keys x all D={w.D}, materialised C-BSG streams, {bitmacs:.3e} bit-MACs in "
-                      f"{dt:.1f} s wall incl. head ranking and quantisation",
-            "seconds": dt,
-        }
-    want = n_rows_req or 2 * nw
-    A0 = A[0] if A.ndim == 3 else A
-    B0 = B[0] if B.ndim == 3 else B
+    A3 = A if A.ndim == 3 else A[None]
+    B3 = B if B.ndim == 3 else B[None]
+    N = B3.shape[1]
+
+    def batches():
+        """Lists of (A_rows, rungs, B) jobs with a description of each batch."""
+        if heads:
+            for img in range(A3.shape[0] // heads):
+                hs = slice(img * heads, (img + 1) * heads)
+                hr = o.head_rungs(A3[hs], oplan)
+                yield [(A3[img * heads + h], np.full(w.M, int(hr["rung"][h])), B3[img * heads + h])
+                       for h in range(heads)], f"image {img} (all {heads} heads x {w.M} query rows)"
+        elif A3.shape[0] > 1:
+            for g in range(A3.shape[0]):
+                cls = o.classify(A3[g], oplan)
+                yield [(A3[g], cls["rung"], B3[g])], f"group {g} (all {w.M} rows)"
+        else:
+            cls = o.classify(A3[0], oplan)
+            per = max(2, -(-(n_rows_req or 4 * nw) // len(w.levels)))
+            for seed in range(11, 10 ** 6):
+                pos = sample_rows(w.M, cls["cuts"], per_rung=per, seed=seed)
+                if n_rows_req:
+                    pos = pos[:n_rows_req]
+                rows = cls["order"][pos]
+                yield [(A3[0][rows], cls["rung"][rows], B3[0])], f"{len(rows)} sampled rows"
+
     t0 = time.perf_counter()
-    cls = o.classify(A0, o.OraclePlan(**okw))
-    per = max(1, -(-want // len(w.levels)))
-    pos = sample_rows(w.M, cls["cuts"], per_rung=max(2, per), seed=11)[:want]
-    rows = cls["order"][pos]
-    out = pooled_rows_product(A0[rows], cls["rung"][rows], B0, okw, n_workers=nw)
+    bitmacs = 0
+    rows_done = 0
+    parts = []
+    with OraclePool(okw, nw) as pool:
+        for jobs, what in batches():
+            for out in pool.run(jobs):
+                bitmacs += int(np.sum(out["L"] * widths)) * N
+                rows_done += out["L"].shape[0]
+            parts.append(what)
+            if (n_rows_req and rows_done >= n_rows_req) or time.perf_counter() - t0 >= seconds:
+                break
     dt = time.perf_counter() - t0
-    bitmacs = int(np.sum(out["L"] * np.diff(o.OraclePlan(**okw).chunk_bounds(), axis=1).T)) * B0.shape[0]
+    kind = ("query rows of whole images, each head at its rung" if heads else
+            "rows of whole groups" if A3.shape[0] > 1 else
+            "output rows of every rung (sorted-position edges plus seeded picks)")
     return {
         "value": bitmacs / dt,
         "unit": "bit-MAC/s",
         "cores": nw,
         "kind": "oracle",
-        "sample": f"{len(rows)} output rows (every rung, sorted-position edges plus seeded picks) x all "
-                  f"{B0.shape[0]} columns x all D={w.D}, materialised C-BSG streams, "
-                  f"{bitmacs:.3e} bit-MACs in {dt:.1f} s wall incl. classification and quantisation",
+        "sample": f"{rows_done} {kind} in {len(parts)} batches ({parts[0]}, ...) x all {N} columns x all "
+                  f"D={w.D}, materialised C-BSG streams, {bitmacs:.3e} bit-MACs in {dt:.1f} s wall incl. "
+                  f"classification and quantisation",
         "seconds": dt,
     }
 
@@ -181,7 +190,7 @@ def main():
     torch.cuda.synchronize()
     table_ms = (time.perf_counter() - t0) * 1e3
     plan = scmp.scmp_plan_create(op=w.kind, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
-                                 n_bands=w.n_bands, tilt=w.tilt)
+                                 n_bands=w.n_bands, tilt=w.tilt, mode=w.mode)
     nch = plan.n_chunks
     # Every buffer of the step is allocated before timing.
     qA = torch.empty((G, M, D), dtype=torch.int8, device=dev)
@@ -189,7 +198,7 @@ def main():
     mA = torch.empty((G, M), dtype=torch.float32, device=dev)
     qB = torch.empty((G, N, D), dtype=torch.int8, device=dev)
     sB = torch.empty((G, N, nch), dtype=torch.float32, device=dev)
-    pB = torch.empty((G, N, D, table.words), dtype=torch.int32, device=dev) if args.algo == "bitserial" else None
+    pB = torch.empty((G, N, D, table.words), dtype=torch.int32, device=dev) if plan.needs_packed(args.algo) else None
     gh = torch.empty((G, M), dtype=torch.float32, device=dev)
     rg = torch.empty((G, M), dtype=torch.uint8, device=dev)
     pm = torch.empty((G, M), dtype=torch.int32, device=dev)
@@ -246,7 +255,9 @@ def main():
     value = bitmacs / (ms_per_step / 1e3)
     L_eff = bitmacs / (G * M * N * D)
 
-    if args.algo == "bitserial":
+    # Unipolar plans run on the bit-serial kernel whatever the algo says.
+    on_valu = args.algo == "bitserial" or plan.unipolar
+    if on_valu:
         achieved = bitmacs / (kern_ms / 1e3) / 1e12
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_BITMACS / 1e12,
                 "unit": "T bit-MAC/s", "frac": achieved / (PEAK_VALU_BITMACS / 1e12), "traffic": None,
@@ -273,7 +284,7 @@ def main():
     # The events bracket one scmp_matmul call: the contraction kernel plus, on
     # the matrix-core path, its two small encode kernels (k_prep_rows,
     # k_prep_cols), which run first on the same stream.
-    roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if args.algo == "bitserial"
+    roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if on_valu
                       else "scmp_matmul = k_prep_rows + k_prep_cols + k_mfma")
     roof["kernel_ms"] = kern_ms
     roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
@@ -281,7 +292,7 @@ def main():
 
     # Arithmetic of the contraction: integer stream counts from int8 codes,
     # on int8 or e2m1 (fp4, exact for these operands) matrix-core operands.
-    if args.algo == "bitserial":
+    if on_valu:
         dtype = "u32 bit-ops"
     else:
         dtype = {(True, False): "i8", (False, True): "fp4(e2m1)", (True, True): "i8+fp4(e2m1)"}.get(
@@ -302,7 +313,7 @@ def main():
         "config": {
             "workload": w.name, "G": G, "M": M, "N": N, "D": D, "levels": list(w.levels),
             "fractions": list(w.fractions) if w.fractions else None, "chunk_d": w.chunk_d,
-            "n_bands": w.n_bands, "tilt": w.tilt, "L_eff": L_eff, "algo": args.algo,
+            "n_bands": w.n_bands, "tilt": w.tilt, "L_eff": L_eff, "algo": args.algo, "mode": w.mode,
             "bit_macs_per_step": bitmacs,
         },
         "roofline": roof,

@@ -67,6 +67,17 @@ typedef enum {
 
 typedef enum { SCMP_OP_LINEAR = 0, SCMP_OP_QK = 1, SCMP_OP_AV = 2 } scmp_op;
 
+/* SC gate of a plan ([PAYN] "Research background and motivation" and Key
+ * design 3: one AND gate for unipolar SC, one XNOR gate for bipolar SC;
+ * [VIT] SC compensation flags: bipolar or unipolar per-row mode).
+ *  BIPOLAR: a stream's level is u = round(P (x + q) / (2 q)); the XNOR
+ *           count decodes as s^A s^B q^2 (2 count - L |c|) / L.
+ *  UNIPOLAR: sign-magnitude; a stream carries |x| at level
+ *           u = round(P |x| / q) (0 -> 0, q -> P) on the same C-BSG streams,
+ *           the AND count is taken with the product of the two signs, and
+ *           decodes as s^A s^B q^2 count / L. */
+typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
+
 /* Contraction kernel.  All give bit-identical counts.
  *  AUTO/MFMA: windowed ternary x paired-binary contraction on the int8
  *             matrix cores (v_mfma_i32_32x32x32_i8); the launch form is
@@ -113,10 +124,11 @@ typedef struct {
   int table_D;               /* contraction width band_L was priced at (0 = not stated) */
   int ceiling;               /* largest allowed length; 0 = Lmax; must be <= Lmax */
   int range_mp;              /* nonzero requests range-based MP (not provided here) */
+  int mode;                  /* scmp_mode; 0 = bipolar */
 } scmp_plan_desc;
 
 typedef struct {
-  int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling;
+  int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling, mode;
 } scmp_plan_info;
 
 /* Name of a status code (static string). */
@@ -192,7 +204,8 @@ int scmp_plan_row_cuts(scmp_plan_t plan, int M, int* cuts_out);
  *               attention rows ([PAYN] Key design 2)            (nullable)
  *   packed_dev  uint32 [G][rows][cols][ceil(Lmax/32)]: the weight side's
  *               full-length counter-domain stream K[u][0..Lmax) with
- *               u = round(P (x_int + q) / (2 q))                (nullable)
+ *               u = round(P (x_int + q) / (2 q)), or u = round(P |x_int| / q)
+ *               for a unipolar plan                             (nullable)
  * cols must equal the plan's D.  Non-finite inputs set a device flag read
  * by scmp_error_flags.  Errors: ARG, PLAN_MISMATCH, HIP. */
 int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const float* X_dev, int G, int rows,
@@ -231,17 +244,23 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
  * XNOR count is exact.  Per chunk c (the whole row when chunk_d is 0) the
  * decode is s^A_ic s^B_jc q^2 (2 count_ijc - L_c |c|) / L_c, summed over
  * chunks in float32 ([PAYN] Key design 1, decode equation).
+ * A unipolar plan (scmp_mode) counts AND instead of XNOR: per index the
+ * count is sign(x_A) sign(x_B) cum[u_B][n1_A], and the chunk decode is
+ * s^A_ic s^B_jc q^2 count_ijc / L_c; it runs on the bit-serial kernel
+ * (AUTO selects it; the MFMA algos return UNSUPPORTED) and needs packedB.
  *   qA_dev int8 [G][M][D], sA_dev float [G][M][n_chunks],
  *   permA_dev int32 [G][M] (NULL only for one rung: identity order),
  *   qB_dev int8 [G][N][D], sB_dev float [G][N][n_chunks],
  *   packedB_dev uint32 [G][N][D][ceil(Lmax/32)] (needed by BITSERIAL only),
- *   counts_dev int32 [G][M][N][n_bands] (nullable): per-band XNOR counts,
+ *   counts_dev int32 [G][M][N][n_bands] (nullable): per-band XNOR counts
+ *   (unipolar: per-band sums of the signed AND counts),
  *   C_dev float (nullable): decoded output at original row order,
  *   workspace_dev / workspace_bytes: scratch of at least
  *   scmp_matmul_workspace_bytes (ignored by BITSERIAL); calls that share a
  *   workspace must be ordered on one stream.
  * At least one of counts_dev and C_dev must be given; ldc >= N.
- * Errors: ARG, PLAN_MISMATCH (table vs plan), WORKSPACE (too small), HIP. */
+ * Errors: ARG, PLAN_MISMATCH (table vs plan), WORKSPACE (too small),
+ * UNSUPPORTED (an MFMA algo with a unipolar plan), HIP. */
 int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                 const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
                 const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
@@ -305,7 +324,7 @@ int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int 
 
 /* Decode counts produced without chunk scales ([PAYN] Key design 1, decode
  * equation): C_ij = s^A_i s^B_j q^2 (2 count_ij - L_i D) / L_i with
- * L_i = L[0][rung_i].  counts_dev int32 [G][M][N][1]; rung_dev uint8 [G][M]
+ * L_i = L[0][rung_i]; for a unipolar plan C_ij = s^A_i s^B_j q^2 count_ij / L_i.  counts_dev int32 [G][M][N][1]; rung_dev uint8 [G][M]
  * (NULL only for one rung).  Errors: ARG, UNSUPPORTED (plan has chunk_d
  * or bands), HIP. */
 int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts_dev,

@@ -10,6 +10,11 @@
 // accumulating popcount per word.  B_w are the packed counter-domain
 // streams written by scmp_quantize_encode.  K-band pull request, "How the
 // banding works": band b uses L[b][k]; the chunk decode is fused.
+//
+// Unipolar plans (AND gate, "Precision As You Need" Key design 3; levels of
+// the magnitudes) count popcount(B_w & T1_w) per word, so per index the
+// count is cum[u_B][n1], taken with the product of the operands' signs;
+// their decode is s^A s^B q^2 count / L.
 
 #include <hip/hip_runtime.h>
 
@@ -27,10 +32,12 @@ __device__ __forceinline__ uint32_t prefix_word(int n, int w) {
   return m <= 0 ? 0u : (m >= 32 ? 0xffffffffu : ((1u << m) - 1u));
 }
 
-template <bool COUNTS>
+template <bool COUNTS, bool UNI>
 __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
   __shared__ __align__(16) uint2 s_t[BS_DC][BS_WMAX][BS_BM];      // (T1, T0) words
   __shared__ __align__(16) uint32_t s_b[BS_DC][BS_WMAX][BS_BN];   // B stream words
+  __shared__ __align__(16) int s_sga[UNI ? BS_DC : 1][BS_BM];     // unipolar: -1 where x_A < 0, else 0
+  __shared__ __align__(16) int s_sgb[UNI ? BS_DC : 1][BS_BN];     // unipolar: -1 where x_B < 0, else 0
   __shared__ uint16_t s_ncum[MAX_LEVELS];
   __shared__ int s_rows[BS_BM];
 
@@ -76,7 +83,11 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
         for (int i = 0; i < 2; ++i) {
           const int dd = dp + i, d = d0 + dd;
           int n1 = 0, n0 = 0;
-          if (row >= 0 && d < dlim) {
+          if (UNI) {
+            const int x = (row >= 0 && d < dlim) ? (int)src[d] : 0;
+            n1 = s_ncum[uni_level_of(x, a.P, a.q)];
+            s_sga[UNI ? dd : 0][r] = x < 0 ? -1 : 0;
+          } else if (row >= 0 && d < dlim) {
             n1 = s_ncum[level_of((int)src[d], a.P, a.q)];
             n0 = L - n1;
           }
@@ -89,10 +100,41 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
         for (int i = 0; i < 2; ++i) {
           const int dd = dp + i, d = d0 + dd;
           for (int w = 0; w < W; ++w) s_b[dd][w][c] = (col < a.N && d < dlim) ? bsrc[(long long)d * a.Wl + w] : 0u;
+          if (UNI)
+            s_sgb[UNI ? dd : 0][c] = (col < a.N && d < dlim && a.qB[((long long)g * a.N + col) * a.D + d] < 0) ? -1 : 0;
         }
       }
       __syncthreads();
-      for (int dd = 0; dd < BS_DC; ++dd) {
+      for (int dd = 0; dd < BS_DC && UNI; ++dd) {
+        int t[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) t[i][j] = 0;
+        for (int w = 0; w < W; ++w) {
+          const uint4 t01 = *(const uint4*)&s_t[dd][w][ty * 4];
+          const uint4 t23 = *(const uint4*)&s_t[dd][w][ty * 4 + 2];
+          const uint4 bw = *(const uint4*)&s_b[dd][w][tx * 4];
+          const uint32_t T1[4] = {t01.x, t01.z, t23.x, t23.z};
+          const uint32_t B[4] = {bw.x, bw.y, bw.z, bw.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[i][j] += __popc(B[j] & T1[i]);
+        }
+        const int4 ma = *(const int4*)&s_sga[UNI ? dd : 0][ty * 4];
+        const int4 mb = *(const int4*)&s_sgb[UNI ? dd : 0][tx * 4];
+        const int MA[4] = {ma.x, ma.y, ma.z, ma.w};
+        const int MB[4] = {mb.x, mb.y, mb.z, mb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int m = MA[i] ^ MB[j];  // -1 where the signs differ
+            cnt[i][j] += (t[i][j] ^ m) - m;
+          }
+      }
+      for (int dd = 0; dd < BS_DC && !UNI; ++dd) {
         for (int w = 0; w < W; ++w) {
           const uint4 t01 = *(const uint4*)&s_t[dd][w][ty * 4];
           const uint4 t23 = *(const uint4*)&s_t[dd][w][ty * 4 + 2];
@@ -117,7 +159,7 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
           for (int j = 0; j < 4; ++j) {
             const int col = col0 + tx * 4 + j;
             const float sb = col < a.N ? a.sB[((long long)g * a.N + col) * a.n_chunks + ch] : 0.0f;
-            cacc[i][j] += (sa * sb) * (scaleL * (float)(2 * cnt[i][j] - L * cw));
+            cacc[i][j] += (sa * sb) * (scaleL * (float)(UNI ? cnt[i][j] : 2 * cnt[i][j] - L * cw));
             if (COUNTS) bacc[i][j] += cnt[i][j];
             cnt[i][j] = 0;
           }
@@ -159,10 +201,16 @@ int launch_bitserial(const MatmulArgs& a, hipStream_t st) {
   if (RT == 0) return SCMP_OK;
   if (RT > 65535) return set_error(SCMP_ERR_ARG, "too many row tiles");
   const dim3 grid((a.N + BS_BN - 1) / BS_BN, RT, a.G);
-  if (a.counts)
-    hipLaunchKernelGGL(k_matmul_bitserial<true>, grid, dim3(256), 0, st, a);
-  else
-    hipLaunchKernelGGL(k_matmul_bitserial<false>, grid, dim3(256), 0, st, a);
+  if (a.unipolar) {
+    if (a.counts)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_matmul_bitserial<true, true>), grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(k_matmul_bitserial<false, true>), grid, dim3(256), 0, st, a);
+  } else if (a.counts) {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_matmul_bitserial<true, false>), grid, dim3(256), 0, st, a);
+  } else {
+    hipLaunchKernelGGL(HIP_KERNEL_NAME(k_matmul_bitserial<false, false>), grid, dim3(256), 0, st, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("bit-serial launch: ") + hipGetErrorString(e));
   return SCMP_OK;

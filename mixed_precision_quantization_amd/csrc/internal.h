@@ -12,6 +12,7 @@ namespace scmp {
 struct Plan {
   int op = 0, p = 8, Lmax = 256, D = 0, chunk_d = 0, n_chunks = 1;
   int n_rungs = 1, n_bands = 1, ceiling = 256;
+  int mode = SCMP_MODE_BIPOLAR;
   int levels[SCMP_MAX_RUNGS] = {};
   double fractions[SCMP_MAX_RUNGS] = {};
   int band_chunks[SCMP_MAX_BANDS] = {};

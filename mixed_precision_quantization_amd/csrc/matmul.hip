@@ -25,13 +25,19 @@ void fill_tiles(MatmulArgs& a, const Plan& P, int BM) {
     a.tile_start[k + 1] = a.tile_start[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
 }
 
-// Validate the arguments and fill MatmulArgs (no device work).
-static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, MatmulArgs& a) {
+// Validate the arguments and fill MatmulArgs (no device work).  Unipolar
+// plans run on the bit-serial kernel: AUTO becomes BITSERIAL.
+static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M, int N, MatmulArgs& a) {
   if (!table || !plan) return set_error(SCMP_ERR_ARG, "table or plan is NULL");
   const Plan& P = plan->plan;
   if (table->p != P.p || table->Lmax != P.Lmax)
     return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
   if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA_ONEPASS) return set_error(SCMP_ERR_ARG, "unknown algo");
+  if (P.mode == SCMP_MODE_UNIPOLAR) {
+    if (algo == SCMP_ALGO_AUTO) algo = SCMP_ALGO_BITSERIAL;
+    if (algo != SCMP_ALGO_BITSERIAL)
+      return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans run on the bit-serial kernel only");
+  }
   if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
@@ -46,6 +52,7 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M,
   a.n_chunks = P.n_chunks;
   a.n_rungs = P.n_rungs;
   a.n_ladder = P.n_rungs;
+  a.unipolar = P.mode == SCMP_MODE_UNIPOLAR;
   a.n_bands = P.n_bands;
   a.q = qmax(P.p);
   a.P = 1 << P.p;
@@ -83,7 +90,7 @@ struct DecodeArgs {
   const uint8_t* rung;
   float* C;
   long long ldc, bsc;
-  int M, N, D, q, n_rungs;
+  int M, N, D, q, n_rungs, unipolar;
   int L[SCMP_MAX_RUNGS];
 };
 
@@ -98,7 +105,8 @@ __global__ void __launch_bounds__(256) k_decode(DecodeArgs a) {
   const float sa = a.sA[(long long)g * a.M + i];
   const float sb = a.sB[(long long)g * a.N + j];
   const float scaleL = (float)(a.q * a.q) / (float)L;
-  a.C[(long long)g * a.bsc + (long long)i * a.ldc + j] = (sa * sb) * (scaleL * (float)(2 * cnt - L * a.D));
+  a.C[(long long)g * a.bsc + (long long)i * a.ldc + j] =
+      (sa * sb) * (scaleL * (float)(a.unipolar ? cnt : 2 * cnt - L * a.D));
 }
 
 }  // namespace scmp
@@ -240,6 +248,7 @@ int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts, co
   a.D = P.D;
   a.q = scmp::qmax(P.p);
   a.n_rungs = P.n_rungs;
+  a.unipolar = P.mode == SCMP_MODE_UNIPOLAR;
   for (int k = 0; k < P.n_rungs; ++k) a.L[k] = P.band_L[0][k];
   hipLaunchKernelGGL(scmp::k_decode, dim3((N + 255) / 256, M, G), dim3(256), 0, (hipStream_t)stream, a);
   hipError_t e = hipGetLastError();

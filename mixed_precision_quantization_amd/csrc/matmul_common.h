@@ -27,6 +27,7 @@ struct MatmulArgs {
   // tiling rung, no permutation); n_ladder is the ladder's rung count.
   const uint8_t* group_rung;
   int n_ladder;
+  int unipolar;  // AND gate, sign-magnitude levels (bit-serial kernel only)
   long long ldc, bsc;
   const uint8_t* pair;
   const uint16_t* cum;
@@ -44,6 +45,13 @@ struct MatmulArgs {
 __device__ __forceinline__ int level_of(int x, int P, int q) {
   const int u = (P * (x + q) + q) / (2 * q);
   return u < 0 ? 0 : (u > P ? P : u);
+}
+
+// Unipolar level of the magnitude, round(P |x| / q) (q is odd: no ties),
+// clamped the same way.
+__device__ __forceinline__ int uni_level_of(int x, int P, int q) {
+  const int u = (2 * P * abs(x) + q) / (2 * q);
+  return u > P ? P : u;
 }
 
 // Rung and first sorted position of a row tile (tiles are numbered bucket

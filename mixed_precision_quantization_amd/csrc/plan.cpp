@@ -78,6 +78,7 @@ std::string fmt(const char* f, long long a = 0, long long b = 0, long long c = 0
 int build_plan(const scmp_plan_desc* d, Plan& P) {
   if (!d) return set_error(SCMP_ERR_ARG, "plan description is NULL");
   if (d->op < SCMP_OP_LINEAR || d->op > SCMP_OP_AV) return set_error(SCMP_ERR_ARG, "unknown op kind");
+  if (d->mode != SCMP_MODE_BIPOLAR && d->mode != SCMP_MODE_UNIPOLAR) return set_error(SCMP_ERR_ARG, "unknown mode");
   if (d->p < 2 || d->p > 8) return set_error(SCMP_ERR_ARG, fmt("p=%lld outside [2, 8]", d->p));
   if (d->Lmax < 1 || d->Lmax > (1 << d->p))
     return set_error(SCMP_ERR_ARG, fmt("Lmax=%lld outside [1, 2^p]", d->Lmax));
@@ -101,6 +102,7 @@ int build_plan(const scmp_plan_desc* d, Plan& P) {
     return set_error(SCMP_ERR_UNSUPPORTED, "K-bands are only defined for linear ops (not qk/av)");
 
   P.op = d->op;
+  P.mode = d->mode;
   P.p = d->p;
   P.Lmax = d->Lmax;
   P.D = d->D;
@@ -265,6 +267,7 @@ int scmp_plan_query(scmp_plan_t plan, scmp_plan_info* out) {
   out->n_rungs = P.n_rungs;
   out->n_bands = P.n_bands;
   out->ceiling = P.ceiling;
+  out->mode = P.mode;
   return SCMP_OK;
 }
 

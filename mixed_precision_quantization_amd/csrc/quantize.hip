@@ -41,6 +41,7 @@ struct QuantArgs {
   const float* X;
   long long bs, rs, cs;
   int rows, cols, chunk_d, n_chunks, q, P, Wl;
+  int unipolar;  // packed streams at the magnitude level round(P |x| / q)
   int8_t* qout;
   float* scales;
   float* metric;
@@ -110,7 +111,8 @@ __global__ void __launch_bounds__(256) k_quantize(QuantArgs a) {
       const int c = idx / a.Wl;
       const int w = idx - c * a.Wl;
       const int xi = qrow[c];
-      const int u = (a.P * (xi + a.q) + a.q) / (2 * a.q);
+      const int u = a.unipolar ? (2 * a.P * abs(xi) + a.q) / (2 * a.q)   // round(P |x| / q)
+                               : (a.P * (xi + a.q) + a.q) / (2 * a.q);  // round(P (x + q) / (2 q))
       prow[idx] = a.K[(long long)u * a.Wl + w];
     }
   }
@@ -223,6 +225,7 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
   a.n_chunks = P.n_chunks;
   a.q = scmp::qmax(P.p);
   a.P = 1 << P.p;
+  a.unipolar = P.mode == SCMP_MODE_UNIPOLAR;
   a.Wl = table->Wl;
   a.qout = q_out;
   a.scales = scales_out;

@@ -28,12 +28,14 @@ SCMP_ERR_WORKSPACE = 7
 SCMP_ERR_HIP = 8
 
 SCMP_OP_LINEAR, SCMP_OP_QK, SCMP_OP_AV = 0, 1, 2
+SCMP_MODE_BIPOLAR, SCMP_MODE_UNIPOLAR = 0, 1
 SCMP_ALGO_AUTO, SCMP_ALGO_BITSERIAL, SCMP_ALGO_MFMA = 0, 1, 2
 SCMP_ALGO_MFMA_PERSISTENT, SCMP_ALGO_MFMA_ONEPASS = 3, 4
 SCMP_MAX_RUNGS = 8
 SCMP_MAX_BANDS = 16
 
 OPS = {"linear": SCMP_OP_LINEAR, "qk": SCMP_OP_QK, "av": SCMP_OP_AV}
+MODES = {"bipolar": SCMP_MODE_BIPOLAR, "unipolar": SCMP_MODE_UNIPOLAR}
 ALGOS = {"auto": SCMP_ALGO_AUTO, "bitserial": SCMP_ALGO_BITSERIAL, "mfma": SCMP_ALGO_MFMA,
          "mfma_persistent": SCMP_ALGO_MFMA_PERSISTENT, "mfma_onepass": SCMP_ALGO_MFMA_ONEPASS}
 
@@ -60,13 +62,13 @@ class PlanDesc(ctypes.Structure):
         ("n_bands", ctypes.c_int), ("band_chunks", ctypes.POINTER(ctypes.c_int)),
         ("tilt", ctypes.c_double), ("band_L", ctypes.POINTER(ctypes.c_int)),
         ("table_chunk_d", ctypes.c_int), ("table_D", ctypes.c_int),
-        ("ceiling", ctypes.c_int), ("range_mp", ctypes.c_int),
+        ("ceiling", ctypes.c_int), ("range_mp", ctypes.c_int), ("mode", ctypes.c_int),
     ]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
-                ("op", "p", "Lmax", "D", "chunk_d", "n_chunks", "n_rungs", "n_bands", "ceiling")]
+                ("op", "p", "Lmax", "D", "chunk_d", "n_chunks", "n_rungs", "n_bands", "ceiling", "mode")]
 
 
 _lib = None
@@ -212,6 +214,15 @@ class Plan:
         for name, _ in PlanInfo._fields_:
             setattr(self, name, getattr(info, name))
 
+    @property
+    def unipolar(self) -> bool:
+        return self.mode == MODES["unipolar"]
+
+    def needs_packed(self, algo: str) -> bool:
+        """Whether the contraction reads packed weight-side streams: the
+        bit-serial kernel does, and it is the one unipolar plans run on."""
+        return algo == "bitserial" or (algo == "auto" and self.unipolar)
+
     def band_lengths(self):
         buf = (ctypes.c_int * (self.n_bands * self.n_rungs))()
         _check("scmp_plan_band_lengths", load().scmp_plan_band_lengths(self.handle, buf))
@@ -248,7 +259,7 @@ def scmp_plan_create(op: str = "linear", p: int = 8, Lmax: int = 256, D: int = 6
                      levels: Sequence[int] = (256,), fractions: Optional[Sequence[float]] = None,
                      n_bands: int = 1, band_chunks: Optional[Sequence[int]] = None, tilt: float = 0.0,
                      band_L=None, table_chunk_d: int = 0, table_D: int = 0, ceiling: int = 0,
-                     range_mp: bool = False) -> Plan:
+                     range_mp: bool = False, mode: str = "bipolar") -> Plan:
     lv = (ctypes.c_int * len(levels))(*[int(v) for v in levels])
     fr = (ctypes.c_double * len(fractions))(*[float(v) for v in fractions]) if fractions else None
     bc = (ctypes.c_int * len(band_chunks))(*[int(v) for v in band_chunks]) if band_chunks else None
@@ -260,7 +271,8 @@ def scmp_plan_create(op: str = "linear", p: int = 8, Lmax: int = 256, D: int = 6
                     ctypes.cast(fr, ctypes.POINTER(ctypes.c_double)) if fr else None, n_bands,
                     ctypes.cast(bc, ctypes.POINTER(ctypes.c_int)) if bc else None, float(tilt),
                     ctypes.cast(bl, ctypes.POINTER(ctypes.c_int)) if bl else None,
-                    table_chunk_d, table_D, ceiling, 1 if range_mp else 0)
+                    table_chunk_d, table_D, ceiling, 1 if range_mp else 0,
+                    MODES[mode] if isinstance(mode, str) else int(mode))
     out = ctypes.c_void_p()
     _check("scmp_plan_create", load().scmp_plan_create(ctypes.byref(desc), ctypes.byref(out)))
     return Plan(out.value)
@@ -446,7 +458,7 @@ def sc_linear(table: Table, plan: Plan, A: torch.Tensor, B: torch.Tensor, algo: 
     every intermediate (device)."""
     qA, sA, mA, _ = scmp_quantize_encode(table, plan, A, stream=stream)
     qB, sB, _, pB = scmp_quantize_encode(table, plan, B, want_metric=False,
-                                         want_packed=(algo == "bitserial"), stream=stream)
+                                         want_packed=plan.needs_packed(algo), stream=stream)
     ghat = rung = perm = thr = None
     if plan.n_rungs > 1:
         ghat, rung, perm, thr = scmp_classify_rows(plan, mA, stream=stream)
@@ -465,7 +477,7 @@ def sc_qk_head_mp(table: Table, plan: Plan, Q: torch.Tensor, K: torch.Tensor, he
     head fractions), and every score of a head runs at its rung."""
     qA, sA, mA, _ = scmp_quantize_encode(table, plan, Q, stream=stream)
     qB, sB, _, pB = scmp_quantize_encode(table, plan, K, want_metric=False,
-                                         want_packed=(algo == "bitserial"), stream=stream)
+                                         want_packed=plan.needs_packed(algo), stream=stream)
     G = qA.shape[0] if qA.dim() == 3 else 1
     if G % heads:
         raise ValueError("G must be a multiple of heads")

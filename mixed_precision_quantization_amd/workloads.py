@@ -35,6 +35,7 @@ class Workload:
     a_dist: str = "normal"        # see draw()
     b_dist: str = "normal"
     extra: dict = field(default_factory=dict)
+    mode: str = "bipolar"         # SC gate: "bipolar" (XNOR) or "unipolar" (AND)
 
     @property
     def metric(self) -> str:
@@ -42,8 +43,8 @@ class Workload:
 
 
 # The five workloads (the fifth has two parts: fc2 with K-bands, and AV),
-# per-query-row and per-head mixed precision on QK^T, and the head-aligned
-# compensator.
+# per-query-row and per-head mixed precision on QK^T, the head-aligned
+# compensator, and the unipolar mode on AV and on the compensator.
 WORKLOADS = {
     "single_64": Workload(
         "single_64", "linear", 1, 64, 64, 64, (64,), seed=1001,
@@ -89,6 +90,19 @@ WORKLOADS = {
         "vitl_qk_head_mp", "qk", 128, 257, 257, 64,
         (256, 128, 64), (0.25, 0.5, 0.25), seed=1009,
         a_dist="head_scaled", b_dist="normal", extra={"heads": 16}),
+    # The unipolar (AND) mode: attention probabilities are non-negative, so
+    # AV is the natural unipolar product (V keeps its signs); same shapes,
+    # draws and ladder as vitl_av_mp.
+    "vitl_av_unipolar": Workload(
+        "vitl_av_unipolar", "av", 128, 257, 64, 257,
+        (256, 128, 64), (0.333, 0.334, 0.333), seed=1006,
+        a_dist="softmax", b_dist="normal", mode="unipolar"),
+    # The head-aligned compensator in the unipolar per-row mode (scmp_vit
+    # README, SC compensation flags): same draws as vitl_comp_head_aligned.
+    "vitl_comp_unipolar": Workload(
+        "vitl_comp_unipolar", "linear", 1, 64 * 257, 1024, 1024,
+        (256,), None, chunk_d=64, seed=1008,
+        a_dist="outlier", b_dist="weight", extra={"bias": True}, mode="unipolar"),
 }
 
 

@@ -179,3 +179,24 @@ def test_device_entry_points_reject_null_handles_without_touching_the_device():
     assert lib.scmp_matmul(None, plan.handle, 0, 1, 1, 1, *([None] * 8), 1, 1, None, 0, None) == scmp.SCMP_ERR_ARG
     size = ctypes.c_size_t(7)
     assert lib.scmp_matmul_workspace_bytes(None, plan.handle, 0, 1, 1, 1, ctypes.byref(size)) == scmp.SCMP_ERR_ARG
+
+
+def test_plan_mode_is_recorded_and_checked():
+    assert scmp.scmp_plan_create(D=64, levels=(128,)).mode == scmp.SCMP_MODE_BIPOLAR
+    uni = scmp.scmp_plan_create(D=64, levels=(128, 64), mode="unipolar")
+    assert uni.mode == scmp.SCMP_MODE_UNIPOLAR and uni.unipolar
+    assert uni.needs_packed("auto") and uni.needs_packed("bitserial") and not uni.needs_packed("mfma")
+    _err(lambda: scmp.scmp_plan_create(D=64, levels=(128,), mode=7), scmp.SCMP_ERR_ARG)
+
+
+def test_group_entry_points_check_arguments_on_the_host():
+    lib = scmp.load()
+    assert lib.scmp_matmul_group_rungs(None, None, 0, 1, 1, 1, *([None] * 6), None, None, 1, 1, None, 0,
+                                       None) == scmp.SCMP_ERR_ARG
+    assert b"group_rung" in lib.scmp_last_error()
+    assert lib.scmp_group_max(None, 0, 5, None, None) == scmp.SCMP_OK        # nothing to do
+    assert lib.scmp_group_max(None, -1, 5, None, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_group_max(None, 3, 0, None, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_group_max(None, 3, 4, None, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_matmul_bias(None, None, 0, 1, 1, 1, *([None] * 7), None, None, 1, 1, None, 0,
+                                None) == scmp.SCMP_ERR_ARG

@@ -25,10 +25,13 @@ RTOL = 1e-5
 ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass")
 
 
-def _skip_unsupported(algo, chunk_d=0, n_bands=1):
-    """The persistent launch takes plans without chunk scales and one band."""
+def _skip_unsupported(algo, chunk_d=0, n_bands=1, mode="bipolar"):
+    """The persistent launch takes plans without chunk scales and one band;
+    unipolar plans run on the bit-serial kernel only."""
     if algo == "mfma_persistent" and ((chunk_d or 0) > 0 or n_bands > 1):
         pytest.skip("the persistent launch needs a single-segment plan (checked in test_persistent_rejects_chunks)")
+    if mode == "unipolar" and algo not in ("bitserial", "auto"):
+        pytest.skip("unipolar plans run on the bit-serial kernel (checked in test_unipolar_rejects_mfma)")
 
 
 @pytest.fixture(scope="module")
@@ -42,7 +45,7 @@ def table():
 
 def _plans(w, **over):
     kw = dict(D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions, n_bands=w.n_bands,
-              tilt=w.tilt)
+              tilt=w.tilt, mode=w.mode)
     kw.update(over)
     gp = scmp.scmp_plan_create(op=w.kind, **kw)
     okw = dict(p=8, Lmax=256, metric=w.metric, **kw)
@@ -234,6 +237,8 @@ SMALL = {
     "vitl_fc2_kband": dict(M=300, N=130, D=512),
     "vitl_av_mp": dict(G=4),
     "vitl_qk_mp": dict(G=4),
+    "vitl_av_unipolar": dict(G=4),
+    "vitl_comp_unipolar": dict(M=200, N=96, D=256),
 }
 
 
@@ -241,7 +246,7 @@ SMALL = {
 @pytest.mark.parametrize("name", list(SMALL))
 def test_small_workload_parity(table, name, algo):
     w = shrink(WORKLOADS[name], **SMALL[name]) if SMALL[name] else WORKLOADS[name]
-    _skip_unsupported(algo, w.chunk_d, w.n_bands)
+    _skip_unsupported(algo, w.chunk_d, w.n_bands, w.mode)
     A, B = _groups(*draw(w))
     plan, okw = _plans(w)
     print(f"  {w.name} G={A.shape[0]} M={w.M} N={w.N} D={w.D}", flush=True)
@@ -325,7 +330,8 @@ def test_standalone_decode_matches_fused(table):
 
 # ----------------------------------------------- full sizes, bench launch --
 
-FULL_GROUPS = {"vitl_qk": (0, 77, 127), "vitl_av_mp": (0, 64, 127), "vitl_qk_mp": (0, 77, 127)}
+FULL_GROUPS = {"vitl_qk": (0, 77, 127), "vitl_av_mp": (0, 64, 127), "vitl_qk_mp": (0, 77, 127),
+               "vitl_av_unipolar": (0, 64, 127)}
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
@@ -344,7 +350,8 @@ def test_full_size_sampled_rows(table, name):
     if w.kind == "linear":
         At, Bt = At[0], Bt[0]
     bench = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="auto", want_counts=False))
-    full = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="mfma", want_counts=True))
+    full = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="bitserial" if plan.unipolar else "mfma",
+                                 want_counts=True))
     torch.cuda.synchronize()
     assert np.array_equal(bench["C"], full["C"])
     groups = FULL_GROUPS.get(name, (0,))
@@ -496,3 +503,45 @@ def test_group_rungs_clamp_and_match_fixed_length(table, algo):
         assert np.array_equal(counts[g].astype(np.int64), orc["band_counts"]), f"group {g}"
         err = np.abs(C[g].astype(np.float64) - orc["C"])
         assert np.all(err <= RTOL * orc["C_abs"]), f"group {g}"
+
+
+# ------------------------------------------------------- unipolar mode --
+
+def test_unipolar_rejects_mfma(table):
+    rng = np.random.default_rng(71)
+    plan = scmp.scmp_plan_create(D=64, levels=(128,), mode="unipolar")
+    A = torch.from_numpy(rng.standard_normal((40, 64)).astype(np.float32)).cuda()
+    for algo in ("mfma", "mfma_persistent", "mfma_onepass"):
+        with pytest.raises(scmp.ScmpError) as e:
+            scmp.sc_linear(table, plan, A, A, algo=algo)
+        assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("L", [1, 31, 33, 64, 97, 255, 256])
+def test_unipolar_every_length_class_and_signs(table, L):
+    """Signed rows and columns with exact zeros, full-scale entries and a
+    ragged tile, at one length, all rows and columns."""
+    rng = np.random.default_rng(72 + L)
+    M, N, D = 70, 67, 80
+    A = rng.standard_normal((M, D)).astype(np.float32)
+    B = rng.standard_normal((N, D)).astype(np.float32)
+    A[3] = 0.0
+    A[5, ::3] = 0.0
+    B[:, 7] = 0.0
+    A[9] = np.abs(A[9])
+    plan = scmp.scmp_plan_create(D=D, levels=(L,), mode="unipolar")
+    okw = dict(p=8, Lmax=256, D=D, levels=(L,), mode="unipolar")
+    print(f"  unipolar L={L}", flush=True)
+    gres = _gpu_path(table, plan, A, B, "auto")
+    _check_group(gres, 0, A, B, okw)
+
+
+def test_unipolar_standalone_decode_matches_fused(table):
+    rng = np.random.default_rng(79)
+    A = rng.standard_normal((50, 64)).astype(np.float32)
+    B = rng.standard_normal((30, 64)).astype(np.float32)
+    plan = scmp.scmp_plan_create(D=64, levels=(256, 64), mode="unipolar")
+    res = scmp.sc_linear(table, plan, torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda(), want_counts=True)
+    C = scmp.scmp_decode(plan, res["counts"], res["sA"], res["sB"], rung=res["rung"])
+    torch.cuda.synchronize()
+    assert torch.equal(C, res["C"])
