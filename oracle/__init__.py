@@ -24,7 +24,10 @@ It is plain, slow and written to be checked by eye against the pages:
   "Tooling";
 * for the unipolar (AND) mode, "Precision As You Need" "Research background
   and motivation" and Key design 3, and the scmp_vit README's SC
-  compensation driver flags (``unipolar.py``).
+  compensation driver flags (``unipolar.py``);
+* for range-based per-weight-group MP, the scmp_vit README's
+  mixed-precision flag table and the K-band pull request's "Guards"
+  (``range_mp.py``).
 
 Every stream is materialised bit by bit and every XNOR is counted; counts are
 int64 and the decode is float64.  Floating point that decides an integer (the
@@ -59,6 +62,7 @@ from .mp import (
 )
 from .decode import decode_terms, decode
 from .unipolar import and_count, and_count_row, decode_unipolar, sign_of, unipolar_level
+from .range_mp import range_levels, range_mp_rows
 from .matmul import (
     OraclePlan,
     classify,
@@ -105,4 +109,6 @@ __all__ = [
     "and_count_row",
     "sign_of",
     "decode_unipolar",
+    "range_levels",
+    "range_mp_rows",
 ]

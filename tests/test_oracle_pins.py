@@ -615,6 +615,55 @@ def test_unipolar_nonnegative_rows_track_the_float_product():
     assert errs[1] < errs[0] and errs[1] < 0.1
 
 
+# ------------------------------------------------ range-based weight MP --
+
+def test_range_levels_hand_example():
+    # Three groups of two rows: ranges 4.0, 1.0 and 0.5 (the last group is
+    # one row, ragged); normalised 1, 0.25, 0.125; threshold 0.3 puts the
+    # last two low, 0.2 only the last, 0 none, anything above 1 all.
+    W = np.array([[1.0, -3.0], [0.5, 0.0],
+                  [2.0, 2.5], [1.5, 2.0],
+                  [-0.25, 0.25]], np.float32)
+    r = o.range_levels(W, 2, 0.3)
+    assert r["range"].tolist() == [4.0, 1.0, 0.5]
+    assert r["norm"].tolist() == [1.0, 0.25, 0.125]
+    assert r["level"].tolist() == [0, 1, 1]
+    assert o.range_levels(W, 2, 0.2)["level"].tolist() == [0, 0, 1]
+    assert o.range_levels(W, 2, 0.0)["level"].tolist() == [0, 0, 0]
+    assert o.range_levels(W, 2, 1.01)["level"].tolist() == [1, 1, 1]
+    assert o.range_levels(np.zeros((4, 3), np.float32), 2, 0.3)["level"].tolist() == [1, 1]
+
+
+def test_range_levels_monotone_in_threshold_and_scale_free():
+    rng = np.random.default_rng(81)
+    W = (rng.standard_normal((1000, 16)) * np.exp(rng.standard_normal((1000, 1)))).astype(np.float32)
+    prev = o.range_levels(W, 64, 0.0)["level"]
+    for t in (0.1, 0.3, 0.5, 0.9):
+        cur = o.range_levels(W, 64, t)["level"]
+        assert np.all(cur >= prev)
+        prev = cur
+    assert np.array_equal(o.range_levels(4 * W, 64, 0.3)["level"], o.range_levels(W, 64, 0.3)["level"])
+
+
+def test_range_mp_columns_run_at_their_group_length():
+    # Columns of a high group equal the uniform product at L_high and those
+    # of a low group the uniform product at L_low; threshold 0 is the
+    # uniform plan at L_high.
+    rng = np.random.default_rng(82)
+    A = rng.standard_normal((5, 32)).astype(np.float32)
+    W = (rng.standard_normal((12, 32)) * np.repeat([1.0, 0.1, 2.0], 4)[:, None]).astype(np.float32)
+    out = o.range_mp_rows(A, W, (256, 64), 0.3, 4)
+    assert out["level"].tolist() == [0, 1, 0]
+    assert out["L_col"].tolist() == [256] * 4 + [64] * 4 + [256] * 4
+    for L, cols in ((256, [0, 1, 2, 3, 8, 9, 10, 11]), (64, [4, 5, 6, 7])):
+        ref = o.rows_product(A, np.zeros(5, np.int64), W[cols], o.OraclePlan(D=32, levels=(L,)))
+        assert np.array_equal(out["counts"][:, cols], ref["counts"])
+        assert np.array_equal(out["C"][:, cols], ref["C"])
+    uni = o.rows_product(A, np.zeros(5, np.int64), W, o.OraclePlan(D=32, levels=(256,)))
+    assert np.array_equal(o.range_mp_rows(A, W, (256, 64), 0.0, 4)["C"], uni["C"])
+    assert not np.array_equal(out["C"], uni["C"])
+
+
 # ---------------------------------------------------- mixed precision ----
 
 def test_rung_cuts_workload_fractions():
