@@ -189,8 +189,11 @@ def main():
     table = scmp.scmp_build_sobol_table(8, 256)
     torch.cuda.synchronize()
     table_ms = (time.perf_counter() - t0) * 1e3
+    ranged = bool(w.extra.get("range_mp"))
     plan = scmp.scmp_plan_create(op=w.kind, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
-                                 n_bands=w.n_bands, tilt=w.tilt, mode=w.mode)
+                                 n_bands=w.n_bands, tilt=w.tilt, mode=w.mode, range_mp=ranged,
+                                 range_threshold=w.extra.get("range_threshold", 0.3),
+                                 range_group=w.extra.get("range_group", 128))
     nch = plan.n_chunks
     # Every buffer of the step is allocated before timing.
     qA = torch.empty((G, M, D), dtype=torch.int8, device=dev)
@@ -216,6 +219,42 @@ def main():
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
     ev = []
+    if ranged:
+        # Range MP: W's groups are classified once, at load time (the weights
+        # are static; the call synchronises); each step quantises W and
+        # stores it in level order, then runs one contraction per level.
+        _, _, rcols, n_lv = scmp.scmp_range_classify(plan, B[0], stream=stream)
+        qBs = torch.empty_like(qB)
+        sBs = torch.empty_like(sB)
+        pBs = torch.empty_like(pB) if pB is not None else None
+        offs = [0, n_lv[0], N]
+        wsk = [torch.empty(max(scmp.scmp_matmul_workspace_bytes(table, plan, G, M, max(n, 1), args.algo), 1),
+                           dtype=torch.uint8, device=dev) for n in n_lv]
+
+    def gather_into(src, dst):
+        scmp.scmp_gather_rows(src, rcols, out=dst, stream=stream)
+
+    def step_range(timed):
+        scmp.scmp_quantize_encode(table, plan, A, q_out=qA, scales_out=sA, metric_out=mA, stream=stream)
+        scmp.scmp_quantize_encode(table, plan, B, q_out=qB, scales_out=sB, packed_out=pB, want_metric=False,
+                                  stream=stream)
+        gather_into(qB, qBs)
+        gather_into(sB, sBs)
+        if pB is not None:
+            gather_into(pB, pBs)
+        if timed:
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        for k in range(2):
+            a0, a1 = offs[k], offs[k + 1]
+            if a1 > a0:
+                scmp.scmp_matmul_range(table, plan, k, qA, sA, qBs[:, a0:a1], sBs[:, a0:a1], rcols[a0:a1], C,
+                                       packedB=None if pBs is None else pBs[:, a0:a1], algo=args.algo,
+                                       workspace=wsk[k], stream=stream)
+        if timed:
+            e1.record(stream)
+            ev.append((e0, e1))
 
     def step(timed):
         scmp.scmp_quantize_encode(table, plan, A, q_out=qA, scales_out=sA, metric_out=mA, stream=stream)
@@ -241,17 +280,23 @@ def main():
             e1.record(stream)
             ev.append((e0, e1))
 
+    run = step_range if ranged else step
     for _ in range(args.warmup):
-        step(False)
+        run(False)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
-        step(True)
+        run(True)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
-    bitmacs, paired = work_per_step(plan, M, N, G, heads)
+    if ranged:
+        lv = plan.band_lengths()[0]
+        bitmacs = G * M * D * (n_lv[0] * lv[0] + n_lv[1] * lv[1])
+        paired = G * M * D * (n_lv[0] * ((lv[0] + 1) // 2) + n_lv[1] * ((lv[1] + 1) // 2))
+    else:
+        bitmacs, paired = work_per_step(plan, M, N, G, heads)
     value = bitmacs / (ms_per_step / 1e3)
     L_eff = bitmacs / (G * M * N * D)
 
@@ -267,8 +312,13 @@ def main():
         # index, only the steps some row of the tile needs, on the int8 or
         # the fp4 matrix cores; the library counts both exactly.  The peak is
         # the mix's: the time both parts take at their dense peaks.
-        issued, issued_fp4 = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo,
-                                                          stream=stream, split=True)
+        if ranged:
+            parts = [scmp.scmp_matmul_issued_macs(table, plan, G, M, n, wsk[k], algo=args.algo, stream=stream,
+                                                  split=True) for k, n in enumerate(n_lv) if n]
+            issued, issued_fp4 = sum(p[0] for p in parts), sum(p[1] for p in parts)
+        else:
+            issued, issued_fp4 = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo,
+                                                              stream=stream, split=True)
         issued_i8 = issued - issued_fp4
         t_peak = 2.0 * issued_i8 / (PEAK_INT8_TOPS * 1e12) + 2.0 * issued_fp4 / (PEAK_FP4_TOPS * 1e12)
         achieved = 2.0 * issued / (kern_ms / 1e3) / 1e12
@@ -286,6 +336,8 @@ def main():
     # k_prep_cols), which run first on the same stream.
     roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if on_valu
                       else "scmp_matmul = k_prep_rows + k_prep_cols + k_mfma")
+    if ranged:
+        roof["kernel"] = "two scmp_matmul_range calls (one per level), each " + roof["kernel"].split(" = ")[1]
     roof["kernel_ms"] = kern_ms
     roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
     roof["valu_bitserial_frac"] = bitmacs / (kern_ms / 1e3) / PEAK_VALU_BITMACS
@@ -314,6 +366,8 @@ def main():
             "workload": w.name, "G": G, "M": M, "N": N, "D": D, "levels": list(w.levels),
             "fractions": list(w.fractions) if w.fractions else None, "chunk_d": w.chunk_d,
             "n_bands": w.n_bands, "tilt": w.tilt, "L_eff": L_eff, "algo": args.algo, "mode": w.mode,
+            "range_mp": {"threshold": w.extra.get("range_threshold", 0.3), "group": plan.range_group, "rows_per_level": list(n_lv)}
+            if ranged else None,
             "bit_macs_per_step": bitmacs,
         },
         "roofline": roof,

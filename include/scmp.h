@@ -123,12 +123,15 @@ typedef struct {
   int table_chunk_d;         /* chunk_d the explicit band_L was priced at (0 = not stated) */
   int table_D;               /* contraction width band_L was priced at (0 = not stated) */
   int ceiling;               /* largest allowed length; 0 = Lmax; must be <= Lmax */
-  int range_mp;              /* nonzero requests range-based MP (not provided here) */
+  int range_mp;              /* nonzero: range-based per-weight-group MP (op LINEAR, two levels,
+                                one band); the contraction then runs through scmp_matmul_range */
   int mode;                  /* scmp_mode; 0 = bipolar */
+  double range_threshold;    /* range MP: groups with normalised range below it take levels[1] */
+  int range_group;           /* range MP: W rows per weight group (0 = 128) */
 } scmp_plan_desc;
 
 typedef struct {
-  int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling, mode;
+  int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling, mode, range_mp, range_group;
 } scmp_plan_info;
 
 /* Name of a status code (static string). */
@@ -167,7 +170,7 @@ int scmp_table_export(scmp_table_t table, uint16_t* r_dev, uint32_t* K_dev, uint
  * equal column width.
  * Errors: ARG, CEILING (any length above the ceiling), ISO_COMPUTE
  * (sum_b D_b L[b][k] > D L_k), UNSUPPORTED (n_bands > 1 with op QK or AV;
- * range_mp with or without bands; chunk_d not a multiple of 32),
+ * range_mp with bands or with op QK / AV; chunk_d not a multiple of 32),
  * PLAN_MISMATCH (table_chunk_d / table_D differ from chunk_d / D). */
 int scmp_plan_create(const scmp_plan_desc* desc, scmp_plan_t* out);
 
@@ -260,7 +263,8 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
  *   workspace must be ordered on one stream.
  * At least one of counts_dev and C_dev must be given; ldc >= N.
  * Errors: ARG, PLAN_MISMATCH (table vs plan), WORKSPACE (too small),
- * UNSUPPORTED (an MFMA algo with a unipolar plan), HIP. */
+ * UNSUPPORTED (an MFMA algo with a unipolar plan; a range-MP plan, which
+ * runs through scmp_matmul_range), HIP. */
 int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                 const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
                 const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
@@ -309,6 +313,49 @@ int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int 
  *   in_dev float [G][M], out_dev float [G]; M >= 1 when G > 0.
  * Errors: ARG, HIP. */
 int scmp_group_max(const float* in_dev, int G, int M, float* out_dev, void* stream);
+
+/* Range-based per-weight-group MP, the weight side's classification
+ * ([VIT] mixed-precision flag table: range MP, its two levels and the
+ * normalised range threshold, a higher threshold putting more groups at low
+ * precision; [KBAND] "Guards": no contraction-axis dispatch).  W's rows
+ * (the output columns of C = X W^T) form groups of range_group consecutive
+ * rows (the last may be short); a group's range is max - min of its float32
+ * weights over all D columns, normalised by the largest group range
+ * (float32; 0 when that is 0).  Groups whose normalised range is below
+ * range_threshold take levels[1], the others levels[0].  Weights are static,
+ * so this runs once when a layer is loaded.
+ *   W_dev float [N][D] with row stride w_row_stride (elements, >= D);
+ *   norm_dev float [n_groups] (nullable), level_dev uint8 [n_groups]
+ *   (nullable); cols_dev int32 [N] (required): the W rows of level 0 in
+ *   order, then those of level 1; n_per_level: host int[2], the number of
+ *   rows of each level.  Synchronises `stream` (the counts are read back).
+ * Errors: ARG (plan without range_mp, sizes), HIP. */
+int scmp_range_classify(scmp_plan_t plan, const float* W_dev, int N, int D, int64_t w_row_stride,
+                        float* norm_dev, uint8_t* level_dev, int32_t* cols_dev, int* n_per_level,
+                        void* stream);
+
+/* Row gather: dst_dev[g][i] = src_dev[g][idx_dev[i]] for rows of row_bytes
+ * bytes, g < G, i < n_idx, with src holding n_src rows per g.  Used to
+ * store a weight side (qB, sB, packed streams) in the level order of
+ * scmp_range_classify.  Indices outside [0, n_src) give zero rows.
+ * Errors: ARG, HIP. */
+int scmp_gather_rows(const void* src_dev, int G, int n_src, size_t row_bytes, const int32_t* idx_dev, int n_idx,
+                     void* dst_dev, void* stream);
+
+/* The range-MP product for the weight rows of one level: every row of A
+ * runs at L = levels[level] ([PAYN] Key design 3 with the length set by
+ * the weight group) against the N compact weight rows qB / sB / packedB
+ * (the level's rows gathered in scmp_range_classify order), and compact
+ * column j is written to C column cols_dev[j] (writes outside [0, ldc) are
+ * dropped).  Two calls, one per level, give the whole product.  The plan
+ * must have range_mp set; rows are in original order (no permutation);
+ * counts_dev, when given, is compact: int32 [G][M][N].  Other arguments,
+ * workspace and errors as scmp_matmul (ARG when level is not 0 or 1). */
+int scmp_matmul_range(scmp_table_t table, scmp_plan_t plan, int algo, int level, int G, int M, int N,
+                      const int8_t* qA_dev, const float* sA_dev, const int8_t* qB_dev,
+                      const uint32_t* packedB_dev, const float* sB_dev, const int32_t* cols_dev,
+                      int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
+                      void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* Diagnostic: synchronise `stream` and return the multiply-accumulates the
  * last MFMA-path contraction with this workspace (scmp_matmul or one of

@@ -20,7 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libscmp.so")
 
-SOURCES = ["plan.cpp", "table.hip", "quantize.hip", "classify.hip", "matmul.hip", "mfma.hip", "bitserial.hip"]
+SOURCES = ["plan.cpp", "table.hip", "quantize.hip", "classify.hip", "matmul.hip", "mfma.hip", "bitserial.hip",
+           "range.hip"]
 
 ARCH = os.environ.get("SCMP_OFFLOAD_ARCH", "gfx950")
 

@@ -187,8 +187,9 @@ __global__ void __launch_bounds__(256) k_matmul_bitserial(MatmulArgs a) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = col0 + tx * 4 + j;
-        if (row >= 0 && col < a.N)
-          a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] =
+        const int ccol = col < a.N ? out_col(a, col) : -1;
+        if (row >= 0 && ccol >= 0)
+          a.C[(long long)g * a.bsc + (long long)row * a.ldc + ccol] =
               cacc[i][j] + (a.bias ? a.bias[(long long)g * a.N + col] : 0.0f);
       }
     }

@@ -13,6 +13,8 @@ struct Plan {
   int op = 0, p = 8, Lmax = 256, D = 0, chunk_d = 0, n_chunks = 1;
   int n_rungs = 1, n_bands = 1, ceiling = 256;
   int mode = SCMP_MODE_BIPOLAR;
+  int range_mp = 0, range_group = 128;  // range-based per-weight-group MP
+  float range_threshold = 0.0f;
   int levels[SCMP_MAX_RUNGS] = {};
   double fractions[SCMP_MAX_RUNGS] = {};
   int band_chunks[SCMP_MAX_BANDS] = {};

@@ -135,21 +135,45 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
 
 }  // extern "C"
 
+// The variants of the contraction beyond scmp_matmul's arguments.
+struct Variant {
+  const float* bias = nullptr;          // added to every row of C
+  const uint8_t* group_rung = nullptr;  // one rung per group
+  int range_level = -1;                 // range MP: every row at this level
+  const int32_t* cmap = nullptr;        // range MP: C column of each compact column
+};
+
 static int matmul_impl(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
                        const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
-                       const float* sB, const float* bias, const uint8_t* group_rung, int32_t* counts, float* C,
-                       int64_t ldc, int64_t batch_stride_c, void* workspace, size_t workspace_bytes,
-                       void* stream) {
+                       const float* sB, const Variant& v, int32_t* counts, float* C, int64_t ldc,
+                       int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
   scmp::clear_error();
+  const float* bias = v.bias;
+  const uint8_t* group_rung = v.group_rung;
   scmp::MatmulArgs a;
   int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
   if (st0 != SCMP_OK) return st0;
   const scmp::Plan& P = plan->plan;
+  if (P.range_mp != (v.range_level >= 0))
+    return set_error(SCMP_ERR_UNSUPPORTED, P.range_mp ? "range-MP plans run through scmp_matmul_range"
+                                                      : "scmp_matmul_range needs a range-MP plan");
   if ((long long)G * M * N == 0) return SCMP_OK;
   if (!qA || !sA || !qB || !sB) return set_error(SCMP_ERR_ARG, "qA, sA, qB and sB are required");
   if (!counts && !C) return set_error(SCMP_ERR_ARG, "at least one of counts and C is required");
   if (C && ldc < N) return set_error(SCMP_ERR_ARG, "ldc must be >= N");
-  if (group_rung) {
+  if (v.range_level >= 0) {
+    // Range MP: every row at the level's length, C columns through cmap.
+    if (v.range_level >= P.n_rungs) return set_error(SCMP_ERR_ARG, "level must be 0 or 1");
+    if (!v.cmap) return set_error(SCMP_ERR_ARG, "cols is required");
+    scmp::group_tiling(a, algo);
+    for (int b = 0; b < P.n_bands; ++b) {
+      a.bandL[b][0] = P.band_L[b][v.range_level];
+      a.pair_off[b][0] = table->pair_off[P.band_L[b][v.range_level]];
+    }
+    a.n_ladder = 1;
+    a.cmap = v.cmap;
+    permA = nullptr;
+  } else if (group_rung) {
     a.group_rung = group_rung;
     scmp::group_tiling(a, algo);
     permA = nullptr;
@@ -179,8 +203,8 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
                 const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
                 void* workspace, size_t workspace_bytes, void* stream) {
-  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, nullptr, nullptr, counts, C,
-                     ldc, batch_stride_c, workspace, workspace_bytes, stream);
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, Variant{}, counts, C, ldc,
+                     batch_stride_c, workspace, workspace_bytes, stream);
 }
 
 int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
@@ -191,8 +215,25 @@ int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int 
     scmp::clear_error();
     return set_error(SCMP_ERR_ARG, "group_rung is NULL (use scmp_matmul)");
   }
-  return matmul_impl(table, plan, algo, G, M, N, qA, sA, nullptr, qB, packedB, sB, nullptr, group_rung, counts, C,
-                     ldc, batch_stride_c, workspace, workspace_bytes, stream);
+  Variant v;
+  v.group_rung = group_rung;
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, nullptr, qB, packedB, sB, v, counts, C, ldc,
+                     batch_stride_c, workspace, workspace_bytes, stream);
+}
+
+int scmp_matmul_range(scmp_table_t table, scmp_plan_t plan, int algo, int level, int G, int M, int N,
+                      const int8_t* qA, const float* sA, const int8_t* qB, const uint32_t* packedB,
+                      const float* sB, const int32_t* cols, int32_t* counts, float* C, int64_t ldc,
+                      int64_t batch_stride_c, void* workspace, size_t workspace_bytes, void* stream) {
+  if (level < 0 || level > 1) {
+    scmp::clear_error();
+    return set_error(SCMP_ERR_ARG, "level must be 0 or 1");
+  }
+  Variant v;
+  v.range_level = level;
+  v.cmap = cols;
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, nullptr, qB, packedB, sB, v, counts, C, ldc,
+                     batch_stride_c, workspace, workspace_bytes, stream);
 }
 
 int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
@@ -203,7 +244,9 @@ int scmp_matmul_bias(scmp_table_t table, scmp_plan_t plan, int algo, int G, int 
     scmp::clear_error();
     return set_error(SCMP_ERR_ARG, "bias is NULL (use scmp_matmul)");
   }
-  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, bias, nullptr, counts, C, ldc,
+  Variant v;
+  v.bias = bias;
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, v, counts, C, ldc,
                      batch_stride_c, workspace, workspace_bytes, stream);
 }
 

@@ -28,6 +28,9 @@ struct MatmulArgs {
   const uint8_t* group_rung;
   int n_ladder;
   int unipolar;  // AND gate, sign-magnitude levels (bit-serial kernel only)
+  // Range MP: C column of each compact weight row (null: the identity).
+  // Stores to columns outside [0, ldc) are dropped.
+  const int32_t* cmap;
   long long ldc, bsc;
   const uint8_t* pair;
   const uint16_t* cum;
@@ -69,6 +72,13 @@ __device__ __forceinline__ int tile_rung(const MatmulArgs& a, int g, int k) {
   if (!a.group_rung) return k;
   const int r = a.group_rung[g];
   return r < a.n_ladder ? r : a.n_ladder - 1;
+}
+
+// C column of compact column col (-1 when the store is to be dropped).
+__device__ __forceinline__ int out_col(const MatmulArgs& a, int col) {
+  if (!a.cmap) return col;
+  const int c = a.cmap[col];
+  return (c >= 0 && c < a.ldc) ? c : -1;
 }
 
 // Original row of a sorted position (the identity without a permutation).

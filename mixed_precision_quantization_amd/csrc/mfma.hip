@@ -734,6 +734,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     const int col = col0 + wcol0 + j * 32 + l32;
     const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
     const float bj = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
+    const int ccol = col < a.N ? out_col(a, col) : -1;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -750,7 +751,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           const float sa = a.sA[(long long)g * a.M + row];
           out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
         }
-        if (a.C) a.C[(long long)g * a.bsc + (long long)row * a.ldc + col] = out + bj;
+        if (a.C && ccol >= 0) a.C[(long long)g * a.bsc + (long long)row * a.ldc + ccol] = out + bj;
       }
   }
 }
@@ -1043,11 +1044,13 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     // are consecutive rows), each used by both column subtiles.
     const float scale0 = (float)qq / (float)L;
     float sb[2], bj[2];
+    int ccol[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int col = col0 + wcol0 + j * 32 + l32;
       sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
       bj[j] = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
+      ccol[j] = col < a.N ? out_col(a, col) : -1;
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1068,8 +1071,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
             if (rowv[e] < 0 || col >= a.N) continue;
             const int cnt2 = (int)acc[i][j][q4 * 4 + e] + rcv[e];
             if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
-            if (a.C)
-              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + col] =
+            if (a.C && ccol[j] >= 0)
+              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + ccol[j]] =
                   (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D)) + bj[j];
           }
       }

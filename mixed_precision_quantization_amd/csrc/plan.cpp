@@ -96,13 +96,23 @@ int build_plan(const scmp_plan_desc* d, Plan& P) {
   // [KBAND] "Guards": range MP has no contraction-axis dispatch.
   if (d->range_mp && d->n_bands > 1)
     return set_error(SCMP_ERR_UNSUPPORTED, "K-bands cannot be combined with range-based MP");
-  if (d->range_mp) return set_error(SCMP_ERR_UNSUPPORTED, "range-based MP is not provided by this library");
+  if (d->range_mp) {
+    // Weight groups exist only where there are weights (linear ops).
+    if (d->op != SCMP_OP_LINEAR) return set_error(SCMP_ERR_UNSUPPORTED, "range-based MP needs a linear op");
+    if (d->n_rungs != 2) return set_error(SCMP_ERR_ARG, "range-based MP takes two levels");
+    if (d->range_group < 0) return set_error(SCMP_ERR_ARG, "range_group must be >= 0");
+    if (!std::isfinite(d->range_threshold) || d->range_threshold < 0.0)
+      return set_error(SCMP_ERR_ARG, "range_threshold must be finite and >= 0");
+  }
   // [KBAND] "Guards": qk / av contract over the head dimension, no band dispatch.
   if (d->n_bands > 1 && d->op != SCMP_OP_LINEAR)
     return set_error(SCMP_ERR_UNSUPPORTED, "K-bands are only defined for linear ops (not qk/av)");
 
   P.op = d->op;
   P.mode = d->mode;
+  P.range_mp = d->range_mp ? 1 : 0;
+  P.range_group = d->range_group > 0 ? d->range_group : 128;
+  P.range_threshold = (float)d->range_threshold;
   P.p = d->p;
   P.Lmax = d->Lmax;
   P.D = d->D;
@@ -268,6 +278,8 @@ int scmp_plan_query(scmp_plan_t plan, scmp_plan_info* out) {
   out->n_bands = P.n_bands;
   out->ceiling = P.ceiling;
   out->mode = P.mode;
+  out->range_mp = P.range_mp;
+  out->range_group = P.range_group;
   return SCMP_OK;
 }
 

@@ -44,7 +44,8 @@ EXPORTED = [
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
-    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
+    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_range_classify",
+    "scmp_gather_rows", "scmp_matmul_range", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
 ]
 
 
@@ -63,12 +64,14 @@ class PlanDesc(ctypes.Structure):
         ("tilt", ctypes.c_double), ("band_L", ctypes.POINTER(ctypes.c_int)),
         ("table_chunk_d", ctypes.c_int), ("table_D", ctypes.c_int),
         ("ceiling", ctypes.c_int), ("range_mp", ctypes.c_int), ("mode", ctypes.c_int),
+        ("range_threshold", ctypes.c_double), ("range_group", ctypes.c_int),
     ]
 
 
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
-                ("op", "p", "Lmax", "D", "chunk_d", "n_chunks", "n_rungs", "n_bands", "ceiling", "mode")]
+                ("op", "p", "Lmax", "D", "chunk_d", "n_chunks", "n_rungs", "n_bands", "ceiling", "mode",
+                 "range_mp", "range_group")]
 
 
 _lib = None
@@ -108,6 +111,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_matmul_group_rungs": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
                                         ctypes.c_size_t, vp]),
         "scmp_group_max": (i, [vp, i, i, vp, vp]),
+        "scmp_range_classify": (i, [vp, vp, i, i, i64, vp, vp, vp, ctypes.POINTER(i), vp]),
+        "scmp_gather_rows": (i, [vp, i, i, ctypes.c_size_t, vp, i, vp, vp]),
+        "scmp_matmul_range": (i, [vp, vp, i, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
+                                  ctypes.c_size_t, vp]),
         "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
                                         ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_ulonglong),
                                         vp]),
@@ -259,7 +266,8 @@ def scmp_plan_create(op: str = "linear", p: int = 8, Lmax: int = 256, D: int = 6
                      levels: Sequence[int] = (256,), fractions: Optional[Sequence[float]] = None,
                      n_bands: int = 1, band_chunks: Optional[Sequence[int]] = None, tilt: float = 0.0,
                      band_L=None, table_chunk_d: int = 0, table_D: int = 0, ceiling: int = 0,
-                     range_mp: bool = False, mode: str = "bipolar") -> Plan:
+                     range_mp: bool = False, mode: str = "bipolar", range_threshold: float = 0.3,
+                     range_group: int = 128) -> Plan:
     lv = (ctypes.c_int * len(levels))(*[int(v) for v in levels])
     fr = (ctypes.c_double * len(fractions))(*[float(v) for v in fractions]) if fractions else None
     bc = (ctypes.c_int * len(band_chunks))(*[int(v) for v in band_chunks]) if band_chunks else None
@@ -272,7 +280,7 @@ def scmp_plan_create(op: str = "linear", p: int = 8, Lmax: int = 256, D: int = 6
                     ctypes.cast(bc, ctypes.POINTER(ctypes.c_int)) if bc else None, float(tilt),
                     ctypes.cast(bl, ctypes.POINTER(ctypes.c_int)) if bl else None,
                     table_chunk_d, table_D, ceiling, 1 if range_mp else 0,
-                    MODES[mode] if isinstance(mode, str) else int(mode))
+                    MODES[mode] if isinstance(mode, str) else int(mode), float(range_threshold), int(range_group))
     out = ctypes.c_void_p()
     _check("scmp_plan_create", load().scmp_plan_create(ctypes.byref(desc), ctypes.byref(out)))
     return Plan(out.value)
@@ -440,6 +448,70 @@ def scmp_group_max(values: torch.Tensor, out=None, stream=None) -> torch.Tensor:
     return out
 
 
+def scmp_range_classify(plan: Plan, W: torch.Tensor, stream=None):
+    """Range-MP weight groups of W [N, D] (float32, unit column stride).
+    Returns (norm float [n_groups], level uint8 [n_groups], cols int32 [N],
+    (rows of level 0, rows of level 1)); synchronises."""
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be 2-D with unit column stride")
+    N, D = W.shape
+    n_groups = -(-N // plan.range_group)
+    norm = torch.empty(n_groups, dtype=torch.float32, device=W.device)
+    level = torch.empty(n_groups, dtype=torch.uint8, device=W.device)
+    cols = torch.empty(N, dtype=torch.int32, device=W.device)
+    counts = (ctypes.c_int * 2)()
+    _check("scmp_range_classify",
+           load().scmp_range_classify(plan.handle, _ptr(W, torch.float32, "W") if W.is_contiguous()
+                                      else ctypes.c_void_p(W.data_ptr()), N, D, W.stride(0),
+                                      _ptr(norm, torch.float32, "norm"), _ptr(level, torch.uint8, "level"),
+                                      _ptr(cols, torch.int32, "cols"), counts, _stream(stream)))
+    return norm, level, cols, (counts[0], counts[1])
+
+
+def scmp_gather_rows(src: torch.Tensor, idx: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """dst[g, i] = src[g, idx[i]] for src [G, n, ...] (or [n, ...]); ``out``
+    (contiguous, same dtype) is allocated when None."""
+    s3 = src if src.dim() >= 3 else src.unsqueeze(0)
+    s3 = s3.contiguous()
+    G, n_src = s3.shape[0], s3.shape[1]
+    row_bytes = s3[0, 0].numel() * s3.element_size() if n_src else 0
+    if out is None:
+        out = torch.empty((G, idx.numel()) + tuple(s3.shape[2:]), dtype=src.dtype, device=src.device)
+    if out.dtype != src.dtype or not out.is_contiguous() or out.numel() != G * idx.numel() * s3[0, 0].numel():
+        raise ValueError("out must be contiguous, of src's dtype and of G x len(idx) rows")
+    _check("scmp_gather_rows", load().scmp_gather_rows(ctypes.c_void_p(s3.data_ptr()), G, n_src, row_bytes,
+                                                        _ptr(idx, torch.int32, "idx"), idx.numel(),
+                                                        ctypes.c_void_p(out.data_ptr()), _stream(stream)))
+    return out if (src.dim() >= 3 or out.dim() < 3) else out[0]
+
+
+def scmp_matmul_range(table: Table, plan: Plan, level: int, qA, sA, qB, sB, cols, C_out, packedB=None,
+                      algo: str = "auto", counts_out=None, workspace=None, stream=None):
+    """One level of a range-MP product: every row of A at levels[level]
+    against the compact weight rows qB [G, n, D] (sB [G, n, n_chunks]),
+    compact column j written to C_out column cols[j] (C_out [G, M, N_total])."""
+    qA3 = qA if qA.dim() == 3 else qA.unsqueeze(0)
+    qB3 = qB if qB.dim() == 3 else qB.unsqueeze(0)
+    G, M, D = qA3.shape
+    n = qB3.shape[1]
+    C3 = C_out if C_out.dim() == 3 else C_out.unsqueeze(0)
+    _need(sA, G * M * plan.n_chunks, "sA")
+    _need(sB, G * n * plan.n_chunks, "sB")
+    _need(cols, n, "cols")
+    _need(counts_out, G * M * n, "counts_out")
+    ws_need = scmp_matmul_workspace_bytes(table, plan, G, M, n, algo)
+    if workspace is None:
+        workspace = torch.empty(max(ws_need, 1), dtype=torch.uint8, device=qA.device)
+    _need(workspace, ws_need, "workspace")
+    _check("scmp_matmul_range", load().scmp_matmul_range(
+        table.handle, plan.handle, ALGOS[algo], int(level), G, M, n, _ptr(qA3, torch.int8, "qA"),
+        _ptr(sA, torch.float32, "sA"), _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"),
+        _ptr(sB, torch.float32, "sB"), _ptr(cols, torch.int32, "cols"), _ptr(counts_out, torch.int32, "counts_out"),
+        _ptr(C3, torch.float32, "C_out"), C3.shape[2], C3.shape[1] * C3.shape[2],
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+    return C_out
+
+
 def scmp_error_flags(stream=None) -> int:
     """Synchronise and return (then clear) the device error flags; raises on NONFINITE."""
     flags = ctypes.c_int(0)
@@ -492,3 +564,35 @@ def sc_qk_head_mp(table: Table, plan: Plan, Q: torch.Tensor, K: torch.Tensor, he
                             group_rung=group_rung, stream=stream)
     return {"qA": qA, "sA": sA, "metric": mA, "head_metric": head_metric, "qB": qB, "sB": sB, "packedB": pB,
             "ghat": ghat, "head_rung": group_rung, "perm": perm, "thresholds": thr, "counts": counts, "C": C}
+
+
+def sc_linear_range(table: Table, plan: Plan, X: torch.Tensor, W: torch.Tensor, algo: str = "auto",
+                    want_counts: bool = False, stream=None):
+    """C = X W^T under range-based per-weight-group MP: W's groups are
+    classified by normalised range (at load time, synchronising), W is
+    quantised once and stored in level order, and each level's columns are
+    contracted at that level's length into their place in C."""
+    norm, level, cols, n_lv = scmp_range_classify(plan, W, stream=stream)
+    qA, sA, mA, _ = scmp_quantize_encode(table, plan, X, stream=stream)
+    qW, sW, _, pW = scmp_quantize_encode(table, plan, W, want_metric=False, want_packed=plan.needs_packed(algo),
+                                         stream=stream)
+    qB = scmp_gather_rows(qW, cols, stream=stream)
+    sB = scmp_gather_rows(sW, cols, stream=stream)
+    pB = scmp_gather_rows(pW, cols, stream=stream) if pW is not None else None
+    G = qA.shape[0] if qA.dim() == 3 else 1
+    M = qA.shape[-2]
+    N = W.shape[0]
+    C = torch.empty((G, M, N), dtype=torch.float32, device=X.device)
+    counts = []
+    off = 0
+    for k in range(2):
+        n = n_lv[k]
+        cnt = torch.empty((G, M, n), dtype=torch.int32, device=X.device) if (want_counts and n) else None
+        if n:
+            scmp_matmul_range(table, plan, k, qA, sA, qB[:, off:off + n], sB[:, off:off + n], cols[off:off + n], C,
+                              packedB=None if pB is None else pB[:, off:off + n], algo=algo, counts_out=cnt,
+                              stream=stream)
+        counts.append(cnt)
+        off += n
+    return {"qA": qA, "sA": sA, "qB": qB, "sB": sB, "norm": norm, "level": level, "cols": cols,
+            "n_per_level": n_lv, "counts": counts, "C": C}

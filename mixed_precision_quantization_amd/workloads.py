@@ -44,7 +44,8 @@ class Workload:
 
 # The five workloads (the fifth has two parts: fc2 with K-bands, and AV),
 # per-query-row and per-head mixed precision on QK^T, the head-aligned
-# compensator, and the unipolar mode on AV and on the compensator.
+# compensator, the unipolar mode on AV and on the compensator, and
+# range-based per-weight-group MP on fc1.
 WORKLOADS = {
     "single_64": Workload(
         "single_64", "linear", 1, 64, 64, 64, (64,), seed=1001,
@@ -103,6 +104,13 @@ WORKLOADS = {
         "vitl_comp_unipolar", "linear", 1, 64 * 257, 1024, 1024,
         (256,), None, chunk_d=64, seed=1008,
         a_dist="outlier", b_dist="weight", extra={"bias": True}, mode="unipolar"),
+    # Range-based per-weight-group MP on fc1 (scmp_vit README, the
+    # mixed-precision flag table defaults: levels 256,128, threshold 0.3),
+    # 128-row weight groups with spread amplitudes.
+    "vitl_fc1_range": Workload(
+        "vitl_fc1_range", "linear", 1, 64 * 257, 4096, 1024,
+        (256, 128), None, seed=1011, a_dist="outlier", b_dist="weight_groups",
+        extra={"range_mp": True, "range_threshold": 0.3, "range_group": 128}),
 }
 
 
@@ -145,6 +153,13 @@ def _draw(rng, dist: str, lead: tuple, rows: int, cols: int) -> np.ndarray:
         x = rng.standard_normal(shape)
         amp = np.exp(0.5 * rng.standard_normal(lead + (1, 1)))
         return x * amp
+    if dist == "weight_groups":
+        # 0.02 N(0, 1) weights, each group of 128 rows scaled by its own
+        # log-normal amplitude exp(0.75 z), so that group ranges differ.
+        x = rng.standard_normal(shape) * 0.02
+        n_groups = -(-rows // 128)
+        amp = np.exp(0.75 * rng.standard_normal(lead + (n_groups, 1)))
+        return x * np.repeat(amp, 128, axis=-2)[..., :rows, :]
     if dist == "gelu":
         return _gelu(rng.standard_normal(shape))
     if dist == "softmax":

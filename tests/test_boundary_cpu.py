@@ -68,7 +68,29 @@ def test_guard_band_above_ceiling_rejected_at_startup():
 def test_guard_kbands_with_range_mp_raises():
     _err(lambda: scmp.scmp_plan_create(D=256, chunk_d=64, levels=(128, 64), n_bands=4, range_mp=True),
          scmp.SCMP_ERR_UNSUPPORTED)
-    _err(lambda: scmp.scmp_plan_create(D=256, levels=(128, 64), range_mp=True), scmp.SCMP_ERR_UNSUPPORTED)
+
+
+def test_range_mp_plan_rules():
+    plan = scmp.scmp_plan_create(D=256, levels=(256, 128), range_mp=True, range_threshold=0.3, range_group=64)
+    assert plan.range_mp == 1 and plan.range_group == 64
+    assert scmp.scmp_plan_create(D=256, levels=(256, 128), range_mp=True, range_group=0).range_group == 128
+    _err(lambda: scmp.scmp_plan_create(op="qk", D=64, levels=(256, 128), range_mp=True), scmp.SCMP_ERR_UNSUPPORTED)
+    _err(lambda: scmp.scmp_plan_create(D=64, levels=(256, 128, 64), range_mp=True), scmp.SCMP_ERR_ARG)
+    _err(lambda: scmp.scmp_plan_create(D=64, levels=(256, 128), range_mp=True, range_threshold=-1.0),
+         scmp.SCMP_ERR_ARG)
+    _err(lambda: scmp.scmp_plan_create(D=64, levels=(256, 128), range_mp=True, range_group=-2), scmp.SCMP_ERR_ARG)
+    lib = scmp.load()
+    # Host-side checks of the range entry points, before any device work.
+    n = (scmp.ctypes.c_int * 2)()
+    bip = scmp.scmp_plan_create(D=64, levels=(256, 128))
+    assert lib.scmp_range_classify(bip.handle, None, 4, 64, 64, None, None, None, n, None) == scmp.SCMP_ERR_ARG
+    rp = scmp.scmp_plan_create(D=64, levels=(256, 128), range_mp=True)
+    assert lib.scmp_range_classify(rp.handle, None, 4, 32, 64, None, None, None, n, None) == \
+        scmp.SCMP_ERR_PLAN_MISMATCH
+    assert lib.scmp_matmul_range(None, rp.handle, 0, 2, 1, 1, 1, *([None] * 8), 1, 1, None, 0,
+                                 None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_gather_rows(None, 1, 4, 16, None, 2, None, None) == scmp.SCMP_ERR_ARG
+    assert lib.scmp_gather_rows(None, 1, 4, 16, None, 0, None, None) == scmp.SCMP_OK
 
 
 def test_guard_table_priced_at_other_chunk_or_width():

@@ -545,3 +545,105 @@ def test_unipolar_standalone_decode_matches_fused(table):
     C = scmp.scmp_decode(plan, res["counts"], res["sA"], res["sB"], rung=res["rung"])
     torch.cuda.synchronize()
     assert torch.equal(C, res["C"])
+
+
+# ------------------------------------------ range-based per-weight-group MP --
+
+def _range_oracle(A, W, levels, thr, gs, rows, chunk_d=0):
+    """Oracle C and compact counts of a range-MP product on ``rows``, per
+    level through the worker pool."""
+    rl = o.range_levels(W, gs, thr)
+    col_level = np.repeat(rl["level"], gs)[: W.shape[0]]
+    C = np.zeros((len(rows), W.shape[0]))
+    C_abs = np.zeros_like(C)
+    counts = []
+    for k, L in enumerate(levels):
+        cols = np.nonzero(col_level == k)[0]
+        if len(cols) == 0:
+            counts.append(None)
+            continue
+        okw = dict(p=8, Lmax=256, D=W.shape[1], chunk_d=chunk_d, levels=(L,))
+        out = pooled_rows_product(A[rows], np.zeros(len(rows), np.int64), W[cols], okw)
+        C[:, cols] = out["C"]
+        C_abs[:, cols] = out["C_abs"]
+        counts.append(out["band_counts"][:, :, 0])
+    return rl, C, C_abs, counts
+
+
+@pytest.mark.parametrize("gs,thr", [(128, 0.3), (64, 0.5), (1, 0.3), (50, 0.0), (50, 1.5)])
+def test_range_classify_matches_oracle(table, gs, thr):
+    rng = np.random.default_rng(91)
+    N, D = 300, 96
+    W = (rng.standard_normal((N, D)) * np.exp(rng.standard_normal((N, 1)))).astype(np.float32)
+    W[17] = 0.0
+    plan = scmp.scmp_plan_create(D=D, levels=(256, 128), range_mp=True, range_threshold=thr, range_group=gs)
+    print(f"  range classify gs={gs} thr={thr}", flush=True)
+    norm, level, cols, n_lv = scmp.scmp_range_classify(plan, torch.from_numpy(W).cuda())
+    rl = o.range_levels(W, gs, thr)
+    assert np.array_equal(norm.cpu().numpy(), rl["norm"])
+    assert np.array_equal(level.cpu().numpy().astype(np.int64), rl["level"])
+    col_level = np.repeat(rl["level"], gs)[:N]
+    want = np.concatenate([np.nonzero(col_level == 0)[0], np.nonzero(col_level == 1)[0]])
+    assert np.array_equal(cols.cpu().numpy().astype(np.int64), want)
+    assert n_lv == (int((col_level == 0).sum()), int((col_level == 1).sum()))
+
+
+def test_gather_rows_matches_indexing(table):
+    rng = np.random.default_rng(92)
+    src = torch.from_numpy(rng.integers(-100, 100, (2, 40, 33)).astype(np.int8)).cuda()
+    idx = torch.tensor([5, 0, 39, 7, 7, -1, 40], dtype=torch.int32, device="cuda")
+    out = scmp.scmp_gather_rows(src, idx)
+    ref = torch.zeros_like(out)
+    ref[:, :5] = src[:, idx[:5].long()]
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)                    # out-of-range indices give zero rows
+    f = torch.from_numpy(rng.standard_normal((1, 40, 4)).astype(np.float32)).cuda()
+    assert torch.equal(scmp.scmp_gather_rows(f, idx[:5]), f[:, idx[:5].long()])
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_range_mp_small(table, algo):
+    rng = np.random.default_rng(93)
+    M, N, D, gs = 150, 300, 160, 64
+    A = rng.standard_normal((M, D)).astype(np.float32)
+    W = (0.02 * rng.standard_normal((N, D)) * np.repeat(np.exp(rng.standard_normal(5)), gs)[:N, None])
+    W = W.astype(np.float32)
+    levels, thr = (256, 96), 0.4
+    plan = scmp.scmp_plan_create(D=D, levels=levels, range_mp=True, range_threshold=thr, range_group=gs)
+    print(f"  range mp small {algo}", flush=True)
+    res = scmp.sc_linear_range(table, plan, torch.from_numpy(A).cuda(), torch.from_numpy(W).cuda(), algo=algo,
+                               want_counts=True)
+    torch.cuda.synchronize()
+    rows = np.arange(M)
+    rl, C, C_abs, counts = _range_oracle(A, W, levels, thr, gs, rows)
+    assert 0 < res["n_per_level"][1] < N                 # both levels present
+    got = res["C"][0].cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - C) <= RTOL * C_abs)
+    for k in range(2):
+        assert np.array_equal(res["counts"][k][0].cpu().numpy().astype(np.int64), counts[k]), f"level {k}"
+
+
+def test_range_mp_rejects_plain_matmul(table):
+    rng = np.random.default_rng(94)
+    plan = scmp.scmp_plan_create(D=64, levels=(256, 128), range_mp=True)
+    A = torch.from_numpy(rng.standard_normal((20, 64)).astype(np.float32)).cuda()
+    with pytest.raises(scmp.ScmpError) as e:
+        scmp.sc_linear(table, plan, A, A)
+    assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
+
+
+def test_range_mp_full_size(table):
+    """The benchmark's workload and launch (AUTO), checked on sampled rows
+    against the oracle, columns of both levels."""
+    w = WORKLOADS["vitl_fc1_range"]
+    X, W = draw(w)
+    plan = scmp.scmp_plan_create(D=w.D, levels=w.levels, range_mp=True, range_threshold=w.extra["range_threshold"],
+                                 range_group=w.extra["range_group"])
+    print("  range mp full size", flush=True)
+    res = scmp.sc_linear_range(table, plan, torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda(), algo="auto")
+    torch.cuda.synchronize()
+    rows = np.array([0, 5000, w.M - 1])
+    rl, C, C_abs, _ = _range_oracle(X, W, w.levels, w.extra["range_threshold"], w.extra["range_group"], rows)
+    got = res["C"][0].cpu().numpy()[rows].astype(np.float64)
+    assert np.all(np.abs(got - C) <= RTOL * C_abs)
+    assert res["n_per_level"][1] == 128 * int(rl["level"].sum())
