@@ -300,8 +300,7 @@ def main():
     value = bitmacs / (ms_per_step / 1e3)
     L_eff = bitmacs / (G * M * N * D)
 
-    # Unipolar plans run on the bit-serial kernel whatever the algo says.
-    on_valu = args.algo == "bitserial" or plan.unipolar
+    on_valu = args.algo == "bitserial"
     if on_valu:
         achieved = bitmacs / (kern_ms / 1e3) / 1e12
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_BITMACS / 1e12,

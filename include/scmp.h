@@ -85,8 +85,8 @@ typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
  *             are several output tiles per block, one block per tile
  *             otherwise).
  *  MFMA_PERSISTENT: the matrix-core path as a persistent grid taking
- *             output tiles from a work counter; plans without chunk scales
- *             and with one band only (UNSUPPORTED otherwise).
+ *             output tiles from a work counter; bipolar plans without chunk
+ *             scales and with one band only (UNSUPPORTED otherwise).
  *  MFMA_ONEPASS: the matrix-core path with one block per output tile.
  *  BITSERIAL: one bit-select + popcount per 32 stream positions on the
  *             vector ALU; needs the packed weight-side streams. */
@@ -249,8 +249,9 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
  * chunks in float32 ([PAYN] Key design 1, decode equation).
  * A unipolar plan (scmp_mode) counts AND instead of XNOR: per index the
  * count is sign(x_A) sign(x_B) cum[u_B][n1_A], and the chunk decode is
- * s^A_ic s^B_jc q^2 count_ijc / L_c; it runs on the bit-serial kernel
- * (AUTO selects it; the MFMA algos return UNSUPPORTED) and needs packedB.
+ * s^A_ic s^B_jc q^2 count_ijc / L_c.  It runs on the bit-serial kernel or
+ * on the one-block-per-tile matrix-core kernel (AUTO and MFMA select it;
+ * MFMA_PERSISTENT returns UNSUPPORTED).
  *   qA_dev int8 [G][M][D], sA_dev float [G][M][n_chunks],
  *   permA_dev int32 [G][M] (NULL only for one rung: identity order),
  *   qB_dev int8 [G][N][D], sB_dev float [G][N][n_chunks],
@@ -263,8 +264,8 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
  *   workspace must be ordered on one stream.
  * At least one of counts_dev and C_dev must be given; ldc >= N.
  * Errors: ARG, PLAN_MISMATCH (table vs plan), WORKSPACE (too small),
- * UNSUPPORTED (an MFMA algo with a unipolar plan; a range-MP plan, which
- * runs through scmp_matmul_range), HIP. */
+ * UNSUPPORTED (MFMA_PERSISTENT with a unipolar plan; a range-MP plan,
+ * which runs through scmp_matmul_range), HIP. */
 int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                 const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
                 const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,

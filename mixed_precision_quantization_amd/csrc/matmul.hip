@@ -25,24 +25,21 @@ void fill_tiles(MatmulArgs& a, const Plan& P, int BM) {
     a.tile_start[k + 1] = a.tile_start[k] + (a.cuts[k + 1] - a.cuts[k] + BM - 1) / BM;
 }
 
-// Validate the arguments and fill MatmulArgs (no device work).  Unipolar
-// plans run on the bit-serial kernel: AUTO becomes BITSERIAL.
+// Validate the arguments and fill MatmulArgs (no device work).
 static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M, int N, MatmulArgs& a) {
   if (!table || !plan) return set_error(SCMP_ERR_ARG, "table or plan is NULL");
   const Plan& P = plan->plan;
   if (table->p != P.p || table->Lmax != P.Lmax)
     return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
   if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA_ONEPASS) return set_error(SCMP_ERR_ARG, "unknown algo");
-  if (P.mode == SCMP_MODE_UNIPOLAR) {
-    if (algo == SCMP_ALGO_AUTO) algo = SCMP_ALGO_BITSERIAL;
-    if (algo != SCMP_ALGO_BITSERIAL)
-      return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans run on the bit-serial kernel only");
-  }
+  if (P.mode == SCMP_MODE_UNIPOLAR && algo == SCMP_ALGO_MFMA_PERSISTENT)
+    return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans have no persistent launch");
   if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
   a = MatmulArgs{};
   a.pair = table->pair;
+  a.K = table->K;
   a.cum = table->cum;
   a.G = G;
   a.M = M;

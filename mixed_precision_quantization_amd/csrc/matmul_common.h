@@ -27,7 +27,8 @@ struct MatmulArgs {
   // tiling rung, no permutation); n_ladder is the ladder's rung count.
   const uint8_t* group_rung;
   int n_ladder;
-  int unipolar;  // AND gate, sign-magnitude levels (bit-serial kernel only)
+  int unipolar;  // AND gate, sign-magnitude levels (bit-serial and staged matrix-core kernels)
+  const uint32_t* K;  // packed indicator rows [P + 1][Wl] (the unipolar operand table)
   // Range MP: C column of each compact weight row (null: the identity).
   // Stores to columns outside [0, ldc) are dropped.
   const int32_t* cmap;

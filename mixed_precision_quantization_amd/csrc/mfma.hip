@@ -214,15 +214,26 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
     const int L = a.bandL[b][k];
     __syncthreads();
     // Everything an element needs at this L, per stored value x (entry
-    // x + 128): window code (13 bits), hh (8 bits) and its n0 = L - n1
-    // (9 bits), so the per-element work is one table read.
+    // x + 128): window code (14 bits), the tile-maximum key hh (8 bits) and
+    // its n0 term (9 bits), so the per-element work is one table read.
+    // Bipolar: the half-window hh of |n1 - n0| with the sign of n1 - n0,
+    // and n0 = L - n1.  Unipolar: the whole prefix of n1 positions with the
+    // sign of x (hh = n1, kept to 8 bits as 255 = "all 16 half-blocks"),
+    // and no n0 term.
     {
       const int x = tid - 128;
-      const int n1 = a.cum[(long long)level_of(x, a.P, a.q) * (a.Lmax + 1) + L];
-      const int diff = 2 * n1 - L;
-      const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
-      const int code = 16 * (2 * hh + (diff < 0 ? 1 : 0));
-      s_lut[tid] = (uint32_t)code | ((uint32_t)hh << 13) | ((uint32_t)(L - n1) << 21);
+      uint32_t e;
+      if (a.unipolar) {
+        const int n1 = a.cum[(long long)uni_level_of(x, a.P, a.q) * (a.Lmax + 1) + L];
+        e = (uint32_t)(16 * (2 * n1 + (x < 0 ? 1 : 0))) | ((uint32_t)min(n1, 255) << 14);
+      } else {
+        const int n1 = a.cum[(long long)level_of(x, a.P, a.q) * (a.Lmax + 1) + L];
+        const int diff = 2 * n1 - L;
+        const int hh = ((diff < 0 ? -diff : diff) + 1) >> 1;
+        const int code = 16 * (2 * hh + (diff < 0 ? 1 : 0));
+        e = (uint32_t)code | ((uint32_t)hh << 14) | ((uint32_t)(L - n1) << 22);
+      }
+      s_lut[tid] = e;
     }
     __syncthreads();
     // The next group's values are read while this group is encoded.
@@ -256,9 +267,9 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
           const bool ok = i < span && (h == 0 ? row_lo : row_hi) >= 0;
           if (ok) {
             const uint32_t e = s_lut[(int)(h == 0 ? x_lo[i] : x_hi[i]) + 128];
-            code[h] = (int)(e & 0x1FFFu);
-            hh[h] = (int)((e >> 13) & 0xFFu);
-            (h == 0 ? rc_lo : rc_hi) += (int)(e >> 21);
+            code[h] = (int)(e & 0x3FFFu);
+            hh[h] = (int)((e >> 14) & 0xFFu);
+            (h == 0 ? rc_lo : rc_hi) += (int)(e >> 22);
           }
         }
         word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
@@ -308,10 +319,16 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
 // quarter q = tid % 4), indices [d0 + 8 q, d0 + 8 q + 8) of each group of
 // 32 in the block's part of the contraction axis.
 __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
-  // Table row offset of each stored value x (entry x + 128).
+  // Table row offset of each stored value x (entry x + 128).  Unipolar:
+  // the magnitude's level row, with the sign of x in bit 0 (row offsets are
+  // multiples of 16).
   __shared__ uint32_t s_off[256];
   const int tid = threadIdx.x;
-  s_off[tid] = (uint32_t)(level_of(tid - 128, a.P, a.q) * PT_STRIDE);
+  {
+    const int x = tid - 128;
+    s_off[tid] = a.unipolar ? (uint32_t)(uni_level_of(x, a.P, a.q) * PT_STRIDE) | (x < 0 ? 1u : 0u)
+                            : (uint32_t)(level_of(x, a.P, a.q) * PT_STRIDE);
+  }
   const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
@@ -328,7 +345,7 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int8_t* src_hi = a.qB + ((long long)g * a.N + (col_hi < a.N ? col_hi : 0)) * a.D;
   const long long tile = (long long)g * w.CT + blockIdx.x;
   const int ngrp = (int)(w.Dp / MF_DC);
-  const uint32_t pad = (uint32_t)((a.P >> 1) * PT_STRIDE);
+  const uint32_t pad = a.unipolar ? 0u : (uint32_t)((a.P >> 1) * PT_STRIDE);
   __syncthreads();
   for (int d0 = plo; d0 < phi; d0 += MF_DC) {
     const int dfirst = d0 + 8 * q;
@@ -406,6 +423,26 @@ __device__ __forceinline__ void stage_pair_table(uint8_t* pt, const MatmulArgs& 
   }
 }
 
+// The unipolar operand table as e2m1 nibbles: row u holds K[u][p] (0 or
+// 1, code 0 or 2) for positions p < 256 (zero past Lmax), position p in
+// nibble p mod 2 of byte p / 2, one LDS row of PT_STRIDE bytes per level.
+// The AND count of a prefix of n1 positions is the sum of its first n1
+// entries, whatever L is.
+__device__ __forceinline__ void stage_uni_table(uint8_t* pt, const MatmulArgs& a, int tid, int nthreads) {
+  for (int idx = tid; idx < (a.P + 1) * 16; idx += nthreads) {
+    const int u = idx >> 4, c = idx & 15;  // 16 positions [16 c, 16 c + 16)
+    const uint32_t word = (c >> 1) < a.Wl ? a.K[(long long)u * a.Wl + (c >> 1)] : 0u;
+    const uint32_t bits = (word >> (16 * (c & 1))) & 0xffffu;
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      lo |= ((bits >> i) & 1u) << (4 * i + 1);
+      hi |= ((bits >> (i + 8)) & 1u) << (4 * i + 1);
+    }
+    *(uint2*)(pt + u * PT_STRIDE + c * 8) = uint2{lo, hi};
+  }
+}
+
 // Operands of one step for this lane half: half-blocks X (row codes hx of
 // rows l32 and l32 + 32, column table offsets ux of columns l32 and l32 + 32,
 // first position kx) and Y.  A from the pattern table, B from the nibble
@@ -431,6 +468,36 @@ __device__ __forceinline__ Frag frags_at(const uint8_t* pat, const uint8_t* pt, 
   return f;
 }
 
+// frags_at for unipolar operands.  Prefixes reach 256 positions, so a
+// pattern offset can pass the table's last entry: entries from 32 on all
+// hold 16 sign nibbles, so the offset is clamped to entry 32 or 33 with the
+// same parity.  B's row offsets carry the sign of B's value in bit 0,
+// applied by flipping the sign bit of every nibble (0x2 -> 0xA; 0x0 ->
+// 0x8, which is also zero).
+__device__ __forceinline__ Frag frags_at_uni(const uint8_t* pat, const uint8_t* pt, uint32_t hx, uint32_t ux,
+                                             uint32_t kx, uint32_t hy, uint32_t uy, uint32_t ky) {
+  auto aoff = [](uint32_t code, uint32_t k) {
+    const uint32_t o = __builtin_elementwise_sub_sat(code, 32u * k);
+    return min(o, 512u + (o & 16u));
+  };
+  Frag f;
+  const v2i ax0 = *(const v2i*)(pat + aoff(hx & 0xffffu, kx));
+  const v2i ax1 = *(const v2i*)(pat + aoff(hx >> 16, kx));
+  const v2i ay0 = *(const v2i*)(pat + aoff(hy & 0xffffu, ky));
+  const v2i ay1 = *(const v2i*)(pat + aoff(hy >> 16, ky));
+  const v2i bx0 = *(const v2i*)(pt + (ux & 0xfffeu) + (kx >> 1));
+  const v2i bx1 = *(const v2i*)(pt + ((ux >> 16) & 0xfffeu) + (kx >> 1));
+  const v2i by0 = *(const v2i*)(pt + (uy & 0xfffeu) + (ky >> 1));
+  const v2i by1 = *(const v2i*)(pt + ((uy >> 16) & 0xfffeu) + (ky >> 1));
+  auto flip = [](uint32_t u, int sh) { return (int)(0u - ((u >> sh) & 1u)) & (int)0x88888888u; };
+  const int sx0 = flip(ux, 0), sx1 = flip(ux, 16), sy0 = flip(uy, 0), sy1 = flip(uy, 16);
+  f.a[0] = v8i{ax0.x, ax0.y, ay0.x, ay0.y, 0, 0, 0, 0};
+  f.a[1] = v8i{ax1.x, ax1.y, ay1.x, ay1.y, 0, 0, 0, 0};
+  f.b[0] = v8i{bx0.x ^ sx0, bx0.y ^ sx0, by0.x ^ sy0, by0.y ^ sy0, 0, 0, 0, 0};
+  f.b[1] = v8i{bx1.x ^ sx1, bx1.y ^ sx1, by1.x ^ sy1, by1.y ^ sy1, 0, 0, 0, 0};
+  return f;
+}
+
 // One step: the wave's 2 x 2 subtiles of 32 x 32.
 __device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Frag& f) {
 #pragma unroll
@@ -447,9 +514,13 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Frag& f) {
 // buffered; one wave lists the stage's work while the stage is stored.
 // Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
 // that also write per-band counts keep a third accumulator set and run one.
-template <bool CHUNKED, bool COUNTS>
+// UNI: the unipolar mode, whose prefixes run up to 16 half-blocks of 16
+// positions (8 for the bipolar half-windows); schedule entries then carry
+// the half-block index j instead of its first position 16 j.
+template <bool CHUNKED, bool COUNTS, bool UNI>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, MfmaWs w) {
   constexpr int BM = MF_BM, BN = MF_BN, DC = MF_DC;
+  constexpr int NLEV = UNI ? 16 : 8;
   // The two gather tables share one object (the largest, laid out first) so
   // that both sit below 64 KB, where a constant base folds into the LDS
   // instruction's offset.
@@ -464,7 +535,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   __shared__ __align__(16) uint32_t s_u[2][DC][BN / 2];  // [index][column pair]
   // Stage schedule: the half-blocks past the stage's full levels in order,
   // then padding entries (a zero half-block), and the steps they take.
-  constexpr int SCHED_N = DC * 8 + 16;
+  constexpr int SCHED_N = DC * NLEV + 16;
   __shared__ __align__(4) uint16_t s_sched[2][SCHED_N];
   __shared__ int s_nsteps[2];
   __shared__ int s_full[2];  // leading levels needed by every index of the stage
@@ -525,23 +596,25 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       // j < ceil(rmx / 16); the leading levels every index needs are swept
       // without a list, the rest are listed level by level, indices in
       // order within a level.  Entry: d * 256 + kk (the byte offset of index
-      // d's words in a stage row, and the first paired position kk = 16 j).
+      // d's words in a stage row, and the first paired position kk = 16 j;
+      // UNI: j itself).
       const int m = tid < DC ? rmx : 0;
       int full = 0;
-      while (full < 8 && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
+      while (full < NLEV && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
       int base = 0;
-      for (int j = full; j < 8; ++j) {
+      for (int j = full; j < NLEV; ++j) {
         const unsigned long long bal = __ballot(m > 16 * j);
         if (bal == 0) break;
         if (m > 16 * j) {
           const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-          s_sched[bf][pos] = (uint16_t)(tid * 256 + 16 * j);
+          s_sched[bf][pos] = (uint16_t)(tid * 256 + (UNI ? j : 16 * j));
         }
         base += __builtin_popcountll(bal);
       }
-      // Padding: position 128 is past every window (A nibbles all zero).
-      if (tid < 16) s_sched[bf][base + tid] = (uint16_t)128u;
+      // Padding: position 16 NLEV is past every window or prefix (A nibbles
+      // all zero).
+      if (tid < 16) s_sched[bf][base + tid] = (uint16_t)(UNI ? NLEV : 16 * NLEV);
       if (tid == 0) s_full[bf] = full;
       if (tid == 0) s_nsteps[bf] = (base + 3) >> 2;
     }
@@ -570,7 +643,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     const float scaleL = (float)qq / (float)L;
     const int dbeg = a.band_cols[b], dend = a.band_cols[b + 1];
     __syncthreads();  // every wave is done with the previous band's table
-    stage_pair_table(s_tab.pt, a, b, k, KLpad, tid, 256);
+    if (UNI) {
+      if (b == 0) stage_uni_table(s_tab.pt, a, tid, 256);  // one table for every L
+    } else {
+      stage_pair_table(s_tab.pt, a, b, k, KLpad, tid, 256);
+    }
     store(buf);
     __syncthreads();
     for (int d0 = dbeg; d0 < dend; d0 += DC) {
@@ -599,6 +676,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
                       *(const uint32_t*)(hbase + oy), *(const uint32_t*)(ubase + oy), e};
         };
         auto frags = [&](const Item& c) __attribute__((always_inline)) {
+          if (UNI)
+            return frags_at_uni(s_pat, s_pt, c.hx, c.ux, 16u * (c.e & 0x1fu), c.hy, c.uy,
+                                16u * ((c.e >> 16) & 0x1fu));
           return frags_at(s_pat, s_pt, c.hx, c.ux, c.e & 0xffu, c.hy, c.uy, (c.e >> 16) & 0xffu);
         };
         // Software-pipelined sweep over steps 0 .. cnt - 1, ent(s) giving the
@@ -637,13 +717,14 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         };
         // Full levels: step 8 j + m takes level j of indices 16 hf + m (X)
         // and 16 hf + 8 + m (Y).  Past the last level the entries fall on
-        // level full <= 8 (position <= 128, inside the table rows): read,
-        // never used.
+        // level full <= NLEV (position <= 16 NLEV <= 256, inside the table
+        // rows): read, never used.
         if (full > 0)
           sweep(8 * full, [&](int st) {
-            const uint32_t j = (uint32_t)(st >> 3) & 15u, m = (uint32_t)(st & 7);
+            const uint32_t j = (uint32_t)(st >> 3) & 31u, m = (uint32_t)(st & 7);
             const uint32_t dx = 16u * hf + m, dy = dx + 8u;
-            return (dx * 256u + 16u * j) | ((dy * 256u + 16u * j) << 16);
+            const uint32_t kj = UNI ? j : 16u * j;
+            return (dx * 256u + kj) | ((dy * 256u + kj) << 16);
           });
         // The rest from the stage's list.
         if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; });
@@ -683,7 +764,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
               for (int j = 0; j < 2; ++j) {
                 const int v = q4 * 4 + e;
                 const int cnt = (int)acc[i][j][v] + rcv[e];
-                cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * (float)(2 * cnt - L * cw));
+                cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * (float)(UNI ? cnt : 2 * cnt - L * cw));
                 if (COUNTS) bacc[i][j][v] += cnt;
                 acc[i][j][v] = 0.0f;
               }
@@ -749,7 +830,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           const int cnt = (int)acc[i][j][v] + s_rc[r];
           if (COUNTS) a.counts[((long long)g * a.M + row) * a.N + col] = cnt;
           const float sa = a.sA[(long long)g * a.M + row];
-          out = (sa * sb) * (scale0 * (float)(2 * cnt - L0 * a.D));
+          out = (sa * sb) * (scale0 * (float)(UNI ? cnt : 2 * cnt - L0 * a.D));
         }
         if (a.C && ccol >= 0) a.C[(long long)g * a.bsc + (long long)row * a.ldc + ccol] = out + bj;
       }
@@ -1131,11 +1212,23 @@ static int device_cus() {
 
 static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStream_t st) {
   const bool counts = a.counts != nullptr;
-  if (a.chunk_d > 0) {
+  if (a.unipolar) {
+    // Unipolar plans: the staged kernel with prefixes of up to 16 half-blocks.
+    if (a.chunk_d > 0) {
+      if (counts)
+        hipLaunchKernelGGL((k_mfma<true, true, true>), grid, dim3(256), 0, st, a, w);
+      else
+        hipLaunchKernelGGL((k_mfma<true, false, true>), grid, dim3(256), 0, st, a, w);
+    } else if (counts) {
+      hipLaunchKernelGGL((k_mfma<false, true, true>), grid, dim3(256), 0, st, a, w);
+    } else {
+      hipLaunchKernelGGL((k_mfma<false, false, true>), grid, dim3(256), 0, st, a, w);
+    }
+  } else if (a.chunk_d > 0) {
     if (counts)
-      hipLaunchKernelGGL((k_mfma<true, true>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<true, true, false>), grid, dim3(256), 0, st, a, w);
     else
-      hipLaunchKernelGGL((k_mfma<true, false>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<true, false, false>), grid, dim3(256), 0, st, a, w);
   } else if (a.launch == 1 ||
              (a.launch == 0 && pers_ok(a, w) &&
               a.tile_start[a.n_rungs] * a.G * w.CT >= 3 * (counts ? 1 : 2) * device_cus())) {
@@ -1149,9 +1242,9 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
       hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
   } else {
     if (counts)
-      hipLaunchKernelGGL((k_mfma<false, true>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<false, true, false>), grid, dim3(256), 0, st, a, w);
     else
-      hipLaunchKernelGGL((k_mfma<false, false>), grid, dim3(256), 0, st, a, w);
+      hipLaunchKernelGGL((k_mfma<false, false, false>), grid, dim3(256), 0, st, a, w);
   }
 }
 

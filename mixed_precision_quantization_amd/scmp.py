@@ -226,9 +226,9 @@ class Plan:
         return self.mode == MODES["unipolar"]
 
     def needs_packed(self, algo: str) -> bool:
-        """Whether the contraction reads packed weight-side streams: the
-        bit-serial kernel does, and it is the one unipolar plans run on."""
-        return algo == "bitserial" or (algo == "auto" and self.unipolar)
+        """Whether the contraction reads packed weight-side streams (the
+        bit-serial kernel does)."""
+        return algo == "bitserial"
 
     def band_lengths(self):
         buf = (ctypes.c_int * (self.n_bands * self.n_rungs))()

@@ -26,12 +26,12 @@ ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass")
 
 
 def _skip_unsupported(algo, chunk_d=0, n_bands=1, mode="bipolar"):
-    """The persistent launch takes plans without chunk scales and one band;
-    unipolar plans run on the bit-serial kernel only."""
+    """The persistent launch takes bipolar plans without chunk scales and one
+    band."""
     if algo == "mfma_persistent" and ((chunk_d or 0) > 0 or n_bands > 1):
         pytest.skip("the persistent launch needs a single-segment plan (checked in test_persistent_rejects_chunks)")
-    if mode == "unipolar" and algo not in ("bitserial", "auto"):
-        pytest.skip("unipolar plans run on the bit-serial kernel (checked in test_unipolar_rejects_mfma)")
+    if mode == "unipolar" and algo == "mfma_persistent":
+        pytest.skip("unipolar plans have no persistent launch (checked in test_unipolar_rejects_persistent)")
 
 
 @pytest.fixture(scope="module")
@@ -350,8 +350,7 @@ def test_full_size_sampled_rows(table, name):
     if w.kind == "linear":
         At, Bt = At[0], Bt[0]
     bench = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="auto", want_counts=False))
-    full = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="bitserial" if plan.unipolar else "mfma",
-                                 want_counts=True))
+    full = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="mfma", want_counts=True))
     torch.cuda.synchronize()
     assert np.array_equal(bench["C"], full["C"])
     groups = FULL_GROUPS.get(name, (0,))
@@ -507,18 +506,18 @@ def test_group_rungs_clamp_and_match_fixed_length(table, algo):
 
 # ------------------------------------------------------- unipolar mode --
 
-def test_unipolar_rejects_mfma(table):
+def test_unipolar_rejects_persistent(table):
     rng = np.random.default_rng(71)
     plan = scmp.scmp_plan_create(D=64, levels=(128,), mode="unipolar")
     A = torch.from_numpy(rng.standard_normal((40, 64)).astype(np.float32)).cuda()
-    for algo in ("mfma", "mfma_persistent", "mfma_onepass"):
-        with pytest.raises(scmp.ScmpError) as e:
-            scmp.sc_linear(table, plan, A, A, algo=algo)
-        assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
+    with pytest.raises(scmp.ScmpError) as e:
+        scmp.sc_linear(table, plan, A, A, algo="mfma_persistent")
+    assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
 
 
+@pytest.mark.parametrize("algo", ["mfma", "bitserial"])
 @pytest.mark.parametrize("L", [1, 31, 33, 64, 97, 255, 256])
-def test_unipolar_every_length_class_and_signs(table, L):
+def test_unipolar_every_length_class_and_signs(table, L, algo):
     """Signed rows and columns with exact zeros, full-scale entries and a
     ragged tile, at one length, all rows and columns."""
     rng = np.random.default_rng(72 + L)
@@ -529,10 +528,11 @@ def test_unipolar_every_length_class_and_signs(table, L):
     A[5, ::3] = 0.0
     B[:, 7] = 0.0
     A[9] = np.abs(A[9])
+    A[11, 3] = 50.0                                  # one full-scale entry: a 256-position prefix at L = 256
     plan = scmp.scmp_plan_create(D=D, levels=(L,), mode="unipolar")
     okw = dict(p=8, Lmax=256, D=D, levels=(L,), mode="unipolar")
-    print(f"  unipolar L={L}", flush=True)
-    gres = _gpu_path(table, plan, A, B, "auto")
+    print(f"  unipolar L={L} {algo}", flush=True)
+    gres = _gpu_path(table, plan, A, B, algo)
     _check_group(gres, 0, A, B, okw)
 
 
