@@ -647,3 +647,59 @@ def test_range_mp_full_size(table):
     got = res["C"][0].cpu().numpy()[rows].astype(np.float64)
     assert np.all(np.abs(got - C) <= RTOL * C_abs)
     assert res["n_per_level"][1] == 128 * int(rl["level"].sum())
+
+
+# ------------------------------------------------ precision and size edges --
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("p,Lmax,levels,chunk_d", [(4, 16, (16, 9, 3), 0), (2, 4, (4, 2), 0), (3, 5, (5, 1), 32),
+                                                    (8, 200, (200, 77), 0)])
+def test_other_precisions_and_table_lengths(p, Lmax, levels, chunk_d, algo):
+    """Tables at p < 8 and Lmax < 2^p: P + 1 levels, q = 2^(p-1) - 1."""
+    _skip_unsupported(algo, chunk_d)
+    rng = np.random.default_rng(100 + p)
+    M, N, D = 150, 90, 70
+    A = rng.standard_normal((M, D)).astype(np.float32)
+    B = rng.standard_normal((N, D)).astype(np.float32)
+    tab = scmp.scmp_build_sobol_table(p, Lmax)
+    try:
+        fr = tuple([1.0 / len(levels)] * len(levels))
+        plan = scmp.scmp_plan_create(p=p, Lmax=Lmax, D=D, chunk_d=chunk_d, levels=levels, fractions=fr)
+        print(f"  p={p} Lmax={Lmax} levels={levels} chunk_d={chunk_d} {algo}", flush=True)
+        gres = _gpu_path(tab, plan, A, B, algo)
+        _check_group(gres, 0, A, B, dict(p=p, Lmax=Lmax, metric="linear", D=D, chunk_d=chunk_d, levels=levels,
+                                          fractions=fr))
+    finally:
+        tab.close()
+
+
+def test_many_small_groups(table):
+    """G = 3000 groups (the grid's group axis), per-group classification."""
+    rng = np.random.default_rng(111)
+    G, M, N, D = 3000, 5, 7, 32
+    A = rng.standard_normal((G, M, D)).astype(np.float32)
+    B = rng.standard_normal((G, N, D)).astype(np.float32)
+    plan = scmp.scmp_plan_create(op="qk", D=D, levels=(64, 32), fractions=(0.6, 0.4))
+    okw = dict(p=8, Lmax=256, metric="linear", D=D, levels=(64, 32), fractions=(0.6, 0.4))
+    print("  many groups", flush=True)
+    gres = _gpu_path(table, plan, A, B, "auto")
+    for g in (0, 1, 1499, 2999):
+        _check_group(gres, g, A[g], B[g], okw)
+
+
+def test_tall_matrix_all_pairs_classification(table):
+    """M = 40000 rows (above the bucketed classifier's limit), sampled rows of
+    every rung, the benchmark's launch."""
+    rng = np.random.default_rng(112)
+    M, N, D = 40000, 40, 64
+    A = rng.standard_normal((M, D)).astype(np.float32)
+    A[:, 5] *= 20.0
+    B = rng.standard_normal((N, D)).astype(np.float32)
+    levels, fr = (256, 128, 64), (0.2, 0.3, 0.5)
+    plan = scmp.scmp_plan_create(D=D, levels=levels, fractions=fr)
+    okw = dict(p=8, Lmax=256, metric="linear", D=D, levels=levels, fractions=fr)
+    print("  tall matrix", flush=True)
+    gres = _gpu_path(table, plan, A, B, "auto")
+    cls = o.classify(A, o.OraclePlan(**okw))
+    rows = cls["order"][sample_rows(M, cls["cuts"], per_rung=4, seed=3)]
+    _check_group(gres, 0, A, B, okw, rows=rows)
