@@ -35,6 +35,9 @@ PEAK_HBM_GBS = 8000.0            # HBM3E, 8 TB/s
 # Vector-ALU bit-serial bound: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz int32
 # ops, two ops (bit-select, popcount) per 32 stream positions.
 PEAK_VALU_BITMACS = 256 * 4 * 16 * 2.4e9 * 16
+# LDS gather bound of the pair-count table form: 32 banks of 4 bytes per CU
+# per clock, one 2-byte table entry per lane: 256 x 32 x 2.4 GHz lookups.
+PEAK_LDS_GATHERS = 256 * 32 * 2.4e9
 
 
 def parse():
@@ -44,10 +47,43 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass"])
+                    choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle sample (0 = 2 per worker)")
     return ap.parse_args()
+
+
+def sources_sha256():
+    """SHA-256 of the library's sources (csrc/ and include/), so that a
+    profile's counters are used only for the kernels they were taken on."""
+    import hashlib
+    h = hashlib.sha256()
+    dirs = [os.path.join(ROOT, "mixed_precision_quantization_amd", "csrc"), os.path.join(ROOT, "include")]
+    for d in dirs:
+        for name in sorted(os.listdir(d)):
+            if name.endswith((".hip", ".h", ".cpp")):
+                h.update(name.encode())
+                with open(os.path.join(d, name), "rb") as f:
+                    h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic(workload, dispatches):
+    """HBM bytes of the contraction kernel per timed call from the committed
+    rocprofv3 summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a
+    plain copy), or None when there is none or the sources have changed
+    since it was taken."""
+    import glob
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"k_*_{workload}.md"))):
+        text = open(path).read()
+        marker = "```json\n"
+        if marker not in text:
+            continue
+        rec = json.loads(text.split(marker)[-1].split("```")[0])
+        if rec.get("workload") != workload or rec.get("sources_sha256") != sources_sha256():
+            return None
+        return (rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"]) * dispatches
+    return None
 
 
 def git_sha():
@@ -301,7 +337,13 @@ def main():
     L_eff = bitmacs / (G * M * N * D)
 
     on_valu = args.algo == "bitserial"
-    if on_valu:
+    if args.algo == "gather":
+        lookups = G * M * N * D
+        achieved = lookups / (kern_ms / 1e3) / 1e9
+        roof = {"bound": "lds", "achieved": achieved, "peak": PEAK_LDS_GATHERS / 1e9, "unit": "G lookups/s",
+                "frac": achieved / (PEAK_LDS_GATHERS / 1e9), "traffic": None,
+                "work": "one 2-byte LDS table lookup per (row, column, index)", "lookups": lookups}
+    elif on_valu:
         achieved = bitmacs / (kern_ms / 1e3) / 1e12
         roof = {"bound": "alu", "achieved": achieved, "peak": PEAK_VALU_BITMACS / 1e12,
                 "unit": "T bit-MAC/s", "frac": achieved / (PEAK_VALU_BITMACS / 1e12), "traffic": None,
@@ -333,10 +375,15 @@ def main():
     # The events bracket one scmp_matmul call: the contraction kernel plus, on
     # the matrix-core path, its two small encode kernels (k_prep_rows,
     # k_prep_cols), which run first on the same stream.
-    roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if on_valu
+    roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if on_valu else
+                      "scmp_matmul = k_pc_tables + k_matmul_gather" if args.algo == "gather"
                       else "scmp_matmul = k_prep_rows + k_prep_cols + k_mfma")
     if ranged:
         roof["kernel"] = "two scmp_matmul_range calls (one per level), each " + roof["kernel"].split(" = ")[1]
+    roof["traffic"] = profiled_traffic(w.name, 2 if ranged else 1) if args.algo not in ("bitserial", "gather") else None
+    roof["traffic_source"] = ("profiles/ summary of this workload (FETCH_SIZE + WRITE_SIZE of the contraction "
+                              "kernel per timed call, scaled by a plain copy); null when the library sources "
+                              "differ from the profiled ones")
     roof["kernel_ms"] = kern_ms
     roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
     roof["valu_bitserial_frac"] = bitmacs / (kern_ms / 1e3) / PEAK_VALU_BITMACS
@@ -345,6 +392,8 @@ def main():
     # on int8 or e2m1 (fp4, exact for these operands) matrix-core operands.
     if on_valu:
         dtype = "u32 bit-ops"
+    elif args.algo == "gather":
+        dtype = "u16 table lookups"
     else:
         dtype = {(True, False): "i8", (False, True): "fp4(e2m1)", (True, True): "i8+fp4(e2m1)"}.get(
             (roof["issued_macs_int8"] > 0, roof["issued_macs_fp4"] > 0), "i8")

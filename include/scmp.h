@@ -89,13 +89,17 @@ typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
  *             scales and with one band only (UNSUPPORTED otherwise).
  *  MFMA_ONEPASS: the matrix-core path with one block per output tile.
  *  BITSERIAL: one bit-select + popcount per 32 stream positions on the
- *             vector ALU; needs the packed weight-side streams. */
+ *             vector ALU; needs the packed weight-side streams.
+ *  GATHER:    one lookup per (row, column, index) in a per-length table
+ *             T_L[u_A][u_B] of XNOR counts (built into the workspace and
+ *             staged whole into LDS); bipolar plans only. */
 typedef enum {
   SCMP_ALGO_AUTO = 0,
   SCMP_ALGO_BITSERIAL = 1,
   SCMP_ALGO_MFMA = 2,
   SCMP_ALGO_MFMA_PERSISTENT = 3,
-  SCMP_ALGO_MFMA_ONEPASS = 4
+  SCMP_ALGO_MFMA_ONEPASS = 4,
+  SCMP_ALGO_GATHER = 5
 } scmp_algo;
 
 typedef struct scmp_table_s* scmp_table_t; /* opaque, library-owned */
@@ -234,7 +238,8 @@ int scmp_classify_rows(scmp_plan_t plan, const float* metric_dev, int G, int M, 
  * largest half-window per index, the per-part or per-chunk n0 sums, the
  * weight side's table offsets (two per column pair and index), index-major
  * copies of both for single-segment plans, sorted-row ids and scales, and
- * a work counter.  Errors: ARG, PLAN_MISMATCH. */
+ * a work counter.  GATHER keeps one count table per (band, rung) length,
+ * (2^p + 1)^2 uint16 each.  Errors: ARG, PLAN_MISMATCH. */
 int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                                 size_t* bytes);
 

@@ -21,7 +21,7 @@ BUILD_DIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libscmp.so")
 
 SOURCES = ["plan.cpp", "table.hip", "quantize.hip", "classify.hip", "matmul.hip", "mfma.hip", "bitserial.hip",
-           "range.hip"]
+           "range.hip", "gather.hip"]
 
 ARCH = os.environ.get("SCMP_OFFLOAD_ARCH", "gfx950")
 

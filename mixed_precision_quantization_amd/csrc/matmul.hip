@@ -31,9 +31,9 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M
   const Plan& P = plan->plan;
   if (table->p != P.p || table->Lmax != P.Lmax)
     return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
-  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA_ONEPASS) return set_error(SCMP_ERR_ARG, "unknown algo");
-  if (P.mode == SCMP_MODE_UNIPOLAR && algo == SCMP_ALGO_MFMA_PERSISTENT)
-    return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans have no persistent launch");
+  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_GATHER) return set_error(SCMP_ERR_ARG, "unknown algo");
+  if (P.mode == SCMP_MODE_UNIPOLAR && (algo == SCMP_ALGO_MFMA_PERSISTENT || algo == SCMP_ALGO_GATHER))
+    return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans have no persistent or gather form");
   if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
@@ -121,6 +121,10 @@ int scmp_matmul_workspace_bytes(scmp_table_t table, scmp_plan_t plan, int algo, 
   int st = scmp::prepare(table, plan, algo, G, M, N, a);
   if (st != SCMP_OK) return st;
   if (algo == SCMP_ALGO_BITSERIAL || (long long)G * M * N == 0) return SCMP_OK;
+  if (algo == SCMP_ALGO_GATHER) {
+    *bytes = scmp::gather_workspace_bytes(a);
+    return SCMP_OK;
+  }
   // Enough for both tilings: rows bucketed by rung, or each group's rows in
   // order (scmp_matmul_group_rungs).
   const size_t by_rung = scmp::mfma_workspace_bytes(a);
@@ -191,7 +195,9 @@ static int matmul_impl(scmp_table_t table, scmp_plan_t plan, int algo, int G, in
   a.ldc = ldc;
   a.bsc = batch_stride_c;
   hipStream_t st = (hipStream_t)stream;
-  return bitserial ? scmp::launch_bitserial(a, st) : scmp::launch_mfma(a, workspace, workspace_bytes, st);
+  if (bitserial) return scmp::launch_bitserial(a, st);
+  if (algo == SCMP_ALGO_GATHER) return scmp::launch_gather(a, workspace, workspace_bytes, st);
+  return scmp::launch_mfma(a, workspace, workspace_bytes, st);
 }
 
 extern "C" {
@@ -257,7 +263,8 @@ int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int 
   scmp::MatmulArgs a;
   int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
   if (st0 != SCMP_OK) return st0;
-  if (algo == SCMP_ALGO_BITSERIAL) return set_error(SCMP_ERR_UNSUPPORTED, "only the MFMA path counts its steps");
+  if (algo == SCMP_ALGO_BITSERIAL || algo == SCMP_ALGO_GATHER)
+    return set_error(SCMP_ERR_UNSUPPORTED, "only the MFMA path counts its steps");
   if ((long long)G * M * N == 0) return SCMP_OK;
   return scmp::mfma_issued_macs(a, workspace, workspace_bytes, (hipStream_t)stream, macs, fp4_macs);
 }

@@ -106,5 +106,7 @@ int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipSt
 
 // Vector-ALU bit-serial path (bitserial.hip).
 int launch_bitserial(const MatmulArgs& a, hipStream_t st);
+size_t gather_workspace_bytes(const MatmulArgs& a);
+int launch_gather(const MatmulArgs& a, void* ws, size_t ws_bytes, hipStream_t st);
 
 }  // namespace scmp

@@ -1231,9 +1231,10 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
       hipLaunchKernelGGL((k_mfma<true, false, false>), grid, dim3(256), 0, st, a, w);
   } else if (a.launch == 1 ||
              (a.launch == 0 && pers_ok(a, w) &&
-              a.tile_start[a.n_rungs] * a.G * w.CT >= 3 * (counts ? 1 : 2) * device_cus())) {
-    // Persistent when every block gets several tiles; a one-pass grid
-    // otherwise (its blocks then need no work counter or table reuse).
+              a.tile_start[a.n_rungs] * a.G * w.CT >= 2 * (counts ? 1 : 2) * device_cus())) {
+    // Persistent when every block gets at least two tiles (the table is
+    // then staged once for several); a one-pass grid otherwise (its blocks
+    // need no work counter or table reuse).
     const int n_items = a.tile_start[a.n_rungs] * a.G * w.CT;
     const int blocks = std::max(1, std::min(n_items, (counts ? 1 : 2) * device_cus()));
     if (counts)

@@ -30,14 +30,15 @@ SCMP_ERR_HIP = 8
 SCMP_OP_LINEAR, SCMP_OP_QK, SCMP_OP_AV = 0, 1, 2
 SCMP_MODE_BIPOLAR, SCMP_MODE_UNIPOLAR = 0, 1
 SCMP_ALGO_AUTO, SCMP_ALGO_BITSERIAL, SCMP_ALGO_MFMA = 0, 1, 2
-SCMP_ALGO_MFMA_PERSISTENT, SCMP_ALGO_MFMA_ONEPASS = 3, 4
+SCMP_ALGO_MFMA_PERSISTENT, SCMP_ALGO_MFMA_ONEPASS, SCMP_ALGO_GATHER = 3, 4, 5
 SCMP_MAX_RUNGS = 8
 SCMP_MAX_BANDS = 16
 
 OPS = {"linear": SCMP_OP_LINEAR, "qk": SCMP_OP_QK, "av": SCMP_OP_AV}
 MODES = {"bipolar": SCMP_MODE_BIPOLAR, "unipolar": SCMP_MODE_UNIPOLAR}
 ALGOS = {"auto": SCMP_ALGO_AUTO, "bitserial": SCMP_ALGO_BITSERIAL, "mfma": SCMP_ALGO_MFMA,
-         "mfma_persistent": SCMP_ALGO_MFMA_PERSISTENT, "mfma_onepass": SCMP_ALGO_MFMA_ONEPASS}
+         "mfma_persistent": SCMP_ALGO_MFMA_PERSISTENT, "mfma_onepass": SCMP_ALGO_MFMA_ONEPASS,
+         "gather": SCMP_ALGO_GATHER}
 
 EXPORTED = [
     "scmp_status_string", "scmp_last_error", "scmp_build_sobol_table", "scmp_table_destroy",

@@ -21,8 +21,8 @@ pytestmark = pytest.mark.gpu
 
 RTOL = 1e-5
 # Contraction kernels: the matrix-core path by size, forced persistent or
-# one block per tile, and the bit-serial path.
-ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass")
+# one block per tile, the bit-serial path and the pair-count gather path.
+ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather")
 
 
 def _skip_unsupported(algo, chunk_d=0, n_bands=1, mode="bipolar"):
@@ -30,8 +30,8 @@ def _skip_unsupported(algo, chunk_d=0, n_bands=1, mode="bipolar"):
     band."""
     if algo == "mfma_persistent" and ((chunk_d or 0) > 0 or n_bands > 1):
         pytest.skip("the persistent launch needs a single-segment plan (checked in test_persistent_rejects_chunks)")
-    if mode == "unipolar" and algo == "mfma_persistent":
-        pytest.skip("unipolar plans have no persistent launch (checked in test_unipolar_rejects_persistent)")
+    if mode == "unipolar" and algo in ("mfma_persistent", "gather"):
+        pytest.skip("unipolar plans have no persistent or gather form (checked in test_unipolar_rejects_persistent)")
 
 
 @pytest.fixture(scope="module")
@@ -510,9 +510,10 @@ def test_unipolar_rejects_persistent(table):
     rng = np.random.default_rng(71)
     plan = scmp.scmp_plan_create(D=64, levels=(128,), mode="unipolar")
     A = torch.from_numpy(rng.standard_normal((40, 64)).astype(np.float32)).cuda()
-    with pytest.raises(scmp.ScmpError) as e:
-        scmp.sc_linear(table, plan, A, A, algo="mfma_persistent")
-    assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
+    for algo in ("mfma_persistent", "gather"):
+        with pytest.raises(scmp.ScmpError) as e:
+            scmp.sc_linear(table, plan, A, A, algo=algo)
+        assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
 
 
 @pytest.mark.parametrize("algo", ["mfma", "bitserial"])
