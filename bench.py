@@ -68,11 +68,11 @@ def sources_sha256():
     return h.hexdigest()
 
 
-def profiled_traffic(workload, dispatches):
+def profiled_traffic(workload, algo, dispatches):
     """HBM bytes of the contraction kernel per timed call from the committed
-    rocprofv3 summary of this workload (FETCH_SIZE + WRITE_SIZE, scaled by a
-    plain copy), or None when there is none or the sources have changed
-    since it was taken."""
+    rocprofv3 summary of this workload and algo (FETCH_SIZE + WRITE_SIZE,
+    scaled by a plain copy), or None when there is none or the sources have
+    changed since it was taken."""
     import glob
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", f"k_*_{workload}.md"))):
         text = open(path).read()
@@ -80,7 +80,9 @@ def profiled_traffic(workload, dispatches):
         if marker not in text:
             continue
         rec = json.loads(text.split(marker)[-1].split("```")[0])
-        if rec.get("workload") != workload or rec.get("sources_sha256") != sources_sha256():
+        if rec.get("workload") != workload or rec.get("algo") != algo:
+            continue
+        if rec.get("sources_sha256") != sources_sha256():
             return None
         return (rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"]) * dispatches
     return None
@@ -380,7 +382,7 @@ def main():
                       else "scmp_matmul = k_prep_rows + k_prep_cols + k_mfma")
     if ranged:
         roof["kernel"] = "two scmp_matmul_range calls (one per level), each " + roof["kernel"].split(" = ")[1]
-    roof["traffic"] = profiled_traffic(w.name, 2 if ranged else 1) if args.algo not in ("bitserial", "gather") else None
+    roof["traffic"] = profiled_traffic(w.name, args.algo, 2 if ranged else 1)
     roof["traffic_source"] = ("profiles/ summary of this workload (FETCH_SIZE + WRITE_SIZE of the contraction "
                               "kernel per timed call, scaled by a plain copy); null when the library sources "
                               "differ from the profiled ones")
