@@ -3,6 +3,7 @@ header declares, and its plan logic (guards, K-band ladder, row cuts,
 budget use) agrees with the oracle.  No device call is made here."""
 
 import ctypes
+import json
 import os
 import re
 import subprocess
@@ -222,3 +223,26 @@ def test_group_entry_points_check_arguments_on_the_host():
     assert lib.scmp_group_max(None, 3, 4, None, None) == scmp.SCMP_ERR_ARG
     assert lib.scmp_matmul_bias(None, None, 0, 1, 1, 1, *([None] * 7), None, None, 1, 1, None, 0,
                                 None) == scmp.SCMP_ERR_ARG
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode != 0 and "one GPU" in r.stderr
+
+
+def test_bench_traffic_is_null_when_sources_differ(tmp_path, monkeypatch):
+    import bench
+    real = bench.sources_sha256()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))        # profiles/ under tmp_path
+    monkeypatch.setattr(bench, "sources_sha256", lambda: real)
+    (tmp_path / "profiles").mkdir()
+    rec = {"workload": "w", "algo": "auto", "fetch_bytes_per_dispatch": 10, "write_bytes_per_dispatch": 5}
+    for sha, expect in ((real, 30), ("0" * 64, None)):
+        text = "summary\n```json\n" + json.dumps(dict(rec, sources_sha256=sha)) + "\n```\n"
+        (tmp_path / "profiles" / "k_mfma_w.md").write_text(text)
+        assert bench.profiled_traffic("w", "auto", 2) == expect
+        assert bench.profiled_traffic("w", "gather", 2) is None
