@@ -184,6 +184,42 @@ __global__ void __launch_bounds__(256) k_quantize_vec(QuantArgs a) {
   if (__ballot(bad) != 0 && lane == 0) atomicOr(&g_quant_flags, 1);
 }
 
+// Rows of any length up to 64 R with unit column stride but no alignment
+// (attention rows of 257 values, say) and one scale per row: one wave per
+// row, four rows per block, lane l holding columns l, l + 64, ... in
+// registers between the max and the quantisation.
+template <int R>
+__global__ void __launch_bounds__(256) k_quantize_wave(QuantArgs a) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = blockIdx.x * 4 + wave;
+  const int g = blockIdx.y;
+  if (row >= a.rows) return;
+  const float* x = a.X + (long long)g * a.bs + (long long)row * a.rs;
+  const long long orow = (long long)g * a.rows + row;
+  int8_t* qrow = a.qout + orow * a.cols;
+  const float qf = (float)a.q;
+  float v[R];
+  bool bad = false;
+  float m = 0.0f;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = 64 * r + lane;
+    v[r] = c < a.cols ? x[c] : 0.0f;
+    bad |= !__builtin_isfinite(v[r]);
+    m = fmaxf(m, fabsf(v[r]));
+  }
+  m = wave_max(m);
+  const float s = m == 0.0f ? 0.0f : m / qf;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int c = 64 * r + lane;
+    if (c < a.cols) qrow[c] = quant_one(v[r], s, qf);
+  }
+  if (lane == 0) a.scales[orow] = s;
+  if (a.metric && lane == 0) a.metric[orow] = m;
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(&g_quant_flags, 1);
+}
+
 int read_clear_quant_flags(hipStream_t st, int* flags) {
   int v = 0, zero = 0;
   hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_quant_flags), sizeof(int), 0, hipMemcpyDeviceToHost, st);
@@ -238,8 +274,20 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
   const bool vec = col_stride == 1 && !packed_out && cols % 4 == 0 && cols <= 4096 && cd_ok &&
                    ((uintptr_t)X % 16) == 0 && row_stride % 4 == 0 && batch_stride % 4 == 0 &&
                    ((uintptr_t)q_out % 4) == 0;
+  // Wave path: unit column stride, one scale per row, no packed streams,
+  // rows up to 1024 values, any alignment.
+  const bool wave = !vec && col_stride == 1 && !packed_out && P.chunk_d <= 0 && cols <= 1024;
   hipStream_t st = (hipStream_t)stream;
-  if (vec) {
+  if (wave) {
+    const dim3 grid((rows + 3) / 4, G);
+    const int R = (cols + 63) / 64;
+    if (R <= 4)
+      hipLaunchKernelGGL(scmp::k_quantize_wave<4>, grid, dim3(256), 0, st, a);
+    else if (R <= 8)
+      hipLaunchKernelGGL(scmp::k_quantize_wave<8>, grid, dim3(256), 0, st, a);
+    else
+      hipLaunchKernelGGL(scmp::k_quantize_wave<16>, grid, dim3(256), 0, st, a);
+  } else if (vec) {
     const dim3 grid((rows + 3) / 4, G);
     const int R = (cols + 255) / 256;
     if (R <= 4)

@@ -153,6 +153,23 @@ def test_quantise_bit_exact_rows_chunks_strides(table):
     assert scmp.scmp_error_flags() == 0
 
 
+@pytest.mark.parametrize("D", [1, 63, 257, 1021, 1024])
+def test_quantise_unaligned_rows(table, D):
+    """Rows of any length and alignment with one scale per row (the
+    one-wave-per-row path), including a view that starts one float in."""
+    rng = np.random.default_rng(21 + D)
+    X = (rng.standard_normal((70, D + 1)) * rng.uniform(1e-3, 1e3, (70, 1))).astype(np.float32)
+    X[4] = 0.0
+    plan = scmp.scmp_plan_create(op="av", D=D, levels=(64,))
+    Xt = torch.from_numpy(X).cuda()[:, 1:]             # 4-byte offset, row stride D + 1
+    print(f"  quantise unaligned D={D}", flush=True)
+    q, s, m, _ = scmp.scmp_quantize_encode(table, plan, Xt)
+    xo, so = o.quantize(X[:, 1:], 8)
+    assert np.array_equal(q[0].cpu().numpy().astype(np.int64), xo)
+    assert np.array_equal(s[0].cpu().numpy(), so)
+    assert np.array_equal(m[0].cpu().numpy(), o.row_metric(X[:, 1:]))
+
+
 def test_nonfinite_input_sets_flag(table):
     X = np.ones((4, 64), dtype=np.float32)
     X[2, 5] = np.nan
