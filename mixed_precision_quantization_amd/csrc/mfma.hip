@@ -169,23 +169,27 @@ __device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out)
 }
 
 // ------------------------------------------------------------ prep A ----
-// grid (RT, n_parts, G), block 256: thread -> (row pair pr = tid / 4,
-// quarter q = tid % 4); per group of 32 contraction indices a thread
-// encodes indices [d0 + 8 q, d0 + 8 q + 8) of both rows of its pair.  The
-// block covers indices [part * part_len, ...) of one tile.
+// grid (RT, n_parts, G), block 256: wave q takes indices [d0 + 8 q,
+// d0 + 8 q + 8) of every group of 32, lane pr the row pair pr (both rows).
+// A wave then holds all 64 pairs of its indices: the tile maximum per index
+// is a wave reduction, and each index-major store covers 64 consecutive
+// pairs.  The block covers indices [part * part_len, ...) of one tile.
 __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   __shared__ uint32_t s_lut[256];
-  __shared__ int s_mx[4][MF_DC];
   __shared__ int s_rows[MF_BM];
+  __shared__ int s_rc[MF_BM];  // n0 sums of the tile's rows over the current chunk or part
   const int tid = threadIdx.x;
   const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, y, MF_BM, k, pos0, nrows);
   k = tile_rung(a, g, k);
-  const int wave = tid >> 6, lane = tid & 63;
-  const int pr = tid >> 2, q = tid & 3;
+  const int lane = tid & 63, q = tid >> 6;
+  const int pr = lane;
   const int p_lo = pair_lo(pr), p_hi = p_lo + 32;
-  if (tid < MF_BM) s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+  if (tid < MF_BM) {
+    s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+    s_rc[tid] = 0;
+  }
   __syncthreads();
   const int row_lo = s_rows[p_lo], row_hi = s_rows[p_hi];
   const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
@@ -194,18 +198,19 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
   const int ngrp = (int)(w.Dp / MF_DC);
   const int plo = part * w.part_len;
   const int phi = min(plo + w.part_len, a.D);
-  int rc_lo = 0, rc_hi = 0;  // n0 sums of this thread's indices
-  // n0 sums of both rows over the four quarters, written by quarter 0.
+  int rc_lo = 0, rc_hi = 0;  // n0 sums of this lane's rows over its indices
+  // n0 sums of the tile's rows over the four waves' indices, written to
+  // slot `slot` (every wave calls this together).
   auto flush_rc = [&](long long slot) {
-    rc_lo += __shfl_xor(rc_lo, 1, 64);
-    rc_lo += __shfl_xor(rc_lo, 2, 64);
-    rc_hi += __shfl_xor(rc_hi, 1, 64);
-    rc_hi += __shfl_xor(rc_hi, 2, 64);
-    if (q == 0) {
-      w.rowc[slot * w.Mp + (long long)y * MF_BM + p_lo] = rc_lo;
-      w.rowc[slot * w.Mp + (long long)y * MF_BM + p_hi] = rc_hi;
-    }
+    atomicAdd(&s_rc[p_lo], rc_lo);
+    atomicAdd(&s_rc[p_hi], rc_hi);
     rc_lo = rc_hi = 0;
+    __syncthreads();
+    if (tid < MF_BM) {
+      w.rowc[slot * w.Mp + (long long)y * MF_BM + tid] = s_rc[tid];
+      s_rc[tid] = 0;
+    }
+    __syncthreads();
   };
   for (int b = 0; b < a.n_bands; ++b) {
     const int lo = max(a.band_cols[b], plo);
@@ -284,25 +289,16 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) di[(long long)i * (w.Mp / 2)] = word[i];
       }
-      // Tile maximum per index: over the 16 pairs of this wave (lanes with
-      // the same quarter), then over the four waves.
+      // Tile maximum per index: over the wave's 64 pairs.
+      int mine = 0;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        int m = mh[i];
-        m = max(m, __shfl_xor(m, 4, 64));
-        m = max(m, __shfl_xor(m, 8, 64));
-        m = max(m, __shfl_xor(m, 16, 64));
-        m = max(m, __shfl_xor(m, 32, 64));
-        if (lane < 4) s_mx[wave][8 * lane + i] = m;
+        const int m = wave_max_i(mh[i]);
+        if (lane == i) mine = m;
       }
-      __syncthreads();
-      if (tid < MF_DC) {
-        const int m = max(max(s_mx[0][tid], s_mx[1][tid]), max(s_mx[2][tid], s_mx[3][tid]));
-        w.maxh[((long long)g * w.RT + y) * w.Dp + d0 + tid] = (uint8_t)m;
-      }
+      if (lane < 8) w.maxh[((long long)g * w.RT + y) * w.Dp + dfirst + lane] = (uint8_t)mine;
       if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D))
         flush_rc((long long)g * a.n_chunks + d0 / a.chunk_d);
-      __syncthreads();  // s_mx is rewritten by the next group
     }
   }
   if (a.chunk_d <= 0) flush_rc((long long)g * w.n_parts + part);
