@@ -721,3 +721,45 @@ def test_tall_matrix_all_pairs_classification(table):
     cls = o.classify(A, o.OraclePlan(**okw))
     rows = cls["order"][sample_rows(M, cls["cuts"], per_rung=4, seed=3)]
     _check_group(gres, 0, A, B, okw, rows=rows)
+
+
+def test_error_paths_launch_nothing(table):
+    """Host-side rejections: a short workspace, a table priced for another
+    precision, a shape that differs from the plan, a missing permutation
+    for several rungs, ldc < N.  Each returns its status and leaves the
+    outputs as they were."""
+    rng = np.random.default_rng(121)
+    plan = scmp.scmp_plan_create(D=64, levels=(128, 64), fractions=(0.5, 0.5))
+    A = torch.from_numpy(rng.standard_normal((100, 64)).astype(np.float32)).cuda()
+    qA, sA, mA, _ = scmp.scmp_quantize_encode(table, plan, A)
+    _, _, perm, _ = scmp.scmp_classify_rows(plan, mA)
+    C = torch.full((1, 100, 100), 7.0, device="cuda")
+    need = scmp.scmp_matmul_workspace_bytes(table, plan, 1, 100, 100, "mfma")
+    short = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
+    lib = scmp.load()
+
+    def call(tab, pl, ws, permA, ldc):
+        return lib.scmp_matmul(tab.handle, pl.handle, scmp.SCMP_ALGO_MFMA, 1, 100, 100,
+                               scmp.ctypes.c_void_p(qA.data_ptr()), scmp.ctypes.c_void_p(sA.data_ptr()),
+                               None if permA is None else scmp.ctypes.c_void_p(permA.data_ptr()),
+                               scmp.ctypes.c_void_p(qA.data_ptr()), None, scmp.ctypes.c_void_p(sA.data_ptr()),
+                               None, scmp.ctypes.c_void_p(C.data_ptr()), ldc, 100 * 100,
+                               scmp.ctypes.c_void_p(ws.data_ptr()), ws.numel(), None)
+
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    assert call(table, plan, short, perm, 100) == scmp.SCMP_ERR_WORKSPACE
+    assert call(table, plan, ws, None, 100) == scmp.SCMP_ERR_ARG           # two rungs need the permutation
+    assert call(table, plan, ws, perm, 99) == scmp.SCMP_ERR_ARG             # ldc < N
+    t4 = scmp.scmp_build_sobol_table(4, 16)
+    try:
+        assert call(t4, plan, ws, perm, 100) == scmp.SCMP_ERR_PLAN_MISMATCH
+        with pytest.raises(scmp.ScmpError) as e:
+            scmp.scmp_quantize_encode(table, plan, A[:, :32])                 # cols != D
+        assert e.value.status == scmp.SCMP_ERR_PLAN_MISMATCH
+    finally:
+        t4.close()
+    torch.cuda.synchronize()
+    assert torch.all(C == 7.0)
+    assert call(table, plan, ws, perm, 100) == scmp.SCMP_OK                   # and the good call runs
+    torch.cuda.synchronize()
+    assert not torch.all(C == 7.0)
