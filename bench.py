@@ -375,11 +375,11 @@ def main():
                 "dense_paired_macs": paired,
                 "dense_paired_frac_of_int8_peak": 2.0 * paired / (kern_ms / 1e3) / 1e12 / PEAK_INT8_TOPS}
     # The events bracket one scmp_matmul call: the contraction kernel plus, on
-    # the matrix-core path, its two small encode kernels (k_prep_rows,
-    # k_prep_cols), which run first on the same stream.
+    # the matrix-core path, its encode kernel (k_prep: row and column
+    # encodes in one launch), which runs first on the same stream.
     roof["kernel"] = ("scmp_matmul = k_matmul_bitserial" if on_valu else
                       "scmp_matmul = k_pc_tables + k_matmul_gather" if args.algo == "gather"
-                      else "scmp_matmul = k_prep_rows + k_prep_cols + k_mfma")
+                      else "scmp_matmul = k_prep (row and column encode) + k_mfma")
     if ranged:
         roof["kernel"] = "two scmp_matmul_range calls (one per level), each " + roof["kernel"].split(" = ")[1]
     roof["traffic"] = profiled_traffic(w.name, args.algo, 2 if ranged else 1)

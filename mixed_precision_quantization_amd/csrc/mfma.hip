@@ -16,13 +16,13 @@
 //   count = n0 + s * sum_{k < hh} B'_k,
 // an exact int8 contraction over ceil(L/2) paired positions per d.
 //
-// Three kernels:
-//  k_prep_rows  per row tile: the window code 16 (2 hh + (s < 0)) (uint16,
+// Two launches (the encode passes share one launch, k_prep):
+//  prep_rows    per row tile: the window code 16 (2 hh + (s < 0)) (uint16,
 //               the byte offset of the row's A fragment in the pattern table)
 //               in bucket order, laid out [d][position], the tile's largest
 //               hh at each d, and the n0 sum of every row over every chunk
 //               ("A side at the row's L").
-//  k_prep_cols  per column tile: the byte offset of each B level's row in
+//  prep_cols    per column tile: the byte offset of each B level's row in
 //               the paired table (uint16), laid out [d][column].
 // Within every 64 positions (columns) the encode kernels store p and p + 32
 // side by side, so one 32-bit LDS read gives a lane both of its row
@@ -174,12 +174,12 @@ __device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out)
 // A wave then holds all 64 pairs of its indices: the tile maximum per index
 // is a wave reduction, and each index-major store covers 64 consecutive
 // pairs.  The block covers indices [part * part_len, ...) of one tile.
-__global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
+__device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, int bx) {
   __shared__ uint32_t s_lut[256];
   __shared__ int s_rows[MF_BM];
   __shared__ int s_rc[MF_BM];  // n0 sums of the tile's rows over the current chunk or part
   const int tid = threadIdx.x;
-  const int y = blockIdx.x, part = blockIdx.y, g = blockIdx.z;
+  const int y = bx, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
   locate_tile(a, y, MF_BM, k, pos0, nrows);
   k = tile_rung(a, g, k);
@@ -314,7 +314,7 @@ __global__ void __launch_bounds__(256) k_prep_rows(MatmulArgs a, MfmaWs w) {
 // grid (CT, n_parts, G), block 256: thread -> (column pair cp = tid / 4,
 // quarter q = tid % 4), indices [d0 + 8 q, d0 + 8 q + 8) of each group of
 // 32 in the block's part of the contraction axis.
-__global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
+__device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, int bx) {
   // Table row offset of each stored value x (entry x + 128).  Unipolar:
   // the magnitude's level row, with the sign of x in bit 0 (row offsets are
   // multiples of 16).
@@ -325,12 +325,12 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
     s_off[tid] = a.unipolar ? (uint32_t)(uni_level_of(x, a.P, a.q) * PT_STRIDE) | (x < 0 ? 1u : 0u)
                             : (uint32_t)(level_of(x, a.P, a.q) * PT_STRIDE);
   }
-  const int c0 = blockIdx.x * MF_BN, g = blockIdx.z;
+  const int c0 = bx * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
   // The contraction (launched after this kernel on the same stream) adds
   // its issued steps to this counter.
-  if (blockIdx.x == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
+  if (bx == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
     w.issued[0] = 0;
     w.issued[1] = 0;
     *w.work = 0;
@@ -339,7 +339,7 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
   const int col_lo = c0 + pair_lo(cp), col_hi = col_lo + 32;
   const int8_t* src_lo = a.qB + ((long long)g * a.N + (col_lo < a.N ? col_lo : 0)) * a.D;
   const int8_t* src_hi = a.qB + ((long long)g * a.N + (col_hi < a.N ? col_hi : 0)) * a.D;
-  const long long tile = (long long)g * w.CT + blockIdx.x;
+  const long long tile = (long long)g * w.CT + bx;
   const int ngrp = (int)(w.Dp / MF_DC);
   const uint32_t pad = a.unipolar ? 0u : (uint32_t)((a.P >> 1) * PT_STRIDE);
   __syncthreads();
@@ -359,11 +359,21 @@ __global__ void __launch_bounds__(256) k_prep_cols(MatmulArgs a, MfmaWs w) {
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst, cp)) = uint4{word[0], word[1], word[2], word[3]};
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst + 4, cp)) = uint4{word[4], word[5], word[6], word[7]};
     if (w.ubi) {
-      uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)blockIdx.x * 64 + cp;
+      uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)bx * 64 + cp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) di[(long long)i * (w.Np / 2)] = word[i];
     }
   }
+}
+
+// Both encode passes in one launch, so that they run side by side: blocks
+// x < RT encode row tile x, the others column tile x - RT (grid
+// (RT + CT, n_parts, G)).
+__global__ void __launch_bounds__(256) k_prep(MatmulArgs a, MfmaWs w) {
+  if ((int)blockIdx.x < w.RT)
+    prep_rows(a, w, (int)blockIdx.x);
+  else
+    prep_cols(a, w, (int)blockIdx.x - w.RT);
 }
 
 // ------------------------------------------------------------- main ----
@@ -1257,8 +1267,7 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
   if (a.launch == 1 && !pers_ok(a, w))
     return set_error(SCMP_ERR_UNSUPPORTED,
                      "the persistent launch needs a plan without chunk scales and one band");
-  hipLaunchKernelGGL(k_prep_rows, dim3(w.RT, w.n_parts, a.G), dim3(256), 0, st, a, w);
-  hipLaunchKernelGGL(k_prep_cols, dim3(w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
+  hipLaunchKernelGGL(k_prep, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   launch_main(a, w, dim3(w.CT, w.RT, a.G), st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("mfma launch: ") + hipGetErrorString(e));
