@@ -145,10 +145,15 @@ def test_chunk_d_must_be_a_multiple_of_32():
 def test_band_ladder_matches_oracle(tilt, levels, n_bands):
     D = 64 * 8 * 3
     chunks = D // 64
-    if max(levels) * (1 + tilt) > 256 and max(levels) < 256:
-        pytest.skip("would exceed the ceiling")
-    plan = scmp.scmp_plan_create(D=D, chunk_d=64, levels=levels, n_bands=n_bands, tilt=tilt)
     want = o.tilt_band_ladder(levels, n_bands, tilt, 256)
+    if np.any(want > 256):
+        # A tilted band above the ceiling: both sides reject it at startup.
+        _err(lambda: scmp.scmp_plan_create(D=D, chunk_d=64, levels=levels, n_bands=n_bands, tilt=tilt),
+             scmp.SCMP_ERR_CEILING)
+        with pytest.raises(ValueError, match="ceiling"):
+            o.check_band_ladder(want, o.band_columns(D, 64, [chunks // n_bands] * n_bands), levels, 256)
+        return
+    plan = scmp.scmp_plan_create(D=D, chunk_d=64, levels=levels, n_bands=n_bands, tilt=tilt)
     assert np.array_equal(np.asarray(plan.band_lengths()), want)
     cols = o.band_columns(D, 64, [chunks // n_bands] * n_bands)
     assert plan.band_columns() == cols.tolist()
