@@ -50,7 +50,24 @@ def parse():
                     choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle sample (0 = 2 per worker)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 256 MiB float32 buffer three times (the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE to bytes)")
     return ap.parse_args()
+
+
+def copy_calibration():
+    """Three plain device copies of 64 Mi float32 (256 MiB): under rocprofv3
+    --pmc FETCH_SIZE / WRITE_SIZE their counts per dispatch give the factor
+    from counter units to bytes."""
+    import torch
+    a = torch.empty(64 * 1024 * 1024, device="cuda")
+    b = torch.empty_like(a)
+    a.fill_(1.0)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": a.numel() * a.element_size(), "copies": 3}), flush=True)
 
 
 def sources_sha256():
@@ -195,6 +212,9 @@ def cpu_baseline(w, A, B, n_rows_req, seconds=12.0):
 
 def main():
     args = parse()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
               f"mode: each GPU would take its own rows (see DESIGN.md)", file=sys.stderr)
