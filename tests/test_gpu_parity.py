@@ -763,3 +763,23 @@ def test_error_paths_launch_nothing(table):
     assert call(table, plan, ws, perm, 100) == scmp.SCMP_OK                   # and the good call runs
     torch.cuda.synchronize()
     assert not torch.all(C == 7.0)
+
+
+def test_two_streams_give_the_sequential_results(table):
+    """Calls on distinct streams (default priority) with their own
+    workspaces run concurrently and give the same bits as one stream."""
+    rng = np.random.default_rng(131)
+    plan = scmp.scmp_plan_create(D=256, levels=(256, 128, 64), fractions=(0.2, 0.3, 0.5))
+    ins = [(torch.from_numpy(rng.standard_normal((600, 256)).astype(np.float32)).cuda(),
+            torch.from_numpy((0.02 * rng.standard_normal((500, 256))).astype(np.float32)).cuda()) for _ in range(2)]
+    ref = [scmp.sc_linear(table, plan, A, B)["C"].clone() for A, B in ins]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    for rep in range(3):
+        res = [None, None]  # every intermediate stays alive until the synchronisation
+        for i, (A, B) in enumerate(ins):
+            with torch.cuda.stream(streams[i]):
+                res[i] = scmp.sc_linear(table, plan, A, B, stream=streams[i])
+        torch.cuda.synchronize()
+        for i in range(2):
+            assert torch.equal(res[i]["C"], ref[i]), f"stream {i}, repetition {rep}"
