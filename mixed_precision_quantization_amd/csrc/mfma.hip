@@ -537,8 +537,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   __shared__ GatherTables s_tab;
   const uint8_t* const s_pt = s_tab.pt;
   const uint8_t* const s_pat = (const uint8_t*)s_tab.pat;
-  __shared__ __align__(16) uint32_t s_h[2][DC][BM / 2];  // stage code words, [index][row pair]
-  __shared__ __align__(16) uint32_t s_u[2][DC][BN / 2];  // [index][column pair]
+  // Stage code words, [pair][index]: rows of SW = DC + 2 words, so that the
+  // 32 pairs of a half-wave's 8-byte reads start on 32 distinct bank pairs
+  // (34 p mod 64 = 2 (17 p mod 32)).
+  constexpr int SW = DC + 2;
+  __shared__ __align__(16) uint32_t s_h[2][BM / 2][SW];  // [row pair][index]
+  __shared__ __align__(16) uint32_t s_u[2][BN / 2][SW];  // [column pair][index]
   // Stage schedule: the half-blocks past the stage's full levels in order,
   // then padding entries (a zero half-block), and the steps they take.
   constexpr int SCHED_N = DC * NLEV + 16;
@@ -571,7 +575,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   // wave and buffer; pieces t and t + 256 hold indices
   // 16 ((t / 32) % 2) + 4 ((t / 64) % 4) + [0, 4) of pairs t % 32 and
   // t % 32 + 32, into named registers so they stay in VGPRs) and stores them
-  // as the stage's [index][pair] words.
+  // as the stage's [pair][index] words (8-byte stores: rows are 8-byte
+  // aligned).
   int4 rh0, rh1, ru0, ru1;
   int rmx = 0;
   const int ngrp = (int)(w.Dp / MF_DC);
@@ -587,23 +592,22 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     if (tid < DC) rmx = w.maxh[((long long)g * w.RT + y) * w.Dp + d0 + tid];
   };
   auto store = [&](int bf) {
-    const int h0[4] = {rh0.x, rh0.y, rh0.z, rh0.w}, h1[4] = {rh1.x, rh1.y, rh1.z, rh1.w};
-    const int u0[4] = {ru0.x, ru0.y, ru0.z, ru0.w}, u1[4] = {ru1.x, ru1.y, ru1.z, ru1.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      s_h[bf][se + i][sp] = (uint32_t)h0[i];
-      s_h[bf][se + i][sp + 32] = (uint32_t)h1[i];
-      s_u[bf][se + i][sp] = (uint32_t)u0[i];
-      s_u[bf][se + i][sp + 32] = (uint32_t)u1[i];
-    }
+    *(uint2*)&s_h[bf][sp][se] = uint2{(uint32_t)rh0.x, (uint32_t)rh0.y};
+    *(uint2*)&s_h[bf][sp][se + 2] = uint2{(uint32_t)rh0.z, (uint32_t)rh0.w};
+    *(uint2*)&s_h[bf][sp + 32][se] = uint2{(uint32_t)rh1.x, (uint32_t)rh1.y};
+    *(uint2*)&s_h[bf][sp + 32][se + 2] = uint2{(uint32_t)rh1.z, (uint32_t)rh1.w};
+    *(uint2*)&s_u[bf][sp][se] = uint2{(uint32_t)ru0.x, (uint32_t)ru0.y};
+    *(uint2*)&s_u[bf][sp][se + 2] = uint2{(uint32_t)ru0.z, (uint32_t)ru0.w};
+    *(uint2*)&s_u[bf][sp + 32][se] = uint2{(uint32_t)ru1.x, (uint32_t)ru1.y};
+    *(uint2*)&s_u[bf][sp + 32][se + 2] = uint2{(uint32_t)ru1.z, (uint32_t)ru1.w};
     if (tid < 64) {
       // Wave 0 lists the stage's half-blocks: index d (lane d < DC holds its
       // tile maximum rmx) needs positions [16 j, 16 j + 16) for every
       // j < ceil(rmx / 16); the leading levels every index needs are swept
       // without a list, the rest are listed level by level, indices in
-      // order within a level.  Entry: d * 256 + kk (the byte offset of index
-      // d's words in a stage row, and the first paired position kk = 16 j;
-      // UNI: j itself).
+      // order within a level.  Entry: (d << 10) | kk (4 d, the byte offset
+      // of index d's word in a stage row, in bits 8-14, and the first paired
+      // position kk = 16 j; UNI: j itself).
       const int m = tid < DC ? rmx : 0;
       int full = 0;
       while (full < NLEV && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
@@ -614,7 +618,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (m > 16 * j) {
           const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((unsigned)(bal >> 32),
                                                                  __builtin_amdgcn_mbcnt_lo((unsigned)bal, 0u));
-          s_sched[bf][pos] = (uint16_t)(tid * 256 + (UNI ? j : 16 * j));
+          s_sched[bf][pos] = (uint16_t)((tid << 10) | (UNI ? j : 16 * j));
         }
         base += __builtin_popcountll(bal);
       }
@@ -666,8 +670,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // windows nest inside it; past a row's own window its A nibbles are
         // zero).  Any four half-blocks may share a step: lanes 0-31 take
         // the first two (X, Y), lanes 32-63 the other two.
-        const char* hbase = (const char*)&s_h[buf][0][wr * 32 + l32];
-        const char* ubase = (const char*)&s_u[buf][0][wc * 32 + l32];
+        const char* hbase = (const char*)&s_h[buf][wr * 32 + l32][0];
+        const char* ubase = (const char*)&s_u[buf][wc * 32 + l32][0];
         const uint32_t* sched = (const uint32_t*)&s_sched[buf][0] + hf;  // entry pairs
         const int n = s_nsteps[buf];
         const int full = s_full[buf];
@@ -677,9 +681,15 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           uint32_t hx, ux, hy, uy, e;
         };
         auto item = [&](uint32_t e) __attribute__((always_inline)) {
-          const uint32_t ox = e & 0x1f00u, oy = (e >> 16) & 0x1f00u;
+          const uint32_t ox = (e >> 8) & 0x7cu, oy = (e >> 24) & 0x7cu;
           return Item{*(const uint32_t*)(hbase + ox), *(const uint32_t*)(ubase + ox),
                       *(const uint32_t*)(hbase + oy), *(const uint32_t*)(ubase + oy), e};
+        };
+        // X and Y on adjacent indices (X even): one 8-byte read per buffer.
+        auto item2 = [&](uint32_t e) __attribute__((always_inline)) {
+          const uint32_t ox = (e >> 8) & 0x7cu;
+          const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
+          return Item{h2.x, u2.x, h2.y, u2.y, e};
         };
         auto frags = [&](const Item& c) __attribute__((always_inline)) {
           if (UNI)
@@ -689,26 +699,27 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         };
         // Software-pipelined sweep over steps 0 .. cnt - 1, ent(s) giving the
         // lane's entry pair of step s (any entry past the end is a zero
-        // half-block): while step s's MFMAs run, the fragments of step s + 1,
-        // the codes of step s + 2 and the entries of step s + 3 are in flight
-        // (LDS reads complete in order, so each is read a step ahead of the
-        // reads it addresses).  Two fragment sets are used in turn.
-        auto sweep = [&](int cnt, auto&& ent) __attribute__((always_inline)) {
+        // half-block) and itm its codes: while step s's MFMAs run, the
+        // fragments of step s + 1, the codes of step s + 2 and the entries of
+        // step s + 3 are in flight (LDS reads complete in order, so each is
+        // read a step ahead of the reads it addresses).  Two fragment sets
+        // are used in turn.
+        auto sweep = [&](int cnt, auto&& ent, auto&& itm) __attribute__((always_inline)) {
           uint32_t e2 = ent(2);
-          const Item c0 = item(ent(0));
-          Item c1 = item(ent(1));
+          const Item c0 = itm(ent(0));
+          Item c1 = itm(ent(1));
           Frag fa = frags(c0), fb;
           int st = 0;
           for (; st + 2 < cnt; st += 2) {
             uint32_t e3 = ent(st + 3);
-            Item c2 = item(e2);
+            Item c2 = itm(e2);
             fb = frags(c1);
             e2 = e3;
             c1 = c2;
             __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
             mma_step(acc, fa);
             e3 = ent(st + 4);
-            c2 = item(e2);
+            c2 = itm(e2);
             fa = frags(c1);
             e2 = e3;
             c1 = c2;
@@ -721,19 +732,22 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           mma_step(acc, fa);
           if (cnt - st == 2) mma_step(acc, fb);
         };
-        // Full levels: step 8 j + m takes level j of indices 16 hf + m (X)
-        // and 16 hf + 8 + m (Y).  Past the last level the entries fall on
+        // Full levels: step 8 j + m takes level j of indices 16 hf + 2 m (X)
+        // and 16 hf + 2 m + 1 (Y).  Past the last level the entries fall on
         // level full <= NLEV (position <= 16 NLEV <= 256, inside the table
         // rows): read, never used.
         if (full > 0)
-          sweep(8 * full, [&](int st) {
-            const uint32_t j = (uint32_t)(st >> 3) & 31u, m = (uint32_t)(st & 7);
-            const uint32_t dx = 16u * hf + m, dy = dx + 8u;
-            const uint32_t kj = UNI ? j : 16u * j;
-            return (dx * 256u + kj) | ((dy * 256u + kj) << 16);
-          });
+          sweep(
+              8 * full,
+              [&](int st) {
+                const uint32_t j = (uint32_t)(st >> 3) & 31u, m = (uint32_t)(st & 7);
+                const uint32_t dx = 16u * hf + 2u * m, dy = dx + 1u;
+                const uint32_t kj = UNI ? j : 16u * j;
+                return ((dx << 10) | kj) | (((dy << 10) | kj) << 16);
+              },
+              item2);
         // The rest from the stage's list.
-        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; });
+        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; }, item);
         if (blockIdx.x == 0 && tid == 0) issued += n + 8 * full;
       }
       const int cend = chunk_end(a, d0);
