@@ -793,6 +793,87 @@ def test_kband_parent_equivalence_and_non_degeneracy():
     assert rel > 1e-4
 
 
+def test_kband_hand_example_p3_golden():
+    # A two-band product worked out by hand (tests/golden/kband_hand_p3.json,
+    # K-band pull request "How the banding works"): band 0 runs L = 8 and
+    # band 1 runs L = 4; swapping the two lengths changes the band counts
+    # and the decoded value, so a reversed band -> length mapping fails.
+    g = json.load(open(os.path.join(GOLDEN, "kband_hand_p3.json")))
+    p = g["p"]
+    A = np.asarray([g["A_row"]], dtype=np.float32)
+    B = np.asarray([g["B_row"]], dtype=np.float32)
+
+    def run(band_L):
+        plan = o.OraclePlan(p=p, Lmax=1 << p, D=g["D"], chunk_d=g["chunk_d"], levels=tuple(g["levels"]),
+                            n_bands=len(g["band_chunks"]), band_chunks=tuple(g["band_chunks"]),
+                            band_L=np.asarray(band_L))
+        return o.rows_product(A, np.zeros(1, dtype=np.int64), B, plan)
+
+    r = run(g["band_L"])
+    assert r["x_a"][0].tolist() == g["x_a"] and r["s_a"][0].tolist() == g["s_a"]
+    assert r["x_b"][0].tolist() == g["x_b"] and r["s_b"][0].tolist() == g["s_b"]
+    assert o.bipolar_level(r["x_a"][0], p).tolist() == g["u_a"]
+    assert o.bipolar_level(r["x_b"][0], p).tolist() == g["u_b"]
+    assert r["counts"][0, 0].tolist() == g["counts_per_chunk"]
+    assert r["band_counts"][0, 0].tolist() == g["band_counts"]
+    assert r["L"][0].tolist() == g["L_per_chunk"]
+    assert r["C"][0, 0] == g["C"]
+    rev = run(g["reversed_band_L"])
+    assert rev["band_counts"][0, 0].tolist() == g["reversed_band_counts"]
+    assert rev["C"][0, 0] == g["reversed_C"]
+
+
+# Band layouts written out by hand: band columns, the band owning each
+# 64-column chunk, and L[b][k] for the ladder (the tilt-0.25 values are the
+# straight-line tilt of 192 / 128 / 64 over four bands, K-band pull request
+# "Tooling"; the ragged case is an explicit table within budget).
+_KBAND_CASES = {
+    "tilt_equal_bands": dict(
+        D=256, levels=(192, 128, 64), n_bands=4, band_chunks=None, tilt=0.25, band_L=None,
+        cols=[(0, 64), (64, 128), (128, 192), (192, 256)], owner=[0, 1, 2, 3],
+        L=[[144, 96, 48], [176, 117, 59], [208, 139, 69], [240, 160, 80]]),
+    "ragged_uneven_bands": dict(
+        D=150, levels=(128, 96, 60), n_bands=2, band_chunks=(2, 1), tilt=0.0,
+        band_L=[[120, 90, 40], [128, 96, 64]],
+        cols=[(0, 128), (128, 150)], owner=[0, 0, 1],
+        L=[[120, 90, 40], [128, 96, 64]]),
+}
+
+
+@pytest.mark.parametrize("case", sorted(_KBAND_CASES))
+def test_kband_each_band_is_the_uniform_product_over_its_own_columns(case):
+    # K-band pull request, "How the banding works": band b of the
+    # contraction axis runs rung k at L[b][k], and the band partial sums add.
+    # Each band's partial count must equal a uniform-length product over
+    # exactly that band's columns at its own L[b][k] (the uniform product is
+    # pinned by the closed-form and unbiasedness pins above), every chunk
+    # must carry its owner band's length, and the mirrored table (band b at
+    # the lengths of band B-1-b) must give different counts.
+    c = _KBAND_CASES[case]
+    rng = np.random.default_rng(17)
+    D = c["D"]
+    A = rng.standard_normal((9, D)).astype(np.float32)
+    A[:, 5] *= 20.0
+    B = (0.02 * rng.standard_normal((7, D))).astype(np.float32)
+    common = dict(D=D, chunk_d=64, levels=c["levels"], n_bands=c["n_bands"], band_chunks=c["band_chunks"])
+    plan = o.OraclePlan(tilt=c["tilt"], band_L=None if c["band_L"] is None else np.asarray(c["band_L"]), **common)
+    out = o.sc_matmul_rows(A, B, plan)
+    assert plan.ladder().tolist() == c["L"]
+    cols, owner = plan.bands()
+    assert [(int(cols[b]), int(cols[b + 1])) for b in range(c["n_bands"])] == c["cols"]
+    assert owner.tolist() == c["owner"]
+    mirrored = o.sc_matmul_rows(A, B, o.OraclePlan(band_L=np.asarray(c["L"])[::-1].copy(), **common))
+    assert set(out["rung"].tolist()) == {0, 1, 2}
+    for i in range(A.shape[0]):
+        k = int(out["rung"][i])
+        assert out["L"][i].tolist() == [c["L"][b][k] for b in c["owner"]]
+        for b, (c0, c1) in enumerate(c["cols"]):
+            uni = o.rows_product(A[i:i + 1, c0:c1], np.zeros(1, dtype=np.int64), B[:, c0:c1],
+                                 o.OraclePlan(D=c1 - c0, chunk_d=64, levels=(c["L"][b][k],)))
+            assert np.array_equal(out["band_counts"][i, :, b], uni["counts"][0].sum(axis=1)), (i, b)
+    assert not np.array_equal(out["band_counts"], mirrored["band_counts"])
+
+
 def test_mp_rows_use_their_rung_length():
     # Each row's count equals a uniform-L run at that row's rung length.
     A, B = _kband_inputs()
