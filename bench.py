@@ -29,7 +29,6 @@ METRIC = "SC bit-MACs/s (M*N*D*L_eff) + % of int-VALU/HBM roofline, ViT-L fc1 MP
 DEFAULT_WORKLOAD = "vitl_fc1_mp"
 
 # MI355X published peaks used for the roofline fractions.
-PEAK_INT8_TOPS = 5000.0          # dense int8 MFMA, 5.0 POP/s
 PEAK_FP4_TOPS = 10100.0          # dense fp4 MFMA, 10.1 PFLOP/s
 PEAK_HBM_GBS = 8000.0            # HBM3E, 8 TB/s
 # Vector-ALU bit-serial bound: 256 CUs x 4 SIMDs x 16 lanes x 2.4 GHz int32
@@ -137,17 +136,30 @@ def work_per_step(plan, M, N, G, heads=0):
     return bitmacs * N * G, paired * N * G
 
 
-def cpu_baseline(w, A, B, n_rows_req, seconds=12.0):
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(w, A, B, n_rows_req, bitmacs_per_step, seconds=12.0):
     """Time the CPU oracle, as it stands, on a bounded sample of output rows
     of the same workload (all columns, all of D), one worker process per
-    core.  Rows are taken batch by batch (per-row rungs: sampled rows of
-    every rung; per-group workloads: whole groups in order; per-head rungs:
-    whole images) until about ``seconds`` of wall time have been spent, or
-    ``n_rows_req`` rows when that is given."""
+    core (at most 16).  Rows are taken batch by batch (per-row rungs:
+    sampled rows of every rung; per-group workloads: whole groups in order;
+    per-head rungs: whole images) until about ``seconds`` of wall time have
+    been spent, or ``n_rows_req`` rows when that is given.  A fixed slice
+    (the first sorted row of every rung; group 0; image 0's first head) is
+    also timed in this process alone, for the one-core rate."""
     import numpy as np
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
     import oracle as o
-    from _oracle_pool import OraclePool, workers
+    from oracle.pool import OraclePool, workers
     from mixed_precision_quantization_amd.workloads import sample_rows
 
     okw = dict(p=8, Lmax=256, D=w.D, chunk_d=w.chunk_d, levels=w.levels, fractions=w.fractions,
@@ -182,6 +194,17 @@ def cpu_baseline(w, A, B, n_rows_req, seconds=12.0):
                 rows = cls["order"][pos]
                 yield [(A3[0][rows], cls["rung"][rows], B3[0])], f"{len(rows)} sampled rows"
 
+    def one_core_slice():
+        if heads:
+            hr = o.head_rungs(A3[:heads], oplan)
+            return A3[0], np.full(w.M, int(hr["rung"][0])), B3[0], f"image 0 head 0 ({w.M} query rows)"
+        cls = o.classify(A3[0], oplan)
+        if A3.shape[0] > 1:
+            return A3[0], cls["rung"], B3[0], f"group 0 (all {w.M} rows)"
+        first = [int(c) for c in cls["cuts"][:-1] if c < w.M]
+        rows = cls["order"][first]
+        return A3[0][rows], cls["rung"][rows], B3[0], f"the first sorted row of each of {len(rows)} rungs"
+
     t0 = time.perf_counter()
     bitmacs = 0
     rows_done = 0
@@ -195,18 +218,32 @@ def cpu_baseline(w, A, B, n_rows_req, seconds=12.0):
             if (n_rows_req and rows_done >= n_rows_req) or time.perf_counter() - t0 >= seconds:
                 break
     dt = time.perf_counter() - t0
+    rate = bitmacs / dt
+
+    A1, r1, B1, what1 = one_core_slice()
+    t1 = time.perf_counter()
+    out1 = o.rows_product(A1, r1, B1, oplan)
+    dt1 = time.perf_counter() - t1
+    bm1 = int(np.sum(out1["L"] * widths)) * N
+
     kind = ("query rows of whole images, each head at its rung" if heads else
             "rows of whole groups" if A3.shape[0] > 1 else
             "output rows of every rung (sorted-position edges plus seeded picks)")
     return {
-        "value": bitmacs / dt,
+        "value": rate,
         "unit": "bit-MAC/s",
         "cores": nw,
         "kind": "oracle",
         "sample": f"{rows_done} {kind} in {len(parts)} batches ({parts[0]}, ...) x all {N} columns x all "
                   f"D={w.D}, materialised C-BSG streams, {bitmacs:.3e} bit-MACs in {dt:.1f} s wall incl. "
-                  f"classification and quantisation",
+                  f"classification and quantisation, {nw} worker processes",
         "seconds": dt,
+        "host_cpu_count": os.cpu_count(),
+        "cpu_model": cpu_model(),
+        "one_core": {"value": bm1 / dt1, "unit": "bit-MAC/s", "seconds": dt1, "bit_macs": bm1,
+                     "sample": f"{what1} x all {N} columns x all D={w.D}, one process"},
+        "full_config_seconds_extrapolated": bitmacs_per_step / rate,
+        "full_config_seconds_extrapolated_one_core": bitmacs_per_step / (bm1 / dt1),
     }
 
 
@@ -371,29 +408,33 @@ def main():
                 "unit": "T bit-MAC/s", "frac": achieved / (PEAK_VALU_BITMACS / 1e12), "traffic": None,
                 "work": "bit-MACs (D * L per output element), two VALU ops per 32"}
     else:
-        # The windowed contraction issues, per 128 x 128 tile and contraction
-        # index, only the steps some row of the tile needs, on the int8 or
-        # the fp4 matrix cores; the library counts both exactly.  The peak is
-        # the mix's: the time both parts take at their dense peaks.
+        # The windowed contraction: per output element and contraction index
+        # the exact count needs the row's window of paired positions (the
+        # useful multiply-accumulates, recorded by the library's encode
+        # pass); the kernel issues, per 128 x 128 tile and index, every
+        # 16-position block up to the tile's largest window.  Both are fp4
+        # (e2m1) MFMA work, priced at the dense fp4 peak.
         if ranged:
-            parts = [scmp.scmp_matmul_issued_macs(table, plan, G, M, n, wsk[k], algo=args.algo, stream=stream,
-                                                  split=True) for k, n in enumerate(n_lv) if n]
-            issued, issued_fp4 = sum(p[0] for p in parts), sum(p[1] for p in parts)
+            issued = sum(scmp.scmp_matmul_issued_macs(table, plan, G, M, n, wsk[k], algo=args.algo, stream=stream)
+                         for k, n in enumerate(n_lv) if n)
+            window = sum(scmp.scmp_matmul_window_macs(table, plan, G, M, n, wsk[k], algo=args.algo, stream=stream)
+                         for k, n in enumerate(n_lv) if n)
         else:
-            issued, issued_fp4 = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo,
-                                                              stream=stream, split=True)
-        issued_i8 = issued - issued_fp4
-        t_peak = 2.0 * issued_i8 / (PEAK_INT8_TOPS * 1e12) + 2.0 * issued_fp4 / (PEAK_FP4_TOPS * 1e12)
-        achieved = 2.0 * issued / (kern_ms / 1e3) / 1e12
-        peak = 2.0 * issued / t_peak / 1e12 if t_peak > 0 else PEAK_INT8_TOPS
-        roof = {"bound": "mfma", "achieved": achieved, "peak": peak, "unit": "TOP/s",
-                "frac": achieved / peak, "traffic": None,
-                "work": "MACs issued per launch x 2: int8 (v_mfma_i32_32x32x32_i8) and fp4 "
-                        "(v_mfma_scale_f32_32x32x64_f8f6f4) steps the data needs; peak = the mix at the "
-                        "dense int8 5.0 and fp4 10.1 POP/s peaks",
-                "issued_macs": issued, "issued_macs_int8": issued_i8, "issued_macs_fp4": issued_fp4,
-                "dense_paired_macs": paired,
-                "dense_paired_frac_of_int8_peak": 2.0 * paired / (kern_ms / 1e3) / 1e12 / PEAK_INT8_TOPS}
+            issued = scmp.scmp_matmul_issued_macs(table, plan, G, M, N, ws, algo=args.algo, stream=stream)
+            window = scmp.scmp_matmul_window_macs(table, plan, G, M, N, ws, algo=args.algo, stream=stream)
+        achieved = 2.0 * window / (kern_ms / 1e3) / 1e12
+        issued_rate = 2.0 * issued / (kern_ms / 1e3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_FP4_TOPS, "unit": "TFLOP/s",
+                "frac": achieved / PEAK_FP4_TOPS, "traffic": None,
+                "work": "window MACs x 2 per launch: per output element and contraction index the "
+                        "half-window ceil(|n1 - n0| / 2) of paired positions the exact count needs "
+                        "(unipolar: the prefix n1), summed by the library; priced at the dense fp4 "
+                        "(e2m1) MFMA peak, the instruction the kernel runs",
+                "window_macs": window, "issued_macs": issued,
+                "issued_frac": issued_rate / PEAK_FP4_TOPS,
+                "padding_frac": 1.0 - window / issued if issued else None,
+                "issued_work": "every 16-position block up to the tile's largest window at each index, "
+                               "per 128 x 128 tile (what the matrix cores execute)"}
     # The events bracket one scmp_matmul call: the contraction kernel plus, on
     # the matrix-core path, its encode kernel (k_prep: row and column
     # encodes in one launch), which runs first on the same stream.
@@ -407,18 +448,22 @@ def main():
                               "kernel per timed call, scaled by a plain copy); null when the library sources "
                               "differ from the profiled ones")
     roof["kernel_ms"] = kern_ms
+    # HBM: the call's algorithmic bytes, the int8 operands read once and the
+    # float32 output written once.
+    alg_bytes = G * (M + N) * D + 4 * G * M * N
+    roof["algorithmic_bytes"] = alg_bytes
+    roof["hbm_frac"] = alg_bytes / (kern_ms / 1e3) / (PEAK_HBM_GBS * 1e9)
     roof["bitmacs_per_s_kernel"] = bitmacs / (kern_ms / 1e3)
-    roof["valu_bitserial_frac"] = bitmacs / (kern_ms / 1e3) / PEAK_VALU_BITMACS
 
-    # Arithmetic of the contraction: integer stream counts from int8 codes,
-    # on int8 or e2m1 (fp4, exact for these operands) matrix-core operands.
+    # Arithmetic of the contraction: integer stream counts, on e2m1 (fp4,
+    # exact for these operands) matrix-core operands with float32
+    # accumulators, on 32-bit words (bit-serial) or 16-bit table entries.
     if on_valu:
         dtype = "u32 bit-ops"
     elif args.algo == "gather":
         dtype = "u16 table lookups"
     else:
-        dtype = {(True, False): "i8", (False, True): "fp4(e2m1)", (True, True): "i8+fp4(e2m1)"}.get(
-            (roof["issued_macs_int8"] > 0, roof["issued_macs_fp4"] > 0), "i8")
+        dtype = "fp4(e2m1)"
     out = {
         "metric": METRIC,
         "value": value,
@@ -446,7 +491,7 @@ def main():
         "git": git_sha(),
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(w, A_np, B_np, args.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(w, A_np, B_np, args.cpu_rows, bitmacs)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -79,11 +79,15 @@ typedef enum { SCMP_OP_LINEAR = 0, SCMP_OP_QK = 1, SCMP_OP_AV = 2 } scmp_op;
 typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
 
 /* Contraction kernel.  All give bit-identical counts.
- *  AUTO/MFMA: windowed ternary x paired-binary contraction on the int8
- *             matrix cores (v_mfma_i32_32x32x32_i8); the launch form is
- *             chosen by size (persistent when the plan allows it and there
- *             are several output tiles per block, one block per tile
- *             otherwise).
+ *  AUTO/MFMA: windowed ternary x paired-binary contraction on the fp4
+ *             matrix cores (v_mfma_scale_f32_32x32x64_f8f6f4, e2m1 operands
+ *             {-1, 0, +1} and {0, 1, 2} at unit scales, float32
+ *             accumulators that hold the integer counts exactly while
+ *             scmp_plan_info.mfma_exact is 1); the launch form is chosen by
+ *             size (persistent when the plan allows it and there are several
+ *             output tiles per block, one block per tile otherwise).  When
+ *             mfma_exact is 0, AUTO runs GATHER (bipolar) or BITSERIAL
+ *             (unipolar) instead and the MFMA forms return UNSUPPORTED.
  *  MFMA_PERSISTENT: the matrix-core path as a persistent grid taking
  *             output tiles from a work counter; bipolar plans without chunk
  *             scales and with one band only (UNSUPPORTED otherwise).
@@ -136,6 +140,12 @@ typedef struct {
 
 typedef struct {
   int op, p, Lmax, D, chunk_d, n_chunks, n_rungs, n_bands, ceiling, mode, range_mp, range_group;
+  /* 1 when the matrix-core forms hold this plan's counts exactly: they
+   * accumulate each segment (D, or one chunk of chunk_d indices) in float32,
+   * one index adding at most L + 1 in magnitude, so the plan needs
+   * segment * (longest L + 1) < 2^24.  When 0, AUTO runs GATHER (bipolar)
+   * or BITSERIAL (unipolar) and the MFMA forms return UNSUPPORTED. */
+  int mfma_exact;
 } scmp_plan_info;
 
 /* Name of a status code (static string). */
@@ -366,14 +376,29 @@ int scmp_matmul_range(scmp_table_t table, scmp_plan_t plan, int algo, int level,
 /* Diagnostic: synchronise `stream` and return the multiply-accumulates the
  * last MFMA-path contraction with this workspace (scmp_matmul or one of
  * its variants above) issued on the matrix cores
- * (every step of every 128 x 128 tile: four MFMAs per wave, 32 x 32 x 32
- * int8 or 32 x 32 x 64 fp4 MACs each).  The count follows from the data: a
- * step is issued when some row of the tile needs it.  *macs receives all of
- * them; fp4_macs (may be NULL) receives the fp4 part.  Errors: ARG,
+ * (every step of every 128 x 128 tile: four MFMAs per wave, 32 x 32 x 64
+ * fp4 MACs each).  The count follows from the data: a step is issued when
+ * some row of the tile needs it, up to the tile's largest window at that
+ * index, in blocks of 16 paired positions.  *macs receives all of them;
+ * fp4_macs (may be NULL) receives the same number (every step is fp4).  Errors: ARG,
  * UNSUPPORTED (BITSERIAL), WORKSPACE, HIP. */
 int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
                             const void* workspace_dev, size_t workspace_bytes, unsigned long long* macs,
                             unsigned long long* fp4_macs, void* stream);
+
+/* Diagnostic: synchronise `stream` and return the multiply-accumulates
+ * the exact count needed in the last MFMA-path contraction with this
+ * workspace: per output element and contraction index, the bipolar
+ * half-window ceil(|n1 - n0| / 2) of paired positions at the row's length
+ * (a unipolar plan: the prefix n1), summed over every row, index and band
+ * and multiplied by N ([PAYN] Key design 3: the SC cost follows the stream
+ * lengths; with the paired windows it follows the windows).  Padding to the
+ * tile's largest window and to 16-position blocks is not counted (see
+ * scmp_matmul_issued_macs).  Errors: ARG, UNSUPPORTED (BITSERIAL, GATHER),
+ * WORKSPACE (no matrix-core call recorded in it), HIP. */
+int scmp_matmul_window_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                            const void* workspace_dev, size_t workspace_bytes, unsigned long long* macs,
+                            void* stream);
 
 /* Decode counts produced without chunk scales ([PAYN] Key design 1, decode
  * equation): C_ij = s^A_i s^B_j q^2 (2 count_ij - L_i D) / L_i with

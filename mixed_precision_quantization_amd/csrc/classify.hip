@@ -18,14 +18,13 @@
 
 namespace scmp {
 
-__device__ int g_classify_flags;
-
 struct ClassifyArgs {
   const float* metric;
   float* ghat;
   uint8_t* rung;
   int32_t* perm;
   float* thr;
+  int* flag;  // this stream's error flag word
   int M, n_rungs;
   int cuts[SCMP_MAX_RUNGS + 1];
 };
@@ -68,7 +67,7 @@ __global__ void __launch_bounds__(512) k_classify(ClassifyArgs a) {
   mx = red[0];
 #pragma unroll
   for (int w = 1; w < CL_WAVES; ++w) mx = fmaxf(mx, red[w]);
-  if (bad && blockIdx.x == 0) atomicOr(&g_classify_flags, 1);
+  if (bad && blockIdx.x == 0) atomicOr(a.flag, 1);
 
   const int i = blockIdx.x * CL_ROWS + lane;
   const float gi = i < a.M ? (mx == 0.0f ? 0.0f : m[i] / mx) : 0.0f;
@@ -171,7 +170,7 @@ __global__ void __launch_bounds__(512) k_classify_bucket(ClassifyArgs a, int set
   mx = s_red[0];
 #pragma unroll
   for (int w = 1; w < CL_WAVES; ++w) mx = fmaxf(mx, s_red[w]);
-  if (bad && blockIdx.x == 0) atomicOr(&g_classify_flags, 1);
+  if (bad && blockIdx.x == 0) atomicOr(a.flag, 1);
 
 #pragma unroll
   for (int u = 0; u < CB_PER; ++u) {
@@ -277,19 +276,6 @@ __global__ void __launch_bounds__(256) k_group_max(const float* in, int M, float
   if (tid == 0) out[g] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
-int read_clear_classify_flags(hipStream_t st, int* flags) {
-  int v = 0, zero = 0;
-  hipError_t e =
-      hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_classify_flags), sizeof(int), 0, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e == hipSuccess)
-    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_classify_flags), &zero, sizeof(int), 0, hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("flag readback: ") + hipGetErrorString(e));
-  *flags |= v;
-  return SCMP_OK;
-}
-
 }  // namespace scmp
 
 using scmp::set_error;
@@ -313,6 +299,8 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   a.n_rungs = P.n_rungs;
   scmp::row_cuts(P, M, a.cuts);
   hipStream_t st = (hipStream_t)stream;
+  const int fs = scmp::stream_flag(st, &a.flag);
+  if (fs != SCMP_OK) return fs;
   const int tiles = (M + scmp::CL_ROWS - 1) / scmp::CL_ROWS;
   if (M <= scmp::CB_MAXM) {
     // Large groups rank two sets of rows per block: every block repeats the

@@ -29,6 +29,20 @@ void row_cuts(const Plan& plan, int M, int* cuts);
 int set_error(int status, const std::string& msg);
 void clear_error();
 
+// Whether the matrix-core kernels hold this plan's counts exactly: they
+// keep each accumulation segment (the whole axis, or one chunk of chunk_d
+// indices) in float32 accumulators, and one index adds at most L + 1 in
+// magnitude (a bipolar half-window of ceil(L / 2) pair sums of at most 2; a
+// unipolar prefix of at most L ones), so every partial sum is an exact
+// integer while segment * (longest L + 1) < 2^24.
+bool mfma_counts_exact(const Plan& plan);
+
+// Device address of the error flag word of `st` on the current device
+// (flags.hip); kernels OR bit 0 into it on a non-finite input.
+int stream_flag(void* st, int** out);
+// Read, clear and OR into *flags the flag word of `st` (synchronises st).
+int read_clear_stream_flags(void* st, int* flags);
+
 inline int qmax(int p) { return (1 << (p - 1)) - 1; }
 
 }  // namespace scmp

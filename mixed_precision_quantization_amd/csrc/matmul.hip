@@ -15,9 +15,6 @@
 
 namespace scmp {
 
-int read_clear_quant_flags(hipStream_t st, int* flags);
-int read_clear_classify_flags(hipStream_t st, int* flags);
-
 void fill_tiles(MatmulArgs& a, const Plan& P, int BM) {
   row_cuts(P, a.M, a.cuts);
   a.tile_start[0] = 0;
@@ -55,6 +52,16 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M
   a.P = 1 << P.p;
   a.Wl = table->Wl;
   a.Lmax = table->Lmax;
+  // Segments too long for exact float32 accumulation leave AUTO to an
+  // integer path and reject the matrix-core forms (mfma_counts_exact).
+  if ((algo == SCMP_ALGO_AUTO || algo == SCMP_ALGO_MFMA || algo == SCMP_ALGO_MFMA_PERSISTENT ||
+       algo == SCMP_ALGO_MFMA_ONEPASS) && !mfma_counts_exact(P)) {
+    if (algo != SCMP_ALGO_AUTO)
+      return set_error(SCMP_ERR_UNSUPPORTED,
+                       "the matrix-core accumulators hold counts exactly only while the accumulation segment "
+                       "(D, or chunk_d) times (longest L + 1) stays below 2^24; use BITSERIAL or GATHER");
+    algo = P.mode == SCMP_MODE_UNIPOLAR ? SCMP_ALGO_BITSERIAL : SCMP_ALGO_GATHER;
+  }
   a.launch = algo == SCMP_ALGO_MFMA_PERSISTENT ? 1 : (algo == SCMP_ALGO_MFMA_ONEPASS ? 2 : 0);
   const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
   fill_tiles(a, P, bitserial ? 64 : 128);
@@ -269,6 +276,21 @@ int scmp_matmul_issued_macs(scmp_table_t table, scmp_plan_t plan, int algo, int 
   return scmp::mfma_issued_macs(a, workspace, workspace_bytes, (hipStream_t)stream, macs, fp4_macs);
 }
 
+int scmp_matmul_window_macs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                            const void* workspace, size_t workspace_bytes, unsigned long long* macs,
+                            void* stream) {
+  scmp::clear_error();
+  if (!macs) return set_error(SCMP_ERR_ARG, "macs is NULL");
+  *macs = 0;
+  scmp::MatmulArgs a;
+  int st0 = scmp::prepare(table, plan, algo, G, M, N, a);
+  if (st0 != SCMP_OK) return st0;
+  if (algo == SCMP_ALGO_BITSERIAL || algo == SCMP_ALGO_GATHER)
+    return set_error(SCMP_ERR_UNSUPPORTED, "only the MFMA path records its windows");
+  if ((long long)G * M * N == 0) return SCMP_OK;
+  return scmp::mfma_window_macs(a, workspace, workspace_bytes, (hipStream_t)stream, macs);
+}
+
 int scmp_decode(scmp_plan_t plan, int G, int M, int N, const int32_t* counts, const float* sA, const float* sB,
                 const uint8_t* rung, float* C, int64_t ldc, int64_t batch_stride_c, void* stream) {
   scmp::clear_error();
@@ -308,9 +330,7 @@ int scmp_error_flags(void* stream, int* flags_out) {
   if (!flags_out) return set_error(SCMP_ERR_ARG, "flags_out is NULL");
   *flags_out = 0;
   hipStream_t st = (hipStream_t)stream;
-  int s = scmp::read_clear_quant_flags(st, flags_out);
-  if (s != SCMP_OK) return s;
-  s = scmp::read_clear_classify_flags(st, flags_out);
+  int s = scmp::read_clear_stream_flags(st, flags_out);
   if (s != SCMP_OK) return s;
   return (*flags_out & 1) ? SCMP_ERR_NONFINITE : SCMP_OK;
 }

@@ -1,4 +1,5 @@
-// Matrix-core XNOR contraction (v_mfma_i32_32x32x32_i8).
+// Matrix-core XNOR contraction on the fp4 matrix cores
+// (v_mfma_scale_f32_32x32x64_f8f6f4, e2m1 operands, float32 accumulators).
 //
 // "Precision As You Need" paper notes, Key design 1 (C-BSG, decode
 // equation) and Key design 3 (early termination per row); K-band pull
@@ -14,7 +15,10 @@
 // paired positions k with sign s, and B becomes the pair sums
 // B'_k = B_lo(k) + B_hi(k) in {0, 1, 2} (table.hip), so
 //   count = n0 + s * sum_{k < hh} B'_k,
-// an exact int8 contraction over ceil(L/2) paired positions per d.
+// an exact contraction over ceil(L/2) paired positions per d: A's ternary
+// window {-1, 0, +1} against B's pair sums {0, 1, 2}, both exact e2m1
+// values, summed in float32 (exact while segment * (L + 1) < 2^24, which the
+// host checks before any launch).
 //
 // Two launches (the encode passes share one launch, k_prep):
 //  prep_rows    per row tile: the window code 16 (2 hh + (s < 0)) (uint16,
@@ -60,7 +64,13 @@ struct MfmaWs {
   uint32_t* ubi;    // [G][Dp][Np/2]  table offset words, by index then column pair
   int32_t* rowid;   // [G][Mp]       original row of each sorted position (-1: none)
   float* sas;       // [G][Mp]       row scale of each sorted position (single-segment plans)
-  unsigned long long* issued;  // [2] MFMA steps issued over the row tiles: int8 steps, fp4 steps
+  // Fixed header at offset 0 (the same place for every size and tiling):
+  // [0] fp4 MFMA steps issued over the row tiles, [1] the number of window
+  // sums, [2] their byte offset in the workspace; k_prep writes [1] and [2]
+  // and clears [0] and the work counter.
+  unsigned long long* hdr;
+  unsigned long long* wsum;    // [G][RT][n_parts] window positions of each encode block's rows (prep_rows)
+  unsigned long long wsum_off; // byte offset of wsum
   unsigned int* work;          // work counter of the persistent contraction
   long long Mp, Np, Dp;
   int RT, CT;
@@ -102,11 +112,12 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const size_t ubi_b = index_major ? ub_b : 0;
   const size_t ri_b = al((size_t)a.G * w.Mp * sizeof(int32_t));
   const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
-  const size_t ts_b = al(2 * sizeof(unsigned long long) + sizeof(unsigned int));
+  const size_t ts_b = al(3 * sizeof(unsigned long long) + sizeof(unsigned int));
+  const size_t wsum_b = al((size_t)a.G * w.RT * w.n_parts * sizeof(unsigned long long));
   char* p = (char*)base;
-  // The step counters first, at an offset that does not depend on the sizes.
-  w.issued = (unsigned long long*)(p ? p + off : nullptr);
-  w.work = (unsigned int*)(p ? p + off + 2 * sizeof(unsigned long long) : nullptr);
+  // The header first, at an offset that does not depend on the sizes.
+  w.hdr = (unsigned long long*)(p ? p + off : nullptr);
+  w.work = (unsigned int*)(p ? p + off + 3 * sizeof(unsigned long long) : nullptr);
   off += ts_b;
   w.hs = (uint32_t*)(p ? p + off : nullptr);
   off += hs_b;
@@ -124,6 +135,9 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   off += ri_b;
   w.sas = (float*)(p ? p + off : nullptr);
   off += sa_b;
+  w.wsum = (unsigned long long*)(p ? p + off : nullptr);
+  w.wsum_off = off;
+  off += wsum_b;
   *total = off;
   return w;
 }
@@ -178,6 +192,7 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
   __shared__ uint32_t s_lut[256];
   __shared__ int s_rows[MF_BM];
   __shared__ int s_rc[MF_BM];  // n0 sums of the tile's rows over the current chunk or part
+  __shared__ unsigned long long s_win;  // window positions of the block's rows and indices
   const int tid = threadIdx.x;
   const int y = bx, part = blockIdx.y, g = blockIdx.z;
   int k, pos0, nrows;
@@ -190,8 +205,13 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
     s_rows[tid] = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
     s_rc[tid] = 0;
   }
+  if (tid == 0) s_win = 0;
   __syncthreads();
   const int row_lo = s_rows[p_lo], row_hi = s_rows[p_hi];
+  // Window positions of this lane's rows (code >> 5: the bipolar half-window
+  // hh of paired positions, or the unipolar prefix n1), summed over its
+  // indices: the multiply-accumulates the exact count needs per column.
+  unsigned int win = 0;
   const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
   const int8_t* src_hi = a.qA + ((long long)g * a.M + (row_hi < 0 ? 0 : row_hi)) * a.D;
   const long long tile = (long long)g * w.RT + y;
@@ -279,6 +299,7 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
         }
         word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
         mh[i] = max(hh[0], hh[1]);
+        win += (uint32_t)(code[0] >> 5) + (uint32_t)(code[1] >> 5);
       }
       // d0 + 32 <= Dp: the whole group is inside the buffer (indices past
       // the band or D get code 0); dfirst is a multiple of 8.
@@ -301,7 +322,15 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
         flush_rc((long long)g * a.n_chunks + d0 / a.chunk_d);
     }
   }
-  if (a.chunk_d <= 0) flush_rc((long long)g * w.n_parts + part);
+  {
+    unsigned long long wv = win;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) wv += __shfl_xor(wv, off, 64);
+    if (lane == 0) atomicAdd(&s_win, wv);
+  }
+  if (a.chunk_d <= 0) flush_rc((long long)g * w.n_parts + part);  // ends on a barrier
+  else __syncthreads();
+  if (tid == 0) w.wsum[((long long)g * w.RT + y) * w.n_parts + part] = s_win;
   if (part == 0 && tid < MF_BM) {
     const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
     const int row = s_rows[tid];
@@ -331,8 +360,9 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
   // The contraction (launched after this kernel on the same stream) adds
   // its issued steps to this counter.
   if (bx == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
-    w.issued[0] = 0;
-    w.issued[1] = 0;
+    w.hdr[0] = 0;
+    w.hdr[1] = (unsigned long long)a.G * w.RT * w.n_parts;
+    w.hdr[2] = w.wsum_off;
     *w.work = 0;
   }
   const int cp = tid >> 2, q = tid & 3;
@@ -815,7 +845,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
   }
-  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.issued + 1, issued);  // fp4 steps
+  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.hdr, issued);  // fp4 steps
 
   if (!CHUNKED) {
     // Each row's n0 sum over the whole contraction axis: the parts' partial
@@ -1182,25 +1212,51 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     item = next;
     cur ^= 1;
   }
-  if (tid == 0 && issued) atomicAdd(w.issued + 1, issued);
+  if (tid == 0 && issued) atomicAdd(w.hdr, issued);
+}
+
+// The header of a workspace the last MFMA-path call used.
+static int read_header(const void* ws, size_t ws_bytes, hipStream_t st, unsigned long long (&h)[3]) {
+  if (!ws || ws_bytes < 3 * sizeof(unsigned long long))
+    return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
+  hipError_t e = hipMemcpyAsync(h, ws, sizeof h, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("work readback: ") + hipGetErrorString(e));
+  return SCMP_OK;
 }
 
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
                      unsigned long long* macs, unsigned long long* fp4_macs) {
-  size_t need = 0;
-  MfmaWs w = ws_layout(a, (void*)ws, &need);
-  if (!ws || ws_bytes < need)
-    return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
-  unsigned long long steps[2] = {0, 0};
-  hipError_t e = hipMemcpyAsync(steps, w.issued, sizeof steps, hipMemcpyDeviceToHost, st);
+  unsigned long long h[3];
+  int s = read_header(ws, ws_bytes, st, h);
+  if (s != SCMP_OK) return s;
+  // A step of a 128 x 128 tile is four 32 x 32 x 64 fp4 MFMAs per wave
+  // (2 x 2 subtiles), four waves: 128 * 128 * 64 MACs, issued by each
+  // column tile.
+  const unsigned long long CT = (unsigned long long)((a.N + MF_BN - 1) / MF_BN);
+  const unsigned long long per_step = CT * 128ull * 128ull * 64ull;
+  *macs = h[0] * per_step;
+  if (fp4_macs) *fp4_macs = h[0] * per_step;
+  return SCMP_OK;
+}
+
+int mfma_window_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
+                     unsigned long long* macs) {
+  unsigned long long h[3];
+  int s = read_header(ws, ws_bytes, st, h);
+  if (s != SCMP_OK) return s;
+  const unsigned long long n = h[1], off = h[2];
+  if (off < 3 * sizeof(unsigned long long) || off > ws_bytes || n > (ws_bytes - off) / sizeof(unsigned long long))
+    return set_error(SCMP_ERR_WORKSPACE, "workspace header does not describe a matrix-core call");
+  std::vector<unsigned long long> sums((size_t)n);
+  hipError_t e = hipSuccess;
+  if (n) e = hipMemcpyAsync(sums.data(), (const char*)ws + off, n * sizeof(unsigned long long),
+                            hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("work readback: ") + hipGetErrorString(e));
-  // A step of a 128 x 128 tile is four MFMAs per wave (2 x 2 subtiles of
-  // 32 x 32), four waves: 128 * 128 * K MACs with K = 32 (int8) or 64
-  // (fp4), issued by each column tile.
-  const unsigned long long per8 = (unsigned long long)w.CT * 128ull * 128ull * 32ull;
-  *macs = steps[0] * per8 + steps[1] * 2 * per8;
-  if (fp4_macs) *fp4_macs = steps[1] * 2 * per8;
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("window readback: ") + hipGetErrorString(e));
+  unsigned long long tot = 0;
+  for (unsigned long long v : sums) tot += v;
+  *macs = tot * (unsigned long long)a.N;
   return SCMP_OK;
 }
 

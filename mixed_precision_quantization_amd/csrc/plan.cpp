@@ -223,6 +223,14 @@ int build_plan(const scmp_plan_desc* d, Plan& P) {
 }
 
 }  // namespace
+bool mfma_counts_exact(const Plan& P) {
+  int maxL = 0;
+  for (int b = 0; b < P.n_bands; ++b)
+    for (int k = 0; k < P.n_rungs; ++k) maxL = P.band_L[b][k] > maxL ? P.band_L[b][k] : maxL;
+  const long long seg = (P.chunk_d > 0 && P.chunk_d < P.D) ? P.chunk_d : P.D;
+  return seg * (long long)(maxL + 1) < (1LL << 24);
+}
+
 }  // namespace scmp
 
 using scmp::set_error;
@@ -280,6 +288,7 @@ int scmp_plan_query(scmp_plan_t plan, scmp_plan_info* out) {
   out->mode = P.mode;
   out->range_mp = P.range_mp;
   out->range_group = P.range_group;
+  out->mfma_exact = scmp::mfma_counts_exact(P) ? 1 : 0;
   return SCMP_OK;
 }
 

@@ -22,8 +22,6 @@
 
 namespace scmp {
 
-__device__ int g_quant_flags;
-
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
@@ -47,6 +45,7 @@ struct QuantArgs {
   float* metric;
   uint32_t* packed;
   const uint32_t* K;
+  int* flag;  // this stream's error flag word
 };
 
 // One block (256 threads, 4 waves) per (row, g).  Per-row scales: the whole
@@ -101,7 +100,7 @@ __global__ void __launch_bounds__(256) k_quantize(QuantArgs a) {
     rowmax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   }
   if (a.metric && threadIdx.x == 0) a.metric[orow] = rowmax;
-  if (bad) atomicOr(&g_quant_flags, 1);
+  if (bad) atomicOr(a.flag, 1);
 
   if (a.packed) {
     __syncthreads();  // the block's integers are visible to the block
@@ -181,7 +180,7 @@ __global__ void __launch_bounds__(256) k_quantize_vec(QuantArgs a) {
     rowmax = wave_max(rowmax);
   }
   if (a.metric && lane == 0) a.metric[orow] = rowmax;
-  if (__ballot(bad) != 0 && lane == 0) atomicOr(&g_quant_flags, 1);
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(a.flag, 1);
 }
 
 // Rows of any length up to 64 R with unit column stride but no alignment
@@ -217,19 +216,7 @@ __global__ void __launch_bounds__(256) k_quantize_wave(QuantArgs a) {
   }
   if (lane == 0) a.scales[orow] = s;
   if (a.metric && lane == 0) a.metric[orow] = m;
-  if (__ballot(bad) != 0 && lane == 0) atomicOr(&g_quant_flags, 1);
-}
-
-int read_clear_quant_flags(hipStream_t st, int* flags) {
-  int v = 0, zero = 0;
-  hipError_t e = hipMemcpyFromSymbolAsync(&v, HIP_SYMBOL(g_quant_flags), sizeof(int), 0, hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e == hipSuccess)
-    e = hipMemcpyToSymbolAsync(HIP_SYMBOL(g_quant_flags), &zero, sizeof(int), 0, hipMemcpyHostToDevice, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("flag readback: ") + hipGetErrorString(e));
-  *flags |= v;
-  return SCMP_OK;
+  if (__ballot(bad) != 0 && lane == 0) atomicOr(a.flag, 1);
 }
 
 }  // namespace scmp
@@ -268,6 +255,9 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
   a.metric = metric_out;
   a.packed = packed_out;
   a.K = table->K;
+  hipStream_t st = (hipStream_t)stream;
+  const int fs = scmp::stream_flag(st, &a.flag);
+  if (fs != SCMP_OK) return fs;
   // Fast path: unit column stride, 16-byte aligned rows, no packed streams,
   // cols a multiple of 4 up to 4096, chunk_d 0 or a power of two in [4, 256].
   const bool cd_ok = P.chunk_d <= 0 || (P.chunk_d >= 4 && P.chunk_d <= 256 && (P.chunk_d & (P.chunk_d - 1)) == 0);
@@ -277,7 +267,6 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
   // Wave path: unit column stride, one scale per row, no packed streams,
   // rows up to 1024 values, any alignment.
   const bool wave = !vec && col_stride == 1 && !packed_out && P.chunk_d <= 0 && cols <= 1024;
-  hipStream_t st = (hipStream_t)stream;
   if (wave) {
     const dim3 grid((rows + 3) / 4, G);
     const int R = (cols + 63) / 64;

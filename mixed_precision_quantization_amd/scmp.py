@@ -46,7 +46,8 @@ EXPORTED = [
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
     "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_range_classify",
-    "scmp_gather_rows", "scmp_matmul_range", "scmp_matmul_issued_macs", "scmp_decode", "scmp_error_flags",
+    "scmp_gather_rows", "scmp_matmul_range", "scmp_matmul_issued_macs", "scmp_matmul_window_macs", "scmp_decode",
+    "scmp_error_flags",
 ]
 
 
@@ -72,7 +73,7 @@ class PlanDesc(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int) for n in
                 ("op", "p", "Lmax", "D", "chunk_d", "n_chunks", "n_rungs", "n_bands", "ceiling", "mode",
-                 "range_mp", "range_group")]
+                 "range_mp", "range_group", "mfma_exact")]
 
 
 _lib = None
@@ -118,6 +119,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                                   ctypes.c_size_t, vp]),
         "scmp_matmul_issued_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t,
                                         ctypes.POINTER(ctypes.c_ulonglong), ctypes.POINTER(ctypes.c_ulonglong),
+                                        vp]),
+        "scmp_matmul_window_macs": (i, [vp, vp, i, i, i, i, vp, ctypes.c_size_t, ctypes.POINTER(ctypes.c_ulonglong),
                                         vp]),
         "scmp_decode": (i, [vp, i, i, i, vp, vp, vp, vp, vp, i64, i64, vp]),
         "scmp_error_flags": (i, [vp, ctypes.POINTER(i)]),
@@ -420,6 +423,19 @@ def scmp_matmul_issued_macs(table: Table, plan: Plan, G: int, M: int, N: int, wo
                                           _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
                                           ctypes.byref(out), ctypes.byref(fp4), _stream(stream)))
     return (int(out.value), int(fp4.value)) if split else int(out.value)
+
+
+def scmp_matmul_window_macs(table: Table, plan: Plan, G: int, M: int, N: int, workspace, algo: str = "auto",
+                            stream=None) -> int:
+    """MACs the exact count needed in the last MFMA-path matmul with
+    ``workspace`` (per element and index the row's window, times N;
+    synchronises)."""
+    out = ctypes.c_ulonglong(0)
+    _check("scmp_matmul_window_macs",
+           load().scmp_matmul_window_macs(table.handle, plan.handle, ALGOS[algo], G, M, N,
+                                          _ptr(workspace, torch.uint8, "workspace"), workspace.numel(),
+                                          ctypes.byref(out), _stream(stream)))
+    return int(out.value)
 
 
 def scmp_decode(plan: Plan, counts, sA, sB, rung=None, C_out=None, stream=None):

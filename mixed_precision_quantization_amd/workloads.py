@@ -221,3 +221,21 @@ def sample_rows(M: int, cuts, per_rung: int = 8, seed: int = 7) -> np.ndarray:
         if n > 0:
             pos.update(int(v) for v in rng.choice(np.arange(lo, hi), size=n, replace=False))
     return np.asarray(sorted(pos), dtype=np.int64)
+
+
+def tile_positions(M: int, cuts, tile: int = 128, seed: int = 7) -> np.ndarray:
+    """Positions in sorted order that touch every row tile: for each rung,
+    its first and last sorted position plus one seeded position inside each
+    run of ``tile`` consecutive positions of the rung (the row tiles of the
+    matrix-core kernels, which take a rung's positions ``tile`` at a
+    time)."""
+    rng = np.random.default_rng(seed)
+    pos = set()
+    for k in range(len(cuts) - 1):
+        lo, hi = int(cuts[k]), int(cuts[k + 1])
+        if hi <= lo:
+            continue
+        pos.update((lo, hi - 1))
+        for t0 in range(lo, hi, tile):
+            pos.add(int(rng.integers(t0, min(t0 + tile, hi))))
+    return np.asarray(sorted(pos), dtype=np.int64)

@@ -1,7 +1,10 @@
-"""Run the CPU oracle over many output rows in a process pool.
+"""Run the CPU oracle over many output rows in a process pool (test
+infrastructure, like the rest of this package: used by the GPU parity tests
+and by the benchmark's CPU-baseline leg).
 
 Workers are spawned (not forked) and import only NumPy and ``oracle``, so
-they never touch the GPU or torch.
+they never touch the GPU or torch.  ``workers()`` is the pool size: one per
+host core, at most 16.
 """
 
 import multiprocessing as mp
@@ -10,7 +13,7 @@ from concurrent.futures import ProcessPoolExecutor
 
 import numpy as np
 
-import oracle as o
+from . import matmul as _m
 
 
 def workers() -> int:
@@ -19,7 +22,7 @@ def workers() -> int:
 
 def _task(args):
     A_rows, rung_rows, B, plan_kw = args
-    return o.rows_product(A_rows, rung_rows, B, o.OraclePlan(**plan_kw))
+    return _m.rows_product(A_rows, rung_rows, B, _m.OraclePlan(**plan_kw))
 
 
 def pooled_rows_product(A_rows, rung_rows, B, plan_kw, n_workers=None):
@@ -27,7 +30,7 @@ def pooled_rows_product(A_rows, rung_rows, B, plan_kw, n_workers=None):
     R = A_rows.shape[0]
     n = min(n_workers or workers(), max(R, 1))
     if n <= 1 or R <= 1:
-        return o.rows_product(A_rows, rung_rows, B, o.OraclePlan(**plan_kw))
+        return _m.rows_product(A_rows, rung_rows, B, _m.OraclePlan(**plan_kw))
     parts = [p for p in np.array_split(np.arange(R), n) if p.size]
     ctx = mp.get_context("spawn")
     with ProcessPoolExecutor(max_workers=len(parts), mp_context=ctx) as ex:

@@ -251,3 +251,19 @@ def test_bench_traffic_is_null_when_sources_differ(tmp_path, monkeypatch):
         (tmp_path / "profiles" / "k_mfma_w.md").write_text(text)
         assert bench.profiled_traffic("w", "auto", 2) == expect
         assert bench.profiled_traffic("w", "gather", 2) is None
+
+
+def test_matrix_core_exactness_limit():
+    # The matrix-core forms sum each accumulation segment in float32; one
+    # index adds at most L + 1, so counts stay exact integers only while
+    # segment * (longest L + 1) < 2^24 (at L = 256: D <= 65280).
+    assert scmp.scmp_plan_create(D=65280, levels=(256,)).mfma_exact == 1
+    assert scmp.scmp_plan_create(D=65281, levels=(256,)).mfma_exact == 0
+    assert scmp.scmp_plan_create(D=65281, levels=(128,)).mfma_exact == 1          # 65281 * 129 < 2^24
+    assert scmp.scmp_plan_create(D=130055, levels=(128,)).mfma_exact == 1         # 130055 * 129 < 2^24
+    assert scmp.scmp_plan_create(D=130056, levels=(128,)).mfma_exact == 0         # 130056 * 129 >= 2^24
+    # With chunk scales each chunk is its own segment.
+    assert scmp.scmp_plan_create(D=200000, chunk_d=64, levels=(256,)).mfma_exact == 1
+    # The longest length of any band or rung sets the bound.
+    assert scmp.scmp_plan_create(D=65281, levels=(256, 64), fractions=(0.5, 0.5)).mfma_exact == 0
+    assert scmp.scmp_plan_create(D=65280, levels=(256, 64), fractions=(0.5, 0.5)).mfma_exact == 1

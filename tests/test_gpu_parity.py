@@ -13,9 +13,9 @@ import pytest
 import torch
 
 import oracle as o
-from _oracle_pool import pooled_rows_product
+from oracle.pool import OraclePool, pooled_rows_product
 from mixed_precision_quantization_amd import scmp
-from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, draw_bias, sample_rows, shrink
+from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, draw_bias, sample_rows, shrink, tile_positions
 
 pytestmark = pytest.mark.gpu
 
@@ -79,6 +79,13 @@ def _check_group(gres, g, A_g, B_g, okw, rows=None):
         assert np.array_equal(gres["thresholds"][g], thr), "thresholds"
     rows = np.arange(M) if rows is None else np.asarray(rows)
     orc = pooled_rows_product(A_g[rows], cls["rung"][rows], B_g, okw)
+    _compare_rows(gres, g, rows, orc)
+    return orc
+
+
+def _compare_rows(gres, g, rows, orc):
+    """Integers, scales and counts of group g's ``rows`` bit-exact against an
+    oracle result, C within the decode tolerance."""
     assert np.array_equal(gres["qA"][g][rows].astype(np.int64), orc["x_a"]), "A integers"
     assert np.array_equal(gres["sA"][g][rows], orc["s_a"]), "A scales"
     assert np.array_equal(gres["qB"][g].astype(np.int64), orc["x_b"]), "B integers"
@@ -90,7 +97,6 @@ def _check_group(gres, g, A_g, B_g, okw, rows=None):
     err = np.abs(C - orc["C"])
     lim = RTOL * orc["C_abs"]
     assert np.all(err <= lim), f"max err/limit {np.max(err / np.maximum(lim, 1e-300)):.3g}"
-    return orc
 
 
 def _groups(A, B):
@@ -179,6 +185,32 @@ def test_nonfinite_input_sets_flag(table):
     scmp.scmp_classify_rows(plan, m)
     assert scmp.scmp_error_flags() & 1
     assert scmp.scmp_error_flags() == 0          # cleared by the read
+
+
+def test_error_flags_are_per_stream(table):
+    """A non-finite input on one stream raises that stream's flag only: a
+    second stream running clean inputs at the same time, and the default
+    stream, read no flag, and reading one stream's flag leaves the other's."""
+    plan = scmp.scmp_plan_create(D=64, levels=(128, 64))
+    bad = np.ones((4, 64), dtype=np.float32)
+    bad[1, 7] = np.nan
+    good = np.ones((4, 64), dtype=np.float32)
+    Xb = torch.from_numpy(bad).cuda()
+    Xg = torch.from_numpy(good).cuda()
+    s_bad, s_good = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s_bad):
+        _, _, mb, _ = scmp.scmp_quantize_encode(table, plan, Xb, stream=s_bad)
+        scmp.scmp_classify_rows(plan, mb, stream=s_bad)
+    with torch.cuda.stream(s_good):
+        _, _, mg, _ = scmp.scmp_quantize_encode(table, plan, Xg, stream=s_good)
+        scmp.scmp_classify_rows(plan, mg, stream=s_good)
+    torch.cuda.synchronize()
+    assert scmp.scmp_error_flags(s_good) == 0
+    assert scmp.scmp_error_flags() == 0
+    assert scmp.scmp_error_flags(s_bad) & 1
+    assert scmp.scmp_error_flags(s_bad) == 0     # cleared by the read
+    assert scmp.scmp_error_flags(s_good) == 0
 
 
 def test_packed_streams_are_table_rows(table):
@@ -347,18 +379,50 @@ def test_standalone_decode_matches_fused(table):
 
 # ----------------------------------------------- full sizes, bench launch --
 
-FULL_GROUPS = {"vitl_qk": (0, 77, 127), "vitl_av_mp": (0, 64, 127), "vitl_qk_mp": (0, 77, 127),
-               "vitl_av_unipolar": (0, 64, 127)}
+def _decode_bound(sA, sB, plan, q=127, bias=None):
+    """Per element, q^2 sum_c |s^A_ic| |s^B_jc| |c| (+ |bias_j|): a bound on
+    the sum of absolute decode terms (each term is at most
+    |s^A s^B| q^2 |c|), float64 on the device, for comparing two decodes of
+    the same counts."""
+    cols = plan.band_columns()
+    D = cols[-1]
+    cd = plan.chunk_d if plan.chunk_d > 0 else D
+    widths = torch.tensor([min(cd, D - c0) for c0 in range(0, D, cd)], dtype=torch.float64, device=sA.device)
+    b = torch.abs(sA.double()) @ (torch.abs(sB.double()) * widths).transpose(-1, -2) * float(q * q)
+    if bias is not None:
+        b = b + torch.abs(bias.double()).unsqueeze(-2)
+    return b
+
+
+def _whole_matrix_vs_bitserial(table, plan, At, Bt, full, bias=None):
+    """The bit-serial kernel (packed streams, bit-select and popcount on the
+    vector ALU: an integer path independent of the matrix-core windows) on
+    the same inputs: every count of the whole matrix equal, every C within
+    1e-5 of the decode bound."""
+    bits = scmp.sc_linear(table, plan, At, Bt, algo="bitserial", want_counts=True, bias=bias)
+    cm = torch.from_numpy(full["counts"]).cuda()
+    assert torch.equal(bits["counts"], cm), f"{int((bits['counts'] != cm).sum())} counts differ from bit-serial"
+    bound = _decode_bound(bits["sA"], bits["sB"], plan, bias=bias)
+    err = torch.abs(bits["C"].double() - torch.from_numpy(full["C"]).cuda().double())
+    assert bool((err <= RTOL * bound).all()), "C differs from the bit-serial decode"
+    torch.cuda.synchronize()
 
 
 @pytest.mark.parametrize("name", list(WORKLOADS))
-def test_full_size_sampled_rows(table, name):
+def test_full_size_every_tile(table, name):
     """Full-size inputs in the launch configuration the benchmark times
-    (MFMA path, fused decode, no counts), checked on sampled rows of every
-    rung; the counts variant is checked bit-exact on the same rows."""
+    (AUTO, fused decode, no counts; the bias workloads without their bias,
+    which test_head_aligned_compensator_full_size adds) against the counts
+    variant, whose counts
+    and C are checked against the oracle on one sorted position in every
+    128-row tile of every rung (plus each rung's edges) -- 16 whole groups
+    for the per-head workloads -- and against the bit-serial kernel on the
+    whole matrix."""
     w = WORKLOADS[name]
     if w.extra.get("heads"):
         pytest.skip("per-head rungs: test_head_mp_full_size")
+    if w.extra.get("range_mp"):
+        pytest.skip("range MP: test_range_mp_full_size")
     A, B = _groups(*draw(w))
     plan, okw = _plans(w)
     print(f"  full {name}", flush=True)
@@ -370,40 +434,61 @@ def test_full_size_sampled_rows(table, name):
     full = _to_np(scmp.sc_linear(table, plan, At, Bt, algo="mfma", want_counts=True))
     torch.cuda.synchronize()
     assert np.array_equal(bench["C"], full["C"])
-    groups = FULL_GROUPS.get(name, (0,))
     for g in range(A.shape[0]):
         if plan.n_rungs > 1:
             perm = full["perm"][g]
             assert np.array_equal(np.sort(perm), np.arange(w.M))
             sizes = np.bincount(full["rung"][g], minlength=plan.n_rungs)
             assert sizes.tolist() == np.diff(plan.row_cuts(w.M)).tolist()
-    for g in groups:
-        cls = o.classify(A[g], o.OraclePlan(**okw))
-        pos = sample_rows(w.M, cls["cuts"], per_rung=3 if w.G == 1 else 2, seed=g)
-        rows = cls["order"][pos]
-        _check_group(full, g, A[g], B[g], okw, rows=rows)
+    _whole_matrix_vs_bitserial(table, plan, At, Bt, full)
+    if A.shape[0] == 1:
+        cls = o.classify(A[0], o.OraclePlan(**okw))
+        rows = cls["order"][tile_positions(w.M, cls["cuts"])]
+        print(f"    oracle on {len(rows)} rows", flush=True)
+        _check_group(full, 0, A[0], B[0], okw, rows=rows)
+    else:
+        groups = sorted({0, A.shape[0] - 1} | set(np.random.default_rng(3).choice(A.shape[0], 14, replace=False).tolist()))
+        print(f"    oracle on {len(groups)} whole groups", flush=True)
+        oplan = o.OraclePlan(**okw)
+        jobs, rungs = [], {}
+        for g in groups:
+            cls = o.classify(A[g], oplan)
+            if oplan.n_rungs > 1:
+                assert np.array_equal(full["rung"][g].astype(np.int64), cls["rung"]), "rungs"
+                assert np.array_equal(full["perm"][g].astype(np.int64), cls["order"]), "bucket permutation"
+            jobs.append((A[g], cls["rung"], B[g]))
+        with OraclePool(okw) as pool:
+            outs = pool.run(jobs)
+        for g, orc in zip(groups, outs):
+            orc["x_b"] = o.quantize(B[g], 8, w.chunk_d)[0]
+            orc["s_b"] = o.quantize(B[g], 8, w.chunk_d)[1]
+            _compare_rows(full, g, np.arange(w.M), orc)
 
 
 # --------------------------------------------- head-aligned compensator --
 
-def _head_aligned_check(table, X, W, b, algo, rows=None):
+def _head_aligned_check(table, X, W, b, algo, rows=None, c_rows=None):
     """GPU scmp_matmul_bias (chunk_d = 64, L = 256) against the oracle's
-    head-aligned compensator (heads summed, bias added); counts bit-exact
-    against the oracle's per-head counts."""
+    head-aligned compensator (heads summed, bias added) on ``c_rows`` (all
+    of ``rows`` when None); counts bit-exact against the oracle's per-head
+    counts on ``rows``."""
     D = X.shape[1]
     plan = scmp.scmp_plan_create(D=D, chunk_d=64, levels=(256,))
     res = _to_np(scmp.sc_linear(table, plan, torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda(), algo=algo,
                                 want_counts=True, bias=torch.from_numpy(b).cuda().reshape(1, -1)))
     torch.cuda.synchronize()
     rows = np.arange(X.shape[0]) if rows is None else np.asarray(rows)
-    orc = o.head_aligned_rows(X, W, b, head_dim=64, L=256, rows=rows)
-    C = res["C"][0][rows].astype(np.float64)
+    c_rows = rows if c_rows is None else np.asarray(c_rows)
+    orc = o.head_aligned_rows(X, W, b, head_dim=64, L=256, rows=c_rows)
+    C = res["C"][0][c_rows].astype(np.float64)
     err = np.abs(C - orc["C"])
     lim = RTOL * orc["C_abs"]
     assert np.all(err <= lim), f"max err/limit {np.max(err / np.maximum(lim, 1e-300)):.3g}"
     okw = dict(p=8, Lmax=256, D=D, chunk_d=64, levels=(256,))
     cnt = pooled_rows_product(X[rows], np.zeros(len(rows), np.int64), W, okw)
     assert np.array_equal(res["counts"][0][rows].astype(np.int64), cnt["band_counts"]), "counts"
+    C = res["C"][0][rows].astype(np.float64)
+    assert np.all(np.abs(C - (cnt["C"] + b[None, :])) <= RTOL * (cnt["C_abs"] + np.abs(b)[None, :])), "C + bias"
 
 
 @pytest.mark.parametrize("algo", ALGOS)
@@ -419,12 +504,16 @@ def test_head_aligned_compensator_small(table, algo):
 
 
 def test_head_aligned_compensator_full_size(table):
+    """The benchmark's launch (AUTO): counts and C + bias on one row in
+    every 128-row tile, the oracle's head-aligned compensator on ten of
+    them."""
     w = WORKLOADS["vitl_comp_head_aligned"]
     X, W = draw(w)
     b = draw_bias(w)
-    rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], np.random.default_rng(5).choice(w.M, 6)]))
-    print("  head-aligned full size", flush=True)
-    _head_aligned_check(table, X, W, b, "auto", rows=rows)
+    rows = tile_positions(w.M, [0, w.M], seed=5)
+    c_rows = np.unique(np.concatenate([[0, 1, w.M // 2, w.M - 1], np.random.default_rng(5).choice(w.M, 6)]))
+    print(f"  head-aligned full size, {len(rows)} rows", flush=True)
+    _head_aligned_check(table, X, W, b, "auto", rows=rows, c_rows=c_rows)
 
 
 # ------------------------------------------------- per-head MP on QK^T --
@@ -475,19 +564,21 @@ def test_head_mp_small(table, algo):
 
 
 def test_head_mp_full_size(table):
-    """The benchmark's launch (AUTO, fused decode), checked on two sampled
-    rows of every head of images 0 and 7; the C of the counts-free launch
-    equals the counted one."""
+    """The benchmark's launch (AUTO, fused decode), checked on every row of
+    every head of images 0 and 7 (32 whole heads) and, on the whole matrix,
+    against the bit-serial kernel; the C of the counts-free launch equals
+    the counted one."""
     w = WORKLOADS["vitl_qk_head_mp"]
     Q, K = draw(w)
     heads = w.extra["heads"]
     plan, _ = _plans(w)
     print("  head mp full size", flush=True)
-    bench = _to_np(scmp.sc_qk_head_mp(table, plan, torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda(), heads,
-                                      algo="auto", want_counts=False))
-    res = _head_mp_check(table, w, Q, K, "auto", images=(0, 7),
-                         rows_of=lambda g: np.array([(g * 37) % w.M, w.M - 1 - g % 5]))
+    Qt, Kt = torch.from_numpy(Q).cuda(), torch.from_numpy(K).cuda()
+    bench = _to_np(scmp.sc_qk_head_mp(table, plan, Qt, Kt, heads, algo="auto", want_counts=False))
+    bits = scmp.sc_qk_head_mp(table, plan, Qt, Kt, heads, algo="bitserial", want_counts=True)
+    res = _head_mp_check(table, w, Q, K, "auto", images=(0, 7))
     assert np.array_equal(bench["C"], res["C"])
+    assert torch.equal(bits["counts"], torch.from_numpy(res["counts"]).cuda()), "counts differ from bit-serial"
     sizes = np.bincount(res["head_rung"].reshape(-1, heads)[0], minlength=plan.n_rungs)
     assert sizes.tolist() == np.diff(plan.row_cuts(heads)).tolist()
 
@@ -651,19 +742,27 @@ def test_range_mp_rejects_plain_matmul(table):
 
 
 def test_range_mp_full_size(table):
-    """The benchmark's workload and launch (AUTO), checked on sampled rows
-    against the oracle, columns of both levels."""
+    """The benchmark's workload and launch (AUTO), checked against the
+    oracle on one row in every 128-row tile (columns of both levels), and
+    against the bit-serial kernel on every count of both levels."""
     w = WORKLOADS["vitl_fc1_range"]
     X, W = draw(w)
     plan = scmp.scmp_plan_create(D=w.D, levels=w.levels, range_mp=True, range_threshold=w.extra["range_threshold"],
                                  range_group=w.extra["range_group"])
     print("  range mp full size", flush=True)
-    res = scmp.sc_linear_range(table, plan, torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda(), algo="auto")
+    Xt, Wt = torch.from_numpy(X).cuda(), torch.from_numpy(W).cuda()
+    res = scmp.sc_linear_range(table, plan, Xt, Wt, algo="auto", want_counts=True)
+    bits = scmp.sc_linear_range(table, plan, Xt, Wt, algo="bitserial", want_counts=True)
     torch.cuda.synchronize()
-    rows = np.array([0, 5000, w.M - 1])
-    rl, C, C_abs, _ = _range_oracle(X, W, w.levels, w.extra["range_threshold"], w.extra["range_group"], rows)
+    for k in range(2):
+        assert torch.equal(res["counts"][k], bits["counts"][k]), f"level {k}: counts differ from bit-serial"
+    rows = tile_positions(w.M, [0, w.M], seed=9)
+    print(f"    oracle on {len(rows)} rows", flush=True)
+    rl, C, C_abs, counts = _range_oracle(X, W, w.levels, w.extra["range_threshold"], w.extra["range_group"], rows)
     got = res["C"][0].cpu().numpy()[rows].astype(np.float64)
     assert np.all(np.abs(got - C) <= RTOL * C_abs)
+    for k in range(2):
+        assert np.array_equal(res["counts"][k][0].cpu().numpy()[rows].astype(np.int64), counts[k]), f"level {k}"
     assert res["n_per_level"][1] == 128 * int(rl["level"].sum())
 
 
