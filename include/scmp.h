@@ -287,6 +287,23 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c,
                 void* workspace_dev, size_t workspace_bytes, void* stream);
 
+/* scmp_matmul for callers that cannot allocate (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * product, kernels and results as scmp_matmul, with the scratch memory
+ * taken from a static device array of the library (64 MiB per device,
+ * held until the process ends) instead of a caller workspace.  The call
+ * allocates nothing.  Every call on one device shares that device's array,
+ * so calls that overlap on one device (other streams, other threads) race
+ * and must be ordered by the caller; the array keeps the last call's
+ * contents, and the kernels clear what must start at zero.  Arguments as
+ * scmp_matmul, without the workspace.
+ * Errors: as scmp_matmul; WORKSPACE when the sizes need more scratch than
+ * 64 MiB (scmp_matmul_workspace_bytes tells), nothing launched. */
+int scmp_matmul_noalloc(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,
+                        const int8_t* qA_dev, const float* sA_dev, const int32_t* permA_dev,
+                        const int8_t* qB_dev, const uint32_t* packedB_dev, const float* sB_dev,
+                        int32_t* counts_dev, float* C_dev, int64_t ldc, int64_t batch_stride_c, void* stream);
+
 /* scmp_matmul with a bias added to every row of C: C_ij = (decode as
  * above) + bias_j.  With chunk_d = 64 and one length L this is the
  * head-aligned SC compensator of [VIT] (its head-aligned compensator

@@ -8,12 +8,41 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
 #include <string>
 
 #include "matmul_common.h"
 #include "table.h"
 
 namespace scmp {
+
+// Scratch memory of scmp_matmul_noalloc: one array per device that runs the
+// library, held until the process ends.  Host code never passes the array's
+// name to a kernel; it uses the device address taken once per device below.
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(64) << 20;
+__device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, taken on the first
+// call on that device (with it current) and kept per device.
+static int scratch_address(void** out) {
+  static std::mutex mu;
+  static void* addr[64] = {nullptr};
+  *out = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("hipGetDevice: ") + hipGetErrorString(e));
+  if (dev < 0 || dev >= 64) return set_error(SCMP_ERR_ARG, "device ordinal above 63");
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return set_error(SCMP_ERR_HIP, std::string("scratch address: ") + hipGetErrorString(e));
+    addr[dev] = p;
+  }
+  *out = addr[dev];
+  return SCMP_OK;
+}
 
 void fill_tiles(MatmulArgs& a, const Plan& P, int BM) {
   row_cuts(P, a.M, a.cuts);
@@ -215,6 +244,27 @@ int scmp_matmul(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, in
                 void* workspace, size_t workspace_bytes, void* stream) {
   return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, Variant{}, counts, C, ldc,
                      batch_stride_c, workspace, workspace_bytes, stream);
+}
+
+int scmp_matmul_noalloc(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N, const int8_t* qA,
+                        const float* sA, const int32_t* permA, const int8_t* qB, const uint32_t* packedB,
+                        const float* sB, int32_t* counts, float* C, int64_t ldc, int64_t batch_stride_c,
+                        void* stream) {
+  scmp::clear_error();
+  size_t need = 0;
+  int st = scmp_matmul_workspace_bytes(table, plan, algo, G, M, N, &need);
+  if (st != SCMP_OK) return st;
+  if (need > scmp::NOALLOC_SCRATCH_BYTES)
+    return set_error(SCMP_ERR_WORKSPACE, "scmp_matmul_noalloc: these sizes need " + std::to_string(need) +
+                                             " bytes of scratch, above its 64 MiB maximum; use scmp_matmul "
+                                             "with a caller workspace");
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scmp::scratch_address(&ws);
+    if (st != SCMP_OK) return st;
+  }
+  return matmul_impl(table, plan, algo, G, M, N, qA, sA, permA, qB, packedB, sB, Variant{}, counts, C, ldc,
+                     batch_stride_c, ws, need > 0 ? scmp::NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 int scmp_matmul_group_rungs(scmp_table_t table, scmp_plan_t plan, int algo, int G, int M, int N,

@@ -45,7 +45,7 @@ EXPORTED = [
     "scmp_table_info", "scmp_table_export", "scmp_plan_create", "scmp_plan_destroy",
     "scmp_plan_query", "scmp_plan_band_lengths", "scmp_plan_band_columns", "scmp_plan_budget_use",
     "scmp_plan_row_cuts", "scmp_quantize_encode", "scmp_classify_rows", "scmp_matmul_workspace_bytes",
-    "scmp_matmul", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_range_classify",
+    "scmp_matmul", "scmp_matmul_noalloc", "scmp_matmul_bias", "scmp_matmul_group_rungs", "scmp_group_max", "scmp_range_classify",
     "scmp_gather_rows", "scmp_matmul_range", "scmp_matmul_issued_macs", "scmp_matmul_window_macs", "scmp_decode",
     "scmp_error_flags",
 ]
@@ -108,6 +108,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         "scmp_classify_rows": (i, [vp, vp, i, i, vp, vp, vp, vp, vp]),
         "scmp_matmul_workspace_bytes": (i, [vp, vp, i, i, i, i, ctypes.POINTER(ctypes.c_size_t)]),
         "scmp_matmul": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t, vp]),
+        "scmp_matmul_noalloc": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp]),
         "scmp_matmul_bias": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp, ctypes.c_size_t,
                                  vp]),
         "scmp_matmul_group_rungs": (i, [vp, vp, i, i, i, i, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, vp,
@@ -409,6 +410,37 @@ def scmp_matmul(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=No
     else:
         _need(bias, G * N, "bias")
         _check("scmp_matmul_bias", load().scmp_matmul_bias(*head, _ptr(bias, torch.float32, "bias"), *tail))
+    return counts_out, C_out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def scmp_matmul_noalloc(table: Table, plan: Plan, qA, sA, qB, sB, permA=None, packedB=None, algo: str = "auto",
+                        counts_out=None, C_out=None, stream=None):
+    """scmp_matmul_noalloc: the product of scmp_matmul with the library's
+    static scratch instead of a workspace.  The outputs must be given
+    (counts_out int32 [G, M, N, n_bands] and / or C_out float [G, M, N]);
+    nothing is allocated here or in the library."""
+    qA3 = qA if qA.dim() == 3 else qA.unsqueeze(0)
+    qB3 = qB if qB.dim() == 3 else qB.unsqueeze(0)
+    G, M, D = qA3.shape
+    G2, N, D2 = qB3.shape
+    if G2 != G or D2 != D:
+        raise ValueError("qA and qB disagree on G or D")
+    if counts_out is None and C_out is None:
+        raise ValueError("give counts_out and / or C_out")
+    _need(sA, G * M * plan.n_chunks, "sA")
+    _need(sB, G * N * plan.n_chunks, "sB")
+    _need(permA, G * M, "permA")
+    _need(packedB, G * N * D * table.words, "packedB")
+    _need(counts_out, G * M * N * plan.n_bands, "counts_out")
+    _need(C_out, G * M * N, "C_out")
+    _check("scmp_matmul_noalloc", load().scmp_matmul_noalloc(
+        table.handle, plan.handle, ALGOS[algo], G, M, N, _ptr(qA3, torch.int8, "qA"), _ptr(sA, torch.float32, "sA"),
+        _ptr(permA, torch.int32, "permA"), _ptr(qB3, torch.int8, "qB"), _ptr(packedB, torch.int32, "packedB"),
+        _ptr(sB, torch.float32, "sB"), _ptr(counts_out, torch.int32, "counts_out"),
+        _ptr(C_out, torch.float32, "C_out"), N, M * N, _stream(stream)))
     return counts_out, C_out
 
 
