@@ -117,29 +117,38 @@ __global__ void __launch_bounds__(256) k_quantize(QuantArgs a) {
   }
 }
 
-// Fast path for unit column stride and 16-byte aligned rows: one wave per
-// row (four rows per block), float4 loads kept in registers between the max
-// and the quantisation, four integers packed per 32-bit store.  Per-chunk
-// scales need chunk_d a power of two in [4, 256]: the chunk of a float4 at
-// column c is c / chunk_d, and the lanes sharing it are chunk_d / 4
-// consecutive lanes (an xor-shuffle group).  R: float4 loads per lane
-// (cols <= 256 R).
-template <int R>
+// Fast path for unit column stride and 16-byte aligned rows: LPR lanes per
+// row (a power of two; 64 / LPR rows per wave, four waves per block),
+// float4 loads kept in registers between the max and the quantisation, four
+// integers packed per 32-bit store.  Per-chunk scales need chunk_d a power of
+// two in [4, 256]: the chunk of a float4 at column c is c / chunk_d, and the
+// lanes sharing it are min(chunk_d / 4, LPR) consecutive lanes (an
+// xor-shuffle group inside the row's lanes).  R: float4 loads per lane
+// (cols <= 4 LPR R).
+template <int R, int LPR>
 __global__ void __launch_bounds__(256) k_quantize_vec(QuantArgs a) {
+  constexpr int RPW = 64 / LPR;  // rows per wave
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = blockIdx.x * 4 + wave;
+  const int sub = lane & (LPR - 1);
+  const int row = (blockIdx.x * 4 + wave) * RPW + lane / LPR;
   const int g = blockIdx.y;
-  if (row >= a.rows) return;
-  const float* x = a.X + (long long)g * a.bs + (long long)row * a.rs;
+  const bool live = row < a.rows;
+  const float* x = a.X + (long long)g * a.bs + (long long)(live ? row : 0) * a.rs;
   const long long orow = (long long)g * a.rows + row;
   int8_t* qrow = a.qout + orow * a.cols;
   const float qf = (float)a.q;
+  // Maximum over the LPR lanes of this row.
+  auto row_max = [](float m) {
+#pragma unroll
+    for (int off = 1; off < LPR; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    return m;
+  };
   float4 v[R];
   bool bad = false;
 #pragma unroll
   for (int r = 0; r < R; ++r) {
-    const int c = 256 * r + 4 * lane;
-    v[r] = c < a.cols ? *(const float4*)(x + c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
+    const int c = 4 * (LPR * r + sub);
+    v[r] = (live && c < a.cols) ? *(const float4*)(x + c) : float4{0.0f, 0.0f, 0.0f, 0.0f};
     bad |= !(__builtin_isfinite(v[r].x) && __builtin_isfinite(v[r].y) && __builtin_isfinite(v[r].z) &&
              __builtin_isfinite(v[r].w));
   }
@@ -154,32 +163,32 @@ __global__ void __launch_bounds__(256) k_quantize_vec(QuantArgs a) {
     float m = 0.0f;
 #pragma unroll
     for (int r = 0; r < R; ++r) m = fmaxf(m, amax4(v[r]));
-    m = wave_max(m);
+    m = row_max(m);
     const float s = m == 0.0f ? 0.0f : m / qf;
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int c = 256 * r + 4 * lane;
-      if (c < a.cols) *(uint32_t*)(qrow + c) = pack(v[r], s);
+      const int c = 4 * (LPR * r + sub);
+      if (live && c < a.cols) *(uint32_t*)(qrow + c) = pack(v[r], s);
     }
-    if (lane == 0) a.scales[orow] = s;
+    if (live && sub == 0) a.scales[orow] = s;
     rowmax = m;
   } else {
-    const int group = a.chunk_d >> 2;  // lanes per chunk (power of two, <= 64)
+    const int group = min(a.chunk_d >> 2, LPR);  // lanes per chunk (power of two)
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       float m = amax4(v[r]);
       for (int off = 1; off < group; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
       const float s = m == 0.0f ? 0.0f : m / qf;
-      const int c = 256 * r + 4 * lane;
-      if (c < a.cols) {
+      const int c = 4 * (LPR * r + sub);
+      if (live && c < a.cols) {
         *(uint32_t*)(qrow + c) = pack(v[r], s);
-        if ((lane & (group - 1)) == 0) a.scales[orow * a.n_chunks + c / a.chunk_d] = s;
+        if ((sub & (group - 1)) == 0) a.scales[orow * a.n_chunks + c / a.chunk_d] = s;
       }
       rowmax = fmaxf(rowmax, m);
     }
-    rowmax = wave_max(rowmax);
+    rowmax = row_max(rowmax);
   }
-  if (a.metric && lane == 0) a.metric[orow] = rowmax;
+  if (a.metric && live && sub == 0) a.metric[orow] = rowmax;
   if (__ballot(bad) != 0 && lane == 0) atomicOr(a.flag, 1);
 }
 
@@ -277,14 +286,29 @@ extern "C" int scmp_quantize_encode(scmp_table_t table, scmp_plan_t plan, const 
     else
       hipLaunchKernelGGL(scmp::k_quantize_wave<16>, grid, dim3(256), 0, st, a);
   } else if (vec) {
-    const dim3 grid((rows + 3) / 4, G);
-    const int R = (cols + 255) / 256;
-    if (R <= 4)
-      hipLaunchKernelGGL(scmp::k_quantize_vec<4>, grid, dim3(256), 0, st, a);
+    // Lanes per row: the float4 count of a row rounded up to a power of two
+    // (4 to 64); rows of more than 256 values take 64 lanes and R loads.
+    int lpr = 4;
+    while (lpr < 64 && 4 * lpr < cols) lpr <<= 1;
+    const int rows_per_block = 4 * (64 / lpr);
+    const dim3 grid((rows + rows_per_block - 1) / rows_per_block, G);
+    const int R = (cols + 4 * lpr - 1) / (4 * lpr);
+    if (lpr == 4)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<1, 4>), grid, dim3(256), 0, st, a);
+    else if (lpr == 8)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<1, 8>), grid, dim3(256), 0, st, a);
+    else if (lpr == 16)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<1, 16>), grid, dim3(256), 0, st, a);
+    else if (lpr == 32)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<1, 32>), grid, dim3(256), 0, st, a);
+    else if (R <= 1)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<1, 64>), grid, dim3(256), 0, st, a);
+    else if (R <= 4)
+      hipLaunchKernelGGL((scmp::k_quantize_vec<4, 64>), grid, dim3(256), 0, st, a);
     else if (R <= 8)
-      hipLaunchKernelGGL(scmp::k_quantize_vec<8>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((scmp::k_quantize_vec<8, 64>), grid, dim3(256), 0, st, a);
     else
-      hipLaunchKernelGGL(scmp::k_quantize_vec<16>, grid, dim3(256), 0, st, a);
+      hipLaunchKernelGGL((scmp::k_quantize_vec<16, 64>), grid, dim3(256), 0, st, a);
   } else {
     hipLaunchKernelGGL(scmp::k_quantize, dim3(rows, G), dim3(256), 0, st, a);
   }
