@@ -46,7 +46,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--algo", default="auto",
-                    choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather"])
+                    choices=["auto", "mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather", "mfma_quarter"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=0, help="rows for the oracle sample (0 = 2 per worker)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -99,6 +99,8 @@ def profiled_traffic(workload, algo, dispatches):
         if rec.get("workload") != workload or rec.get("algo") != algo:
             continue
         if rec.get("sources_sha256") != sources_sha256():
+            return None
+        if "fetch_bytes_per_dispatch" not in rec or "write_bytes_per_dispatch" not in rec:
             return None
         return (rec["fetch_bytes_per_dispatch"] + rec["write_bytes_per_dispatch"]) * dispatches
     return None

@@ -85,13 +85,24 @@ typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
  *             accumulators that hold the integer counts exactly while
  *             scmp_plan_info.mfma_exact is 1); the launch form is chosen by
  *             size (persistent when the plan allows it and there are several
- *             output tiles per block, one block per tile otherwise).  When
- *             mfma_exact is 0, AUTO runs GATHER (bipolar) or BITSERIAL
- *             (unipolar) instead and the MFMA forms return UNSUPPORTED.
+ *             output tiles per block, one block per tile otherwise); AUTO
+ *             takes the quarter form (below) for persistent plans with
+ *             D >= 512 where at least half of the 128-row tiles run streams
+ *             of length <= 96 (MFMA never does).  When mfma_exact is 0, AUTO runs GATHER
+ *             (bipolar) or BITSERIAL (unipolar) instead and the MFMA forms
+ *             return UNSUPPORTED.
  *  MFMA_PERSISTENT: the matrix-core path as a persistent grid taking
  *             output tiles from a work counter; bipolar plans without chunk
  *             scales and with one band only (UNSUPPORTED otherwise).
  *  MFMA_ONEPASS: the matrix-core path with one block per output tile.
+ *  MFMA_QUARTER: the persistent grid with the first 16 paired positions
+ *             of each index taken 8 at a time (operands from 17 x 17-entry
+ *             pair tables of window and pair-sum classes), so that indices
+ *             whose windows end by position 8 cost half a step; the same
+ *             plans as MFMA_PERSISTENT with the band starting on a multiple
+ *             of 32 and D rounded up to 32 at most 4096 (UNSUPPORTED
+ *             otherwise).  Its workspace is larger (quarter codes: 1 byte
+ *             per row and index, 1 byte per column, index and ladder rung).
  *  BITSERIAL: one bit-select + popcount per 32 stream positions on the
  *             vector ALU; needs the packed weight-side streams.
  *  GATHER:    one lookup per (row, column, index) in a per-length table
@@ -103,7 +114,8 @@ typedef enum {
   SCMP_ALGO_MFMA = 2,
   SCMP_ALGO_MFMA_PERSISTENT = 3,
   SCMP_ALGO_MFMA_ONEPASS = 4,
-  SCMP_ALGO_GATHER = 5
+  SCMP_ALGO_GATHER = 5,
+  SCMP_ALGO_MFMA_QUARTER = 6
 } scmp_algo;
 
 typedef struct scmp_table_s* scmp_table_t; /* opaque, library-owned */

@@ -57,9 +57,10 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M
   const Plan& P = plan->plan;
   if (table->p != P.p || table->Lmax != P.Lmax)
     return set_error(SCMP_ERR_PLAN_MISMATCH, "table p / Lmax differ from the plan");
-  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_GATHER) return set_error(SCMP_ERR_ARG, "unknown algo");
-  if (P.mode == SCMP_MODE_UNIPOLAR && (algo == SCMP_ALGO_MFMA_PERSISTENT || algo == SCMP_ALGO_GATHER))
-    return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans have no persistent or gather form");
+  if (algo < SCMP_ALGO_AUTO || algo > SCMP_ALGO_MFMA_QUARTER) return set_error(SCMP_ERR_ARG, "unknown algo");
+  if (P.mode == SCMP_MODE_UNIPOLAR &&
+      (algo == SCMP_ALGO_MFMA_PERSISTENT || algo == SCMP_ALGO_GATHER || algo == SCMP_ALGO_MFMA_QUARTER))
+    return set_error(SCMP_ERR_UNSUPPORTED, "unipolar plans have no persistent, quarter or gather form");
   if (G < 0 || M < 0 || N < 0) return set_error(SCMP_ERR_ARG, "negative size");
   if (G > 65535) return set_error(SCMP_ERR_ARG, "G must be <= 65535");
   if (table->P + 1 > MAX_LEVELS) return set_error(SCMP_ERR_ARG, "table has too many levels");
@@ -84,14 +85,18 @@ static int prepare(scmp_table_t table, scmp_plan_t plan, int& algo, int G, int M
   // Segments too long for exact float32 accumulation leave AUTO to an
   // integer path and reject the matrix-core forms (mfma_counts_exact).
   if ((algo == SCMP_ALGO_AUTO || algo == SCMP_ALGO_MFMA || algo == SCMP_ALGO_MFMA_PERSISTENT ||
-       algo == SCMP_ALGO_MFMA_ONEPASS) && !mfma_counts_exact(P)) {
+       algo == SCMP_ALGO_MFMA_ONEPASS || algo == SCMP_ALGO_MFMA_QUARTER) && !mfma_counts_exact(P)) {
     if (algo != SCMP_ALGO_AUTO)
       return set_error(SCMP_ERR_UNSUPPORTED,
                        "the matrix-core accumulators hold counts exactly only while the accumulation segment "
                        "(D, or chunk_d) times (longest L + 1) stays below 2^24; use BITSERIAL or GATHER");
     algo = P.mode == SCMP_MODE_UNIPOLAR ? SCMP_ALGO_BITSERIAL : SCMP_ALGO_GATHER;
   }
-  a.launch = algo == SCMP_ALGO_MFMA_PERSISTENT ? 1 : (algo == SCMP_ALGO_MFMA_ONEPASS ? 2 : 0);
+  a.launch = algo == SCMP_ALGO_MFMA_PERSISTENT ? 1
+             : algo == SCMP_ALGO_MFMA_ONEPASS   ? 2
+             : algo == SCMP_ALGO_MFMA_QUARTER   ? 3
+                                                : 0;
+  a.auto_quarter = algo == SCMP_ALGO_AUTO ? 1 : 0;
   const bool bitserial = algo == SCMP_ALGO_BITSERIAL;
   fill_tiles(a, P, bitserial ? 64 : 128);
   for (int b = 0; b <= P.n_bands; ++b) a.band_cols[b] = P.band_cols[b];

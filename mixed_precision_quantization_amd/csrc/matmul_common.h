@@ -36,7 +36,8 @@ struct MatmulArgs {
   const uint8_t* pair;
   const uint16_t* cum;
   int G, M, N, D, chunk_d, n_chunks, n_rungs, n_bands, q, P, Wl, Lmax;
-  int launch;  // matrix-core launch form: 0 by size, 1 persistent, 2 one block per tile
+  int launch;  // matrix-core launch form: 0 by size, 1 persistent, 2 one block per tile, 3 quarter (persistent)
+  int auto_quarter;  // launch 0 may take the quarter form (AUTO; not MFMA)
   int cuts[SCMP_MAX_RUNGS + 1];
   int tile_start[SCMP_MAX_RUNGS + 1];  // first row tile of each rung (128 rows; 64 for bit-serial)
   int band_cols[SCMP_MAX_BANDS + 1];

@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cmath>
 #include <string>
 #include <vector>
 
@@ -51,6 +52,7 @@ namespace scmp {
 constexpr int MF_BM = 128, MF_BN = 128, MF_DC = 32;
 constexpr int PT_STRIDE = 144;  // bytes per level row of the paired table in LDS
 constexpr int PREP_BLOCKS = 1024;  // encode blocks aimed for (tiles x parts of the contraction axis)
+constexpr int PERS_QUEUES = 8;     // work queues of the persistent contraction (counters in the workspace header)
 
 
 struct MfmaWs {
@@ -64,14 +66,28 @@ struct MfmaWs {
   uint32_t* ubi;    // [G][Dp][Np/2]  table offset words, by index then column pair
   int32_t* rowid;   // [G][Mp]       original row of each sorted position (-1: none)
   float* sas;       // [G][Mp]       row scale of each sorted position (single-segment plans)
-  // Fixed header at offset 0 (the same place for every size and tiling):
-  // [0] fp4 MFMA steps issued over the row tiles, [1] the number of window
-  // sums, [2] their byte offset in the workspace; k_prep writes [1] and [2]
-  // and clears [0] and the work counter.
+  // Fixed header at offset 0 (the same place for every size and tiling),
+  // written by k_prep: [0] the number of step slots, [1] their byte offset,
+  // [2] the number of window sums, [3] their byte offset.  k_prep also
+  // clears the work counters that follow.
   unsigned long long* hdr;
+  uint32_t* steps;             // [G][RT][CT][4] wave steps (four fp4 MFMAs each) of every output tile
+  unsigned long long steps_off; // byte offset of steps
   unsigned long long* wsum;    // [G][RT][n_parts] window positions of each encode block's rows (prep_rows)
   unsigned long long wsum_off; // byte offset of wsum
-  unsigned int* work;          // work counter of the persistent contraction
+  unsigned int* work;          // [PERS_QUEUES] work counters of the persistent contraction
+  // Quarter codes of the quarter contraction (k_mfma_qpt; null when another
+  // kernel runs): per (row pair, index pair) the byte offsets of the two
+  // rows' entries in the A pair table for paired positions [0, 8); per
+  // (column pair, index pair, ladder rung) those in the rung's B pair
+  // table.  Layout: qcode_index.
+  uint32_t* hq;   // [G][RT] tiles
+  uint32_t* uq;   // [n_ladder][G][CT] tiles
+  int qpt_on;     // the quarter contraction runs: k_prep writes hq / uq
+  // Tile order of the staged kernel: 0 = its (CT, RT, G) grid; 1 = a 1-D
+  // grid where XCD x takes row tiles (g, y) with (g RT + y) = x (mod 8), each
+  // with all its column tiles in turn (staged_tile).
+  int row_units;
   long long Mp, Np, Dp;
   int RT, CT;
   // The encode kernels split the contraction axis into n_parts parts of
@@ -79,6 +95,53 @@ struct MfmaWs {
   // are the chunk sums; otherwise the decode adds the parts' partial sums).
   int n_parts, part_len;
 };
+
+// Whether the quarter contraction (k_mfma_qpt) can run this call: a
+// bipolar plan with one band starting on a group boundary and no chunk
+// scales (one accumulation segment), an int item count, and per-tile maxima
+// that fit the kernel's LDS copy.
+constexpr int QPT_MAX_DP = 4096;
+static bool qpt_capable(const MatmulArgs& a, int RT, int CT, long long Dp) {
+  if (a.unipolar || a.chunk_d > 0 || a.n_bands != 1 || a.band_cols[0] % MF_DC != 0) return false;
+  if (Dp > QPT_MAX_DP) return false;
+  return (double)RT * a.G * CT < 2147483647.0;
+}
+
+// Whether the workspace holds the quarter codes: the quarter launch was
+// asked for (launch 3), or AUTO may take it (long contraction axes).  This
+// depends on nothing that the workspace query does not see, so a call never
+// needs more workspace than the query reported.
+static bool quarter_buffers(const MatmulArgs& a, const MfmaWs& w) {
+  if (!qpt_capable(a, w.RT, w.CT, w.Dp)) return false;
+  return a.launch == 3 || (a.launch == 0 && a.auto_quarter && a.D >= 512);
+}
+
+// Whether the quarter contraction is the one to run (when the persistent
+// grid runs at all and its codes are in the workspace): asked for, or chosen
+// by AUTO when at least half of the row tiles run streams of at most 96,
+// where most indices of a tile need no more than 8 paired positions and the
+// quarter steps halve the matrix-core work.  Elsewhere its per-group
+// two-mode schedule costs more than it saves (measured: the mixed-precision
+// MLP projection with 55% of its rows at 64 and 96 faster; uniform 128 and
+// 256 on the same shape, and D = 64 attention scores, slower).
+static bool quarter_chosen(const MatmulArgs& a) {
+  if (a.launch == 3) return true;
+  if (a.group_rung) return false;
+  int short_tiles = 0;
+  for (int k = 0; k < a.n_rungs; ++k)
+    if (a.bandL[0][k] <= 96) short_tiles += a.tile_start[k + 1] - a.tile_start[k];
+  return 2 * short_tiles >= a.tile_start[a.n_rungs] && a.tile_start[a.n_rungs] > 0;
+}
+
+// Quarter-code layout: for tile plane t (a row or column tile), group grp
+// and lane half h, the 64 pairs of the tile hold 8 words each: word 2 s + p
+// is index pair 4 s + 2 h + p of the group (indices 8 s + 4 h + 2 p and
+// + 1), low half for the pair's first row (column), high half for the
+// second.  A lane reads its 8 words as two 16-byte pieces; 32 lanes read one
+// contiguous kilobyte.
+__device__ __forceinline__ long long qcode_index(long long plane, int ngrp, int grp, int h, int pr) {
+  return (((plane * ngrp + grp) * 2 + h) * 64 + pr) * 8;
+}
 
 static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   MfmaWs w{};
@@ -112,13 +175,20 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   const size_t ubi_b = index_major ? ub_b : 0;
   const size_t ri_b = al((size_t)a.G * w.Mp * sizeof(int32_t));
   const size_t sa_b = al((size_t)a.G * w.Mp * sizeof(float));
-  const size_t ts_b = al(3 * sizeof(unsigned long long) + sizeof(unsigned int));
+  const size_t ts_b = al(4 * sizeof(unsigned long long) + PERS_QUEUES * sizeof(unsigned int));
+  const size_t st_b = al((size_t)a.G * w.RT * w.CT * 4 * sizeof(uint32_t));
   const size_t wsum_b = al((size_t)a.G * w.RT * w.n_parts * sizeof(unsigned long long));
+  const bool qpt = quarter_buffers(a, w);
+  const size_t hq_b = qpt ? al((size_t)a.G * w.Mp * w.Dp) : 0;
+  const size_t uq_b = qpt ? al((size_t)a.n_ladder * a.G * w.Np * w.Dp) : 0;
   char* p = (char*)base;
   // The header first, at an offset that does not depend on the sizes.
   w.hdr = (unsigned long long*)(p ? p + off : nullptr);
-  w.work = (unsigned int*)(p ? p + off + 3 * sizeof(unsigned long long) : nullptr);
+  w.work = (unsigned int*)(p ? p + off + 4 * sizeof(unsigned long long) : nullptr);
   off += ts_b;
+  w.steps = (uint32_t*)(p ? p + off : nullptr);
+  w.steps_off = off;
+  off += st_b;
   w.hs = (uint32_t*)(p ? p + off : nullptr);
   off += hs_b;
   w.maxh = (uint8_t*)(p ? p + off : nullptr);
@@ -138,9 +208,20 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
   w.wsum = (unsigned long long*)(p ? p + off : nullptr);
   w.wsum_off = off;
   off += wsum_b;
+  w.hq = (qpt && p) ? (uint32_t*)(p + off) : nullptr;
+  off += hq_b;
+  w.uq = (qpt && p) ? (uint32_t*)(p + off) : nullptr;
+  off += uq_b;
   *total = off;
   return w;
 }
+
+// Makes a loaded value available here, on every path.  The output stores
+// of an epilogue sit in conditional blocks; a value whose first use is
+// inside one of them would otherwise be awaited again in each later block,
+// behind every store issued since (stores and loads share one counter).
+__device__ __forceinline__ void settle(float& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle(int& v) { asm volatile("" : "+v"(v)); }
 
 __device__ __forceinline__ int wave_max_i(int v) {
 #pragma unroll
@@ -180,6 +261,55 @@ __device__ __forceinline__ void load8(const int8_t* src, int valid, int8_t* out)
 #pragma unroll
     for (int i = 0; i < 8; ++i) out[i] = i < valid ? src[i] : (int8_t)0;
   }
+}
+
+// Pair-table classes of paired positions [0, 8) (quarter 0).  A row's
+// quarter of index d is n = min(hh, 8) leading sign nibbles: class 0 when
+// n = 0, else 2 n - 1 + neg (17 classes).  A B level's quarter at length L
+// is fixed by c = the sum of its eight pair sums (0..16): the pair sums rise
+// monotonically with the level, so equal sums mean equal patterns (17
+// classes).  A pair table holds, at entry 17 c1 + c2, the 8-byte operand of
+// two indices (classes c1, c2).
+constexpr int QPT_CLASSES = 17;
+constexpr int QPT_ENTRIES = QPT_CLASSES * QPT_CLASSES;
+__device__ __forceinline__ int a_class(int code) {
+  const int n = min(code >> 5, 8);
+  return n == 0 ? 0 : 2 * n - 1 + ((code >> 4) & 1);
+}
+// The 8 e2m1 nibbles of A class a: n leading sign nibbles (0x2 = +1,
+// 0xA = -1), then zeros.
+__device__ __forceinline__ uint32_t a_class_word(int a) {
+  if (a == 0) return 0u;
+  const int n = (a + (a & 1)) >> 1;
+  const bool neg = (a & 1) == 0;
+  const uint32_t v = 0x22222222u & (n >= 8 ? 0xffffffffu : ((1u << (4 * n)) - 1u));
+  return neg ? (v | (v << 2)) : v;
+}
+// Byte offset of the pair-table entry of classes (c1, c2).
+__device__ __forceinline__ uint32_t qpt_off(int c1, int c2) { return (uint32_t)(c1 * QPT_CLASSES + c2) * 8u; }
+
+// Output tile of a staged-kernel block.  Workgroups are dispatched to the
+// 8 XCDs in turn (block b to XCD b mod 8), each XCD with its own L2.  With
+// row_units, block b = 8 s + x takes the s-th tile of XCD x: row tile
+// u = x + 8 (s / CT) (u = g RT + y) and column tile s mod CT, so a row
+// tile's codes are read by one XCD, which keeps them for all its column
+// tiles, while the column codes are shared by the row tiles that XCD runs
+// at once.  Blocks past the last row tile return at once (false).
+__device__ __forceinline__ bool staged_tile(const MatmulArgs& a, const MfmaWs& w, int& g, int& y, int& bx) {
+  if (!w.row_units) {
+    bx = (int)blockIdx.x;
+    y = (int)blockIdx.y;
+    g = (int)blockIdx.z;
+    return true;
+  }
+  const unsigned b = blockIdx.x, s = b >> 3;
+  const unsigned j = s / (unsigned)w.CT;
+  const long long u = (long long)(b & 7u) + 8LL * j;
+  if (u >= (long long)a.G * w.RT) return false;
+  bx = (int)(s - j * (unsigned)w.CT);
+  g = (int)(u / w.RT);
+  y = (int)(u - (long long)g * w.RT);
+  return true;
 }
 
 // ------------------------------------------------------------ prep A ----
@@ -284,6 +414,7 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
       }
       uint32_t word[8];
       int mh[8];
+      int cw[2][8];  // window codes of the lane's two rows
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         int code[2] = {0, 0}, hh[2] = {0, 0};
@@ -298,6 +429,8 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
           }
         }
         word[i] = (uint32_t)code[0] | ((uint32_t)code[1] << 16);
+        cw[0][i] = code[0];
+        cw[1][i] = code[1];
         mh[i] = max(hh[0], hh[1]);
         win += (uint32_t)(code[0] >> 5) + (uint32_t)(code[1] >> 5);
       }
@@ -309,6 +442,20 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
         uint32_t* di = w.hsi + ((long long)g * w.Dp + dfirst) * (w.Mp / 2) + (long long)y * 64 + pr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) di[(long long)i * (w.Mp / 2)] = word[i];
+      }
+      if (w.qpt_on) {
+        // Quarter codes of this lane's two rows: this wave's 8 indices are
+        // quarter-step q of the group (d0 is a multiple of 32 here).
+        uint32_t qw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t lo = qpt_off(a_class(cw[0][2 * t]), a_class(cw[0][2 * t + 1]));
+          const uint32_t hi = qpt_off(a_class(cw[1][2 * t]), a_class(cw[1][2 * t + 1]));
+          qw[t] = lo | (hi << 16);
+        }
+        const long long plane = (long long)g * w.RT + y;
+        *(uint2*)(w.hq + qcode_index(plane, ngrp, d0 >> 5, 0, pr) + 2 * q) = uint2{qw[0], qw[1]};
+        *(uint2*)(w.hq + qcode_index(plane, ngrp, d0 >> 5, 1, pr) + 2 * q) = uint2{qw[2], qw[3]};
       }
       // Tile maximum per index: over the wave's 64 pairs.
       int mine = 0;
@@ -348,11 +495,25 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
   // the magnitude's level row, with the sign of x in bit 0 (row offsets are
   // multiples of 16).
   __shared__ uint32_t s_off[256];
+  __shared__ uint16_t s_lev[256];  // bipolar level of each stored value (quarter contraction)
+  // Quarter-0 classes of every ladder rung and level: the sum of the pair
+  // sums of paired positions [0, 8).
+  __shared__ uint8_t s_bc[SCMP_MAX_RUNGS][MAX_LEVELS];
   const int tid = threadIdx.x;
   {
     const int x = tid - 128;
     s_off[tid] = a.unipolar ? (uint32_t)(uni_level_of(x, a.P, a.q) * PT_STRIDE) | (x < 0 ? 1u : 0u)
                             : (uint32_t)(level_of(x, a.P, a.q) * PT_STRIDE);
+    s_lev[tid] = (uint16_t)level_of(x, a.P, a.q);
+  }
+  if (w.qpt_on) {
+    for (int idx = tid; idx < a.n_ladder * (a.P + 1); idx += 256) {
+      const int k = idx / (a.P + 1), u = idx - k * (a.P + 1);
+      const int L = a.bandL[0][k];
+      const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
+      const uint2 x = *(const uint2*)(a.pair + a.pair_off[0][k] + (long long)u * KLpad);
+      s_bc[k][u] = (uint8_t)(((x.x + x.y) * 0x01010101u) >> 24);  // bytes <= 2: no carries
+    }
   }
   const int c0 = bx * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
@@ -360,10 +521,11 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
   // The contraction (launched after this kernel on the same stream) adds
   // its issued steps to this counter.
   if (bx == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
-    w.hdr[0] = 0;
-    w.hdr[1] = (unsigned long long)a.G * w.RT * w.n_parts;
-    w.hdr[2] = w.wsum_off;
-    *w.work = 0;
+    w.hdr[0] = (unsigned long long)a.G * w.RT * w.CT * 4;
+    w.hdr[1] = w.steps_off;
+    w.hdr[2] = (unsigned long long)a.G * w.RT * w.n_parts;
+    w.hdr[3] = w.wsum_off;
+    for (int i = 0; i < PERS_QUEUES; ++i) w.work[i] = 0;
   }
   const int cp = tid >> 2, q = tid & 3;
   const int col_lo = c0 + pair_lo(cp), col_hi = col_lo + 32;
@@ -388,6 +550,29 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
     }
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst, cp)) = uint4{word[0], word[1], word[2], word[3]};
     *(uint4*)(w.ub + enc_word(tile, ngrp, dfirst + 4, cp)) = uint4{word[4], word[5], word[6], word[7]};
+    if (w.qpt_on) {
+      // Quarter codes of both columns for every ladder rung: this thread's
+      // 8 indices are quarter-step q of the group.
+      int lv[2][8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        lv[0][i] = (i < span && col_lo < a.N) ? s_lev[(int)x_lo[i] + 128] : (a.P >> 1);
+        lv[1][i] = (i < span && col_hi < a.N) ? s_lev[(int)x_hi[i] + 128] : (a.P >> 1);
+      }
+      const long long rung_stride = (long long)a.G * w.CT * ngrp * 1024;
+      for (int k = 0; k < a.n_ladder; ++k) {
+        uint32_t qw[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint32_t lo = qpt_off(s_bc[k][lv[0][2 * t]], s_bc[k][lv[0][2 * t + 1]]);
+          const uint32_t hi = qpt_off(s_bc[k][lv[1][2 * t]], s_bc[k][lv[1][2 * t + 1]]);
+          qw[t] = lo | (hi << 16);
+        }
+        uint32_t* base = w.uq + (long long)k * rung_stride;
+        *(uint2*)(base + qcode_index(tile, ngrp, d0 >> 5, 0, cp) + 2 * q) = uint2{qw[0], qw[1]};
+        *(uint2*)(base + qcode_index(tile, ngrp, d0 >> 5, 1, cp) + 2 * q) = uint2{qw[2], qw[3]};
+      }
+    }
     if (w.ubi) {
       uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)bx * 64 + cp;
 #pragma unroll
@@ -441,6 +626,13 @@ __device__ __forceinline__ void init_patterns(uint32_t* pat, int tid, int nthrea
   }
 }
 
+// Four pair-sum bytes (0, 1 or 2) as four e2m1 nibbles (value v -> code
+// 2 v): byte k of wd becomes nibble k of the result's low 16 bits.
+__device__ __forceinline__ uint32_t pair_nibbles(uint32_t wd) {
+  const uint32_t t = wd << 1;  // bytes <= 2: doubling never carries
+  return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
+}
+
 // The paired table of band b, rung k as e2m1 nibbles (value v -> code 2 v,
 // position p in nibble p mod 2 of byte p / 2), one LDS row of PT_STRIDE
 // bytes per B level.
@@ -451,11 +643,8 @@ __device__ __forceinline__ void stage_pair_table(uint8_t* pt, const MatmulArgs& 
   for (int idx = tid; idx < (a.P + 1) * vec_per_row; idx += nthreads) {
     const int u = idx / vec_per_row, v = idx - u * vec_per_row;
     const uint4 x = *(const uint4*)(src + (long long)u * KLpad + v * 16);
-    auto pack = [](uint32_t wd) {
-      const uint32_t t = wd << 1;  // bytes <= 2: doubling never carries
-      return (t & 0xFu) | ((t >> 4) & 0xF0u) | ((t >> 8) & 0xF00u) | ((t >> 12) & 0xF000u);
-    };
-    *(uint2*)(pt + u * PT_STRIDE + v * 8) = uint2{pack(x.x) | (pack(x.y) << 16), pack(x.z) | (pack(x.w) << 16)};
+    *(uint2*)(pt + u * PT_STRIDE + v * 8) =
+        uint2{pair_nibbles(x.x) | (pair_nibbles(x.y) << 16), pair_nibbles(x.z) | (pair_nibbles(x.w) << 16)};
   }
 }
 
@@ -584,12 +773,13 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   __shared__ __align__(16) float s_sa[BM];    // row scale of that chunk
 
   const int tid = threadIdx.x;
-  const int g = blockIdx.z, y = blockIdx.y;  // y: encode tile (128 rows of one rung)
+  int g, y, bx;  // y: encode tile (128 rows of one rung); bx: column tile
+  if (!staged_tile(a, w, g, y, bx)) return;
   int k, pos0, nrows;
   locate_tile(a, y, BM, k, pos0, nrows);
   k = tile_rung(a, g, k);
   const long long prow0 = (long long)y * BM;
-  const int col0 = blockIdx.x * BN;
+  const int col0 = bx * BN;
   for (int r = tid; r < BM; r += 256) s_rows[r] = r < nrows ? row_of(a, g, pos0 + r) : -1;
   init_patterns(s_tab.pat, tid, 256);
 
@@ -611,7 +801,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   int rmx = 0;
   const int ngrp = (int)(w.Dp / MF_DC);
   const uint32_t* hblk = w.hs + enc_word((long long)g * w.RT + y, ngrp, 0, 0) + 4 * tid;
-  const uint32_t* ublk = w.ub + enc_word((long long)g * w.CT + blockIdx.x, ngrp, 0, 0) + 4 * tid;
+  const uint32_t* ublk = w.ub + enc_word((long long)g * w.CT + bx, ngrp, 0, 0) + 4 * tid;
   const int sp = tid & 31, se = 16 * ((tid >> 5) & 1) + 4 * ((tid >> 6) & 3);
   auto fetch = [&](int d0) {
     const long long gb = (long long)(d0 >> 5) << 11;
@@ -673,7 +863,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         if (CHUNKED) cacc[i][j][v] = 0.0f;
         if (COUNTS) bacc[i][j][v] = 0;
       }
-  unsigned long long issued = 0;  // fp4 MFMA steps of this row tile (counted by the x == 0 blocks)
+  // A wave whose 64 rows or 64 columns all lie past the tile's valid ones
+  // (the last row tile of a rung, the last column tile) has nothing to
+  // contract: it still stages and synchronises with the block, but issues no
+  // MFMA.  Each wave counts its own steps (64 x 64 x 64 MACs each).
+  const bool wave_live = wrow0 < nrows && col0 + wcol0 < a.N;
+  uint32_t issued = 0;
 
   int buf = 0;
   fetch(a.band_cols[0]);
@@ -766,7 +961,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // and 16 hf + 2 m + 1 (Y).  Past the last level the entries fall on
         // level full <= NLEV (position <= 16 NLEV <= 256, inside the table
         // rows): read, never used.
-        if (full > 0)
+        if (full > 0 && wave_live)
           sweep(
               8 * full,
               [&](int st) {
@@ -777,8 +972,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
               },
               item2);
         // The rest from the stage's list.
-        if (n > 0) sweep(n, [&](int st) { return sched[2 * st]; }, item);
-        if (blockIdx.x == 0 && tid == 0) issued += n + 8 * full;
+        if (n > 0 && wave_live) sweep(n, [&](int st) { return sched[2 * st]; }, item);
+        if (wave_live) issued += n + 8 * full;
       }
       const int cend = chunk_end(a, d0);
       if (CHUNKED && min(dn, dend) >= cend) {
@@ -845,7 +1040,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
     }
     if (dend < a.D) buf ^= 1;  // the next band starts on the other buffer
   }
-  if (blockIdx.x == 0 && tid == 0) atomicAdd(w.hdr, issued);  // fp4 steps
+  if (lane == 0) w.steps[(((long long)g * w.RT + y) * w.CT + bx) * 4 + wave] = issued;
 
   if (!CHUNKED) {
     // Each row's n0 sum over the whole contraction axis: the parts' partial
@@ -855,6 +1050,8 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + prow0 + r;
       for (int pt = 0; pt < w.n_parts; ++pt) tot += rc0[(long long)pt * w.Mp];
       s_rc[r] = tot;
+      const int row = s_rows[r];
+      s_sa[r] = row >= 0 ? a.sA[(long long)g * a.M + row] : 0.0f;
     }
     __syncthreads();
   }
@@ -863,9 +1060,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int col = col0 + wcol0 + j * 32 + l32;
-    const float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
-    const float bj = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
-    const int ccol = col < a.N ? out_col(a, col) : -1;
+    float sb = (!CHUNKED && col < a.N) ? a.sB[(long long)g * a.N + col] : 0.0f;
+    float bj = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
+    int ccol = col < a.N ? out_col(a, col) : -1;
+    settle(sb);
+    settle(bj);
+    settle(ccol);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -879,8 +1079,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         } else {
           const int cnt = (int)acc[i][j][v] + s_rc[r];
           if (COUNTS) a.counts[((long long)g * a.M + row) * a.N + col] = cnt;
-          const float sa = a.sA[(long long)g * a.M + row];
-          out = (sa * sb) * (scale0 * (float)(UNI ? cnt : 2 * cnt - L0 * a.D));
+          out = (s_sa[r] * sb) * (scale0 * (float)(UNI ? cnt : 2 * cnt - L0 * a.D));
         }
         if (a.C && ccol >= 0) a.C[(long long)g * a.bsc + (long long)row * a.ldc + ccol] = out + bj;
       }
@@ -928,6 +1127,22 @@ __device__ __forceinline__ PersItem pers_item(const MatmulArgs& a, int CT, int i
   return it;
 }
 
+// Work queues.  With CT a multiple of PERS_QUEUES, the items of column
+// tiles x = q (mod PERS_QUEUES) form queue q, in the order above (per row
+// tile, the queue's column tiles in turn); otherwise there is one queue.
+// Block b starts on queue b mod PERS_QUEUES: workgroups are dispatched to
+// the 8 XCDs in turn, so each XCD's L2 serves the codes of its own column
+// tiles only.  A block whose queue is empty takes items from the others.
+// Item ids are q * per + t (t-th item of queue q, per items per queue).
+__device__ __forceinline__ PersItem pers_item_q(const MatmulArgs& a, int CT, int nq, int per, int id) {
+  const int qi = id / per, t = id - qi * per;
+  const int cpq = CT / nq;  // column tiles per queue
+  const int f = t / cpq;    // row-tile unit (rung, group, row tile)
+  PersItem it = pers_item(a, 1, f);
+  it.x = (t - f * cpq) * nq + qi;
+  return it;
+}
+
 template <bool COUNTS>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a, MfmaWs w, int n_items) {
   struct __align__(16) GatherTables {
@@ -963,16 +1178,28 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
   };
 
+  const int nq = (w.CT % PERS_QUEUES == 0) ? PERS_QUEUES : 1;
+  const int per = n_items / nq;
+  const int home = (int)(blockIdx.x % (unsigned)nq);
+  // Next item id for this block (n_items when every queue is empty).
+  auto fetch = [&]() {
+    for (int i = 0; i < nq; ++i) {
+      const int qi = (home + i) % nq;
+      const unsigned t = atomicAdd(w.work + qi, 1u);
+      if (t < (unsigned)per) return qi * per + (int)t;
+    }
+    return n_items;
+  };
   init_patterns(s_pat, tid, 256);
   if (tid == 0) {
-    s_item[0] = (int)atomicAdd(w.work, 1u);
-    s_item[1] = (int)atomicAdd(w.work, 1u);
+    s_item[0] = fetch();
+    s_item[1] = s_item[0] < n_items ? fetch() : n_items;
   }
   __syncthreads();
   int item = s_item[0];
   if (item >= n_items) return;
   if (tid < MF_BM) {
-    const PersItem it = pers_item(a, w.CT, item);
+    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
     int row, rc;
     float sa;
     row_data(it.g, it.y, row, rc, sa);
@@ -986,21 +1213,20 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
                       __attribute__((always_inline)) { return scmp::frags_at(pat, s_pt, hx, ux, kx, hy, uy, ky); };
   v16f acc[2][2];
   auto mma = [&](const Frag& f) __attribute__((always_inline)) { mma_step(acc, f); };
-  unsigned long long issued = 0;  // fp4 MFMA steps of the column-0 tiles
+  uint32_t issued = 0;  // this wave's steps in the current tile (64 x 64 x 64 MACs each)
   int staged_k = -1;
   int cur = 0;
 
   while (true) {
-    const PersItem it = pers_item(a, w.CT, item);
+    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
     const int k = tile_rung(a, it.g, it.k), g = it.g, y = it.y;
     const int col0 = it.x * MF_BN;
-    const bool count_steps = it.x == 0;
     const int next = s_item[cur ^ 1];
     // The next tile's row data, read now and stored after this tile.
     int nrow = -1, nrc = 0;
     float nsa = 0.0f;
     if (next < n_items && tid < MF_BM) {
-      const PersItem nt = pers_item(a, w.CT, next);
+      const PersItem nt = pers_item_q(a, w.CT, nq, per, next);
       row_data(nt.g, nt.y, nrow, nrc, nsa);
     }
     const int L = a.bandL[0][k];
@@ -1070,7 +1296,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
           if (s0 + r < nsteps) mma(fr[r & 1]);
         }
       }
-      if (count_steps) issued += nsteps;
+      issued += nsteps;
     };
 
     const int dbeg = a.band_cols[0], dend = a.band_cols[1];
@@ -1139,7 +1365,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
             mma(fb);
           }
         }
-        if (count_steps) issued += 8 * full;
+        issued += 8 * full;
       }
       // The next group adds at most 256 entries.
       if (cnt > FL_LIST - 256 - PAD4 || (grp == ngrp - 1 && cnt > 0)) {
@@ -1163,13 +1389,15 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
       }
     }
 
+    if (lane == 0) w.steps[(long long)item * 4 + wave] = issued;
+    issued = 0;
     // The next tile's row data into the other buffer; the tile after it.
     if (tid < MF_BM) {
       s_rows[cur ^ 1][tid] = nrow;
       s_rc[cur ^ 1][tid] = nrc;
       s_sa[cur ^ 1][tid] = nsa;
     }
-    if (tid == 0) s_item[cur] = next < n_items ? (int)atomicAdd(w.work, 1u) : n_items;
+    if (tid == 0) s_item[cur] = next < n_items ? fetch() : n_items;
 
     // Decode: rows four at a time (accumulator entries v = 4 q .. 4 q + 3
     // are consecutive rows), each used by both column subtiles.
@@ -1182,6 +1410,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
       sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
       bj[j] = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
       ccol[j] = col < a.N ? out_col(a, col) : -1;
+      settle(sb[j]);
+      settle(bj[j]);
+      settle(ccol[j]);
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -1212,12 +1443,447 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     item = next;
     cur ^= 1;
   }
-  if (tid == 0 && issued) atomicAdd(w.hdr, issued);
+}
+
+// ---------------------------------------------------------- quarters ----
+// The single-segment contraction with paired positions [0, 16) taken a
+// quarter (8 positions) at a time.  Per output tile (from the work queues
+// of k_mfma_pers) two passes run:
+//  pass 1  per group of 32 indices, quarter 0 (positions [0, 8)) in four
+//          steps of 8 indices each, and quarter 1 (positions [8, 16)) in
+//          four more when some index of the group needs them.  A lane's
+//          operand for 4 indices is two 8-byte entries of a pair table
+//          (A: the 17 x 17 window classes; B: the rung's 17 x 17 pair-sum
+//          classes), found through the quarter codes k_prep wrote, so a
+//          step costs the eight LDS reads of a 16-position step of
+//          k_mfma_pers while covering twice the indices.
+//  pass 2  paired positions from 16 on, as in k_mfma_pers: levels of 16
+//          positions every index of a group needs are swept from the
+//          group's codes, the others are listed and swept from the wave's
+//          LDS list.
+// The tile's per-index maxima (needed by both passes) are staged in LDS,
+// read during the previous tile.
+template <bool COUNTS>
+__global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, MfmaWs w, int n_items) {
+  struct __align__(16) GatherTables {
+    uint8_t pt[MAX_LEVELS * PT_STRIDE];
+    uint32_t pat[PAT_WORDS];
+    uint2 apt[QPT_ENTRIES];  // A pair table of quarter 0 (window classes of two indices)
+    uint2 bpt[QPT_ENTRIES];  // B pair table of quarter 0 for the staged rung
+    uint32_t bpat[QPT_CLASSES];
+  };
+  __shared__ GatherTables s_tab;
+  __shared__ __align__(8) uint32_t s_list[4][FL_LIST];
+  __shared__ __align__(16) int s_rows[2][MF_BM];
+  __shared__ __align__(16) int s_rc[2][MF_BM];
+  __shared__ __align__(16) float s_sa[2][MF_BM];
+  __shared__ __align__(16) uint8_t s_maxh[2][QPT_MAX_DP];  // tile maximum of every index
+  __shared__ int s_item[2];
+  uint8_t* const s_pt = s_tab.pt;
+  uint32_t* const s_pat = s_tab.pat;
+  constexpr int PAD4 = 8 * FL_RING + 4;
+  constexpr int MX_PER = QPT_MAX_DP / 16 / 256;  // uint4 pieces of the maxima per thread
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wr = wave >> 1, wc = wave & 1;
+  const int l32 = lane & 31, hf = lane >> 5;
+  const int wrow0 = wr * 64, wcol0 = wc * 64;
+  uint32_t* const list = s_list[wave];
+  const int qq = a.q * a.q;
+  const int ngrp_all = (int)(w.Dp / MF_DC);
+  const int n_mx = (int)(w.Dp >> 4);  // uint4 pieces of one tile's maxima
+
+  const int nq = (w.CT % PERS_QUEUES == 0) ? PERS_QUEUES : 1;
+  const int per = n_items / nq;
+  const int home = (int)(blockIdx.x % (unsigned)nq);
+  auto fetch = [&]() {
+    for (int i = 0; i < nq; ++i) {
+      const int qi = (home + i) % nq;
+      const unsigned t = atomicAdd(w.work + qi, 1u);
+      if (t < (unsigned)per) return qi * per + (int)t;
+    }
+    return n_items;
+  };
+  auto row_data = [&](int g, int y, int& row, int& rc, float& sa) __attribute__((always_inline)) {
+    const long long pos = (long long)g * w.Mp + (long long)y * MF_BM + tid;
+    row = w.rowid[pos];
+    sa = w.sas[pos];
+    rc = 0;
+    const int32_t* rc0 = w.rowc + (long long)g * w.n_parts * w.Mp + (long long)y * MF_BM + tid;
+    for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
+  };
+  auto maxh_load = [&](int g, int y, uint4 (&mx)[MX_PER]) __attribute__((always_inline)) {
+    const uint4* src = (const uint4*)(w.maxh + ((long long)g * w.RT + y) * w.Dp);
+#pragma unroll
+    for (int i = 0; i < MX_PER; ++i) {
+      const int idx = tid + 256 * i;
+      mx[i] = idx < n_mx ? src[idx] : uint4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto maxh_store = [&](int buf, const uint4 (&mx)[MX_PER]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < MX_PER; ++i) {
+      const int idx = tid + 256 * i;
+      if (idx < n_mx) ((uint4*)s_maxh[buf])[idx] = mx[i];
+    }
+  };
+
+  init_patterns(s_pat, tid, 256);
+  for (int e = tid; e < QPT_ENTRIES; e += 256)
+    s_tab.apt[e] = uint2{a_class_word(e / QPT_CLASSES), a_class_word(e % QPT_CLASSES)};
+  if (tid == 0) {
+    s_item[0] = fetch();
+    s_item[1] = s_item[0] < n_items ? fetch() : n_items;
+  }
+  __syncthreads();
+  int item = s_item[0];
+  if (item >= n_items) return;
+  {
+    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    if (tid < MF_BM) {
+      int row, rc;
+      float sa;
+      row_data(it.g, it.y, row, rc, sa);
+      s_rows[0][tid] = row;
+      s_rc[0][tid] = rc;
+      s_sa[0][tid] = sa;
+    }
+    uint4 mx[MX_PER];
+    maxh_load(it.g, it.y, mx);
+    maxh_store(0, mx);
+  }
+
+  const uint8_t* const pat = (const uint8_t*)s_pat;
+  auto frags_at = [&](uint32_t hx, uint32_t ux, uint32_t kx, uint32_t hy, uint32_t uy, uint32_t ky)
+                      __attribute__((always_inline)) { return scmp::frags_at(pat, s_pt, hx, ux, kx, hy, uy, ky); };
+  v16f acc[2][2];
+  auto mma = [&](const Frag& f) __attribute__((always_inline)) { mma_step(acc, f); };
+  uint32_t issued = 0;  // this wave's steps in the current tile (64 x 64 x 64 MACs each)
+  int staged_k = -1;
+  int cur = 0;
+
+  while (true) {
+    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    const int k = tile_rung(a, it.g, it.k), g = it.g, y = it.y;
+    const int col0 = it.x * MF_BN;
+    const int next = s_item[cur ^ 1];
+    const int L = a.bandL[0][k];
+    if (k != staged_k) {
+      // Every wave finished the previous tile (the loop ends on a barrier).
+      const int KLpad = ((((L + 1) >> 1) + 31) & ~31);
+      stage_pair_table(s_pt, a, 0, k, KLpad, tid, 256);
+      // The rung's quarter-0 patterns by class (every level writes the
+      // pattern of its class; levels of one class write the same word),
+      // then the B pair table.
+      for (int u = tid; u <= a.P; u += 256) {
+        const uint2 x = *(const uint2*)(a.pair + a.pair_off[0][k] + (long long)u * KLpad);
+        s_tab.bpat[((x.x + x.y) * 0x01010101u) >> 24] = pair_nibbles(x.x) | (pair_nibbles(x.y) << 16);
+      }
+      __syncthreads();
+      for (int e = tid; e < QPT_ENTRIES; e += 256)
+        s_tab.bpt[e] = uint2{s_tab.bpat[e / QPT_CLASSES], s_tab.bpat[e % QPT_CLASSES]};
+      __syncthreads();
+      staged_k = k;
+    }
+
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+    const int dbeg = a.band_cols[0], dend = a.band_cols[1];
+    const int ngrp = (dend - dbeg + 31) / 32;
+    const uint8_t* const mxs = s_maxh[cur];
+
+    // ---- pass 1: paired positions [0, 16).  A group whose 32 maxima are
+    // all at most 8 (and one positive) takes quarter 0 only: four steps of
+    // 8 indices from the pair tables.  Any other group with a positive
+    // maximum takes level 0 as 16-position steps from its codes, eight steps
+    // of 4 indices.
+    {
+      // Uniform bases of this tile's codes and 32-bit lane offsets (words).
+      const uint32_t* const hq_t = w.hq + qcode_index((long long)g * w.RT + y, ngrp_all, dbeg / 32, 0, 0);
+      const uint32_t* const uq_t = w.uq + (long long)k * ((long long)a.G * w.CT * ngrp_all * 1024) +
+                                   qcode_index((long long)g * w.CT + it.x, ngrp_all, dbeg / 32, 0, 0);
+      const uint32_t* const hs_t = w.hs + enc_word((long long)g * w.RT + y, ngrp_all, 0, 0);
+      const uint32_t* const ub_t = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0);
+      const unsigned qa_off = (unsigned)((hf * 64 + wr * 32 + l32) * 8), qb_off = (unsigned)((hf * 64 + wc * 32 + l32) * 8);
+      const unsigned ha_off = (unsigned)((8 * wr + hf) * 128 + 4 * l32), hb_off = (unsigned)((8 * wc + hf) * 128 + 4 * l32);
+      const char* const apt = (const char*)s_tab.apt;
+      const char* const bpt = (const char*)s_tab.bpt;
+      // Mode of a group (uniform): 0 nothing, 1 quarter 0, 2 level 0.
+      auto mode_of = [&](int grp) __attribute__((always_inline)) {
+        const int m = grp < ngrp ? (int)mxs[32 * grp + l32] : 0;
+        return __builtin_amdgcn_readfirstlane(__ballot(m > 8) ? 2 : (__ballot(m > 0) ? 1 : 0));
+      };
+      // A group's codes in its mode, always as four 16-byte loads per
+      // buffer (the same loads in every mode, so the waits stay exact):
+      // quarter 0, pieces 0 and 1 hold its 8 words of A (B), pieces 2 and 3
+      // repeat them; otherwise the codes of indices d0 + 16 hf + m, m < 16.
+      auto load_codes = [&](int grp, int md, uint32_t* h, uint32_t* u) __attribute__((always_inline)) {
+        const bool qm = md == 1;
+        const uint4* hp = qm ? (const uint4*)(hq_t + ((unsigned)grp << 10) + qa_off)
+                             : (const uint4*)(hs_t + ((unsigned)(dbeg / 32 + grp) << 11) + ha_off);
+        const uint4* up = qm ? (const uint4*)(uq_t + ((unsigned)grp << 10) + qb_off)
+                             : (const uint4*)(ub_t + ((unsigned)(dbeg / 32 + grp) << 11) + hb_off);
+        const int stride = qm ? 1 : 64;  // uint4 between pieces
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int pi = qm ? (i & 1) : i;
+          const uint4 th = hp[stride * pi], tu = up[stride * pi];
+          h[4 * i] = th.x;
+          h[4 * i + 1] = th.y;
+          h[4 * i + 2] = th.z;
+          h[4 * i + 3] = th.w;
+          u[4 * i] = tu.x;
+          u[4 * i + 1] = tu.y;
+          u[4 * i + 2] = tu.z;
+          u[4 * i + 3] = tu.w;
+        }
+      };
+      // Quarter-step s: per row (column) subtile two 8-byte pair-table
+      // entries, index pairs 2 s and 2 s + 1 of the lane half (code words
+      // 2 s, 2 s + 1; low half subtile 0, high half subtile 1).
+      auto qfrag = [&](const uint32_t* ch, const uint32_t* cu, int st) __attribute__((always_inline)) {
+        const uint32_t wa0 = ch[2 * st], wa1 = ch[2 * st + 1], wb0 = cu[2 * st], wb1 = cu[2 * st + 1];
+        const v2i a00 = *(const v2i*)(apt + (wa0 & 0xffffu)), a01 = *(const v2i*)(apt + (wa1 & 0xffffu));
+        const v2i a10 = *(const v2i*)(apt + (wa0 >> 16)), a11 = *(const v2i*)(apt + (wa1 >> 16));
+        const v2i b00 = *(const v2i*)(bpt + (wb0 & 0xffffu)), b01 = *(const v2i*)(bpt + (wb1 & 0xffffu));
+        const v2i b10 = *(const v2i*)(bpt + (wb0 >> 16)), b11 = *(const v2i*)(bpt + (wb1 >> 16));
+        Frag f;
+        f.a[0] = v8i{a00.x, a00.y, a01.x, a01.y, 0, 0, 0, 0};
+        f.a[1] = v8i{a10.x, a10.y, a11.x, a11.y, 0, 0, 0, 0};
+        f.b[0] = v8i{b00.x, b00.y, b01.x, b01.y, 0, 0, 0, 0};
+        f.b[1] = v8i{b10.x, b10.y, b11.x, b11.y, 0, 0, 0, 0};
+        return f;
+      };
+      // One group's pass-1 steps; each step's fragments are read while the
+      // previous step's MFMAs run.
+      auto sweep = [&](const uint32_t* ch, const uint32_t* cu, int md) __attribute__((always_inline)) {
+        if (md == 1) {
+          Frag fa = qfrag(ch, cu, 0), fb = qfrag(ch, cu, 1);
+          __builtin_amdgcn_sched_barrier(0);
+          mma(fa);
+          fa = qfrag(ch, cu, 2);
+          __builtin_amdgcn_sched_barrier(0);
+          mma(fb);
+          fb = qfrag(ch, cu, 3);
+          __builtin_amdgcn_sched_barrier(0);
+          mma(fa);
+          __builtin_amdgcn_sched_barrier(0);
+          mma(fb);
+          issued += 4;
+        } else if (md == 2) {
+          // Step m pairs indices d0 + 16 hf + m (X) and d0 + 16 hf + 8 + m
+          // (Y) in lane half hf, at paired positions [0, 16).
+          Frag fa = frags_at(ch[0], cu[0], 0u, ch[8], cu[8], 0u), fb;
+#pragma unroll
+          for (int m = 0; m < 8; m += 2) {
+            fb = frags_at(ch[m + 1], cu[m + 1], 0u, ch[m + 9], cu[m + 9], 0u);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fa);
+            if (m + 2 < 8) fa = frags_at(ch[m + 2], cu[m + 2], 0u, ch[m + 10], cu[m + 10], 0u);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
+          }
+          issued += 8;
+        }
+      };
+      if (ngrp > 0) {
+        uint32_t ha[16], ua[16], hb[16], ub[16];
+        int ma = mode_of(0), mb;
+        load_codes(0, ma, ha, ua);
+        for (int grp = 0; grp < ngrp; grp += 2) {
+          mb = mode_of(grp + 1);
+          load_codes(grp + 1, mb, hb, ub);
+          sweep(ha, ua, ma);
+          if (grp + 1 >= ngrp) break;
+          ma = mode_of(grp + 2);
+          load_codes(grp + 2, ma, ha, ua);
+          sweep(hb, ub, mb);
+        }
+      }
+    }
+
+    // The next tile's row data and maxima, read now and stored after the
+    // tile (pass 2 and the decode cover their latency).
+    int nrow = -1, nrc = 0;
+    float nsa = 0.0f;
+    uint4 nmx[MX_PER];
+    if (next < n_items) {
+      const PersItem nt = pers_item_q(a, w.CT, nq, per, next);
+      if (tid < MF_BM) row_data(nt.g, nt.y, nrow, nrc, nsa);
+      maxh_load(nt.g, nt.y, nmx);
+    }
+
+    // ---- pass 2: paired positions from 16 on.
+    {
+      const uint32_t* hrow = w.hs + enc_word((long long)g * w.RT + y, ngrp_all, 0, 0) + (8 * wr + hf) * 128 + 4 * l32;
+      const uint32_t* urow = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0) + (8 * wc + hf) * 128 + 4 * l32;
+      const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
+      const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
+      const long long hstr = w.Mp / 2, ustr = w.Np / 2;
+      auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hcol[(long long)d * hstr]; };
+      auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ucol[(long long)d * ustr]; };
+      auto list_sweep = [&](int cnt, int dpad) __attribute__((always_inline)) {
+        if (lane < PAD4) list[cnt + lane] = ((uint32_t)dpad << 4) | 8u;
+        const int nsteps = (cnt + 3) >> 2;
+        uint2 re[FL_RING];
+        uint32_t rhx[FL_RING], rux[FL_RING], rhy[FL_RING], ruy[FL_RING];
+        auto fill = [&](int r, uint2 e) __attribute__((always_inline)) {
+          re[r] = e;
+          rhx[r] = hword(e.x >> 4);
+          rux[r] = uword(e.x >> 4);
+          rhy[r] = hword(e.y >> 4);
+          ruy[r] = uword(e.y >> 4);
+        };
+        auto frags_r = [&](int r) __attribute__((always_inline)) {
+          return frags_at(rhx[r], rux[r], 16u * (re[r].x & 15u), rhy[r], ruy[r], 16u * (re[r].y & 15u));
+        };
+        const uint2* lst = (const uint2*)list;
+#pragma unroll
+        for (int r = 0; r < FL_RING; ++r) fill(r, lst[2 * r + hf]);
+        uint2 enext = lst[2 * FL_RING + hf];
+        Frag fr[2];
+        fr[0] = frags_r(0);
+        for (int s0 = 0; s0 < nsteps; s0 += FL_RING) {
+#pragma unroll
+          for (int r = 0; r < FL_RING; ++r) {
+            fr[(r + 1) & 1] = frags_r((r + 1) % FL_RING);
+            fill(r, enext);
+            enext = lst[2 * (s0 + r + FL_RING + 1) + hf];
+            __builtin_amdgcn_sched_barrier(0);
+            if (s0 + r < nsteps) mma(fr[r & 1]);
+          }
+        }
+        issued += nsteps;
+      };
+      int cnt = 0;
+      for (int grp = 0; grp < ngrp; ++grp) {
+        const int d0 = dbeg + 32 * grp;
+        const int nl = (mxs[32 * grp + l32] + 15) >> 4;  // levels of 16 positions this index needs
+        if ((unsigned)__ballot(nl > 1) == 0) continue;
+        int full = 1;  // levels [1, full) are swept for every index of the group
+        for (int j = 1; j < 8; ++j) {
+          const unsigned bal = (unsigned)__ballot(nl > j);
+          if (bal == 0) break;
+          if (bal == 0xffffffffu && j == full) {
+            ++full;
+            continue;
+          }
+          if (hf == 0 && nl > j)
+            list[cnt + (int)__builtin_amdgcn_mbcnt_lo(bal, 0u)] = ((uint32_t)(d0 + l32) << 4) | (uint32_t)j;
+          cnt += __builtin_popcount(bal);
+        }
+        if (full > 1) {
+          // This group's codes: indices d0 + 16 hf + m, m < 16.
+          uint32_t ch[16], cu[16];
+          const uint4* hp = (const uint4*)(hrow + ((long long)(d0 >> 5) << 11));
+          const uint4* up = (const uint4*)(urow + ((long long)(d0 >> 5) << 11));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const uint4 th = hp[64 * i], tu = up[64 * i];
+            ch[4 * i] = th.x;
+            ch[4 * i + 1] = th.y;
+            ch[4 * i + 2] = th.z;
+            ch[4 * i + 3] = th.w;
+            cu[4 * i] = tu.x;
+            cu[4 * i + 1] = tu.y;
+            cu[4 * i + 2] = tu.z;
+            cu[4 * i + 3] = tu.w;
+          }
+          Frag fa = frags_at(ch[0], cu[0], 16u, ch[8], cu[8], 16u), fb;
+          for (int j = 1; j < full; ++j) {
+            const uint32_t kk = 16u * j;
+#pragma unroll
+            for (int m = 0; m < 8; m += 2) {
+              fb = frags_at(ch[m + 1], cu[m + 1], kk, ch[m + 9], cu[m + 9], kk);
+              __builtin_amdgcn_sched_barrier(0);
+              mma(fa);
+              // Next: step m + 2 of this level or step 0 of the next level
+              // (after the last level: read, unused; position <= 128 stays
+              // inside the table rows).
+              if (m + 2 < 8)
+                fa = frags_at(ch[m + 2], cu[m + 2], kk, ch[m + 10], cu[m + 10], kk);
+              else
+                fa = frags_at(ch[0], cu[0], kk + 16u, ch[8], cu[8], kk + 16u);
+              __builtin_amdgcn_sched_barrier(0);
+              mma(fb);
+            }
+          }
+          issued += 8 * (full - 1);
+        }
+        // The next group adds at most 224 entries.
+        if (cnt > FL_LIST - 256 - PAD4) {
+          list_sweep(cnt, d0);
+          cnt = 0;
+        }
+      }
+      if (cnt > 0) list_sweep(cnt, dbeg);
+    }
+
+    if (lane == 0) w.steps[(long long)item * 4 + wave] = issued;
+    issued = 0;
+    // The next tile's row data and maxima into the other buffers; the tile
+    // after it.
+    if (tid < MF_BM) {
+      s_rows[cur ^ 1][tid] = nrow;
+      s_rc[cur ^ 1][tid] = nrc;
+      s_sa[cur ^ 1][tid] = nsa;
+    }
+    if (next < n_items) maxh_store(cur ^ 1, nmx);
+    if (tid == 0) s_item[cur] = next < n_items ? fetch() : n_items;
+
+    const float scale0 = (float)qq / (float)L;
+    float sb[2], bj[2];
+    int ccol[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int col = col0 + wcol0 + j * 32 + l32;
+      sb[j] = col < a.N ? a.sB[(long long)g * a.N + col] : 0.0f;
+      bj[j] = (a.bias && col < a.N) ? a.bias[(long long)g * a.N + col] : 0.0f;
+      ccol[j] = col < a.N ? out_col(a, col) : -1;
+      settle(sb[j]);
+      settle(bj[j]);
+      settle(ccol[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int r0 = wrow0 + i * 32 + q4 * 8 + hf * 4;
+        const int4 rw = *(const int4*)&s_rows[cur][r0];
+        const int4 rc = *(const int4*)&s_rc[cur][r0];
+        const float4 sa = *(const float4*)&s_sa[cur][r0];
+        const int rowv[4] = {rw.x, rw.y, rw.z, rw.w};
+        const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
+        const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            const int col = col0 + wcol0 + j * 32 + l32;
+            if (rowv[e] < 0 || col >= a.N) continue;
+            const int cnt2 = (int)acc[i][j][q4 * 4 + e] + rcv[e];
+            if (COUNTS) a.counts[((long long)g * a.M + rowv[e]) * a.N + col] = cnt2;
+            if (a.C && ccol[j] >= 0)
+              a.C[(long long)g * a.bsc + (long long)rowv[e] * a.ldc + ccol[j]] =
+                  (sav[e] * sb[j]) * (scale0 * (float)(2 * cnt2 - L * a.D)) + bj[j];
+          }
+      }
+    __syncthreads();  // publishes the next tile's row data, maxima and item
+    if (next >= n_items) break;
+    item = next;
+    cur ^= 1;
+  }
 }
 
 // The header of a workspace the last MFMA-path call used.
-static int read_header(const void* ws, size_t ws_bytes, hipStream_t st, unsigned long long (&h)[3]) {
-  if (!ws || ws_bytes < 3 * sizeof(unsigned long long))
+static int read_header(const void* ws, size_t ws_bytes, hipStream_t st, unsigned long long (&h)[4]) {
+  if (!ws || ws_bytes < 4 * sizeof(unsigned long long))
     return set_error(SCMP_ERR_WORKSPACE, "workspace smaller than scmp_matmul_workspace_bytes reports");
   hipError_t e = hipMemcpyAsync(h, ws, sizeof h, hipMemcpyDeviceToHost, st);
   if (e == hipSuccess) e = hipStreamSynchronize(st);
@@ -1225,37 +1891,43 @@ static int read_header(const void* ws, size_t ws_bytes, hipStream_t st, unsigned
   return SCMP_OK;
 }
 
+// Sum of n values of type T at byte offset off of the workspace.
+template <typename T>
+static int sum_slots(const void* ws, size_t ws_bytes, unsigned long long n, unsigned long long off, hipStream_t st,
+                     unsigned long long* out) {
+  if (off < 4 * sizeof(unsigned long long) || off > ws_bytes || n > (ws_bytes - off) / sizeof(T))
+    return set_error(SCMP_ERR_WORKSPACE, "workspace header does not describe a matrix-core call");
+  std::vector<T> v((size_t)n);
+  hipError_t e = hipSuccess;
+  if (n) e = hipMemcpyAsync(v.data(), (const char*)ws + off, n * sizeof(T), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("readback: ") + hipGetErrorString(e));
+  unsigned long long tot = 0;
+  for (T x : v) tot += x;
+  *out = tot;
+  return SCMP_OK;
+}
+
 int mfma_issued_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
                      unsigned long long* macs, unsigned long long* fp4_macs) {
-  unsigned long long h[3];
+  (void)a;
+  unsigned long long h[4], steps = 0;
   int s = read_header(ws, ws_bytes, st, h);
+  if (s == SCMP_OK) s = sum_slots<uint32_t>(ws, ws_bytes, h[0], h[1], st, &steps);
   if (s != SCMP_OK) return s;
-  // A step of a 128 x 128 tile is four 32 x 32 x 64 fp4 MFMAs per wave
-  // (2 x 2 subtiles), four waves: 128 * 128 * 64 MACs, issued by each
-  // column tile.
-  const unsigned long long CT = (unsigned long long)((a.N + MF_BN - 1) / MF_BN);
-  const unsigned long long per_step = CT * 128ull * 128ull * 64ull;
-  *macs = h[0] * per_step;
-  if (fp4_macs) *fp4_macs = h[0] * per_step;
+  // A wave step is four 32 x 32 x 64 fp4 MFMAs (2 x 2 subtiles of the
+  // wave's 64 x 64 part of the tile): 64 * 64 * 64 MACs.
+  *macs = steps * 64ull * 64ull * 64ull;
+  if (fp4_macs) *fp4_macs = *macs;
   return SCMP_OK;
 }
 
 int mfma_window_macs(const MatmulArgs& a, const void* ws, size_t ws_bytes, hipStream_t st,
                      unsigned long long* macs) {
-  unsigned long long h[3];
+  unsigned long long h[4], tot = 0;
   int s = read_header(ws, ws_bytes, st, h);
+  if (s == SCMP_OK) s = sum_slots<unsigned long long>(ws, ws_bytes, h[2], h[3], st, &tot);
   if (s != SCMP_OK) return s;
-  const unsigned long long n = h[1], off = h[2];
-  if (off < 3 * sizeof(unsigned long long) || off > ws_bytes || n > (ws_bytes - off) / sizeof(unsigned long long))
-    return set_error(SCMP_ERR_WORKSPACE, "workspace header does not describe a matrix-core call");
-  std::vector<unsigned long long> sums((size_t)n);
-  hipError_t e = hipSuccess;
-  if (n) e = hipMemcpyAsync(sums.data(), (const char*)ws + off, n * sizeof(unsigned long long),
-                            hipMemcpyDeviceToHost, st);
-  if (e == hipSuccess) e = hipStreamSynchronize(st);
-  if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("window readback: ") + hipGetErrorString(e));
-  unsigned long long tot = 0;
-  for (unsigned long long v : sums) tot += v;
   *macs = tot * (unsigned long long)a.N;
   return SCMP_OK;
 }
@@ -1286,6 +1958,36 @@ static int device_cus() {
   return cached[dev];
 }
 
+// Whether the persistent grid runs (bipolar single-segment plans): forced
+// by the caller, or by size when every block gets at least two tiles (the
+// table is then staged once for several); a one-pass grid otherwise (its
+// blocks need no work counter or table reuse).
+static bool use_persistent(const MatmulArgs& a, const MfmaWs& w) {
+  if (a.unipolar || a.chunk_d > 0) return false;
+  if (a.launch == 1 || a.launch == 3) return true;
+  const bool counts = a.counts != nullptr;
+  return a.launch == 0 && pers_ok(a, w) &&
+         (long long)a.tile_start[a.n_rungs] * a.G * w.CT >= 2LL * (counts ? 1 : 2) * device_cus();
+}
+
+// Whether the staged kernel runs in row-tile units per XCD (staged_tile).
+// Estimated code bytes fetched, per contraction index, over the launch:
+//  grid order: consecutive column tiles of a row tile land on different
+//    XCDs, so each row tile is read by min(CT, 8) of them, while an XCD's
+//    column tiles stay in its L2;
+//  row units: every row tile is read once, and each XCD reads all the
+//    column codes once per round of the row tiles it runs at once (about
+//    64 blocks per XCD, two per CU).
+static bool staged_row_units(const MatmulArgs& a, const MfmaWs& w) {
+  const double rows = (double)a.G * w.Mp, cols = (double)a.G * w.Np;
+  const double units = (double)a.G * w.RT;
+  const double at_once = std::max(1.0, 64.0 / w.CT);  // row tiles per XCD in flight
+  const double rounds = std::ceil(units / (8.0 * at_once));
+  const double grid_order = std::min(w.CT, 8) * rows + cols;
+  const double row_order = rows + 8.0 * cols * rounds;
+  return row_order < 0.75 * grid_order && 8.0 * std::ceil(units / 8.0) * w.CT < 2147483647.0;
+}
+
 static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStream_t st) {
   const bool counts = a.counts != nullptr;
   if (a.unipolar) {
@@ -1305,18 +2007,21 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
       hipLaunchKernelGGL((k_mfma<true, true, false>), grid, dim3(256), 0, st, a, w);
     else
       hipLaunchKernelGGL((k_mfma<true, false, false>), grid, dim3(256), 0, st, a, w);
-  } else if (a.launch == 1 ||
-             (a.launch == 0 && pers_ok(a, w) &&
-              a.tile_start[a.n_rungs] * a.G * w.CT >= 2 * (counts ? 1 : 2) * device_cus())) {
-    // Persistent when every block gets at least two tiles (the table is
-    // then staged once for several); a one-pass grid otherwise (its blocks
-    // need no work counter or table reuse).
+  } else if (use_persistent(a, w)) {
+    // The quarter contraction when the workspace holds its codes, the
+    // 16-position one otherwise.
     const int n_items = a.tile_start[a.n_rungs] * a.G * w.CT;
     const int blocks = std::max(1, std::min(n_items, (counts ? 1 : 2) * device_cus()));
-    if (counts)
+    if (w.qpt_on) {
+      if (counts)
+        hipLaunchKernelGGL((k_mfma_qpt<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      else
+        hipLaunchKernelGGL((k_mfma_qpt<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+    } else if (counts) {
       hipLaunchKernelGGL((k_mfma_pers<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
-    else
+    } else {
       hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+    }
   } else {
     if (counts)
       hipLaunchKernelGGL((k_mfma<false, true, false>), grid, dim3(256), 0, st, a, w);
@@ -1337,8 +2042,16 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
   if (a.launch == 1 && !pers_ok(a, w))
     return set_error(SCMP_ERR_UNSUPPORTED,
                      "the persistent launch needs a plan without chunk scales and one band");
+  if (a.launch == 3 && (!pers_ok(a, w) || !w.hq || !w.uq))
+    return set_error(SCMP_ERR_UNSUPPORTED,
+                     "the quarter contraction needs a bipolar plan without chunk scales, one band starting on a "
+                     "multiple of 32 and a padded contraction axis of at most 4096");
+  w.qpt_on = (w.hq && w.uq && use_persistent(a, w) && quarter_chosen(a)) ? 1 : 0;
+  w.row_units = (!use_persistent(a, w) && staged_row_units(a, w)) ? 1 : 0;
   hipLaunchKernelGGL(k_prep, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
-  launch_main(a, w, dim3(w.CT, w.RT, a.G), st);
+  const dim3 grid = w.row_units ? dim3((unsigned)(8 * (((long long)a.G * w.RT + 7) / 8) * w.CT))
+                                : dim3(w.CT, w.RT, a.G);
+  launch_main(a, w, grid, st);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return set_error(SCMP_ERR_HIP, std::string("mfma launch: ") + hipGetErrorString(e));
   return SCMP_OK;

@@ -20,18 +20,20 @@ from mixed_precision_quantization_amd.workloads import WORKLOADS, draw, draw_bia
 pytestmark = pytest.mark.gpu
 
 RTOL = 1e-5
-# Contraction kernels: the matrix-core path by size, forced persistent or
-# one block per tile, the bit-serial path and the pair-count gather path.
-ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather")
+# Contraction kernels: the matrix-core path by size, forced persistent, one
+# block per tile or quarter steps, the bit-serial path and the pair-count
+# gather path.
+ALGOS = ("mfma", "bitserial", "mfma_persistent", "mfma_onepass", "gather", "mfma_quarter")
 
 
 def _skip_unsupported(algo, chunk_d=0, n_bands=1, mode="bipolar"):
-    """The persistent launch takes bipolar plans without chunk scales and one
-    band."""
-    if algo == "mfma_persistent" and ((chunk_d or 0) > 0 or n_bands > 1):
-        pytest.skip("the persistent launch needs a single-segment plan (checked in test_persistent_rejects_chunks)")
-    if mode == "unipolar" and algo in ("mfma_persistent", "gather"):
-        pytest.skip("unipolar plans have no persistent or gather form (checked in test_unipolar_rejects_persistent)")
+    """The persistent and quarter launches take bipolar plans without chunk
+    scales and one band."""
+    if algo in ("mfma_persistent", "mfma_quarter") and ((chunk_d or 0) > 0 or n_bands > 1):
+        pytest.skip("the persistent launches need a single-segment plan (checked in test_persistent_rejects_chunks)")
+    if mode == "unipolar" and algo in ("mfma_persistent", "gather", "mfma_quarter"):
+        pytest.skip("unipolar plans have no persistent, quarter or gather form "
+                    "(checked in test_unipolar_rejects_persistent)")
 
 
 @pytest.fixture(scope="module")
@@ -361,9 +363,27 @@ def test_persistent_rejects_chunks(table):
     A = torch.from_numpy(rng.standard_normal((40, 128)).astype(np.float32)).cuda()
     plan = scmp.scmp_plan_create(D=128, chunk_d=64, levels=(64,))
     q, s, m, _ = scmp.scmp_quantize_encode(table, plan, A)
+    for algo in ("mfma_persistent", "mfma_quarter"):
+        with pytest.raises(scmp.ScmpError) as ei:
+            scmp.scmp_matmul(table, plan, q, s, q, s, algo=algo, want_counts=True)
+        assert ei.value.status == scmp.SCMP_ERR_UNSUPPORTED
+
+
+def test_quarter_rejects_long_axes(table):
+    """The quarter launch keeps a tile's index maxima in LDS: a padded axis
+    above 4096 is UNSUPPORTED, and AUTO runs such a plan on another form,
+    with the same counts as the persistent launch."""
+    rng = np.random.default_rng(27)
+    A = torch.from_numpy(rng.standard_normal((60, 4100)).astype(np.float32)).cuda()
+    plan = scmp.scmp_plan_create(D=4100, levels=(64,))
+    q, s, _, _ = scmp.scmp_quantize_encode(table, plan, A)
     with pytest.raises(scmp.ScmpError) as ei:
-        scmp.scmp_matmul(table, plan, q, s, q, s, algo="mfma_persistent", want_counts=True)
+        scmp.scmp_matmul(table, plan, q, s, q, s, algo="mfma_quarter", want_counts=True)
     assert ei.value.status == scmp.SCMP_ERR_UNSUPPORTED
+    c_auto, _ = scmp.scmp_matmul(table, plan, q, s, q, s, algo="auto", want_counts=True)
+    c_pers, _ = scmp.scmp_matmul(table, plan, q, s, q, s, algo="mfma_persistent", want_counts=True)
+    torch.cuda.synchronize()
+    assert torch.equal(c_auto, c_pers)
 
 
 def test_standalone_decode_matches_fused(table):
@@ -618,7 +638,7 @@ def test_unipolar_rejects_persistent(table):
     rng = np.random.default_rng(71)
     plan = scmp.scmp_plan_create(D=64, levels=(128,), mode="unipolar")
     A = torch.from_numpy(rng.standard_normal((40, 64)).astype(np.float32)).cuda()
-    for algo in ("mfma_persistent", "gather"):
+    for algo in ("mfma_persistent", "gather", "mfma_quarter"):
         with pytest.raises(scmp.ScmpError) as e:
             scmp.sc_linear(table, plan, A, A, algo=algo)
         assert e.value.status == scmp.SCMP_ERR_UNSUPPORTED
@@ -882,3 +902,36 @@ def test_two_streams_give_the_sequential_results(table):
         torch.cuda.synchronize()
         for i in range(2):
             assert torch.equal(res[i]["C"], ref[i]), f"stream {i}, repetition {rep}"
+
+
+@pytest.mark.parametrize("algo", ["mfma", "mfma_persistent", "mfma_onepass", "mfma_quarter"])
+def test_window_macs_match_the_host_count(table, algo):
+    """scmp_matmul_window_macs equals N times the sum, over rows and
+    indices, of the half-window ceil(|n1 - n0| / 2) at the row's length
+    (n1 = cum[u_A][L] from the oracle's table and levels); the issued MACs
+    cover it, in whole 64 x 64 x 64 wave steps."""
+    rng = np.random.default_rng(141)
+    M, N, D = 333, 200, 160
+    levels, fractions = (256, 128, 64), (0.2, 0.3, 0.5)
+    A = rng.standard_normal((M, D)).astype(np.float32)
+    A[:, 9] *= 20.0
+    B = (0.02 * rng.standard_normal((N, D))).astype(np.float32)
+    plan = scmp.scmp_plan_create(D=D, levels=levels, fractions=fractions)
+    At, Bt = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    qA, sA, mA, _ = scmp.scmp_quantize_encode(table, plan, At)
+    qB, sB, _, _ = scmp.scmp_quantize_encode(table, plan, Bt, want_metric=False)
+    _, rung, perm, _ = scmp.scmp_classify_rows(plan, mA)
+    ws = torch.empty(scmp.scmp_matmul_workspace_bytes(table, plan, 1, M, N, algo), dtype=torch.uint8, device="cuda")
+    scmp.scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, algo=algo, workspace=ws)
+    window = scmp.scmp_matmul_window_macs(table, plan, 1, M, N, ws, algo=algo)
+    issued = scmp.scmp_matmul_issued_macs(table, plan, 1, M, N, ws, algo=algo)
+    oplan = o.OraclePlan(D=D, levels=levels, fractions=fractions)
+    cls = o.classify(A, oplan)
+    x_a, _ = o.quantize(A, 8)
+    cum = o.cumulative_table(oplan.table())
+    u = o.bipolar_level(x_a, 8)
+    L = np.asarray(levels)[cls["rung"]][:, None]
+    n1 = cum[u, L]
+    hh = (np.abs(2 * n1 - L) + 1) // 2
+    assert window == int(hh.sum()) * N
+    assert issued >= window and issued % (64 * 64 * 64) == 0

@@ -17,7 +17,7 @@ PLANS = {
     "mp_rows": dict(D=256, levels=(256, 128, 64), fractions=(0.2, 0.3, 0.5)),
     "kband_chunks": dict(D=256, chunk_d=64, levels=(256, 192, 128, 64), n_bands=4, tilt=0.25),
 }
-FORMS = {"mp_rows": ("auto", "mfma_persistent", "mfma_onepass", "gather"),
+FORMS = {"mp_rows": ("auto", "mfma_persistent", "mfma_onepass", "gather", "mfma_quarter"),
          "kband_chunks": ("auto", "mfma_onepass", "gather")}
 
 
