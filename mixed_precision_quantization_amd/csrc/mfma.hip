@@ -88,6 +88,9 @@ struct MfmaWs {
   // grid where XCD x takes row tiles (g, y) with (g RT + y) = x (mod 8), each
   // with all its column tiles in turn (staged_tile).
   int row_units;
+  // The index-major copies are written only when a persistent form runs
+  // (the staged kernel reads the blocked buffers alone).
+  int im_on;
   long long Mp, Np, Dp;
   int RT, CT;
   // The encode kernels split the contraction axis into n_parts parts of
@@ -438,7 +441,7 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
       // the band or D get code 0); dfirst is a multiple of 8.
       *(uint4*)(w.hs + enc_word(tile, ngrp, dfirst, pr)) = uint4{word[0], word[1], word[2], word[3]};
       *(uint4*)(w.hs + enc_word(tile, ngrp, dfirst + 4, pr)) = uint4{word[4], word[5], word[6], word[7]};
-      if (w.hsi) {
+      if (w.hsi && w.im_on) {
         uint32_t* di = w.hsi + ((long long)g * w.Dp + dfirst) * (w.Mp / 2) + (long long)y * 64 + pr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) di[(long long)i * (w.Mp / 2)] = word[i];
@@ -573,7 +576,7 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
         *(uint2*)(base + qcode_index(tile, ngrp, d0 >> 5, 1, cp) + 2 * q) = uint2{qw[2], qw[3]};
       }
     }
-    if (w.ubi) {
+    if (w.ubi && w.im_on) {
       uint32_t* di = w.ubi + ((long long)g * w.Dp + dfirst) * (w.Np / 2) + (long long)bx * 64 + cp;
 #pragma unroll
       for (int i = 0; i < 8; ++i) di[(long long)i * (w.Np / 2)] = word[i];
@@ -1127,20 +1130,26 @@ __device__ __forceinline__ PersItem pers_item(const MatmulArgs& a, int CT, int i
   return it;
 }
 
-// Work queues.  With CT a multiple of PERS_QUEUES, the items of column
-// tiles x = q (mod PERS_QUEUES) form queue q, in the order above (per row
-// tile, the queue's column tiles in turn); otherwise there is one queue.
-// Block b starts on queue b mod PERS_QUEUES: workgroups are dispatched to
-// the 8 XCDs in turn, so each XCD's L2 serves the codes of its own column
-// tiles only.  A block whose queue is empty takes items from the others.
-// Item ids are q * per + t (t-th item of queue q, per items per queue).
-__device__ __forceinline__ PersItem pers_item_q(const MatmulArgs& a, int CT, int nq, int per, int id) {
-  const int qi = id / per, t = id - qi * per;
-  const int cpq = CT / nq;  // column tiles per queue
-  const int f = t / cpq;    // row-tile unit (rung, group, row tile)
-  PersItem it = pers_item(a, 1, f);
-  it.x = (t - f * cpq) * nq + qi;
-  return it;
+// Work queues.  Items are numbered in the order above: id = f CT + x for
+// row-tile unit f (rung, group, row tile) and column tile x.  When CT is a
+// multiple of PERS_QC, queue q = PERS_QC h + c holds the items of the units
+// f = h (mod PERS_QR) and column tiles x = c (mod PERS_QC), unit by unit;
+// otherwise one queue holds every item.  Block b starts on queue
+// b mod PERS_QUEUES: workgroups are dispatched to the 8 XCDs in turn, so an
+// XCD's L2 serves the codes of one quarter of the column tiles and of half
+// of the row tiles (each row tile's codes are fetched by 4 XCDs, each column
+// tile's by 2).  A block whose queue is empty takes items from the others.
+constexpr int PERS_QR = 2, PERS_QC = 4;  // PERS_QR x PERS_QC = PERS_QUEUES
+static_assert(PERS_QR * PERS_QC == PERS_QUEUES, "queue grid");
+__device__ __forceinline__ int queue_size(int U, int CT, int q) {
+  const int h = q / PERS_QC;
+  return ((U - h + PERS_QR - 1) / PERS_QR) * (CT / PERS_QC);
+}
+__device__ __forceinline__ int queue_item(int CT, int q, int t) {
+  const int h = q / PERS_QC, c = q - h * PERS_QC;
+  const int cpq = CT / PERS_QC;
+  const int i = t / cpq, j = t - i * cpq;
+  return (PERS_QR * i + h) * CT + PERS_QC * j + c;
 }
 
 template <bool COUNTS>
@@ -1178,15 +1187,20 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     for (int pt = 0; pt < w.n_parts; ++pt) rc += rc0[(long long)pt * w.Mp];
   };
 
-  const int nq = (w.CT % PERS_QUEUES == 0) ? PERS_QUEUES : 1;
-  const int per = n_items / nq;
+  const int U = n_items / w.CT;  // row-tile units
+  const bool grid_q = w.CT % PERS_QC == 0 && U >= PERS_QR;
+  const int nq = grid_q ? PERS_QUEUES : 1;
   const int home = (int)(blockIdx.x % (unsigned)nq);
   // Next item id for this block (n_items when every queue is empty).
   auto fetch = [&]() {
     for (int i = 0; i < nq; ++i) {
       const int qi = (home + i) % nq;
       const unsigned t = atomicAdd(w.work + qi, 1u);
-      if (t < (unsigned)per) return qi * per + (int)t;
+      if (!grid_q) {
+        if (t < (unsigned)n_items) return (int)t;
+      } else if (t < (unsigned)queue_size(U, w.CT, qi)) {
+        return queue_item(w.CT, qi, (int)t);
+      }
     }
     return n_items;
   };
@@ -1199,7 +1213,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
   int item = s_item[0];
   if (item >= n_items) return;
   if (tid < MF_BM) {
-    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    const PersItem it = pers_item(a, w.CT, item);
     int row, rc;
     float sa;
     row_data(it.g, it.y, row, rc, sa);
@@ -1218,7 +1232,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
   int cur = 0;
 
   while (true) {
-    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    const PersItem it = pers_item(a, w.CT, item);
     const int k = tile_rung(a, it.g, it.k), g = it.g, y = it.y;
     const int col0 = it.x * MF_BN;
     const int next = s_item[cur ^ 1];
@@ -1226,7 +1240,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     int nrow = -1, nrc = 0;
     float nsa = 0.0f;
     if (next < n_items && tid < MF_BM) {
-      const PersItem nt = pers_item_q(a, w.CT, nq, per, next);
+      const PersItem nt = pers_item(a, w.CT, next);
       row_data(nt.g, nt.y, nrow, nrc, nsa);
     }
     const int L = a.bandL[0][k];
@@ -1494,14 +1508,19 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
   const int ngrp_all = (int)(w.Dp / MF_DC);
   const int n_mx = (int)(w.Dp >> 4);  // uint4 pieces of one tile's maxima
 
-  const int nq = (w.CT % PERS_QUEUES == 0) ? PERS_QUEUES : 1;
-  const int per = n_items / nq;
+  const int U = n_items / w.CT;  // row-tile units
+  const bool grid_q = w.CT % PERS_QC == 0 && U >= PERS_QR;
+  const int nq = grid_q ? PERS_QUEUES : 1;
   const int home = (int)(blockIdx.x % (unsigned)nq);
   auto fetch = [&]() {
     for (int i = 0; i < nq; ++i) {
       const int qi = (home + i) % nq;
       const unsigned t = atomicAdd(w.work + qi, 1u);
-      if (t < (unsigned)per) return qi * per + (int)t;
+      if (!grid_q) {
+        if (t < (unsigned)n_items) return (int)t;
+      } else if (t < (unsigned)queue_size(U, w.CT, qi)) {
+        return queue_item(w.CT, qi, (int)t);
+      }
     }
     return n_items;
   };
@@ -1540,7 +1559,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
   int item = s_item[0];
   if (item >= n_items) return;
   {
-    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    const PersItem it = pers_item(a, w.CT, item);
     if (tid < MF_BM) {
       int row, rc;
       float sa;
@@ -1564,7 +1583,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
   int cur = 0;
 
   while (true) {
-    const PersItem it = pers_item_q(a, w.CT, nq, per, item);
+    const PersItem it = pers_item(a, w.CT, item);
     const int k = tile_rung(a, it.g, it.k), g = it.g, y = it.y;
     const int col0 = it.x * MF_BN;
     const int next = s_item[cur ^ 1];
@@ -1714,7 +1733,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
     float nsa = 0.0f;
     uint4 nmx[MX_PER];
     if (next < n_items) {
-      const PersItem nt = pers_item_q(a, w.CT, nq, per, next);
+      const PersItem nt = pers_item(a, w.CT, next);
       if (tid < MF_BM) row_data(nt.g, nt.y, nrow, nrc, nsa);
       maxh_load(nt.g, nt.y, nmx);
     }
@@ -2047,7 +2066,8 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
                      "the quarter contraction needs a bipolar plan without chunk scales, one band starting on a "
                      "multiple of 32 and a padded contraction axis of at most 4096");
   w.qpt_on = (w.hq && w.uq && use_persistent(a, w) && quarter_chosen(a)) ? 1 : 0;
-  w.row_units = (!use_persistent(a, w) && staged_row_units(a, w)) ? 1 : 0;
+  w.im_on = use_persistent(a, w) ? 1 : 0;
+  w.row_units = (!w.im_on && staged_row_units(a, w)) ? 1 : 0;
   hipLaunchKernelGGL(k_prep, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   const dim3 grid = w.row_units ? dim3((unsigned)(8 * (((long long)a.G * w.RT + 7) / 8) * w.CT))
                                 : dim3(w.CT, w.RT, a.G);
