@@ -226,11 +226,30 @@ static MfmaWs ws_layout(const MatmulArgs& a, void* base, size_t* total) {
 __device__ __forceinline__ void settle(float& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void settle(int& v) { asm volatile("" : "+v"(v)); }
 
-__device__ __forceinline__ int wave_max_i(int v) {
+// Maxima over the wave's 64 lanes of v[0..8), as a transposing butterfly:
+// at offsets 32, 16 and 8 each lane keeps half of its remaining values and
+// sends the other half to its partner (4 + 2 + 1 exchanges), then offsets
+// 4, 2 and 1 reduce the single value left.  Lane l returns the maximum of
+// v[l >> 3] (10 exchanges instead of 8 x 6).
+__device__ __forceinline__ int wave_max8(const int (&v)[8], int lane) {
+  int a4[4], a2[2];
+  const bool u32 = lane & 32, u16 = lane & 16, u8 = lane & 8;
 #pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
-  return v;
+  for (int i = 0; i < 4; ++i) {
+    const int keep = u32 ? v[i + 4] : v[i], send = u32 ? v[i] : v[i + 4];
+    a4[i] = max(keep, __shfl_xor(send, 32, 64));
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int keep = u16 ? a4[i + 2] : a4[i], send = u16 ? a4[i] : a4[i + 2];
+    a2[i] = max(keep, __shfl_xor(send, 16, 64));
+  }
+  int a1 = max(u8 ? a2[1] : a2[0], __shfl_xor(u8 ? a2[0] : a2[1], 8, 64));
+#pragma unroll
+  for (int off = 4; off > 0; off >>= 1) a1 = max(a1, __shfl_xor(a1, off, 64));
+  return a1;
 }
+
 
 // Row (column) pairs.  A 128-wide tile has 64 pairs; pair pr holds
 // positions lo(pr) and lo(pr) + 32 with lo(pr) = 64 (pr / 32) + pr mod 32,
@@ -460,14 +479,10 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
         *(uint2*)(w.hq + qcode_index(plane, ngrp, d0 >> 5, 0, pr) + 2 * q) = uint2{qw[0], qw[1]};
         *(uint2*)(w.hq + qcode_index(plane, ngrp, d0 >> 5, 1, pr) + 2 * q) = uint2{qw[2], qw[3]};
       }
-      // Tile maximum per index: over the wave's 64 pairs.
-      int mine = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int m = wave_max_i(mh[i]);
-        if (lane == i) mine = m;
-      }
-      if (lane < 8) w.maxh[((long long)g * w.RT + y) * w.Dp + dfirst + lane] = (uint8_t)mine;
+      // Tile maximum per index: over the wave's 64 pairs (lane l holds
+      // index dfirst + (l >> 3)).
+      const int mine = wave_max8(mh, lane);
+      if ((lane & 7) == 0) w.maxh[((long long)g * w.RT + y) * w.Dp + dfirst + (lane >> 3)] = (uint8_t)mine;
       if (a.chunk_d > 0 && ((d0 + MF_DC) % a.chunk_d == 0 || d0 + MF_DC >= a.D))
         flush_rc((long long)g * a.n_chunks + d0 / a.chunk_d);
     }
@@ -521,8 +536,8 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
   const int c0 = bx * MF_BN, g = blockIdx.z;
   const int plo = blockIdx.y * w.part_len;
   const int phi = (int)min((long long)plo + w.part_len, w.Dp);
-  // The contraction (launched after this kernel on the same stream) adds
-  // its issued steps to this counter.
+  // The workspace header (where the step slots and window sums are) and
+  // the work counters of the contraction launched after this kernel.
   if (bx == 0 && blockIdx.y == 0 && blockIdx.z == 0 && tid == 0) {
     w.hdr[0] = (unsigned long long)a.G * w.RT * w.CT * 4;
     w.hdr[1] = w.steps_off;
@@ -538,12 +553,27 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
   const int ngrp = (int)(w.Dp / MF_DC);
   const uint32_t pad = a.unipolar ? 0u : (uint32_t)((a.P >> 1) * PT_STRIDE);
   __syncthreads();
+  // The next group's values are read while this group is encoded.
+  int8_t nx_lo[8], nx_hi[8];
+  if (plo < phi) {
+    const int span = max(0, min(8, a.D - (plo + 8 * q)));
+    load8(src_lo + plo + 8 * q, col_lo < a.N ? span : 0, nx_lo);
+    load8(src_hi + plo + 8 * q, col_hi < a.N ? span : 0, nx_hi);
+  }
   for (int d0 = plo; d0 < phi; d0 += MF_DC) {
     const int dfirst = d0 + 8 * q;
     const int span = max(0, min(8, a.D - dfirst));
     int8_t x_lo[8], x_hi[8];
-    load8(src_lo + dfirst, col_lo < a.N ? span : 0, x_lo);
-    load8(src_hi + dfirst, col_hi < a.N ? span : 0, x_hi);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x_lo[i] = nx_lo[i];
+      x_hi[i] = nx_hi[i];
+    }
+    if (d0 + MF_DC < phi) {
+      const int nspan = max(0, min(8, a.D - (dfirst + MF_DC)));
+      load8(src_lo + dfirst + MF_DC, col_lo < a.N ? nspan : 0, nx_lo);
+      load8(src_hi + dfirst + MF_DC, col_hi < a.N ? nspan : 0, nx_hi);
+    }
     uint32_t word[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
