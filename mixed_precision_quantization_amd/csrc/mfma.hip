@@ -1161,23 +1161,24 @@ __device__ __forceinline__ PersItem pers_item(const MatmulArgs& a, int CT, int i
 }
 
 // Work queues.  Items are numbered in the order above: id = f CT + x for
-// row-tile unit f (rung, group, row tile) and column tile x.  When CT is a
-// multiple of PERS_QC, queue q = PERS_QC h + c holds the items of the units
-// f = h (mod PERS_QR) and column tiles x = c (mod PERS_QC), unit by unit;
-// otherwise one queue holds every item.  Block b starts on queue
-// b mod PERS_QUEUES: workgroups are dispatched to the 8 XCDs in turn, so an
-// XCD's L2 serves the codes of one quarter of the column tiles and of half
-// of the row tiles (each row tile's codes are fetched by 4 XCDs, each column
-// tile's by 2).  A block whose queue is empty takes items from the others.
+// row-tile unit f (rung, group, row tile) and column tile x.  With at least
+// PERS_QC column tiles and PERS_QR units, queue q = PERS_QC h + c holds the
+// items of the units f = h (mod PERS_QR) and column tiles x = c
+// (mod PERS_QC), unit by unit; otherwise one queue holds every item.  Block
+// b starts on queue b mod PERS_QUEUES: workgroups are dispatched to the 8
+// XCDs in turn, so an XCD's L2 serves the codes of one quarter of the
+// column tiles and of half of the row tiles (each row tile's codes are
+// fetched by 4 XCDs, each column tile's by 2).  A block whose queue is
+// empty takes items from the others.
 constexpr int PERS_QR = 2, PERS_QC = 4;  // PERS_QR x PERS_QC = PERS_QUEUES
 static_assert(PERS_QR * PERS_QC == PERS_QUEUES, "queue grid");
 __device__ __forceinline__ int queue_size(int U, int CT, int q) {
-  const int h = q / PERS_QC;
-  return ((U - h + PERS_QR - 1) / PERS_QR) * (CT / PERS_QC);
+  const int h = q / PERS_QC, c = q - h * PERS_QC;
+  return ((U - h + PERS_QR - 1) / PERS_QR) * ((CT - c + PERS_QC - 1) / PERS_QC);
 }
 __device__ __forceinline__ int queue_item(int CT, int q, int t) {
   const int h = q / PERS_QC, c = q - h * PERS_QC;
-  const int cpq = CT / PERS_QC;
+  const int cpq = (CT - c + PERS_QC - 1) / PERS_QC;  // column tiles x = c (mod PERS_QC)
   const int i = t / cpq, j = t - i * cpq;
   return (PERS_QR * i + h) * CT + PERS_QC * j + c;
 }
@@ -1218,7 +1219,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
   };
 
   const int U = n_items / w.CT;  // row-tile units
-  const bool grid_q = w.CT % PERS_QC == 0 && U >= PERS_QR;
+  const bool grid_q = w.CT >= PERS_QC && U >= PERS_QR;
   const int nq = grid_q ? PERS_QUEUES : 1;
   const int home = (int)(blockIdx.x % (unsigned)nq);
   // Next item id for this block (n_items when every queue is empty).
@@ -1539,7 +1540,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
   const int n_mx = (int)(w.Dp >> 4);  // uint4 pieces of one tile's maxima
 
   const int U = n_items / w.CT;  // row-tile units
-  const bool grid_q = w.CT % PERS_QC == 0 && U >= PERS_QR;
+  const bool grid_q = w.CT >= PERS_QC && U >= PERS_QR;
   const int nq = grid_q ? PERS_QUEUES : 1;
   const int home = (int)(blockIdx.x % (unsigned)nq);
   auto fetch = [&]() {

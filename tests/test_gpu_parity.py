@@ -904,6 +904,28 @@ def test_two_streams_give_the_sequential_results(table):
             assert torch.equal(res[i]["C"], ref[i]), f"stream {i}, repetition {rep}"
 
 
+@pytest.mark.parametrize("algo", ["mfma_persistent", "mfma_quarter"])
+def test_work_queue_grid_with_uneven_queues(table, algo):
+    """The persistent launches take tiles from a 2 x 4 grid of work queues
+    (row-tile parity x column tile mod 4) when there are at least 4 column
+    tiles.  Here 3 groups of 3 row tiles (one per rung) give an odd number
+    of row-tile units and 6 column tiles (the last one ragged) split 2, 2,
+    1, 1 over the column classes, so the queues are uneven and blocks steal
+    from each other: every count of the whole matrix equals the bit-serial
+    kernel's, and group 0 equals the oracle."""
+    rng = np.random.default_rng(151)
+    G, M, N, D = 3, 333, 700, 96
+    A = rng.standard_normal((G, M, D)).astype(np.float32)
+    A[:, :, 5] *= 20.0
+    B = rng.standard_normal((G, N, D)).astype(np.float32)
+    kw = dict(D=D, levels=(128, 96, 64), fractions=(0.333, 0.334, 0.333))
+    plan = scmp.scmp_plan_create(op="qk", **kw)
+    gres = _gpu_path(table, plan, A, B, algo)
+    At, Bt = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    _whole_matrix_vs_bitserial(table, plan, At, Bt, gres)
+    _check_group(gres, 0, A[0], B[0], dict(p=8, Lmax=256, metric="linear", **kw))
+
+
 @pytest.mark.parametrize("algo", ["mfma", "mfma_persistent", "mfma_onepass", "mfma_quarter"])
 def test_window_macs_match_the_host_count(table, algo):
     """scmp_matmul_window_macs equals N times the sum, over rows and
