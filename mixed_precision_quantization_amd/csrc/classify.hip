@@ -110,6 +110,58 @@ __global__ void __launch_bounds__(512) k_classify(ClassifyArgs a) {
   }
 }
 
+// Groups of at most CS_MAXM rows (attention heads of 257 queries): one
+// block ranks the whole group, one row per thread, against every key of the
+// group in LDS (the same rank as above; every lane reads the same key at
+// once, an LDS broadcast).  The work per group is M^2 comparisons, a few
+// hundred cycles at these sizes, against the bucket form's 2048-bucket
+// clear and scan repeated by each of its blocks.
+constexpr int CS_MAXM = 512;
+
+__global__ void __launch_bounds__(CS_MAXM) k_classify_small(ClassifyArgs a) {
+  __shared__ float s_key[CS_MAXM];
+  __shared__ float s_red[CS_MAXM / 64];
+  const int g = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int M = a.M;
+  const float* m = a.metric + (long long)g * M;
+  const bool live = tid < M;
+  const float v = live ? m[tid] : 0.0f;
+  float mx = live ? fmaxf(0.0f, v) : 0.0f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
+  if (lane == 0) s_red[wave] = mx;
+  const bool bad = live && !__builtin_isfinite(v);
+  if (__ballot(bad) && lane == 0) atomicOr(a.flag, 1);
+  __syncthreads();
+  mx = s_red[0];
+#pragma unroll
+  for (int w = 1; w < CS_MAXM / 64; ++w) mx = fmaxf(mx, s_red[w]);
+  const float gi = live ? (mx == 0.0f ? 0.0f : v / mx) : 0.0f;
+  const float ki = rank_key(gi);
+  if (live) s_key[tid] = ki;
+  __syncthreads();
+  // rank_i = #{j : key_j > key_i, or key_j == key_i and j < i}.
+  int rank = 0;
+  for (int j = 0; j < M; ++j) {
+    const float kj = s_key[j];
+    rank += (kj > ki) || (kj == ki && j < tid);
+  }
+  if (!live) return;
+  a.ghat[(long long)g * M + tid] = gi;
+  a.perm[(long long)g * M + rank] = tid;
+  int k = 0;
+  while (k + 1 < a.n_rungs && rank >= a.cuts[k + 1]) ++k;
+  if (a.rung) a.rung[(long long)g * M + tid] = (uint8_t)k;
+  if (a.thr) {
+    for (int kk = 1; kk < a.n_rungs; ++kk) {
+      if (rank == a.cuts[kk] - 1) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = gi;
+      if (a.cuts[kk] == 0 && tid == 0) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = 1.0f;
+    }
+  }
+}
+
 // Groups of at most CB_MAXM rows take a bucket form with O(M) work per
 // block instead of O(M^2): every block buckets all of its group's keys by
 // value in LDS (a monotone map, so every key of a higher bucket sorts
@@ -302,7 +354,9 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   const int fs = scmp::stream_flag(st, &a.flag);
   if (fs != SCMP_OK) return fs;
   const int tiles = (M + scmp::CL_ROWS - 1) / scmp::CL_ROWS;
-  if (M <= scmp::CB_MAXM) {
+  if (M <= scmp::CS_MAXM) {
+    hipLaunchKernelGGL(scmp::k_classify_small, dim3(G), dim3(scmp::CS_MAXM), 0, st, a);
+  } else if (M <= scmp::CB_MAXM) {
     // Large groups rank two sets of rows per block: every block repeats the
     // group's O(M) bucketing, so fewer, fuller blocks cost less.
     const int sets = M > 8192 ? 2 : 1;

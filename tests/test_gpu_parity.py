@@ -232,9 +232,12 @@ def test_packed_streams_are_table_rows(table):
 
 # -------------------------------------------------------------- classify --
 
-def test_classify_matches_oracle_with_ties(table):
+@pytest.mark.parametrize("M", [1000, 512, 257])
+def test_classify_matches_oracle_with_ties(table, M):
+    """Bucketed groups (1000 rows) and groups ranked by one block each (at
+    most 512 rows), with runs of equal keys, quarter steps and zeros."""
     rng = np.random.default_rng(22)
-    G, M = 3, 1000
+    G = 3
     g = rng.uniform(0, 3, (G, M)).astype(np.float32)
     g[0, 100:200] = g[0, 50]                     # ties
     g[1] = np.round(g[1] * 4) / 4                # many ties
