@@ -943,12 +943,6 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           return Item{*(const uint32_t*)(hbase + ox), *(const uint32_t*)(ubase + ox),
                       *(const uint32_t*)(hbase + oy), *(const uint32_t*)(ubase + oy), e};
         };
-        // X and Y on adjacent indices (X even): one 8-byte read per buffer.
-        auto item2 = [&](uint32_t e) __attribute__((always_inline)) {
-          const uint32_t ox = (e >> 8) & 0x7cu;
-          const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
-          return Item{h2.x, u2.x, h2.y, u2.y, e};
-        };
         auto frags = [&](const Item& c) __attribute__((always_inline)) {
           if (UNI)
             return frags_at_uni(s_pat, s_pt, c.hx, c.ux, 16u * (c.e & 0x1fu), c.hy, c.uy,
@@ -990,11 +984,18 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           mma_step(acc, fa);
           if (cnt - st == 2) mma_step(acc, fb);
         };
-        // Full levels: step 8 j + m takes level j of indices 16 hf + 2 m (X)
-        // and 16 hf + 2 m + 1 (Y).  Past the last level the entries fall on
-        // level full <= NLEV (position <= 16 NLEV <= 256, inside the table
-        // rows): read, never used.
-        if (full > 0 && wave_live)
+        // Full levels.  Step 8 j + m takes level j of indices 16 hf + 2 m (X)
+        // and 16 hf + 2 m + 1 (Y); both codes of a buffer come in one 8-byte
+        // read.  With one or two levels the steps run level by level, and
+        // past the last level the entries fall on level full <= NLEV
+        // (position <= 16 NLEV <= 256, inside the table rows): read, never
+        // used.
+        auto item2 = [&](uint32_t e) __attribute__((always_inline)) {
+          const uint32_t ox = (e >> 8) & 0x7cu;
+          const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
+          return Item{h2.x, u2.x, h2.y, u2.y, e};
+        };
+        if (full > 0 && full < 3 && wave_live)
           sweep(
               8 * full,
               [&](int st) {
@@ -1004,6 +1005,45 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
                 return ((dx << 10) | kj) | (((dy << 10) | kj) << 16);
               },
               item2);
+        // With three or more, pair by pair: pair m takes its levels
+        // 0 .. full - 1 in turn, so its codes are read once for all of them;
+        // the next pair's codes are read while this pair's steps run, and
+        // each step's fragments a step ahead.  After the last step the
+        // fragments of pair 7, level 0 are read and not used.
+        if (full >= 3 && wave_live) {
+          auto codes_of = [&](int m) __attribute__((always_inline)) {
+            const uint32_t ox = (16u * hf + 2u * (uint32_t)m) << 2;
+            const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
+            return Item{h2.x, u2.x, h2.y, u2.y, 0u};
+          };
+          auto at = [&](Item c, int j) __attribute__((always_inline)) {
+            const uint32_t kj = UNI ? (uint32_t)j : 16u * (uint32_t)j;
+            c.e = kj | (kj << 16);
+            return frags(c);
+          };
+          Item c = codes_of(0);
+          Frag fa = at(c, 0), fb;
+          for (int m = 0; m < 8; ++m) {
+            const Item cn = codes_of(m < 7 ? m + 1 : 7);
+            int j = 0;
+            for (; j + 2 <= full; j += 2) {
+              fb = at(c, j + 1);
+              __builtin_amdgcn_sched_barrier(0);
+              mma_step(acc, fa);
+              const bool more = j + 2 < full;
+              fa = at(more ? c : cn, more ? j + 2 : 0);
+              __builtin_amdgcn_sched_barrier(0);
+              mma_step(acc, fb);
+            }
+            if (j < full) {
+              fb = at(cn, 0);
+              __builtin_amdgcn_sched_barrier(0);
+              mma_step(acc, fa);
+              fa = fb;
+            }
+            c = cn;
+          }
+        }
         // The rest from the stage's list.
         if (n > 0 && wave_live) sweep(n, [&](int st) { return sched[2 * st]; }, item);
         if (wave_live) issued += n + 8 * full;
