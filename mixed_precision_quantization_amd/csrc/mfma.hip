@@ -88,8 +88,8 @@ struct MfmaWs {
   // grid where XCD x takes row tiles (g, y) with (g RT + y) = x (mod 8), each
   // with all its column tiles in turn (staged_tile).
   int row_units;
-  // The index-major copies are written only when a persistent form runs
-  // (the staged kernel reads the blocked buffers alone).
+  // The index-major copies are written only when k_mfma_pers runs (the
+  // staged and quarter kernels read the blocked buffers alone).
   int im_on;
   long long Mp, Np, Dp;
   int RT, CT;
@@ -1813,11 +1813,16 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
     {
       const uint32_t* hrow = w.hs + enc_word((long long)g * w.RT + y, ngrp_all, 0, 0) + (8 * wr + hf) * 128 + 4 * l32;
       const uint32_t* urow = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0) + (8 * wc + hf) * 128 + 4 * l32;
-      const uint32_t* hcol = w.hsi + (long long)g * w.Dp * (w.Mp / 2) + (long long)y * 64 + wr * 32 + l32;
-      const uint32_t* ucol = w.ubi + (long long)g * w.Dp * (w.Np / 2) + (long long)it.x * 64 + wc * 32 + l32;
-      const long long hstr = w.Mp / 2, ustr = w.Np / 2;
-      auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hcol[(long long)d * hstr]; };
-      auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ucol[(long long)d * ustr]; };
+      // List codes come from the blocked buffers (enc_word order: index d of
+      // this lane's pair at the word below), so that k_prep writes no
+      // index-major copies for this form; its lists are short.
+      const uint32_t* hblk = w.hs + enc_word((long long)g * w.RT + y, ngrp_all, 0, 0) + 1024 * wr + 4 * l32;
+      const uint32_t* ublk = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0) + 1024 * wc + 4 * l32;
+      auto blk = [](uint32_t d) __attribute__((always_inline)) {
+        return ((d >> 5) << 11) + ((((d & 15u) >> 2) * 2u + ((d >> 4) & 1u)) << 7) + (d & 3u);
+      };
+      auto hword = [&](uint32_t d) __attribute__((always_inline)) { return hblk[blk(d)]; };
+      auto uword = [&](uint32_t d) __attribute__((always_inline)) { return ublk[blk(d)]; };
       auto list_sweep = [&](int cnt, int dpad) __attribute__((always_inline)) {
         if (lane < PAD4) list[cnt + lane] = ((uint32_t)dpad << 4) | 8u;
         const int nsteps = (cnt + 3) >> 2;
@@ -2137,8 +2142,8 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
                      "the quarter contraction needs a bipolar plan without chunk scales, one band starting on a "
                      "multiple of 32 and a padded contraction axis of at most 4096");
   w.qpt_on = (w.hq && w.uq && use_persistent(a, w) && quarter_chosen(a)) ? 1 : 0;
-  w.im_on = use_persistent(a, w) ? 1 : 0;
-  w.row_units = (!w.im_on && staged_row_units(a, w)) ? 1 : 0;
+  w.im_on = (use_persistent(a, w) && !w.qpt_on) ? 1 : 0;
+  w.row_units = (!use_persistent(a, w) && staged_row_units(a, w)) ? 1 : 0;
   hipLaunchKernelGGL(k_prep, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   const dim3 grid = w.row_units ? dim3((unsigned)(8 * (((long long)a.G * w.RT + 7) / 8) * w.CT))
                                 : dim3(w.CT, w.RT, a.G);
