@@ -256,7 +256,8 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); this path has no multi-GPU "
-              f"mode: each GPU would take its own rows (see DESIGN.md)", file=sys.stderr)
+              f"mode: sharded, each GPU would take a block of X rows with a replicated W and exchange only the "
+              f"row-metric maximum and quantile cuts", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
