@@ -797,7 +797,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   __shared__ __align__(16) uint32_t s_u[2][BN / 2][SW];  // [column pair][index]
   // Stage schedule: the half-blocks past the stage's full levels in order,
   // then padding entries (a zero half-block), and the steps they take.
-  constexpr int SCHED_N = DC * NLEV + 16;
+  constexpr int SCHED_N = DC * NLEV + 64;
   __shared__ __align__(4) uint16_t s_sched[2][SCHED_N];
   __shared__ int s_nsteps[2];
   __shared__ int s_full[2];  // leading levels needed by every index of the stage
@@ -820,8 +820,14 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const int wr = wave >> 1, wc = wave & 1;
   const int l32 = lane & 31, hf = lane >> 5;
   const int qq = a.q * a.q;
-  const int wrow0 = wr * 64;  // first row of this wave
-  const int wcol0 = wc * 64;  // first column of this wave
+  // With at most 64 columns (one column tile, the second half of it empty)
+  // and one accumulation segment, the two column waves of a row share its
+  // 64 x 64 subtile: wave wc takes every other step of each sweep, and the
+  // two accumulators are added at the end (integer counts in float32,
+  // exact).
+  const bool ksplit = !CHUNKED && a.N <= 64;
+  const int wrow0 = wr * 64;                // first row of this wave
+  const int wcol0 = ksplit ? 0 : wc * 64;   // first column of this wave
 
   // Stage loader: thread t reads 16-byte pieces t and t + 256 of the
   // stage's blocks of row and column code words (one contiguous 4 KB per
@@ -876,8 +882,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         base += __builtin_popcountll(bal);
       }
       // Padding: position 16 NLEV is past every window or prefix (A nibbles
-      // all zero).
-      if (tid < 16) s_sched[bf][base + tid] = (uint16_t)(UNI ? NLEV : 16 * NLEV);
+      // all zero); 64 entries cover the steps a sweep reads ahead, also when
+      // two waves share the steps.
+      s_sched[bf][base + tid] = (uint16_t)(UNI ? NLEV : 16 * NLEV);
       if (tid == 0) s_full[bf] = full;
       if (tid == 0) s_nsteps[bf] = (base + 3) >> 2;
     }
@@ -929,7 +936,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // zero).  Any four half-blocks may share a step: lanes 0-31 take
         // the first two (X, Y), lanes 32-63 the other two.
         const char* hbase = (const char*)&s_h[buf][wr * 32 + l32][0];
-        const char* ubase = (const char*)&s_u[buf][wc * 32 + l32][0];
+        const char* ubase = (const char*)&s_u[buf][(wcol0 >> 1) + l32][0];  // column pairs of this wave's columns
         const uint32_t* sched = (const uint32_t*)&s_sched[buf][0] + hf;  // entry pairs
         const int n = s_nsteps[buf];
         const int full = s_full[buf];
@@ -995,10 +1002,13 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
           return Item{h2.x, u2.x, h2.y, u2.y, e};
         };
+        const int sh = ksplit ? 1 : 0;  // step s of a shared sweep is step 2 s + wc
+        const int s_off = ksplit ? wc : 0;
         if (full > 0 && full < 3 && wave_live)
           sweep(
-              8 * full,
-              [&](int st) {
+              (8 * full) >> sh,
+              [&](int st0) {
+                const int st = (st0 << sh) + s_off;
                 const uint32_t j = (uint32_t)(st >> 3) & 31u, m = (uint32_t)(st & 7);
                 const uint32_t dx = 16u * hf + 2u * m, dy = dx + 1u;
                 const uint32_t kj = UNI ? j : 16u * j;
@@ -1021,10 +1031,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
             c.e = kj | (kj << 16);
             return frags(c);
           };
-          Item c = codes_of(0);
+          // Shared: wave wc takes the pairs m = wc (mod 2).
+          const int mstep = 1 << sh;
+          Item c = codes_of(s_off);
           Frag fa = at(c, 0), fb;
-          for (int m = 0; m < 8; ++m) {
-            const Item cn = codes_of(m < 7 ? m + 1 : 7);
+          for (int m = s_off; m < 8; m += mstep) {
+            const Item cn = codes_of(m + mstep < 8 ? m + mstep : m);
             int j = 0;
             for (; j + 2 <= full; j += 2) {
               fb = at(c, j + 1);
@@ -1045,8 +1057,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           }
         }
         // The rest from the stage's list.
-        if (n > 0 && wave_live) sweep(n, [&](int st) { return sched[2 * st]; }, item);
-        if (wave_live) issued += n + 8 * full;
+        const int n_mine = ksplit ? (n + 1 - wc) >> 1 : n;
+        if (n_mine > 0 && wave_live) sweep(n_mine, [&](int st) { return sched[2 * ((st << sh) + s_off)]; }, item);
+        if (wave_live) issued += n_mine + ((8 * full) >> sh);
       }
       const int cend = chunk_end(a, d0);
       if (CHUNKED && min(dn, dend) >= cend) {
@@ -1127,6 +1140,28 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       s_sa[r] = row >= 0 ? a.sA[(long long)g * a.M + row] : 0.0f;
     }
     __syncthreads();
+  }
+  if (ksplit) {
+    // The second column wave of each row hands its partial accumulators
+    // over through the stage buffers, free after the barrier above (16 KB
+    // per wave row: s_h for row 0, s_u for row 1), and leaves.
+    float* const red = (float*)(wr == 0 ? &s_h[0][0][0] : &s_u[0][0][0]);
+    if (wc == 1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) red[((i * 2 + j) * 16 + v) * 64 + lane] = acc[i][j][v];
+    }
+    __syncthreads();
+    if (wc == 1) return;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] += red[((i * 2 + j) * 16 + v) * 64 + lane];
   }
   const int L0 = a.bandL[0][k];
   const float scale0 = (float)qq / (float)L0;

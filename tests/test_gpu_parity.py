@@ -907,6 +907,28 @@ def test_two_streams_give_the_sequential_results(table):
             assert torch.equal(res[i]["C"], ref[i]), f"stream {i}, repetition {rep}"
 
 
+@pytest.mark.parametrize("mode", ["bipolar", "unipolar"])
+@pytest.mark.parametrize("N", [1, 33, 64])
+def test_narrow_outputs_shared_by_column_waves(table, mode, N):
+    """With at most 64 output columns the staged kernel's two column waves
+    of a row share its 64 x 64 subtile (every other step of each sweep) and
+    add their accumulators: with per-row rungs and windows of every length,
+    every count equals the bit-serial kernel's and group 0 equals the
+    oracle."""
+    rng = np.random.default_rng(161 + N)
+    G, M, D = 3, 257, 257
+    A = rng.standard_normal((G, M, D)).astype(np.float32)
+    A[:, :, 7] *= 30.0
+    A[:, 5] = 0.0
+    B = rng.standard_normal((G, N, D)).astype(np.float32)
+    kw = dict(D=D, levels=(256, 128, 64), fractions=(0.333, 0.334, 0.333), mode=mode)
+    plan = scmp.scmp_plan_create(op="qk", **kw)
+    gres = _gpu_path(table, plan, A, B, "mfma_onepass")
+    At, Bt = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    _whole_matrix_vs_bitserial(table, plan, At, Bt, gres)
+    _check_group(gres, 0, A[0], B[0], dict(p=8, Lmax=256, metric="linear", **kw))
+
+
 @pytest.mark.parametrize("algo", ["mfma_persistent", "mfma_quarter"])
 def test_work_queue_grid_with_uneven_queues(table, algo):
     """The persistent launches take tiles from a 2 x 4 grid of work queues
