@@ -88,9 +88,9 @@ typedef enum { SCMP_MODE_BIPOLAR = 0, SCMP_MODE_UNIPOLAR = 1 } scmp_mode;
  *             output tiles per block, one block per tile otherwise); AUTO
  *             takes the quarter form (below) for persistent plans with
  *             D >= 512 where at least half of the 128-row tiles run streams
- *             of length <= 96 (MFMA never does).  When mfma_exact is 0, AUTO runs GATHER
- *             (bipolar) or BITSERIAL (unipolar) instead and the MFMA forms
- *             return UNSUPPORTED.
+ *             of length <= 96 (MFMA never does).  When mfma_exact is 0,
+ *             AUTO runs GATHER (bipolar) or BITSERIAL (unipolar) instead and
+ *             the MFMA forms return UNSUPPORTED.
  *  MFMA_PERSISTENT: the matrix-core path as a persistent grid taking
  *             output tiles from a work counter; bipolar plans without chunk
  *             scales and with one band only (UNSUPPORTED otherwise).
