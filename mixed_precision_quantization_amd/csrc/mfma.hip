@@ -340,8 +340,17 @@ __device__ __forceinline__ bool staged_tile(const MatmulArgs& a, const MfmaWs& w
 // A wave then holds all 64 pairs of its indices: the tile maximum per index
 // is a wave reduction, and each index-major store covers 64 consecutive
 // pairs.  The block covers indices [part * part_len, ...) of one tile.
+constexpr int PR_STRIDE = 40;  // bytes per staged row (32 values + 8 of padding: conflict-free 8-byte reads)
+
+// STAGED: rows not on 8-byte boundaries (D not a multiple of 8) take the
+// staged loader below; the others one 8-byte load per lane and row.
+template <bool STAGED>
 __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, int bx) {
   __shared__ uint32_t s_lut[256];
+  // A group's values of the tile's rows, staged [row][index] in two
+  // buffers: the rows are read along their length (8 lanes per row, four
+  // bytes each), then each lane takes its two rows' 8 values from here.
+  __shared__ __align__(16) uint8_t s_stage[2][MF_BM][PR_STRIDE];
   __shared__ int s_rows[MF_BM];
   __shared__ int s_rc[MF_BM];  // n0 sums of the tile's rows over the current chunk or part
   __shared__ unsigned long long s_win;  // window positions of the block's rows and indices
@@ -360,12 +369,46 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
   if (tid == 0) s_win = 0;
   __syncthreads();
   const int row_lo = s_rows[p_lo], row_hi = s_rows[p_hi];
+  const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
+  const int8_t* src_hi = a.qA + ((long long)g * a.M + (row_hi < 0 ? 0 : row_hi)) * a.D;
+  // Staged loader: thread t reads bytes [4 j, 4 j + 4) (j = t % 8) of the group's
+  // 32 values of rows t / 8 + 32 k (k < 4), from the aligned 32-bit words
+  // that hold them (funnel-shifted by the row's misalignment; a word is
+  // read only when it holds a value of the group, so no read passes the
+  // word of the row's last valid value).
+  const int lj = tid & 7, lr = tid >> 3;
+  const int8_t* lrow[4];
+  unsigned lsh[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    const int row = s_rows[lr + 32 * kk];
+    lrow[kk] = row >= 0 ? a.qA + ((long long)g * a.M + row) * a.D : nullptr;
+    lsh[kk] = (unsigned)((uintptr_t)lrow[kk] & 3u);
+  }
+  uint32_t lw[4][2];
+  auto gload = [&](int d0, int vcount) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) {
+      lw[kk][0] = lw[kk][1] = 0u;
+      if (lrow[kk] && vcount > 0) {
+        const uintptr_t A = (uintptr_t)(lrow[kk] + d0);
+        const uint32_t* p = (const uint32_t*)(A - lsh[kk]);
+        const uintptr_t end = A + (uintptr_t)vcount;  // one past the group's last value
+        const uintptr_t w0 = (uintptr_t)(p + lj);
+        if (w0 < end) lw[kk][0] = p[lj];
+        if (w0 + 4 < end) lw[kk][1] = p[lj + 1];
+      }
+    }
+  };
+  auto sstore = [&](int buf) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk)
+      *(uint32_t*)&s_stage[buf][lr + 32 * kk][4 * lj] = __builtin_amdgcn_alignbyte(lw[kk][1], lw[kk][0], lsh[kk]);
+  };
   // Window positions of this lane's rows (code >> 5: the bipolar half-window
   // hh of paired positions, or the unipolar prefix n1), summed over its
   // indices: the multiply-accumulates the exact count needs per column.
   unsigned int win = 0;
-  const int8_t* src_lo = a.qA + ((long long)g * a.M + (row_lo < 0 ? 0 : row_lo)) * a.D;
-  const int8_t* src_hi = a.qA + ((long long)g * a.M + (row_hi < 0 ? 0 : row_hi)) * a.D;
   const long long tile = (long long)g * w.RT + y;
   const int ngrp = (int)(w.Dp / MF_DC);
   const int plo = part * w.part_len;
@@ -413,9 +456,14 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
       s_lut[tid] = e;
     }
     __syncthreads();
-    // The next group's values are read while this group is encoded.
+    // The next group's values are read while this group is encoded: rows
+    // whose values sit on 8-byte boundaries (D a multiple of 8) as one
+    // 8-byte load per lane and row; other rows through the stage.
+    int sbuf = 0;
     int8_t nx_lo[8], nx_hi[8];
-    {
+    if constexpr (STAGED) {
+      gload(lo, min(MF_DC, dend - lo));
+    } else {
       const int span = max(0, min(8, dend - (lo + 8 * q)));
       load8(src_lo + lo + 8 * q, row_lo >= 0 ? span : 0, nx_lo);
       load8(src_hi + lo + 8 * q, row_hi >= 0 ? span : 0, nx_hi);
@@ -424,15 +472,31 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
       const int dfirst = d0 + 8 * q;
       const int span = max(0, min(8, dend - dfirst));
       int8_t x_lo[8], x_hi[8];
+      if constexpr (STAGED) {
+        sstore(sbuf);
+        if (d0 + MF_DC < dend) gload(d0 + MF_DC, min(MF_DC, dend - d0 - MF_DC));
+        __syncthreads();
+        const uint2 vl = *(const uint2*)&s_stage[sbuf][p_lo][8 * q];
+        const uint2 vh = *(const uint2*)&s_stage[sbuf][p_hi][8 * q];
+        const int8_t* bl = (const int8_t*)&vl;
+        const int8_t* bh = (const int8_t*)&vh;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        x_lo[i] = nx_lo[i];
-        x_hi[i] = nx_hi[i];
-      }
-      if (d0 + MF_DC < dend) {
-        const int nspan = max(0, min(8, dend - (dfirst + MF_DC)));
-        load8(src_lo + dfirst + MF_DC, row_lo >= 0 ? nspan : 0, nx_lo);
-        load8(src_hi + dfirst + MF_DC, row_hi >= 0 ? nspan : 0, nx_hi);
+        for (int i = 0; i < 8; ++i) {
+          x_lo[i] = bl[i];
+          x_hi[i] = bh[i];
+        }
+        sbuf ^= 1;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x_lo[i] = nx_lo[i];
+          x_hi[i] = nx_hi[i];
+        }
+        if (d0 + MF_DC < dend) {
+          const int nspan = max(0, min(8, dend - (dfirst + MF_DC)));
+          load8(src_lo + dfirst + MF_DC, row_lo >= 0 ? nspan : 0, nx_lo);
+          load8(src_hi + dfirst + MF_DC, row_hi >= 0 ? nspan : 0, nx_hi);
+        }
       }
       uint32_t word[8];
       int mh[8];
@@ -617,9 +681,10 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
 // Both encode passes in one launch, so that they run side by side: blocks
 // x < RT encode row tile x, the others column tile x - RT (grid
 // (RT + CT, n_parts, G)).
+template <bool STAGED>
 __global__ void __launch_bounds__(256) k_prep(MatmulArgs a, MfmaWs w) {
   if ((int)blockIdx.x < w.RT)
-    prep_rows(a, w, (int)blockIdx.x);
+    prep_rows<STAGED>(a, w, (int)blockIdx.x);
   else
     prep_cols(a, w, (int)blockIdx.x - w.RT);
 }
@@ -2179,7 +2244,10 @@ int launch_mfma(const MatmulArgs& a0, void* ws, size_t ws_bytes, hipStream_t st)
   w.qpt_on = (w.hq && w.uq && use_persistent(a, w) && quarter_chosen(a)) ? 1 : 0;
   w.im_on = (use_persistent(a, w) && !w.qpt_on) ? 1 : 0;
   w.row_units = (!use_persistent(a, w) && staged_row_units(a, w)) ? 1 : 0;
-  hipLaunchKernelGGL(k_prep, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
+  if (a.D & 7)
+    hipLaunchKernelGGL(k_prep<true>, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
+  else
+    hipLaunchKernelGGL(k_prep<false>, dim3(w.RT + w.CT, w.n_parts, a.G), dim3(256), 0, st, a, w);
   const dim3 grid = w.row_units ? dim3((unsigned)(8 * (((long long)a.G * w.RT + 7) / 8) * w.CT))
                                 : dim3(w.CT, w.RT, a.G);
   launch_main(a, w, grid, st);
