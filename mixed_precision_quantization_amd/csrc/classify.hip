@@ -110,18 +110,22 @@ __global__ void __launch_bounds__(512) k_classify(ClassifyArgs a) {
   }
 }
 
-// Groups of at most CS_MAXM rows (attention heads of 257 queries): one
-// block ranks the whole group, one row per thread, against every key of the
-// group in LDS (the same rank as above; every lane reads the same key at
-// once, an LDS broadcast).  The work per group is M^2 comparisons, a few
-// hundred cycles at these sizes, against the bucket form's 2048-bucket
-// clear and scan repeated by each of its blocks.
+// Groups of at most CS_MAXM rows (attention heads of 257 queries): each
+// block stages the whole group's keys in LDS and ranks CS_ROWS of its rows
+// (the same rank as above), eight lanes per row, lane s of a row comparing
+// the keys j = s (mod 8); the eight partial counts meet in a butterfly.  A
+// wave's eight rows read the same eight consecutive keys at once, so the
+// reads broadcast without bank conflicts.  The work per group is M^2
+// comparisons, spread over ceil(M / CS_ROWS) blocks, against the bucket
+// form's 2048-bucket clear and scan repeated by each of its blocks.
 constexpr int CS_MAXM = 512;
+constexpr int CS_ROWS = 64;  // rows ranked per block (512 threads, 8 per row)
 
 __global__ void __launch_bounds__(CS_MAXM) k_classify_small(ClassifyArgs a) {
   __shared__ float s_key[CS_MAXM];
+  __shared__ float s_g[CS_MAXM];
   __shared__ float s_red[CS_MAXM / 64];
-  const int g = blockIdx.x;
+  const int g = blockIdx.y;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int M = a.M;
@@ -133,31 +137,41 @@ __global__ void __launch_bounds__(CS_MAXM) k_classify_small(ClassifyArgs a) {
   for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off, 64));
   if (lane == 0) s_red[wave] = mx;
   const bool bad = live && !__builtin_isfinite(v);
-  if (__ballot(bad) && lane == 0) atomicOr(a.flag, 1);
+  if (blockIdx.x == 0 && __ballot(bad) && lane == 0) atomicOr(a.flag, 1);
   __syncthreads();
   mx = s_red[0];
 #pragma unroll
   for (int w = 1; w < CS_MAXM / 64; ++w) mx = fmaxf(mx, s_red[w]);
-  const float gi = live ? (mx == 0.0f ? 0.0f : v / mx) : 0.0f;
-  const float ki = rank_key(gi);
-  if (live) s_key[tid] = ki;
-  __syncthreads();
-  // rank_i = #{j : key_j > key_i, or key_j == key_i and j < i}.
-  int rank = 0;
-  for (int j = 0; j < M; ++j) {
-    const float kj = s_key[j];
-    rank += (kj > ki) || (kj == ki && j < tid);
+  if (live) {
+    const float gj = mx == 0.0f ? 0.0f : v / mx;
+    s_g[tid] = gj;
+    s_key[tid] = rank_key(gj);
   }
-  if (!live) return;
-  a.ghat[(long long)g * M + tid] = gi;
-  a.perm[(long long)g * M + rank] = tid;
+  __syncthreads();
+  // rank_i = #{j : key_j > key_i, or key_j == key_i and j < i}.  Every lane
+  // takes part in the butterfly; rows past M read a key and drop the count.
+  const int i = blockIdx.x * CS_ROWS + (tid >> 3), s = tid & 7;
+  const bool row_live = i < M;
+  const float ki = row_live ? s_key[i] : 0.0f;
+  int rank = 0;
+  for (int j = s; j < M; j += 8) {
+    const float kj = s_key[j];
+    rank += (kj > ki) || (kj == ki && j < i);
+  }
+  rank += __shfl_xor(rank, 1, 64);
+  rank += __shfl_xor(rank, 2, 64);
+  rank += __shfl_xor(rank, 4, 64);
+  if (!row_live || s != 0) return;
+  const float gi = s_g[i];
+  a.ghat[(long long)g * M + i] = gi;
+  a.perm[(long long)g * M + rank] = i;
   int k = 0;
   while (k + 1 < a.n_rungs && rank >= a.cuts[k + 1]) ++k;
-  if (a.rung) a.rung[(long long)g * M + tid] = (uint8_t)k;
+  if (a.rung) a.rung[(long long)g * M + i] = (uint8_t)k;
   if (a.thr) {
     for (int kk = 1; kk < a.n_rungs; ++kk) {
       if (rank == a.cuts[kk] - 1) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = gi;
-      if (a.cuts[kk] == 0 && tid == 0) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = 1.0f;
+      if (a.cuts[kk] == 0 && i == 0) a.thr[(long long)g * (a.n_rungs - 1) + kk - 1] = 1.0f;
     }
   }
 }
@@ -355,7 +369,8 @@ extern "C" int scmp_classify_rows(scmp_plan_t plan, const float* metric, int G, 
   if (fs != SCMP_OK) return fs;
   const int tiles = (M + scmp::CL_ROWS - 1) / scmp::CL_ROWS;
   if (M <= scmp::CS_MAXM) {
-    hipLaunchKernelGGL(scmp::k_classify_small, dim3(G), dim3(scmp::CS_MAXM), 0, st, a);
+    hipLaunchKernelGGL(scmp::k_classify_small, dim3((M + scmp::CS_ROWS - 1) / scmp::CS_ROWS, G), dim3(scmp::CS_MAXM), 0,
+                       st, a);
   } else if (M <= scmp::CB_MAXM) {
     // Large groups rank two sets of rows per block: every block repeats the
     // group's O(M) bucketing, so fewer, fuller blocks cost less.

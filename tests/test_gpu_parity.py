@@ -178,6 +178,26 @@ def test_quantise_unaligned_rows(table, D):
     assert np.array_equal(m[0].cpu().numpy(), o.row_metric(X[:, 1:]))
 
 
+@pytest.mark.parametrize("G,M,D", [(128, 257, 257), (64, 257, 257), (40, 257, 100), (20, 1000, 1021)])
+def test_quantise_unaligned_rows_batched(table, G, M, D):
+    """Many groups of unaligned rows on the one-scale-per-row path
+    (attention probabilities of 128 heads, say), with a zero row and a view
+    that starts one float in."""
+    rng = np.random.default_rng(23 + G + D)
+    X = (rng.standard_normal((G, M, D + 1)) * rng.uniform(1e-3, 1e3, (G, M, 1))).astype(np.float32)
+    X[1, 5] = 0.0
+    plan = scmp.scmp_plan_create(op="av", D=D, levels=(64,))
+    Xt = torch.from_numpy(X).cuda()[:, :, 1:]
+    print(f"  quantise unaligned G={G} M={M} D={D}", flush=True)
+    q, s, m, _ = scmp.scmp_quantize_encode(table, plan, Xt)
+    qc, sc, mc = q.cpu().numpy(), s.cpu().numpy(), m.cpu().numpy()
+    for g in range(G):
+        xo, so = o.quantize(X[g, :, 1:], 8)
+        assert np.array_equal(qc[g].astype(np.int64), xo), g
+        assert np.array_equal(sc[g], so), g
+        assert np.array_equal(mc[g], o.row_metric(X[g, :, 1:])), g
+
+
 def test_nonfinite_input_sets_flag(table):
     X = np.ones((4, 64), dtype=np.float32)
     X[2, 5] = np.nan
@@ -232,14 +252,17 @@ def test_packed_streams_are_table_rows(table):
 
 # -------------------------------------------------------------- classify --
 
-@pytest.mark.parametrize("M", [1000, 512, 257])
+@pytest.mark.parametrize("M", [1000, 512, 257, 65, 64, 1])
 def test_classify_matches_oracle_with_ties(table, M):
     """Bucketed groups (1000 rows) and groups ranked by one block each (at
     most 512 rows), with runs of equal keys, quarter steps and zeros."""
     rng = np.random.default_rng(22)
     G = 3
     g = rng.uniform(0, 3, (G, M)).astype(np.float32)
-    g[0, 100:200] = g[0, 50]                     # ties
+    if M > 50:
+        g[0, 100:200] = g[0, 50]                 # ties
+    else:
+        g[0, M // 2:] = g[0, 0]
     g[1] = np.round(g[1] * 4) / 4                # many ties
     g[2, :10] = 0.0
     levels, fr = (256, 192, 128, 96, 64), (0.1, 0.15, 0.2, 0.25, 0.3)
