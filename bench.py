@@ -84,6 +84,59 @@ def sources_sha256():
     return h.hexdigest()
 
 
+class TimingEvents:
+    """Pairs of HIP timing events recorded on one stream, created before the
+    timed steps.  They are created with hipEventDisableSystemFence: an event
+    that only times the work between two records needs no system-scope
+    fence, so recording one adds no cache writeback or invalidation to the
+    stream and leaves the following kernels unperturbed.  Read them after a
+    device synchronisation."""
+
+    FLAGS = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+    def __init__(self, n):
+        import ctypes
+        self._c = ctypes
+        self._lib = ctypes.CDLL("libamdhip64.so")
+        self._pairs = []
+        for _ in range(n):
+            pair = []
+            for _ in range(2):
+                e = ctypes.c_void_p()
+                st = self._lib.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.FLAGS))
+                if st != 0:
+                    raise RuntimeError(f"hipEventCreateWithFlags failed ({st})")
+                pair.append(e)
+            self._pairs.append(pair)
+        self._used = 0
+
+    def start(self, stream):
+        self._check(self._lib.hipEventRecord(self._pairs[self._used][0], self._c.c_void_p(stream.cuda_stream)))
+
+    def stop(self, stream):
+        self._check(self._lib.hipEventRecord(self._pairs[self._used][1], self._c.c_void_p(stream.cuda_stream)))
+        self._used += 1
+
+    def mean_ms(self):
+        out = []
+        for a, b in self._pairs[:self._used]:
+            ms = self._c.c_float(0.0)
+            self._check(self._lib.hipEventElapsedTime(self._c.byref(ms), a, b))
+            out.append(ms.value)
+        return float(sum(out) / len(out))
+
+    def close(self):
+        for pair in self._pairs:
+            for e in pair:
+                self._lib.hipEventDestroy(e)
+        self._pairs = []
+
+    @staticmethod
+    def _check(st):
+        if st != 0:
+            raise RuntimeError(f"HIP event call failed ({st})")
+
+
 def profiled_traffic(workload, algo, dispatches):
     """HBM bytes of the contraction kernel per timed call from the committed
     rocprofv3 summary of this workload and algo (FETCH_SIZE + WRITE_SIZE,
@@ -316,7 +369,7 @@ def main():
     ws_bytes = scmp.scmp_matmul_workspace_bytes(table, plan, G, M, N, args.algo)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
-    ev = []
+    ev = TimingEvents(args.steps)
     if ranged:
         # Range MP: W's groups are classified once, at load time (the weights
         # are static; the call synchronises); each step quantises W and
@@ -341,9 +394,7 @@ def main():
         if pB is not None:
             gather_into(pB, pBs)
         if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            ev.start(stream)
         for k in range(2):
             a0, a1 = offs[k], offs[k + 1]
             if a1 > a0:
@@ -351,8 +402,7 @@ def main():
                                        packedB=None if pBs is None else pBs[:, a0:a1], algo=args.algo,
                                        workspace=wsk[k], stream=stream)
         if timed:
-            e1.record(stream)
-            ev.append((e0, e1))
+            ev.stop(stream)
 
     def step(timed):
         scmp.scmp_quantize_encode(table, plan, A, q_out=qA, scales_out=sA, metric_out=mA, stream=stream)
@@ -369,14 +419,11 @@ def main():
                                     stream=stream)
             perm = pm
         if timed:
-            e0 = torch.cuda.Event(enable_timing=True)
-            e1 = torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
+            ev.start(stream)
         scmp.scmp_matmul(table, plan, qA, sA, qB, sB, permA=perm, packedB=pB, algo=args.algo, C_out=C,
                          want_C=True, workspace=ws, bias=bias, group_rung=group_rung, stream=stream)
         if timed:
-            e1.record(stream)
-            ev.append((e0, e1))
+            ev.stop(stream)
 
     run = step_range if ranged else step
     for _ in range(args.warmup):
@@ -388,7 +435,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    kern_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_ms = ev.mean_ms()
+    ev.close()
     if ranged:
         lv = plan.band_lengths()[0]
         bitmacs = G * M * D * (n_lv[0] * lv[0] + n_lv[1] * lv[1])
