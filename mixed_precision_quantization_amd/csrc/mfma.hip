@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstddef>
 #include <cmath>
 #include <string>
 #include <vector>
@@ -310,6 +311,25 @@ __device__ __forceinline__ uint32_t a_class_word(int a) {
 // Byte offset of the pair-table entry of classes (c1, c2).
 __device__ __forceinline__ uint32_t qpt_off(int c1, int c2) { return (uint32_t)(c1 * QPT_CLASSES + c2) * 8u; }
 
+// The tables of the quarter contraction in LDS: the paired table of the
+// staged rung, the A patterns (PAT_WORDS, below), the A and B pair tables
+// of quarter 0 and the B patterns by class.  The quarter codes k_prep writes
+// are byte offsets from the pattern table (A) and from the paired table (B),
+// so a quarter step and a 16-position step of level 0 read their operands
+// through the same two bases and one code path serves both.
+constexpr int PAT_WORDS = 258 * 4;
+struct __align__(16) QptTables {
+  uint8_t pt[MAX_LEVELS * PT_STRIDE];
+  uint32_t pat[PAT_WORDS];
+  uint2 apt[QPT_ENTRIES];  // A pair table of quarter 0 (window classes of two indices)
+  uint2 bpt[QPT_ENTRIES];  // B pair table of quarter 0 for the staged rung
+  uint32_t bpat[QPT_CLASSES];
+};
+constexpr uint32_t QPT_A_BASE = (uint32_t)(offsetof(QptTables, apt) - offsetof(QptTables, pat));
+constexpr uint32_t QPT_B_BASE = (uint32_t)(offsetof(QptTables, bpt) - offsetof(QptTables, pt));
+static_assert(QPT_A_BASE + QPT_ENTRIES * 8 <= 65536 && QPT_B_BASE + QPT_ENTRIES * 8 <= 65536,
+              "quarter codes are 16-bit offsets");
+
 // Output tile of a staged-kernel block.  Workgroups are dispatched to the
 // 8 XCDs in turn (block b to XCD b mod 8), each XCD with its own L2.  With
 // row_units, block b = 8 s + x takes the s-th tile of XCD x: row tile
@@ -535,8 +555,8 @@ __device__ __forceinline__ void prep_rows(const MatmulArgs& a, const MfmaWs& w, 
         uint32_t qw[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t lo = qpt_off(a_class(cw[0][2 * t]), a_class(cw[0][2 * t + 1]));
-          const uint32_t hi = qpt_off(a_class(cw[1][2 * t]), a_class(cw[1][2 * t + 1]));
+          const uint32_t lo = QPT_A_BASE + qpt_off(a_class(cw[0][2 * t]), a_class(cw[0][2 * t + 1]));
+          const uint32_t hi = QPT_A_BASE + qpt_off(a_class(cw[1][2 * t]), a_class(cw[1][2 * t + 1]));
           qw[t] = lo | (hi << 16);
         }
         const long long plane = (long long)g * w.RT + y;
@@ -661,8 +681,8 @@ __device__ __forceinline__ void prep_cols(const MatmulArgs& a, const MfmaWs& w, 
         uint32_t qw[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          const uint32_t lo = qpt_off(s_bc[k][lv[0][2 * t]], s_bc[k][lv[0][2 * t + 1]]);
-          const uint32_t hi = qpt_off(s_bc[k][lv[1][2 * t]], s_bc[k][lv[1][2 * t + 1]]);
+          const uint32_t lo = QPT_B_BASE + qpt_off(s_bc[k][lv[0][2 * t]], s_bc[k][lv[0][2 * t + 1]]);
+          const uint32_t hi = QPT_B_BASE + qpt_off(s_bc[k][lv[1][2 * t]], s_bc[k][lv[1][2 * t + 1]]);
           qw[t] = lo | (hi << 16);
         }
         uint32_t* base = w.uq + (long long)k * rung_stride;
@@ -711,7 +731,6 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 // offset max(c - 32 kk, 0): entry 2 (hh - kk) + neg when hh > kk (the first
 // clamp(hh - kk, 0, 16) positions), a zero entry (0 or 1) otherwise.  Rows
 // with equal fragments read one address (an LDS broadcast).
-constexpr int PAT_WORDS = 258 * 4;
 __device__ __forceinline__ void init_patterns(uint32_t* pat, int tid, int nthreads) {
   for (int w = tid; w < PAT_WORDS; w += nthreads) {
     const int e = w >> 2, wd = w & 3, n = min(e >> 1, 16);
@@ -1650,14 +1669,7 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
 // read during the previous tile.
 template <bool COUNTS>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, MfmaWs w, int n_items) {
-  struct __align__(16) GatherTables {
-    uint8_t pt[MAX_LEVELS * PT_STRIDE];
-    uint32_t pat[PAT_WORDS];
-    uint2 apt[QPT_ENTRIES];  // A pair table of quarter 0 (window classes of two indices)
-    uint2 bpt[QPT_ENTRIES];  // B pair table of quarter 0 for the staged rung
-    uint32_t bpat[QPT_CLASSES];
-  };
-  __shared__ GatherTables s_tab;
+  __shared__ QptTables s_tab;
   __shared__ __align__(8) uint32_t s_list[4][FL_LIST];
   __shared__ __align__(16) int s_rows[2][MF_BM];
   __shared__ __align__(16) int s_rc[2][MF_BM];
@@ -1788,11 +1800,15 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
     const int ngrp = (dend - dbeg + 31) / 32;
     const uint8_t* const mxs = s_maxh[cur];
 
-    // ---- pass 1: paired positions [0, 16).  A group whose 32 maxima are
-    // all at most 8 (and one positive) takes quarter 0 only: four steps of
-    // 8 indices from the pair tables.  Any other group with a positive
-    // maximum takes level 0 as 16-position steps from its codes, eight steps
-    // of 4 indices.
+    // ---- pass 1: paired positions [0, 16), as units of four steps.  A
+    // group whose 32 maxima are all at most 8 (and one positive) is one
+    // unit: quarter 0, 8 indices per step from the pair tables.  Any other
+    // group with a positive maximum is two units: level 0 as 16-position
+    // steps of 4 indices, indices d0 + 16 hf + m and + 8 (m < 4: unit 0,
+    // else unit 1).  Quarter codes are offsets from the same two tables as
+    // the window and level codes, so every unit is one code path: its codes
+    // are two 16-byte pieces per buffer (step s pairs word s of the first
+    // with word s of the second) and the accumulators stay in place.
     {
       // Uniform bases of this tile's codes and 32-bit lane offsets (words).
       const uint32_t* const hq_t = w.hq + qcode_index((long long)g * w.RT + y, ngrp_all, dbeg / 32, 0, 0);
@@ -1802,98 +1818,124 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
       const uint32_t* const ub_t = w.ub + enc_word((long long)g * w.CT + it.x, ngrp_all, 0, 0);
       const unsigned qa_off = (unsigned)((hf * 64 + wr * 32 + l32) * 8), qb_off = (unsigned)((hf * 64 + wc * 32 + l32) * 8);
       const unsigned ha_off = (unsigned)((8 * wr + hf) * 128 + 4 * l32), hb_off = (unsigned)((8 * wc + hf) * 128 + 4 * l32);
-      const char* const apt = (const char*)s_tab.apt;
-      const char* const bpt = (const char*)s_tab.bpt;
-      // Mode of a group (uniform): 0 nothing, 1 quarter 0, 2 level 0.
-      auto mode_of = [&](int grp) __attribute__((always_inline)) {
-        const int m = grp < ngrp ? (int)mxs[32 * grp + l32] : 0;
-        return __builtin_amdgcn_readfirstlane(__ballot(m > 8) ? 2 : (__ballot(m > 0) ? 1 : 0));
-      };
-      // A group's codes in its mode, always as four 16-byte loads per
-      // buffer (the same loads in every mode, so the waits stay exact):
-      // quarter 0, pieces 0 and 1 hold its 8 words of A (B), pieces 2 and 3
-      // repeat them; otherwise the codes of indices d0 + 16 hf + m, m < 16.
-      auto load_codes = [&](int grp, int md, uint32_t* h, uint32_t* u) __attribute__((always_inline)) {
-        const bool qm = md == 1;
-        const uint4* hp = qm ? (const uint4*)(hq_t + ((unsigned)grp << 10) + qa_off)
-                             : (const uint4*)(hs_t + ((unsigned)(dbeg / 32 + grp) << 11) + ha_off);
-        const uint4* up = qm ? (const uint4*)(uq_t + ((unsigned)grp << 10) + qb_off)
-                             : (const uint4*)(ub_t + ((unsigned)(dbeg / 32 + grp) << 11) + hb_off);
-        const int stride = qm ? 1 : 64;  // uint4 between pieces
+      // Group modes as bit masks (uniform): nz, some index of the group
+      // needs positions; gt, some index needs more than 8.  Lane l looks at
+      // groups l and l + 64 (ngrp <= QPT_MAX_DP / 32 = 128).
+      uint64_t nz[2], gt[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int pi = qm ? (i & 1) : i;
-          const uint4 th = hp[stride * pi], tu = up[stride * pi];
-          h[4 * i] = th.x;
-          h[4 * i + 1] = th.y;
-          h[4 * i + 2] = th.z;
-          h[4 * i + 3] = th.w;
-          u[4 * i] = tu.x;
-          u[4 * i + 1] = tu.y;
-          u[4 * i + 2] = tu.z;
-          u[4 * i + 3] = tu.w;
-        }
-      };
-      // Quarter-step s: per row (column) subtile two 8-byte pair-table
-      // entries, index pairs 2 s and 2 s + 1 of the lane half (code words
-      // 2 s, 2 s + 1; low half subtile 0, high half subtile 1).
-      auto qfrag = [&](const uint32_t* ch, const uint32_t* cu, int st) __attribute__((always_inline)) {
-        const uint32_t wa0 = ch[2 * st], wa1 = ch[2 * st + 1], wb0 = cu[2 * st], wb1 = cu[2 * st + 1];
-        const v2i a00 = *(const v2i*)(apt + (wa0 & 0xffffu)), a01 = *(const v2i*)(apt + (wa1 & 0xffffu));
-        const v2i a10 = *(const v2i*)(apt + (wa0 >> 16)), a11 = *(const v2i*)(apt + (wa1 >> 16));
-        const v2i b00 = *(const v2i*)(bpt + (wb0 & 0xffffu)), b01 = *(const v2i*)(bpt + (wb1 & 0xffffu));
-        const v2i b10 = *(const v2i*)(bpt + (wb0 >> 16)), b11 = *(const v2i*)(bpt + (wb1 >> 16));
-        Frag f;
-        f.a[0] = v8i{a00.x, a00.y, a01.x, a01.y, 0, 0, 0, 0};
-        f.a[1] = v8i{a10.x, a10.y, a11.x, a11.y, 0, 0, 0, 0};
-        f.b[0] = v8i{b00.x, b00.y, b01.x, b01.y, 0, 0, 0, 0};
-        f.b[1] = v8i{b10.x, b10.y, b11.x, b11.y, 0, 0, 0, 0};
-        return f;
-      };
-      // One group's pass-1 steps; each step's fragments are read while the
-      // previous step's MFMAs run.
-      auto sweep = [&](const uint32_t* ch, const uint32_t* cu, int md) __attribute__((always_inline)) {
-        if (md == 1) {
-          Frag fa = qfrag(ch, cu, 0), fb = qfrag(ch, cu, 1);
-          __builtin_amdgcn_sched_barrier(0);
-          mma(fa);
-          fa = qfrag(ch, cu, 2);
-          __builtin_amdgcn_sched_barrier(0);
-          mma(fb);
-          fb = qfrag(ch, cu, 3);
-          __builtin_amdgcn_sched_barrier(0);
-          mma(fa);
-          __builtin_amdgcn_sched_barrier(0);
-          mma(fb);
-          issued += 4;
-        } else if (md == 2) {
-          // Step m pairs indices d0 + 16 hf + m (X) and d0 + 16 hf + 8 + m
-          // (Y) in lane half hf, at paired positions [0, 16).
-          Frag fa = frags_at(ch[0], cu[0], 0u, ch[8], cu[8], 0u), fb;
+      for (int h = 0; h < 2; ++h) {
+        const int grp = lane + 64 * h;
+        uint32_t any = 0, big = 0;
+        if (grp < ngrp) {
+          const uint4* m4 = (const uint4*)(mxs + 32 * grp);
 #pragma unroll
-          for (int m = 0; m < 8; m += 2) {
-            fb = frags_at(ch[m + 1], cu[m + 1], 0u, ch[m + 9], cu[m + 9], 0u);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fa);
-            if (m + 2 < 8) fa = frags_at(ch[m + 2], cu[m + 2], 0u, ch[m + 10], cu[m + 10], 0u);
-            __builtin_amdgcn_sched_barrier(0);
-            mma(fb);
+          for (int i = 0; i < 2; ++i) {
+            const uint4 v = m4[i];
+            const uint32_t x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              // A byte exceeds 8 when its high nibble is set or its low
+              // nibble plus 7 carries into bit 4 (no carry leaves a byte).
+              any |= x[e];
+              big |= (x[e] & 0xF0F0F0F0u) | (((x[e] & 0x0F0F0F0Fu) + 0x07070707u) & 0x10101010u);
+            }
           }
-          issued += 8;
+        }
+        nz[h] = __ballot(any != 0);
+        gt[h] = __ballot(big != 0);
+      }
+      // The first group from gr on with a positive maximum, or ngrp.
+      auto first_from = [&](int gr) __attribute__((always_inline)) {
+        if (gr < 64) {
+          const uint64_t m = nz[0] & (~0ull << gr);
+          if (m) return (int)__builtin_ctzll(m);
+          gr = 64;
+        }
+        if (gr < 128) {
+          const uint64_t m = nz[1] & (~0ull << (gr - 64));
+          if (m) return 64 + (int)__builtin_ctzll(m);
+        }
+        return ngrp;
+      };
+      auto level0 = [&](int gr) __attribute__((always_inline)) {
+        return ((gr < 64 ? gt[0] >> gr : gt[1] >> (gr - 64)) & 1ull) != 0;
+      };
+      // The codes of unit u of group gr: quarter codes (pieces 0 and 1 of
+      // the lane's 8 words) or level codes (pieces u and u + 2 of its 16).
+      auto unit_load = [&](int gr, int u, uint32_t (&ca)[8], uint32_t (&cb)[8]) __attribute__((always_inline)) {
+        const bool l0 = level0(gr);
+        const uint4* hp = l0 ? (const uint4*)(hs_t + ((unsigned)(dbeg / 32 + gr) << 11) + ha_off) + 64 * u
+                             : (const uint4*)(hq_t + ((unsigned)gr << 10) + qa_off);
+        const uint4* up = l0 ? (const uint4*)(ub_t + ((unsigned)(dbeg / 32 + gr) << 11) + hb_off) + 64 * u
+                             : (const uint4*)(uq_t + ((unsigned)gr << 10) + qb_off);
+        const int o1 = l0 ? 128 : 1;  // uint4 from the first piece to the second
+        const uint4 h0 = hp[0], h1 = hp[o1], u0 = up[0], u1 = up[o1];
+        ca[0] = h0.x;
+        ca[1] = h0.y;
+        ca[2] = h0.z;
+        ca[3] = h0.w;
+        ca[4] = h1.x;
+        ca[5] = h1.y;
+        ca[6] = h1.z;
+        ca[7] = h1.w;
+        cb[0] = u0.x;
+        cb[1] = u0.y;
+        cb[2] = u0.z;
+        cb[3] = u0.w;
+        cb[4] = u1.x;
+        cb[5] = u1.y;
+        cb[6] = u1.z;
+        cb[7] = u1.w;
+      };
+      // One unit's four steps; each step's fragments are read while the
+      // previous step's MFMAs run.
+      auto unit_sweep = [&](const uint32_t (&ca)[8], const uint32_t (&cb)[8]) __attribute__((always_inline)) {
+        Frag fa = frags_at(ca[0], cb[0], 0u, ca[4], cb[4], 0u);
+        Frag fb = frags_at(ca[1], cb[1], 0u, ca[5], cb[5], 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa);
+        fa = frags_at(ca[2], cb[2], 0u, ca[6], cb[6], 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fb);
+        fb = frags_at(ca[3], cb[3], 0u, ca[7], cb[7], 0u);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fb);
+        issued += 4;
+      };
+      // The unit after (gr, u); gr = ngrp when none is left.
+      auto advance = [&](int& gr, int& u) __attribute__((always_inline)) {
+        if (u == 0 && level0(gr)) {
+          u = 1;
+        } else {
+          u = 0;
+          gr = first_from(gr + 1);
         }
       };
-      if (ngrp > 0) {
-        uint32_t ha[16], ua[16], hb[16], ub[16];
-        int ma = mode_of(0), mb;
-        load_codes(0, ma, ha, ua);
-        for (int grp = 0; grp < ngrp; grp += 2) {
-          mb = mode_of(grp + 1);
-          load_codes(grp + 1, mb, hb, ub);
-          sweep(ha, ua, ma);
-          if (grp + 1 >= ngrp) break;
-          ma = mode_of(grp + 2);
-          load_codes(grp + 2, ma, ha, ua);
-          sweep(hb, ub, mb);
+      int cg = first_from(0), cu = 0;
+      if (cg < ngrp) {
+        // Two code buffers in turn, the next unit's codes read during the
+        // current unit (when none is left, the current codes are read again
+        // into the free buffer, so every iteration issues the same loads).
+        uint32_t ca0[8], cb0[8], ca1[8], cb1[8];
+        unit_load(cg, cu, ca0, cb0);
+        while (true) {
+          int ng = cg, nu = cu;
+          advance(ng, nu);
+          const bool more1 = ng < ngrp;
+          unit_load(more1 ? ng : cg, more1 ? nu : cu, ca1, cb1);
+          unit_sweep(ca0, cb0);
+          if (!more1) break;
+          cg = ng;
+          cu = nu;
+          advance(ng, nu);
+          const bool more2 = ng < ngrp;
+          unit_load(more2 ? ng : cg, more2 ? nu : cu, ca0, cb0);
+          unit_sweep(ca1, cb1);
+          if (!more2) break;
+          cg = ng;
+          cu = nu;
         }
       }
     }
