@@ -994,6 +994,23 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
   const bool wave_live = wrow0 < nrows && col0 + wcol0 < a.N;
   uint32_t issued = 0;
 
+  // Chunk scales: thread r < BM keeps row r's n0 sum and scale of the next
+  // chunk to decode in registers, read one chunk ahead, so that a chunk's
+  // decode does not wait for them.
+  int pf_rc = 0;
+  float pf_sa = 0.0f;
+  int pf_row = -1;
+  auto prefetch_chunk = [&](int ch) __attribute__((always_inline)) {
+    if (tid < BM && ch < a.n_chunks) {
+      pf_rc = w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + prow0 + tid];
+      pf_sa = pf_row >= 0 ? a.sA[((long long)g * a.M + pf_row) * a.n_chunks + ch] : 0.0f;
+    }
+  };
+  if (CHUNKED) {
+    pf_row = tid < nrows ? row_of(a, g, pos0 + tid) : -1;
+    prefetch_chunk(a.band_cols[0] / a.chunk_d);
+  }
+
   int buf = 0;
   fetch(a.band_cols[0]);
   for (int b = 0; b < a.n_bands; ++b) {
@@ -1150,11 +1167,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         // Chunk complete: add each row's n0 sum, decode with the chunk scales.
         const int ch = d0 / a.chunk_d;
         const int cw = cend - ch * a.chunk_d;
-        for (int r = tid; r < BM; r += 256) {
-          const int row = s_rows[r];
-          s_rc[r] = w.rowc[((long long)g * a.n_chunks + ch) * w.Mp + prow0 + r];
-          s_sa[r] = row >= 0 ? a.sA[((long long)g * a.M + row) * a.n_chunks + ch] : 0.0f;
+        if (tid < BM) {
+          s_rc[tid] = pf_rc;
+          s_sa[tid] = pf_sa;
         }
+        prefetch_chunk(ch + 1);  // bands are whole chunks in order
         __syncthreads();
         float sb[2];
 #pragma unroll
@@ -1174,15 +1191,20 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
             const int rcv[4] = {rc.x, rc.y, rc.z, rc.w};
             const float sav[4] = {sa.x, sa.y, sa.z, sa.w};
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
+            for (int e = 0; e < 4; ++e) {
+              // The chunk term's integer 2 count - L |c| (UNI: count) as
+              // 2 acc + (2 n0 - L |c|) in float32: every operand and the
+              // result are integers below 2^24, so it is exact.
+              const float gam = (float)(UNI ? rcv[e] : 2 * rcv[e] - L * cw);
 #pragma unroll
               for (int j = 0; j < 2; ++j) {
                 const int v = q4 * 4 + e;
-                const int cnt = (int)acc[i][j][v] + rcv[e];
-                cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * (float)(UNI ? cnt : 2 * cnt - L * cw));
-                if (COUNTS) bacc[i][j][v] += cnt;
+                const float t = UNI ? acc[i][j][v] + gam : fmaf(2.0f, acc[i][j][v], gam);
+                cacc[i][j][v] += (sav[e] * sb[j]) * (scaleL * t);
+                if (COUNTS) bacc[i][j][v] += (int)acc[i][j][v] + rcv[e];
                 acc[i][j][v] = 0.0f;
               }
+            }
           }
         __syncthreads();  // s_rc / s_sa are rewritten at the next chunk
       }
