@@ -721,24 +721,25 @@ __global__ void __launch_bounds__(256) k_prep(MatmulArgs a, MfmaWs w) {
 // nibbles 16-31 (the MFMA sums both), so one step of four MFMAs per wave
 // covers four half-blocks of its 64 x 64 tile.
 typedef int v2i __attribute__((ext_vector_type(2)));
+typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 
-// A patterns: entry e (16-byte stride, first 8 bytes used) holds
-// min(e / 2, 16) leading sign nibbles, 0xA (-1) when e is odd and 0x2 (+1)
-// otherwise, then zero nibbles.  A row whose window code is
-// c = 16 (2 hh + neg) finds its fragment for positions [kk, kk + 16) at byte
-// offset max(c - 32 kk, 0): entry 2 (hh - kk) + neg when hh > kk (the first
-// clamp(hh - kk, 0, 16) positions), a zero entry (0 or 1) otherwise.  Rows
-// with equal fragments read one address (an LDS broadcast).
+// A patterns: entry e (16 bytes, 32 nibbles) holds min(e / 2, 32) leading
+// sign nibbles, 0xA (-1) when e is odd and 0x2 (+1) otherwise, then zero
+// nibbles.  A row whose window code is c = 16 (2 hh + neg) finds its
+// fragment for positions [kk, kk + 16) in the first 8 bytes at byte offset
+// max(c - 32 kk, 0): entry 2 (hh - kk) + neg when hh > kk (the first
+// clamp(hh - kk, 0, 16) positions), a zero entry (0 or 1) otherwise; the
+// whole 16 bytes there are positions [kk, kk + 32).  Rows with equal
+// fragments read one address (an LDS broadcast).
 __device__ __forceinline__ void init_patterns(uint32_t* pat, int tid, int nthreads) {
   for (int w = tid; w < PAT_WORDS; w += nthreads) {
-    const int e = w >> 2, wd = w & 3, n = min(e >> 1, 16);
+    const int e = w >> 2, wd = w & 3, n = min(e >> 1, 32);
     const uint32_t one = (e & 1) ? 0xAu : 0x2u;
     uint32_t x = 0;
-    if (wd < 2)
-      for (int nib = 0; nib < 8; ++nib)
-        if (wd * 8 + nib < n) x |= one << (4 * nib);
+    for (int nib = 0; nib < 8; ++nib)
+      if (wd * 8 + nib < n) x |= one << (4 * nib);
     pat[w] = x;
   }
 }
@@ -837,6 +838,37 @@ __device__ __forceinline__ Frag frags_at_uni(const uint8_t* pat, const uint8_t* 
   f.a[1] = v8i{ax1.x, ax1.y, ay1.x, ay1.y, 0, 0, 0, 0};
   f.b[0] = v8i{bx0.x ^ sx0, bx0.y ^ sx0, by0.x ^ sy0, by0.y ^ sy0, 0, 0, 0, 0};
   f.b[1] = v8i{bx1.x ^ sx1, bx1.y ^ sx1, by1.x ^ sy1, by1.y ^ sy1, 0, 0, 0, 0};
+  return f;
+}
+
+// Operands of one step that takes two consecutive levels of one index
+// (positions [kk, kk + 32), kk a multiple of 32): X is level kk / 16 and
+// Y the next, both from one 16-byte read per subtile, A from the pattern
+// table (whose entries hold 32 nibbles) and B from the row's nibbles at
+// kk / 2 (16-byte aligned: rows are PT_STRIDE = 9 x 16 bytes).  UNI: the
+// unipolar prefix with offsets clamped to entry 64 or 65 (32 sign nibbles)
+// and B's sign applied to all 32 nibbles.
+template <bool UNI>
+__device__ __forceinline__ Frag frags_at2(const uint8_t* pat, const uint8_t* pt, uint32_t h, uint32_t u, uint32_t kk) {
+  auto aoff = [](uint32_t code, uint32_t k) {
+    const uint32_t o = __builtin_elementwise_sub_sat(code, 32u * k);
+    return UNI ? min(o, 1024u + (o & 16u)) : o;
+  };
+  const uint32_t bm = UNI ? 0xfffeu : 0xffffu;
+  const v4i a0 = *(const v4i*)(pat + aoff(h & 0xffffu, kk));
+  const v4i a1 = *(const v4i*)(pat + aoff(h >> 16, kk));
+  v4i b0 = *(const v4i*)(pt + (u & bm) + (kk >> 1));
+  v4i b1 = *(const v4i*)(pt + ((u >> 16) & bm) + (kk >> 1));
+  if (UNI) {
+    const int s0 = (int)(0u - (u & 1u)) & (int)0x88888888u, s1 = (int)(0u - ((u >> 16) & 1u)) & (int)0x88888888u;
+    b0 ^= v4i{s0, s0, s0, s0};
+    b1 ^= v4i{s1, s1, s1, s1};
+  }
+  Frag f;
+  f.a[0] = v8i{a0.x, a0.y, a0.z, a0.w, 0, 0, 0, 0};
+  f.a[1] = v8i{a1.x, a1.y, a1.z, a1.w, 0, 0, 0, 0};
+  f.b[0] = v8i{b0.x, b0.y, b0.z, b0.w, 0, 0, 0, 0};
+  f.b[1] = v8i{b1.x, b1.y, b1.z, b1.w, 0, 0, 0, 0};
   return f;
 }
 
@@ -1105,58 +1137,56 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
         };
         const int sh = ksplit ? 1 : 0;  // step s of a shared sweep is step 2 s + wc
         const int s_off = ksplit ? wc : 0;
-        if (full > 0 && full < 3 && wave_live)
-          sweep(
-              (8 * full) >> sh,
-              [&](int st0) {
-                const int st = (st0 << sh) + s_off;
-                const uint32_t j = (uint32_t)(st >> 3) & 31u, m = (uint32_t)(st & 7);
-                const uint32_t dx = 16u * hf + 2u * m, dy = dx + 1u;
-                const uint32_t kj = UNI ? j : 16u * j;
-                return ((dx << 10) | kj) | (((dy << 10) | kj) << 16);
-              },
-              item2);
-        // With three or more, pair by pair: pair m takes its levels
-        // 0 .. full - 1 in turn, so its codes are read once for all of them;
-        // the next pair's codes are read while this pair's steps run, and
-        // each step's fragments a step ahead.  After the last step the
-        // fragments of pair 7, level 0 are read and not used.
-        if (full >= 3 && wave_live) {
+        // Full levels [0, 2 fp) in level pairs: index pair m (indices
+        // 16 hf + 2 m and + 1, both codes of a buffer in one 8-byte read)
+        // takes steps (x, jp): index 2 m + x at levels 2 jp and 2 jp + 1,
+        // one 16-byte fragment read per subtile.  The next pair's codes are
+        // read while this pair's steps run, each step's fragments a step
+        // ahead; after the last step the fragments of the last pair's first
+        // step are read again and not used.
+        const int fp = full >> 1;
+        if (fp > 0 && wave_live) {
           auto codes_of = [&](int m) __attribute__((always_inline)) {
             const uint32_t ox = (16u * hf + 2u * (uint32_t)m) << 2;
             const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
             return Item{h2.x, u2.x, h2.y, u2.y, 0u};
           };
-          auto at = [&](Item c, int j) __attribute__((always_inline)) {
-            const uint32_t kj = UNI ? (uint32_t)j : 16u * (uint32_t)j;
-            c.e = kj | (kj << 16);
-            return frags(c);
+          auto at2 = [&](uint32_t h, uint32_t u, int jp) __attribute__((always_inline)) {
+            return frags_at2<UNI>(s_pat, s_pt, h, u, 32u * (uint32_t)jp);
           };
           // Shared: wave wc takes the pairs m = wc (mod 2).
           const int mstep = 1 << sh;
           Item c = codes_of(s_off);
-          Frag fa = at(c, 0), fb;
+          Frag fa = at2(c.hx, c.ux, 0), fb;
           for (int m = s_off; m < 8; m += mstep) {
             const Item cn = codes_of(m + mstep < 8 ? m + mstep : m);
-            int j = 0;
-            for (; j + 2 <= full; j += 2) {
-              fb = at(c, j + 1);
+            for (int jp = 0; jp < fp; ++jp) {
+              fb = at2(c.hy, c.uy, jp);
               __builtin_amdgcn_sched_barrier(0);
               mma_step(acc, fa);
-              const bool more = j + 2 < full;
-              fa = at(more ? c : cn, more ? j + 2 : 0);
+              const bool more = jp + 1 < fp;
+              fa = at2(more ? c.hx : cn.hx, more ? c.ux : cn.ux, more ? jp + 1 : 0);
               __builtin_amdgcn_sched_barrier(0);
               mma_step(acc, fb);
-            }
-            if (j < full) {
-              fb = at(cn, 0);
-              __builtin_amdgcn_sched_barrier(0);
-              mma_step(acc, fa);
-              fa = fb;
             }
             c = cn;
           }
         }
+        // An odd last full level (2 fp): step m takes it for indices
+        // 16 hf + 2 m (X) and + 1 (Y).  Past the end the entries fall on
+        // the next level (position <= 16 NLEV <= 256, inside the table
+        // rows): read, never used.
+        if ((full & 1) && wave_live)
+          sweep(
+              8 >> sh,
+              [&](int st0) {
+                const int st = (st0 << sh) + s_off;
+                const uint32_t j = (uint32_t)(2 * fp + (st >> 3)) & 31u, m = (uint32_t)(st & 7);
+                const uint32_t dx = 16u * hf + 2u * m, dy = dx + 1u;
+                const uint32_t kj = UNI ? j : 16u * j;
+                return ((dx << 10) | kj) | (((dy << 10) | kj) << 16);
+              },
+              item2);
         // The rest from the stage's list.
         const int n_mine = ksplit ? (n + 1 - wc) >> 1 : n;
         if (n_mine > 0 && wave_live) sweep(n_mine, [&](int st) { return sched[2 * ((st << sh) + s_off)]; }, item);
