@@ -986,6 +986,11 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
       const int m = tid < DC ? rmx : 0;
       int full = 0;
       while (full < NLEV && (unsigned)__ballot(m > 16 * full) == 0xffffffffu) ++full;
+      // An odd count is rounded up when at least 24 of the 32 indices also
+      // need the next level: the level pair then replaces the two-index
+      // steps of the last level and those indices' list entries (for the
+      // others every row's A nibbles there are zero: windows nest).
+      if ((full & 1) && full < NLEV && __builtin_popcountll(__ballot(m > 16 * full)) >= 24) ++full;
       int base = 0;
       for (int j = full; j < NLEV; ++j) {
         const unsigned long long bal = __ballot(m > 16 * j);
