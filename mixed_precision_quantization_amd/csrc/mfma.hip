@@ -1901,26 +1901,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
         nz[h] = __ballot(any != 0);
         gt[h] = __ballot(big != 0);
       }
-      // The first group from gr on with a positive maximum, or ngrp.
-      auto first_from = [&](int gr) __attribute__((always_inline)) {
-        if (gr < 64) {
-          const uint64_t m = nz[0] & (~0ull << gr);
-          if (m) return (int)__builtin_ctzll(m);
-          gr = 64;
-        }
-        if (gr < 128) {
-          const uint64_t m = nz[1] & (~0ull << (gr - 64));
-          if (m) return 64 + (int)__builtin_ctzll(m);
-        }
-        return ngrp;
-      };
-      auto level0 = [&](int gr) __attribute__((always_inline)) {
-        return ((gr < 64 ? gt[0] >> gr : gt[1] >> (gr - 64)) & 1ull) != 0;
-      };
       // The codes of unit u of group gr: quarter codes (pieces 0 and 1 of
       // the lane's 8 words) or level codes (pieces u and u + 2 of its 16).
-      auto unit_load = [&](int gr, int u, uint32_t (&ca)[8], uint32_t (&cb)[8]) __attribute__((always_inline)) {
-        const bool l0 = level0(gr);
+      auto unit_load = [&](bool l0, int gr, int u, uint32_t (&ca)[8], uint32_t (&cb)[8]) __attribute__((always_inline)) {
         const uint4* hp = l0 ? (const uint4*)(hs_t + ((unsigned)(dbeg / 32 + gr) << 11) + ha_off) + 64 * u
                              : (const uint4*)(hq_t + ((unsigned)gr << 10) + qa_off);
         const uint4* up = l0 ? (const uint4*)(ub_t + ((unsigned)(dbeg / 32 + gr) << 11) + hb_off) + 64 * u
@@ -1961,38 +1944,55 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_qpt(MatmulArgs a, 
         mma(fb);
         issued += 4;
       };
-      // The unit after (gr, u); gr = ngrp when none is left.
-      auto advance = [&](int& gr, int& u) __attribute__((always_inline)) {
-        if (u == 0 && level0(gr)) {
-          u = 1;
-        } else {
-          u = 0;
-          gr = first_from(gr + 1);
+      // The quarter groups, then the level-0 groups, each in group order,
+      // with two code buffers in turn: the next unit's codes are read during
+      // the current unit (after the last unit the current codes are read
+      // again into the free buffer, so every iteration issues the same
+      // loads).  Counts are exact integers in float32, so the order of the
+      // steps does not change them.
+      uint64_t msk[2] = {nz[0] & ~gt[0], nz[1] & ~gt[1]};
+      // Takes the lowest group left in msk, or returns -1.
+      auto pop = [&]() __attribute__((always_inline)) {
+        if (msk[0]) {
+          const int b = (int)__builtin_ctzll(msk[0]);
+          msk[0] &= msk[0] - 1;
+          return b;
         }
+        if (msk[1]) {
+          const int b = (int)__builtin_ctzll(msk[1]);
+          msk[1] &= msk[1] - 1;
+          return 64 + b;
+        }
+        return -1;
       };
-      int cg = first_from(0), cu = 0;
-      if (cg < ngrp) {
-        // Two code buffers in turn, the next unit's codes read during the
-        // current unit (when none is left, the current codes are read again
-        // into the free buffer, so every iteration issues the same loads).
-        uint32_t ca0[8], cb0[8], ca1[8], cb1[8];
-        unit_load(cg, cu, ca0, cb0);
+      uint32_t ca0[8], cb0[8], ca1[8], cb1[8];
+      int cg = pop();
+      if (cg >= 0) {
+        unit_load(false, cg, 0, ca0, cb0);
         while (true) {
-          int ng = cg, nu = cu;
-          advance(ng, nu);
-          const bool more1 = ng < ngrp;
-          unit_load(more1 ? ng : cg, more1 ? nu : cu, ca1, cb1);
+          const int g1 = pop();
+          unit_load(false, g1 >= 0 ? g1 : cg, 0, ca1, cb1);
           unit_sweep(ca0, cb0);
-          if (!more1) break;
-          cg = ng;
-          cu = nu;
-          advance(ng, nu);
-          const bool more2 = ng < ngrp;
-          unit_load(more2 ? ng : cg, more2 ? nu : cu, ca0, cb0);
+          if (g1 < 0) break;
+          cg = pop();
+          unit_load(false, cg >= 0 ? cg : g1, 0, ca0, cb0);
           unit_sweep(ca1, cb1);
-          if (!more2) break;
-          cg = ng;
-          cu = nu;
+          if (cg < 0) break;
+        }
+      }
+      msk[0] = gt[0];
+      msk[1] = gt[1];
+      cg = pop();
+      if (cg >= 0) {
+        unit_load(true, cg, 0, ca0, cb0);
+        while (true) {
+          unit_load(true, cg, 1, ca1, cb1);
+          unit_sweep(ca0, cb0);
+          const int g1 = pop();
+          unit_load(true, g1 >= 0 ? g1 : cg, 0, ca0, cb0);
+          unit_sweep(ca1, cb1);
+          if (g1 < 0) break;
+          cg = g1;
         }
       }
     }
