@@ -1710,11 +1710,12 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
 // The single-segment contraction with paired positions [0, 16) taken a
 // quarter (8 positions) at a time.  Per output tile (from the work queues
 // of k_mfma_pers) two passes run:
-//  pass 1  per group of 32 indices, quarter 0 (positions [0, 8)) in four
-//          steps of 8 indices each, and quarter 1 (positions [8, 16)) in
-//          four more when some index of the group needs them.  A lane's
-//          operand for 4 indices is two 8-byte entries of a pair table
-//          (A: the 17 x 17 window classes; B: the rung's 17 x 17 pair-sum
+//  pass 1  per group of 32 indices whose maxima are all at most 8,
+//          quarter 0 (positions [0, 8)) in four steps of 8 indices each;
+//          per other group with a positive maximum, positions [0, 16) in
+//          eight steps of 4 indices (level 0).  A lane's operand for 4
+//          indices of quarter 0 is two 8-byte entries of a pair table (A:
+//          the 17 x 17 window classes; B: the rung's 17 x 17 pair-sum
 //          classes), found through the quarter codes k_prep wrote, so a
 //          step costs the eight LDS reads of a 16-position step of
 //          k_mfma_pers while covering twice the indices.
