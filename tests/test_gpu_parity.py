@@ -952,6 +952,60 @@ def test_narrow_outputs_shared_by_column_waves(table, mode, N):
     _check_group(gres, 0, A[0], B[0], dict(p=8, Lmax=256, metric="linear", **kw))
 
 
+# Stages of 32 indices as (f, k): every index needs f levels of 16 paired
+# positions, k of them one more (the level counts and the 24-of-32 rule for
+# rounding an odd count up, around its threshold).
+_STAGE_LEVELS = ((1, 0), (1, 23), (1, 24), (1, 32), (2, 0), (2, 24), (3, 8), (3, 23), (3, 24), (3, 25), (4, 32),
+                 (5, 24), (5, 31), (6, 10), (7, 23), (7, 24), (7, 32), (8, 0))
+
+
+def _integer_for_levels(mode, L=256):
+    """The smallest quantised magnitude t whose window at length L needs
+    exactly n levels of 16 positions, for every n reached (from the oracle's
+    level maps and table)."""
+    K = o.indicator_table(o.sobol_points(8, L), 256)
+    cum = o.cumulative_table(K)
+    first = {}
+    for t in range(128):
+        if mode == "bipolar":
+            n1 = int(cum[int(o.bipolar_level(np.array([t]))[0]), L])
+            win = (abs(2 * n1 - L) + 1) // 2
+        else:
+            win = int(cum[int(o.unipolar_level(np.array([t]))[0]), L])
+        first.setdefault((win + 15) // 16, t)
+    return first
+
+
+@pytest.mark.parametrize("mode", ["bipolar", "unipolar"])
+@pytest.mark.parametrize("chunk_d", [0, 32])
+def test_full_levels_of_every_count_and_parity(table, mode, chunk_d):
+    """The staged kernel sweeps a stage's full levels two per step and
+    rounds an odd count up when at least 24 of the stage's 32 indices need
+    the next level.  Every row has the same magnitudes (random signs), so
+    each stage's tile maxima follow _STAGE_LEVELS exactly; with chunk
+    scales each chunk's last index holds 127 (its scale is then 1, and
+    that index needs every level).  Counts bit-exact against the oracle."""
+    rng = np.random.default_rng(171 + chunk_d + (mode == "unipolar"))
+    t_of = _integer_for_levels(mode)
+    M, N = 128, 64
+    D = 32 * len(_STAGE_LEVELS)
+    mag = np.zeros(D)
+    for s_i, (f, k) in enumerate(_STAGE_LEVELS):
+        n = np.full(32, f)
+        n[rng.permutation(32)[:k]] = f + 1
+        mag[32 * s_i:32 * s_i + 32] = [t_of[min(int(x), max(t_of))] for x in n]
+    mag[D - 1] = 127.0                                   # the per-row scale is 1
+    if chunk_d:
+        mag[chunk_d - 1::chunk_d] = 127.0                # and each chunk's
+    signs = np.where(rng.random((M, D)) < 0.5, -1.0, 1.0)
+    A = (signs * mag[None, :]).astype(np.float32)
+    B = rng.standard_normal((N, D)).astype(np.float32)
+    kw = dict(D=D, levels=(256,), chunk_d=chunk_d, mode=mode)
+    plan = scmp.scmp_plan_create(**kw)
+    gres = _gpu_path(table, plan, A, B, "mfma_onepass")
+    _check_group(gres, 0, A, B, dict(p=8, Lmax=256, metric="linear", **kw))
+
+
 @pytest.mark.parametrize("algo", ["mfma_persistent", "mfma_quarter"])
 def test_work_queue_grid_with_uneven_queues(table, algo):
     """The persistent launches take tiles from a 2 x 4 grid of work queues
