@@ -78,10 +78,11 @@ struct MfmaWs {
   unsigned long long wsum_off; // byte offset of wsum
   unsigned int* work;          // [PERS_QUEUES] work counters of the persistent contraction
   // Quarter codes of the quarter contraction (k_mfma_qpt; null when another
-  // kernel runs): per (row pair, index pair) the byte offsets of the two
-  // rows' entries in the A pair table for paired positions [0, 8); per
-  // (column pair, index pair, ladder rung) those in the rung's B pair
-  // table.  Layout: qcode_index.
+  // kernel runs): per (row pair, index pair) the two rows' entries in the A
+  // pair table for paired positions [0, 8), as byte offsets from the A
+  // pattern table; per (column pair, index pair, ladder rung) those in the
+  // rung's B pair table, as byte offsets from the paired table (QptTables).
+  // Layout: qcode_index.
   uint32_t* hq;   // [G][RT] tiles
   uint32_t* uq;   // [n_ladder][G][CT] tiles
   int qpt_on;     // the quarter contraction runs: k_prep writes hq / uq
@@ -885,7 +886,9 @@ __device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Frag& f) {
 // One block per 128 x 128 output tile (grid: column tiles, row tiles,
 // groups); handles chunk scales and K-bands.  The tile's row and column
 // codes pass through LDS 32 contraction indices (a stage) at a time, double
-// buffered; one wave lists the stage's work while the stage is stored.
+// buffered; one wave lists the stage's work while the stage is stored.  The
+// levels every index of a stage needs are swept two per step (one index,
+// levels 2 j and 2 j + 1), the rest from the stage's list.
 // Two blocks per CU (2 waves per SIMD) for the timed variants; the variants
 // that also write per-band counts keep a third accumulator set and run one.
 // UNI: the unipolar mode, whose prefixes run up to 16 half-blocks of 16
@@ -1129,12 +1132,9 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma(MatmulArgs a, Mfma
           mma_step(acc, fa);
           if (cnt - st == 2) mma_step(acc, fb);
         };
-        // Full levels.  Step 8 j + m takes level j of indices 16 hf + 2 m (X)
-        // and 16 hf + 2 m + 1 (Y); both codes of a buffer come in one 8-byte
-        // read.  With one or two levels the steps run level by level, and
-        // past the last level the entries fall on level full <= NLEV
-        // (position <= 16 NLEV <= 256, inside the table rows): read, never
-        // used.
+        // Codes of a two-index step (the form of an odd last full level):
+        // indices 16 hf + 2 m (X) and 16 hf + 2 m + 1 (Y) of one level, both
+        // codes of a buffer in one 8-byte read.
         auto item2 = [&](uint32_t e) __attribute__((always_inline)) {
           const uint32_t ox = (e >> 8) & 0x7cu;
           const uint2 h2 = *(const uint2*)(hbase + ox), u2 = *(const uint2*)(ubase + ox);
