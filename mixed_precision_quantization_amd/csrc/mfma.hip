@@ -873,6 +873,31 @@ __device__ __forceinline__ Frag frags_at2(const uint8_t* pat, const uint8_t* pt,
   return f;
 }
 
+// A step in either of two forms from the same eight 8-byte reads: with
+// pair, X and Y are levels kx / 16 and kx / 16 + 1 of the index of hx, ux
+// (Y is the 8 bytes after X); otherwise as frags_at with ky = kx.  The form
+// is then a choice of addresses, so code that reads one or the other ahead
+// of time (the first step of a group or level) needs no branch.
+__device__ __forceinline__ Frag frags_sel(const uint8_t* pat, const uint8_t* pt, uint32_t hx, uint32_t ux,
+                                          uint32_t hy, uint32_t uy, uint32_t kx, bool pair) {
+  const uint8_t* ax0 = pat + __builtin_elementwise_sub_sat(hx & 0xffffu, 32u * kx);
+  const uint8_t* ax1 = pat + __builtin_elementwise_sub_sat(hx >> 16, 32u * kx);
+  const uint8_t* bx0 = pt + (ux & 0xffffu) + (kx >> 1);
+  const uint8_t* bx1 = pt + (ux >> 16) + (kx >> 1);
+  const uint8_t* ay0 = pair ? ax0 + 8 : pat + __builtin_elementwise_sub_sat(hy & 0xffffu, 32u * kx);
+  const uint8_t* ay1 = pair ? ax1 + 8 : pat + __builtin_elementwise_sub_sat(hy >> 16, 32u * kx);
+  const uint8_t* by0 = pair ? bx0 + 8 : pt + (uy & 0xffffu) + (kx >> 1);
+  const uint8_t* by1 = pair ? bx1 + 8 : pt + (uy >> 16) + (kx >> 1);
+  const v2i a0 = *(const v2i*)ax0, a0y = *(const v2i*)ay0, a1 = *(const v2i*)ax1, a1y = *(const v2i*)ay1;
+  const v2i b0 = *(const v2i*)bx0, b0y = *(const v2i*)by0, b1 = *(const v2i*)bx1, b1y = *(const v2i*)by1;
+  Frag f;
+  f.a[0] = v8i{a0.x, a0.y, a0y.x, a0y.y, 0, 0, 0, 0};
+  f.a[1] = v8i{a1.x, a1.y, a1y.x, a1y.y, 0, 0, 0, 0};
+  f.b[0] = v8i{b0.x, b0.y, b0y.x, b0y.y, 0, 0, 0, 0};
+  f.b[1] = v8i{b1.x, b1.y, b1y.x, b1y.y, 0, 0, 0, 0};
+  return f;
+}
+
 // One step: the wave's 2 x 2 subtiles of 32 x 32.
 __device__ __forceinline__ void mma_step(v16f (&acc)[2][2], const Frag& f) {
 #pragma unroll
@@ -1399,7 +1424,14 @@ __device__ __forceinline__ int queue_item(int CT, int q, int t) {
   return (PERS_QR * i + h) * CT + PERS_QC * j + c;
 }
 
-template <bool COUNTS>
+// PAIRS: full levels swept two per step (one index, levels 2 j and 2 j + 1)
+// as in the staged kernel, with each group's first step read at the
+// previous group's end in the form its sweep starts with.  Chosen for short
+// contraction axes (attention scores, where most groups have several full
+// levels); on long axes with mostly one full level per group the
+// level-by-level form is faster.
+constexpr int PERS_PAIRS_MAX_D = 128;  // longest contraction axis that takes PAIRS
+template <bool COUNTS, bool PAIRS>
 __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a, MfmaWs w, int n_items) {
   struct __align__(16) GatherTables {
     uint8_t pt[MAX_LEVELS * PT_STRIDE];
@@ -1584,14 +1616,31 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
     };
     int cnt = 0;  // entries in this wave's list
     // fa: the fragments of the group's first step, read at the end of the
-    // previous group.
+    // previous group (PAIRS: in the form its sweep starts with).
     Frag fa;
+    // PAIRS: whether a group has two or more full levels, i.e. every index
+    // needs positions past 16 (d0: its first index, m: this lane's maximum).
+    auto two_full = [&](int d0, int m) __attribute__((always_inline)) {
+      const int nl = d0 + l32 < dend ? (m + 15) >> 4 : 0;
+      return (unsigned)__ballot(nl > 1) == 0xffffffffu;
+    };
+    // A group's first step: levels 0 and 1 of index d0 + 16 hf (PAIRS, two
+    // or more full levels), else indices d0 + 16 hf and + 8 at level 0.
+    auto first_step = [&](const uint32_t* h, const uint32_t* u, int d0, int m) __attribute__((always_inline)) {
+      if constexpr (PAIRS)
+        return frags_sel(pat, s_pt, h[0], u[0], h[8], u[8], 0u, two_full(d0, m));
+      else
+        return frags_at(h[0], u[0], 0u, h[8], u[8], 0u);
+    };
     // One group: its codes (ch, cu) and this lane's index maximum (mx) are
-    // in registers; nh, nu: the next group's codes.  A full level takes 8
+    // in registers; nh, nu, nmx: the next group's.  A full level takes 8
     // steps: step m pairs indices d0 + 16 hf + m (X) and d0 + 16 hf + 8 + m
-    // (Y) in lane half hf.
+    // (Y) in lane half hf.  PAIRS: levels [0, 2 fp) go two per step, step
+    // (i, jp) taking index d0 + 16 hf + i at levels 2 jp (X) and 2 jp + 1
+    // (Y), one 16-byte read per operand subtile, and an odd last level as
+    // above.
     auto group = [&](int grp, const uint32_t* ch, const uint32_t* cu, int mx, const uint32_t* nh,
-                     const uint32_t* nu) __attribute__((always_inline)) {
+                     const uint32_t* nu, int nmx) __attribute__((always_inline)) {
       const int d0 = dbeg + 32 * grp;
       const int nl = d0 + l32 < dend ? (mx + 15) >> 4 : 0;
       int full = 0;
@@ -1606,7 +1655,44 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
           list[cnt + (int)__builtin_amdgcn_mbcnt_lo(bal, 0u)] = ((uint32_t)(d0 + l32) << 4) | (uint32_t)j;
         cnt += __builtin_popcount(bal);
       }
-      if (full > 0) {
+      if constexpr (PAIRS) {
+        const int fp = full >> 1;
+        Frag fb;
+        for (int jp = 0; jp < fp; ++jp) {
+          const uint32_t kk = 32u * jp;
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            fb = frags_at2<false>(pat, s_pt, ch[i + 1], cu[i + 1], kk);
+            __builtin_amdgcn_sched_barrier(0);  // keep these reads ahead of the MFMAs
+            mma(fa);
+            // Next: step i + 2, else the first step of the next level pair
+            // or of the odd last level, in its form (after the last level:
+            // read, unused; position <= 128 stays inside the table rows).
+            if (i + 2 < 16)
+              fa = frags_at2<false>(pat, s_pt, ch[i + 2], cu[i + 2], kk);
+            else
+              fa = frags_sel(pat, s_pt, ch[0], cu[0], ch[8], cu[8], kk + 32u, jp + 1 < fp);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
+          }
+        }
+        for (int j = 2 * fp; j < full; ++j) {
+          const uint32_t kk = 16u * j;
+#pragma unroll
+          for (int m = 0; m < 8; m += 2) {
+            fb = frags_at(ch[m + 1], cu[m + 1], kk, ch[m + 9], cu[m + 9], kk);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fa);
+            if (m + 2 < 8)
+              fa = frags_at(ch[m + 2], cu[m + 2], kk, ch[m + 10], cu[m + 10], kk);
+            else
+              fa = frags_at(ch[0], cu[0], kk + 16u, ch[8], cu[8], kk + 16u);
+            __builtin_amdgcn_sched_barrier(0);
+            mma(fb);
+          }
+        }
+        issued += 8 * full;
+      } else if (full > 0) {
         Frag fb;
         for (int j = 0; j < full; ++j) {
           const uint32_t kk = 16u * j;
@@ -1634,19 +1720,19 @@ __global__ void __launch_bounds__(256, COUNTS ? 1 : 2) k_mfma_pers(MatmulArgs a,
         cnt = 0;
       }
       // The next group's first step.
-      fa = frags_at(nh[0], nu[0], 0u, nh[8], nu[8], 0u);
+      fa = first_step(nh, nu, d0 + 32, nmx);
     };
     if (ngrp > 0) {
       uint32_t ha[16], ua[16], hb[16], ub[16];
       int ma, mb = 0;
       load_group(dbeg, ha, ua, ma);
-      fa = frags_at(ha[0], ua[0], 0u, ha[8], ua[8], 0u);
+      fa = first_step(ha, ua, dbeg, ma);
       for (int grp = 0; grp < ngrp; grp += 2) {
         load_group(dbeg + 32 * min(grp + 1, ngrp - 1), hb, ub, mb);
-        group(grp, ha, ua, ma, hb, ub);
+        group(grp, ha, ua, ma, hb, ub, mb);
         if (grp + 1 >= ngrp) break;
         load_group(dbeg + 32 * min(grp + 2, ngrp - 1), ha, ua, ma);
-        group(grp + 1, hb, ub, mb, ha, ua);
+        group(grp + 1, hb, ub, mb, ha, ua, ma);
       }
     }
 
@@ -2312,10 +2398,15 @@ static void launch_main(const MatmulArgs& a, const MfmaWs& w, dim3 grid, hipStre
         hipLaunchKernelGGL((k_mfma_qpt<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
       else
         hipLaunchKernelGGL((k_mfma_qpt<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+    } else if (a.D <= PERS_PAIRS_MAX_D) {
+      if (counts)
+        hipLaunchKernelGGL((k_mfma_pers<true, true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      else
+        hipLaunchKernelGGL((k_mfma_pers<false, true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
     } else if (counts) {
-      hipLaunchKernelGGL((k_mfma_pers<true>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers<true, false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
     } else {
-      hipLaunchKernelGGL((k_mfma_pers<false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
+      hipLaunchKernelGGL((k_mfma_pers<false, false>), dim3(blocks), dim3(256), 0, st, a, w, n_items);
     }
   } else {
     if (counts)
